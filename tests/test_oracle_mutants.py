@@ -1,0 +1,98 @@
+"""Plant plausible mistakes in a copy of the reference decoder and check that the pins catch each.
+
+Every mutant rewrites one spot of ``oracle/decoder.py`` in memory (the file
+is never touched), loads the copy as a separate module and runs the pins.
+At least one pin has to fail.  This shows that the pins would notice such a
+slip in the oracle itself.
+"""
+
+import os
+import types
+
+import pytest
+
+from . import oracle_pins
+
+SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "decoder.py")
+
+MUTANTS = {
+    "rope_interleaved_pairs": (
+        "a, b = x[..., :half], x[..., half:]\n    return np.concatenate([a * cos - b * sin, a * sin + b * cos], axis=-1)",
+        "a, b = x[..., 0::2], x[..., 1::2]\n    return np.concatenate([a * cos - b * sin, a * sin + b * cos], axis=-1)",
+    ),
+    "rope_sign_flip": ("[a * cos - b * sin, a * sin + b * cos]", "[a * cos + b * sin, -a * sin + b * cos]"),
+    "rope_wrong_frequency": ("-2.0 * i / head_dim", "-1.0 * i / head_dim"),
+    "attention_no_scale": ("k[g] @ q[h] / np.sqrt(hd)", "k[g] @ q[h]"),
+    "gqa_modulo_map": ("g = h // group", "g = h % k.shape[0]"),
+    "causal_excludes_current": (
+        "kc = self.k_cache[session, l, :, : position + 1]",
+        "kc = self.k_cache[session, l, :, : position]",
+    ),
+    "attention_residual_dropped": ('x = x + self.mat(lw["wo"]) @ o', 'x = self.mat(lw["wo"]) @ o'),
+    "ffn_residual_dropped": ('x = x + self.mat(lw["w_down"]) @ a', 'x = self.mat(lw["w_down"]) @ a'),
+    "silu_on_up_branch": (
+        'a = silu(self.mat(lw["w_gate"]) @ h2) * (self.mat(lw["w_up"]) @ h2)',
+        'a = (self.mat(lw["w_gate"]) @ h2) * silu(self.mat(lw["w_up"]) @ h2)',
+    ),
+    "rmsnorm_eps_outside_sqrt": ("x / np.sqrt(ms + eps) * gain", "x / (np.sqrt(ms) + eps) * gain"),
+    "rmsnorm_sum_not_mean": ("ms = np.mean(x * x, axis=-1, keepdims=True)", "ms = np.sum(x * x, axis=-1, keepdims=True)"),
+    "k_cached_before_rope": (
+        "            k = apply_rope(k, cos, sin)\n            self.k_cache[session, l, :, position] = self._store(k)",
+        "            self.k_cache[session, l, :, position] = self._store(k)\n            k = apply_rope(k, cos, sin)",
+    ),
+    "ffn_uses_attention_gain": ('h2 = rms_norm(x, self.mat(lw["ffn_norm"])', 'h2 = rms_norm(x, self.mat(lw["attn_norm"])'),
+    "final_norm_skipped": ('hf = rms_norm(x, self.mat(w["final_norm"]), m.norm_eps)\n        return', "hf = x\n        return"),
+    "lm_head_tied_to_embedding": ('return self.mat(w["lm_head"]) @ hf', 'return self.mat(w["embed"]) @ hf'),
+    "wk_wv_swapped": (
+        'k = (self.mat(lw["wk"]) @ h).reshape(hkv, hd)\n            v = (self.mat(lw["wv"]) @ h)',
+        'k = (self.mat(lw["wv"]) @ h).reshape(hkv, hd)\n            v = (self.mat(lw["wk"]) @ h)',
+    ),
+    "wo_transposed": ('x = x + self.mat(lw["wo"]) @ o', 'x = x + self.mat(lw["wo"]).T @ o'),
+    "argmax_ties_to_last": (
+        "return np.argmax(l32, axis=-1).astype(np.int32)",
+        "return (l32.shape[-1] - 1 - np.argmax(l32[..., ::-1], axis=-1)).astype(np.int32)",
+    ),
+    "bf16_truncates": ("rounded = ((bits + 0x7FFF + keep_odd) >> 16) << 16", "rounded = (bits >> 16) << 16"),
+    "bf16_ties_away": ("rounded = ((bits + 0x7FFF + keep_odd) >> 16) << 16", "rounded = ((bits + 0x8000) >> 16) << 16"),
+    "kv_not_rounded_to_cache_type": ('if dtype == "bf16":\n        f32 = round_f32_to_bf16(f32)', "if False:\n        pass"),
+    "softmax_no_max_shift": ("e = np.exp(s - m)", "e = np.exp(s)"),
+    "rope_position_off_by_one": ("angle = np.float64(position) * theta", "angle = np.float64(position + 1) * theta"),
+}
+
+# cheapest pins first: a mutant stops at its first failing pin
+PIN_ORDER = [
+    oracle_pins.pin_softmax,
+    oracle_pins.pin_rope,
+    oracle_pins.pin_attention,
+    oracle_pins.pin_gqa,
+    oracle_pins.pin_rmsnorm,
+    oracle_pins.pin_argmax,
+    oracle_pins.pin_identity_layers,
+    oracle_pins.pin_brute_force,
+    oracle_pins.pin_brute_force_prefilled,
+    oracle_pins.pin_incremental_equals_full,
+    oracle_pins.pin_silu,
+    lambda mod: oracle_pins.pin_bf16(mod, n_random=1 << 14),
+]
+
+
+def _load_mutant(name: str) -> types.ModuleType:
+    src = open(SRC_PATH, encoding="utf-8").read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutant {name}: pattern must occur exactly once"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _load_mutant(name)
+    for pin in PIN_ORDER:
+        try:
+            with __import__("warnings").catch_warnings():
+                __import__("warnings").simplefilter("ignore")
+                pin(mod)
+        except Exception:
+            return
+    pytest.fail(f"no pin caught mutant {name}")
