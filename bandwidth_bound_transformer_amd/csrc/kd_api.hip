@@ -1,0 +1,336 @@
+// kd_api.hip -- host side of the C ABI declared in include/kd.h.
+//
+// kd_init fixes everything ahead of the first step: the weight layout, the
+// work plan, and every device buffer ("Why is real-time AI inference 56x more
+// expensive?", section "decide everything ahead of time"). kd_step is then a
+// single cooperative launch on the caller's stream, with no allocation and no
+// synchronisation ("keep the work resident on the GPU": per step the host
+// only hands over the input and takes the output).
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "kd.h"
+#include "kd_device.h"
+#include "kd_pack.h"
+
+namespace {
+
+constexpr int kRing = 12;
+
+struct Buffers {
+  uint8_t* blob = nullptr;
+  uint8_t* embed = nullptr;
+  uint8_t* norms = nullptr;
+  uint64_t* ll = nullptr;
+  uint32_t* flags = nullptr;  // [0] sticky status bits, [1] abort flag
+};
+
+void free_buffers(Buffers& b) {
+  if (b.blob) (void)hipFree(b.blob);
+  if (b.embed) (void)hipFree(b.embed);
+  if (b.norms) (void)hipFree(b.norms);
+  if (b.ll) (void)hipFree(b.ll);
+  if (b.flags) (void)hipFree(b.flags);
+  b = Buffers{};
+}
+
+typedef void (*KernelFn)(kd::Params);
+
+KernelFn pick_kernel(int wbytes, int hd) {
+  if (wbytes == 2 && hd == 128) return kd::decode_step_kernel<kRing, 2, 2, 128>;
+  if (wbytes == 2 && hd == 64) return kd::decode_step_kernel<kRing, 2, 2, 64>;
+  if (wbytes == 4 && hd == 128) return kd::decode_step_kernel<kRing, 4, 4, 128>;
+  if (wbytes == 4 && hd == 64) return kd::decode_step_kernel<kRing, 4, 4, 64>;
+  return nullptr;
+}
+
+}  // namespace
+
+struct kd_handle {
+  int device = 0;
+  kd_config cfg{};
+  kd::Dims m{};
+  kd::LLLayout lo{};
+  Buffers buf;
+  KernelFn kernel = nullptr;
+  uint32_t seq = 0;
+  int64_t lds_bytes = 0;
+};
+
+namespace {
+
+bool dtype_ok(int32_t t) { return t == KD_DTYPE_F32 || t == KD_DTYPE_BF16; }
+int dtype_bytes(int32_t t) { return t == KD_DTYPE_BF16 ? 2 : 4; }
+
+// Structural checks that need no device.
+int check_config(const kd_config* c) {
+  if (!c) return KD_ERR_INVALID_ARG;
+  if (c->n_layers <= 0 || c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->ffn_dim <= 0 || c->vocab <= 0 || c->max_seq <= 0 || c->batch <= 0)
+    return KD_ERR_INVALID_ARG;
+  if (c->n_q_heads % c->n_kv_heads != 0 || c->head_dim % 2 != 0) return KD_ERR_INVALID_ARG;
+  if (!dtype_ok(c->weight_dtype) || !dtype_ok(c->kv_dtype)) return KD_ERR_INVALID_ARG;
+  if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f)) return KD_ERR_INVALID_ARG;
+  if (c->max_seq > (1 << 24) || c->vocab > (1 << 30)) return KD_ERR_INVALID_ARG;
+  return KD_OK;
+}
+
+// Limits of this implementation for a valid configuration, given the grid size.
+int check_supported(const kd_config* c, const kd::Dims& m) {
+  if (c->batch != 1) return KD_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return KD_ERR_UNSUPPORTED;
+  if (c->weight_dtype != c->kv_dtype) return KD_ERR_UNSUPPORTED;
+  if (m.G > kd::kMaxGroup) return KD_ERR_UNSUPPORTED;
+  if (m.d > kd::kMaxDim || m.qdim > kd::kMaxDim || m.d % 64 != 0) return KD_ERR_UNSUPPORTED;
+  if ((int64_t)m.d * m.wbytes % kd::kPacketBytes || (int64_t)m.qdim * m.wbytes % kd::kPacketBytes) return KD_ERR_UNSUPPORTED;
+  if (m.F % m.vpl != 0) return KD_ERR_UNSUPPORTED;
+  if (m.nwg % 2 != 0) return KD_ERR_UNSUPPORTED;
+  // per-workgroup and per-wave bookkeeping must fit the LDS arrays
+  const int64_t nrow_max = kd::ceil_div(m.d, m.nwg);
+  if (nrow_max > 64 || (int64_t)m.nwg * nrow_max > kd::kMaxDim) return KD_ERR_UNSUPPORTED;
+  auto max_segs = [&](int64_t nrows_total, int64_t C) {
+    int64_t worst = 0;
+    for (int64_t w = 0; w < m.nwg; ++w) {
+      const int64_t R = kd::part_lo(nrows_total, m.nwg, w + 1) - kd::part_lo(nrows_total, m.nwg, w);
+      const int64_t T = R * C;
+      for (int v = 0; v < kd::kComputeWaves; ++v) {
+        const int64_t lo = kd::part_lo(T, kd::kComputeWaves, v), hi = kd::part_lo(T, kd::kComputeWaves, v + 1);
+        if (hi > lo) worst = std::max(worst, (hi - 1) / C - lo / C + 1);
+      }
+    }
+    return worst;
+  };
+  if (max_segs(m.nqkv, m.cd) > kd::kSegR || max_segs(m.d, m.cq) > kd::kSegR || max_segs(m.V, m.cd) > kd::kSegR)
+    return KD_ERR_UNSUPPORTED;
+  for (int64_t w = 0; w < m.nwg; ++w) {
+    const int64_t nf = kd::ffn_lo(m, w + 1) - kd::ffn_lo(m, w);
+    const int64_t Tgu = 2 * nf * m.cd, g = nf / m.vpl, Td = (m.d / 64) * g;
+    for (int v = 0; v < kd::kComputeWaves; ++v) {
+      const int64_t lo = kd::part_lo(Tgu, kd::kComputeWaves, v), hi = kd::part_lo(Tgu, kd::kComputeWaves, v + 1);
+      if (hi > lo && (hi - 1) / m.cd - lo / m.cd + 1 > kd::kSegR) return KD_ERR_UNSUPPORTED;
+      const int64_t dlo = kd::part_lo(Td, kd::kComputeWaves, v), dhi = kd::part_lo(Td, kd::kComputeWaves, v + 1);
+      if (dhi > dlo && (dhi - 1) / g - dlo / g + 1 > kd::kSegC) return KD_ERR_UNSUPPORTED;
+    }
+  }
+  // attention split at every position the cache can hold
+  for (int32_t p = 0; p < c->max_seq; ++p) {
+    const kd::AttPlan a = kd::att_plan(m, p);
+    if (a.NC > kd::max_chunks(m)) return KD_ERR_UNSUPPORTED;
+    if ((int64_t)a.NC * (a.MS + 2) > kd::kMergeWords + 64) return KD_ERR_UNSUPPORTED;
+    const int64_t pk = kd::ceil_div(a.CH, m.ppp);
+    if (kd::ceil_div(pk, kd::kComputeWaves) * m.ppp > kd::kScorePos) return KD_ERR_UNSUPPORTED;
+  }
+  return KD_OK;
+}
+
+#define KD_TRY(expr)                                \
+  do {                                              \
+    if ((expr) != hipSuccess) { rc = KD_ERR_HIP; goto fail; } \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* kd_strerror(int code) {
+  switch (code) {
+    case KD_OK: return "success";
+    case KD_ERR_INVALID_ARG: return "invalid argument";
+    case KD_ERR_UNSUPPORTED: return "configuration not supported by this build";
+    case KD_ERR_NO_DEVICE: return "no HIP device available";
+    case KD_ERR_OOM: return "device memory allocation failed";
+    case KD_ERR_HIP: return "HIP runtime call failed";
+    case KD_ERR_LAUNCH: return "cooperative kernel launch rejected";
+    default: return "unknown error code";
+  }
+}
+
+int kd_kv_layout(const kd_config* cfg, size_t* bytes, size_t strides[6]) {
+  const int rc0 = check_config(cfg);
+  if (rc0 != KD_OK) return rc0;
+  if (!bytes || !strides) return KD_ERR_INVALID_ARG;
+  const size_t S = (size_t)kd::ceil_div((int64_t)cfg->max_seq + 7, 16) * 16;
+  const size_t hd = (size_t)cfg->head_dim;
+  strides[5] = 1;
+  strides[4] = hd;
+  strides[3] = S * hd;
+  strides[2] = (size_t)cfg->n_kv_heads * strides[3];
+  strides[1] = (size_t)cfg->batch * strides[2];
+  strides[0] = 2 * strides[1];
+  *bytes = (size_t)cfg->n_layers * strides[0] * (size_t)dtype_bytes(cfg->kv_dtype);
+  return KD_OK;
+}
+
+int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
+  if (!out) return KD_ERR_INVALID_ARG;
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc != KD_OK) return rc;
+  if (!w || !w->embed || !w->layers || !w->final_norm || !w->lm_head) return KD_ERR_INVALID_ARG;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const kd_layer_weights& lw = w->layers[l];
+    if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.w_gate || !lw.w_up || !lw.w_down)
+      return KD_ERR_INVALID_ARG;
+  }
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return KD_ERR_NO_DEVICE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KD_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return KD_ERR_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return KD_ERR_UNSUPPORTED;
+  int coop = 0;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return KD_ERR_UNSUPPORTED;
+
+  const int wb = dtype_bytes(cfg->weight_dtype), kb = dtype_bytes(cfg->kv_dtype);
+  const int nwg = prop.multiProcessorCount;
+  const kd::Dims m = kd::make_dims(cfg->n_layers, cfg->d_model, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->ffn_dim,
+                                   cfg->vocab, cfg->max_seq, nwg, wb, kb);
+  rc = check_supported(cfg, m);
+  if (rc != KD_OK) return rc;
+  KernelFn kern = pick_kernel(wb, cfg->head_dim);
+  if (!kern) return KD_ERR_UNSUPPORTED;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, kd::kThreads, 0) != hipSuccess) return KD_ERR_HIP;
+  if (occ < 1) return KD_ERR_UNSUPPORTED;
+  hipFuncAttributes fattr;
+  if (hipFuncGetAttributes(&fattr, (const void*)kern) != hipSuccess) return KD_ERR_HIP;
+
+  kd_handle* h = new (std::nothrow) kd_handle();
+  if (!h) return KD_ERR_OOM;
+  h->device = dev;
+  h->cfg = *cfg;
+  h->m = m;
+  h->lo = kd::ll_layout(m);
+  h->kernel = kern;
+  h->lds_bytes = (int64_t)fattr.sharedSizeBytes;
+
+  uint8_t* tmp = nullptr;
+  {
+    const int64_t d = m.d;
+    const size_t blob_bytes = (size_t)m.blob_elems * wb;
+    if (hipMalloc(&h->buf.blob, blob_bytes) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
+    if (hipMalloc(&h->buf.embed, (size_t)m.V * d * wb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
+    if (hipMalloc(&h->buf.norms, (size_t)(2 * m.L + 1) * d * wb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
+    if (hipMalloc(&h->buf.ll, (size_t)h->lo.total * 8) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
+    if (hipMalloc(&h->buf.flags, 256) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
+    if (hipMalloc(&tmp, (size_t)2 * m.F * d * wb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
+    KD_TRY(hipMemset(h->buf.ll, 0, (size_t)h->lo.total * 8));
+    KD_TRY(hipMemset(h->buf.flags, 0, 256));
+    const size_t row = (size_t)d * wb;
+    for (int l = 0; l < m.L; ++l) {
+      const kd_layer_weights& lw = w->layers[l];
+      uint8_t* lay = h->buf.blob + (size_t)l * m.layer_elems * wb;
+      KD_TRY(hipMemcpy(lay + m.off_qkv * wb, lw.wq, (size_t)m.qdim * row, hipMemcpyHostToDevice));
+      KD_TRY(hipMemcpy(lay + (m.off_qkv + (int64_t)m.qdim * d) * wb, lw.wk, (size_t)m.kvdim * row, hipMemcpyHostToDevice));
+      KD_TRY(hipMemcpy(lay + (m.off_qkv + (int64_t)(m.qdim + m.kvdim) * d) * wb, lw.wv, (size_t)m.kvdim * row, hipMemcpyHostToDevice));
+      KD_TRY(hipMemcpy(lay + m.off_o * wb, lw.wo, (size_t)d * m.qdim * wb, hipMemcpyHostToDevice));
+      KD_TRY(hipMemcpy(tmp, lw.w_gate, (size_t)m.F * row, hipMemcpyHostToDevice));
+      KD_TRY(hipMemcpy(tmp + (size_t)m.F * row, lw.w_up, (size_t)m.F * row, hipMemcpyHostToDevice));
+      if (wb == 2)
+        hipLaunchKernelGGL(kd::pack_gate_up_kernel<uint16_t>, dim3(4096), dim3(256), 0, 0, (uint16_t*)(lay + m.off_gu * wb),
+                           (const uint16_t*)tmp, (const uint16_t*)(tmp + (size_t)m.F * row), m);
+      else
+        hipLaunchKernelGGL(kd::pack_gate_up_kernel<float>, dim3(4096), dim3(256), 0, 0, (float*)(lay + m.off_gu * wb),
+                           (const float*)tmp, (const float*)(tmp + (size_t)m.F * row), m);
+      KD_TRY(hipGetLastError());
+      KD_TRY(hipDeviceSynchronize());
+      KD_TRY(hipMemcpy(tmp, lw.w_down, (size_t)d * m.F * wb, hipMemcpyHostToDevice));
+      if (wb == 2)
+        hipLaunchKernelGGL(kd::pack_down_kernel<uint16_t>, dim3(4096), dim3(256), 0, 0, (uint16_t*)(lay + m.off_d * wb),
+                           (const uint16_t*)tmp, m);
+      else
+        hipLaunchKernelGGL(kd::pack_down_kernel<float>, dim3(4096), dim3(256), 0, 0, (float*)(lay + m.off_d * wb),
+                           (const float*)tmp, m);
+      KD_TRY(hipGetLastError());
+      KD_TRY(hipDeviceSynchronize());
+      KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * l) * row, lw.attn_norm, row, hipMemcpyHostToDevice));
+      KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * l + 1) * row, lw.ffn_norm, row, hipMemcpyHostToDevice));
+    }
+    KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * m.L) * row, w->final_norm, row, hipMemcpyHostToDevice));
+    KD_TRY(hipMemcpy(h->buf.blob + (size_t)m.off_lm * wb, w->lm_head, (size_t)m.V * row, hipMemcpyHostToDevice));
+    KD_TRY(hipMemcpy(h->buf.embed, w->embed, (size_t)m.V * row, hipMemcpyHostToDevice));
+    KD_TRY(hipDeviceSynchronize());
+    (void)hipFree(tmp);
+    tmp = nullptr;
+  }
+  *out = h;
+  return KD_OK;
+
+fail:
+  if (tmp) (void)hipFree(tmp);
+  free_buffers(h->buf);
+  delete h;
+  return rc;
+}
+
+int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* logits, void* stream) {
+  if (!h || !tokens || !positions || !kv) return KD_ERR_INVALID_ARG;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return KD_ERR_HIP;
+  if (cur != h->device && hipSetDevice(h->device) != hipSuccess) return KD_ERR_HIP;
+  kd::Params P{};
+  P.blob = h->buf.blob;
+  P.embed = h->buf.embed;
+  P.norms = h->buf.norms;
+  P.ll = h->buf.ll;
+  P.lo = h->lo;
+  P.kv = (uint8_t*)kv;
+  P.tokens = tokens;
+  P.positions = positions;
+  P.logits = logits;
+  P.status = h->buf.flags;
+  P.abortf = h->buf.flags + 1;
+  if (++h->seq == 0) ++h->seq;  // tag 0 never names a live vector
+  P.seq = h->seq;
+  P.max_seq = h->cfg.max_seq;
+  P.eps = h->cfg.norm_eps;
+  P.rope_base = h->cfg.rope_base;
+  P.m = h->m;
+  void* args[] = {&P};
+  const hipError_t e = hipLaunchCooperativeKernel((const void*)h->kernel, dim3(h->m.nwg), dim3(kd::kThreads), args, 0,
+                                                  (hipStream_t)stream);
+  int rc = KD_OK;
+  if (e != hipSuccess) rc = KD_ERR_LAUNCH;
+  if (cur != h->device) (void)hipSetDevice(cur);
+  return rc;
+}
+
+int kd_device_status(kd_handle* h, uint32_t* bits, int clear) {
+  if (!h || !bits) return KD_ERR_INVALID_ARG;
+  if (hipSetDevice(h->device) != hipSuccess) return KD_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) return KD_ERR_HIP;
+  uint32_t f[2] = {0, 0};
+  if (hipMemcpy(f, h->buf.flags, sizeof(f), hipMemcpyDeviceToHost) != hipSuccess) return KD_ERR_HIP;
+  *bits = f[0];
+  if (clear && hipMemset(h->buf.flags, 0, sizeof(f)) != hipSuccess) return KD_ERR_HIP;
+  return KD_OK;
+}
+
+void kd_destroy(kd_handle* h) {
+  if (!h) return;
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  (void)hipSetDevice(h->device);
+  (void)hipDeviceSynchronize();
+  free_buffers(h->buf);
+  if (cur >= 0) (void)hipSetDevice(cur);
+  delete h;
+}
+
+int kd_get_info(kd_handle* h, int64_t info[8]) {
+  if (!h || !info) return KD_ERR_INVALID_ARG;
+  for (int i = 0; i < 8; ++i) info[i] = 0;
+  info[0] = h->m.nwg;
+  info[1] = kd::kThreads;
+  info[2] = h->m.blob_elems * h->m.wbytes + (int64_t)h->m.V * h->m.d * h->m.wbytes + (int64_t)(2 * h->m.L + 1) * h->m.d * h->m.wbytes;
+  info[3] = h->lds_bytes;
+  info[4] = kRing;
+  return KD_OK;
+}
+
+}  // extern "C"

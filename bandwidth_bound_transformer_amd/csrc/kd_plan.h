@@ -1,0 +1,133 @@
+// kd_plan.h -- static work plan of one decode step, shared by the host packer and the kernel.
+//
+// The whole schedule of a step is fixed before the first call: which workgroup
+// streams which weight rows, which KV positions each wave reads and where every
+// intermediate vector lives ("Why is real-time AI inference 56x more expensive?",
+// section "decide everything ahead of time"). Only the attention split depends
+// on the current position, and that is integer arithmetic every wave repeats.
+#pragma once
+#include <stdint.h>
+
+#ifdef __HIPCC__
+#define KD_HD __host__ __device__ __forceinline__
+#else
+#define KD_HD inline
+#endif
+
+namespace kd {
+
+constexpr int kThreads = 512;          // 8 waves of 64 lanes per workgroup
+constexpr int kComputeWaves = 7;       // waves 1..7 stream packets; wave 0 is the control wave
+constexpr int kPacketBytes = 1024;     // one 16-byte load by each of 64 lanes
+constexpr int kMaxDim = 4096;          // largest d_model and n_q_heads*head_dim held in LDS
+constexpr int kMaxGroup = 4;           // largest q heads per kv head
+constexpr int kMaxHeadDim = 128;
+constexpr int kChunkMin = 64;          // attention chunk bounds (positions per unit)
+constexpr int kChunkMax = 256;
+constexpr int kMergeWords = 2048;      // largest LL gather of one merge unit
+constexpr int kSegR = 96;              // row partials kept per compute wave
+constexpr int kSegC = 12;              // 64-row blocks kept per compute wave (down projection)
+constexpr int kScorePos = 48;          // attention scores kept per compute wave
+
+// Tag kinds of the vectors exchanged between workgroups (LL words carry value|tag).
+enum Kind : int { kQKV = 0, kATTP = 1, kO = 2, kXP = 3, kDP = 4, kX = 5, kLM = 6 };
+
+// Start of part i when n items are cut into `parts` contiguous parts.
+KD_HD int64_t part_lo(int64_t n, int64_t parts, int64_t i) { return n * i / parts; }
+// Part that holds item i (inverse of part_lo), for n > 0.
+KD_HD int64_t part_of(int64_t n, int64_t parts, int64_t i) { return (parts * i + parts - 1) / n; }
+
+KD_HD int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Dims {
+  int32_t L, d, hq, hkv, hd, F, V, S, nwg;  // S: KV positions allocated per (layer, slot, session, head)
+  int32_t wbytes, kvbytes;                 // 2 (bf16) or 4 (f32)
+  int32_t G, qdim, kvdim, nqkv;            // nqkv = qdim + 2*kvdim rows of the fused QKV matrix
+  int32_t vpl;                             // weight values per 16-byte lane load
+  int32_t kv_vpl;                          // KV values per 16-byte lane load
+  int32_t lpp, ppp;                        // lanes per KV position, KV positions per packet
+  int32_t cd, cq;                          // packets per weight row for K = d and K = qdim
+  int64_t off_qkv, off_o, off_gu, off_d, layer_elems, off_lm;  // element offsets in the packed blob
+  int64_t blob_elems;
+};
+
+KD_HD Dims make_dims(int L, int d, int hq, int hkv, int hd, int F, int V, int max_seq, int nwg, int wbytes, int kvbytes) {
+  Dims m{};
+  m.L = L; m.d = d; m.hq = hq; m.hkv = hkv; m.hd = hd; m.F = F; m.V = V; m.nwg = nwg;
+  // the last packet of an attention chunk may cover up to 7 positions past the current one
+  m.S = (int32_t)(ceil_div((int64_t)max_seq + 7, 16) * 16);
+  m.wbytes = wbytes; m.kvbytes = kvbytes;
+  m.G = hq / hkv; m.qdim = hq * hd; m.kvdim = hkv * hd; m.nqkv = m.qdim + 2 * m.kvdim;
+  m.vpl = 16 / wbytes; m.kv_vpl = 16 / kvbytes;
+  m.lpp = hd / m.kv_vpl; m.ppp = 64 / m.lpp;
+  m.cd = d * wbytes / kPacketBytes; m.cq = m.qdim * wbytes / kPacketBytes;
+  m.off_qkv = 0;
+  m.off_o = m.off_qkv + (int64_t)m.nqkv * d;
+  m.off_gu = m.off_o + (int64_t)d * m.qdim;
+  m.off_d = m.off_gu + (int64_t)2 * F * d;
+  m.layer_elems = m.off_d + (int64_t)d * F;
+  m.off_lm = (int64_t)L * m.layer_elems;
+  m.blob_elems = m.off_lm + (int64_t)V * d;
+  return m;
+}
+
+// FFN columns owned by workgroup w: [ffn_lo(w), ffn_lo(w+1)), aligned to whole 16-byte lane loads.
+KD_HD int64_t ffn_lo(const Dims& m, int64_t w) { return (int64_t)m.vpl * part_lo(m.F / m.vpl, m.nwg, w); }
+
+// Element offset of workgroup w's down-projection packets inside a layer's down block.
+KD_HD int64_t down_wg_off(const Dims& m, int64_t w) { return (int64_t)m.d * ffn_lo(m, w); }
+
+// Attention split of one step at position p (P = p+1 positions attended).
+struct AttPlan {
+  int32_t P, CH, NC, units, MS, nmerge;
+};
+
+KD_HD AttPlan att_plan(const Dims& m, int32_t p) {
+  AttPlan a{};
+  a.P = p + 1;
+  int64_t work = (int64_t)a.P * m.hkv;
+  int64_t k = ceil_div(work, (int64_t)m.nwg * kChunkMax);
+  if (k < 1) k = 1;
+  int64_t ch = ceil_div(work, k * m.nwg);
+  ch = ceil_div(ch, m.ppp) * m.ppp;
+  if (ch < kChunkMin) ch = kChunkMin;
+  if (ch > kChunkMax) ch = kChunkMax;
+  a.CH = (int32_t)ch;
+  a.NC = (int32_t)ceil_div(a.P, ch);
+  a.units = a.NC * m.hkv;
+  int32_t ms = m.hd;
+  while (ms > 2 && (int64_t)a.NC * (ms + 2) > kMergeWords) ms /= 2;
+  a.MS = ms;
+  a.nmerge = m.hq * (m.hd / ms);
+  return a;
+}
+
+// Most chunks any step of a cache with S positions can use (sizes the partial buffer).
+KD_HD int32_t max_chunks(const Dims& m) { return (int32_t)ceil_div(m.S, kChunkMin); }
+
+// Word offsets of the exchange buffers (64-bit LL words) for one session.
+struct LLLayout {
+  int64_t qkv, attp, o, xp, dp, x, lm, total;
+};
+
+KD_HD LLLayout ll_layout(const Dims& m) {
+  LLLayout l{};
+  int64_t at = 0;
+  auto take = [&](int64_t n) { int64_t r = at; at += (n + 1) / 2 * 2; return r; };
+  l.qkv = take(m.nqkv);
+  l.attp = take((int64_t)m.hq * max_chunks(m) * (m.hd + 2));
+  l.o = take(m.qdim);
+  l.xp = take(m.d);
+  l.dp = take((int64_t)m.nwg * m.d);
+  l.x = take(m.d);
+  l.lm = take((int64_t)m.nwg * 2);
+  l.total = at;
+  return l;
+}
+
+// Tag of vector `kind` of layer `layer` (layer == L for the LM head) in step `seq`.
+KD_HD uint32_t ll_tag(const Dims& m, uint32_t seq, int layer, int kind) {
+  return seq * (uint32_t)(8 * (m.L + 1)) + (uint32_t)(8 * layer + kind);
+}
+
+}  // namespace kd

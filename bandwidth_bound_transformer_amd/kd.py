@@ -1,0 +1,244 @@
+"""Python binding of libkd.so: argument marshalling only.
+
+The functions here have the names of the C ABI in include/kd.h and do no
+arithmetic of the decode step; every step runs in the HIP library. Torch is
+used only for device memory and streams: device buffers are passed as
+``tensor.data_ptr()``, streams as ``torch.cuda.Stream.cuda_stream``.
+
+If libkd.so has not been built, importing this module still works, but every
+call raises. Nothing here falls back to a CPU path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkd.so")
+
+KD_OK = 0
+KD_ERR_INVALID_ARG = -1
+KD_ERR_UNSUPPORTED = -2
+KD_ERR_NO_DEVICE = -3
+KD_ERR_OOM = -4
+KD_ERR_HIP = -5
+KD_ERR_LAUNCH = -6
+
+KD_STATUS_TOKEN_RANGE = 0x1
+KD_STATUS_POS_OVERFLOW = 0x2
+KD_STATUS_SYNC_TIMEOUT = 0x4
+KD_STATUS_NAN = 0x8
+
+KD_DTYPE_F32 = 0
+KD_DTYPE_BF16 = 1
+
+EXPORTS = (
+    "kd_init",
+    "kd_kv_layout",
+    "kd_step",
+    "kd_device_status",
+    "kd_destroy",
+    "kd_strerror",
+    "kd_get_info",
+)
+
+
+class KDError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+class kd_config(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32),
+        ("d_model", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("ffn_dim", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("max_seq", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("norm_eps", ctypes.c_float),
+        ("rope_base", ctypes.c_float),
+        ("weight_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+    ]
+
+
+class kd_layer_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")]
+
+
+class kd_weights(ctypes.Structure):
+    _fields_ = [
+        ("embed", ctypes.c_void_p),
+        ("layers", ctypes.POINTER(kd_layer_weights)),
+        ("final_norm", ctypes.c_void_p),
+        ("lm_head", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libkd.so from the package directory (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} not built; run `python -m bandwidth_bound_transformer_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.kd_init.argtypes = [ctypes.POINTER(kd_config), ctypes.POINTER(kd_weights), ctypes.POINTER(ctypes.c_void_p)]
+        lib.kd_init.restype = ctypes.c_int
+        lib.kd_kv_layout.argtypes = [ctypes.POINTER(kd_config), ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+        lib.kd_kv_layout.restype = ctypes.c_int
+        lib.kd_step.argtypes = [ctypes.c_void_p] * 6
+        lib.kd_step.restype = ctypes.c_int
+        lib.kd_device_status.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
+        lib.kd_device_status.restype = ctypes.c_int
+        lib.kd_destroy.argtypes = [ctypes.c_void_p]
+        lib.kd_destroy.restype = None
+        lib.kd_strerror.argtypes = [ctypes.c_int]
+        lib.kd_strerror.restype = ctypes.c_char_p
+        lib.kd_get_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
+        lib.kd_get_info.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return library().kd_strerror(int(code)).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != KD_OK:
+        raise KDError(code, what)
+
+
+def make_config(shape, batch: int = 1, max_seq: int = 1) -> kd_config:
+    """kd_config of a ``workloads.ModelShape``."""
+    dt = {"f32": KD_DTYPE_F32, "bf16": KD_DTYPE_BF16}
+    return kd_config(
+        shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim,
+        shape.vocab, max_seq, batch, shape.norm_eps, shape.rope_base, dt[shape.weight_dtype], dt[shape.kv_dtype],
+    )
+
+
+def _host_ptr(a: np.ndarray) -> int:
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError("weight arrays must be C-contiguous")
+    return a.ctypes.data
+
+
+def kd_kv_layout(cfg: kd_config):
+    """(bytes, element strides[6]) of the caller-owned KV cache."""
+    nbytes = ctypes.c_size_t()
+    strides = (ctypes.c_size_t * 6)()
+    _check(library().kd_kv_layout(ctypes.byref(cfg), ctypes.byref(nbytes), strides), "kd_kv_layout")
+    return nbytes.value, tuple(strides)
+
+
+def kd_init(cfg: kd_config, weights: dict) -> int:
+    """Pack ``weights`` (dict from ``workloads.make_weights``) onto the current device; returns a handle."""
+    names = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+    layers = (kd_layer_weights * cfg.n_layers)()
+    for i, lw in enumerate(weights["layers"]):
+        for n in names:
+            setattr(layers[i], n, _host_ptr(lw[n]))
+    w = kd_weights(_host_ptr(weights["embed"]), layers, _host_ptr(weights["final_norm"]), _host_ptr(weights["lm_head"]))
+    h = ctypes.c_void_p()
+    _check(library().kd_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)), "kd_init")
+    return h.value
+
+
+def _dev_ptr(t) -> int | None:
+    if t is None:
+        return None
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    return int(t)
+
+
+def kd_step(handle: int, tokens, positions, kv, logits=None, stream=None) -> None:
+    """Enqueue one decode step (device buffers as torch tensors or raw pointers)."""
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(
+        library().kd_step(handle, _dev_ptr(tokens), _dev_ptr(positions), _dev_ptr(kv), _dev_ptr(logits), s),
+        "kd_step",
+    )
+
+
+def kd_device_status(handle: int, clear: bool = False) -> int:
+    bits = ctypes.c_uint32()
+    _check(library().kd_device_status(handle, ctypes.byref(bits), int(bool(clear))), "kd_device_status")
+    return bits.value
+
+
+def kd_destroy(handle: int | None) -> None:
+    library().kd_destroy(handle)
+
+
+def kd_strerror(code: int) -> str:
+    return strerror(code)
+
+
+def kd_get_info(handle: int) -> dict:
+    info = (ctypes.c_int64 * 8)()
+    _check(library().kd_get_info(handle, info), "kd_get_info")
+    return {
+        "workgroups": info[0],
+        "threads": info[1],
+        "packed_weight_bytes": info[2],
+        "lds_bytes": info[3],
+        "ring_packets": info[4],
+    }
+
+
+class Decoder:
+    """A handle plus the device buffers one session needs (torch for memory and streams only)."""
+
+    def __init__(self, shape, weights: dict, max_seq: int, batch: int = 1, device: str = "cuda:0"):
+        import torch
+
+        self.torch = torch
+        self.device = torch.device(device)
+        self.shape = shape
+        self.cfg = make_config(shape, batch, max_seq)
+        with torch.cuda.device(self.device):
+            self.handle = kd_init(self.cfg, weights)
+        nbytes, self.kv_strides = kd_kv_layout(self.cfg)
+        kv_dtype = torch.bfloat16 if shape.kv_dtype == "bf16" else torch.float32
+        elems = nbytes // (2 if shape.kv_dtype == "bf16" else 4)
+        self.kv = torch.zeros(elems, dtype=kv_dtype, device=self.device)
+        self.s_alloc = self.kv_strides[3] // shape.head_dim
+        self.tokens = torch.zeros(batch, dtype=torch.int32, device=self.device)
+        self.positions = torch.zeros(batch, dtype=torch.int32, device=self.device)
+        self.logits = torch.zeros(batch, shape.vocab, dtype=torch.float32, device=self.device)
+
+    def kv_view(self):
+        """The cache as [L][2][B][Hkv][S][hd] (a view of the flat buffer)."""
+        m = self.shape
+        return self.kv.view(m.n_layers, 2, self.cfg.batch, m.n_kv_heads, self.s_alloc, m.head_dim)
+
+    def step(self, write_logits: bool = True, stream=None) -> None:
+        kd_step(self.handle, self.tokens, self.positions, self.kv, self.logits if write_logits else None,
+                stream if stream is not None else self.torch.cuda.current_stream(self.device))
+
+    def status(self, clear: bool = False) -> int:
+        return kd_device_status(self.handle, clear)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            kd_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):  # pragma: no cover - best effort
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,169 @@
+/*
+ * kd.h -- C ABI of the bandwidth-bound decode library (libkd.so) for AMD MI355X (gfx950).
+ *
+ * One call of kd_step runs one decode step of a pre-norm decoder. The step
+ * covers token embedding, then per layer RMSNorm, fused QKV projection, RoPE,
+ * KV-cache append, grouped-query attention over the cache, output projection,
+ * RMSNorm and the SwiGLU feed-forward block, then the final norm, the LM head
+ * and a greedy argmax. All of it runs as one persistent kernel launch with no
+ * host round trip between operations.
+ *
+ * Why this shape:
+ *  - Batch-1 decode is bound by memory bandwidth. Every generated token reads
+ *    every weight and the whole KV cache, so the weight layout is packed for
+ *    aligned, coalesced streaming ("Kog 3000 tok/s real-time inference:
+ *    memory-bandwidth optimisation and request-level concurrency trade-offs",
+ *    section "three-layer strategy for memory-bandwidth optimisation").
+ *  - A single persistent kernel removes kernel-boundary and launch overhead
+ *    ("Real-time LLM inference on standard data-centre GPUs (3,000 tokens/s
+ *    single request)", section "technical principles").
+ *  - Per step the host only feeds the input tokens and takes the output. The
+ *    schedule and all memory are fixed before the first call, and nothing is
+ *    allocated per step ("Why is real-time AI inference 56x more expensive?
+ *    Continuous inference and resident kernels", sections "keep the work
+ *    resident on the GPU" and "decide everything ahead of time").
+ *
+ * Conventions
+ *  - Every function returns KD_OK (0) or a negative KD_ERR_* code. The
+ *    library never prints, never aborts and never throws across this ABI.
+ *  - Pointers documented as "host" are CPU memory. Pointers documented as
+ *    "device" are memory of the GPU that was current at kd_init.
+ *  - Calls on one handle must not overlap. kd_step launches on the caller's
+ *    stream; steps of one handle must be issued on a single stream (or be
+ *    otherwise ordered), because the handle owns the step's scratch memory.
+ */
+#ifndef KD_H_
+#define KD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define KD_OK 0
+#define KD_ERR_INVALID_ARG (-1) /* NULL pointer, inconsistent or out-of-range configuration value */
+#define KD_ERR_UNSUPPORTED (-2) /* valid but not implemented here (e.g. head_dim not 64/128, non-gfx950 GPU) */
+#define KD_ERR_NO_DEVICE (-3)   /* no HIP device visible */
+#define KD_ERR_OOM (-4)         /* device memory allocation failed */
+#define KD_ERR_HIP (-5)         /* a HIP runtime call failed */
+#define KD_ERR_LAUNCH (-6)      /* the cooperative launch was rejected (grid cannot be co-resident) */
+
+/* ---- sticky device status bits (kd_device_status) ------------------------ */
+#define KD_STATUS_TOKEN_RANGE 0x1u     /* an input token was outside [0, vocab): that step wrote nothing */
+#define KD_STATUS_POS_OVERFLOW 0x2u    /* a position was outside [0, max_seq): that step wrote nothing */
+#define KD_STATUS_SYNC_TIMEOUT 0x4u    /* an inter-workgroup wait timed out; the step was abandoned */
+#define KD_STATUS_NAN 0x8u             /* a NaN reached the logits; the argmax skipped it */
+
+/* ---- number formats ---------------------------------------------------------- */
+#define KD_DTYPE_F32 0  /* IEEE binary32 */
+#define KD_DTYPE_BF16 1 /* bfloat16: the top 16 bits of a binary32 */
+
+/*
+ * Model and run configuration, fixed at kd_init.
+ *   d_model      = n_q_heads * head_dim is not required, but q_dim = n_q_heads*head_dim
+ *                  and d_model must both be multiples of 512 (bf16) / 256 (f32) elements,
+ *                  and d_model a multiple of 64.
+ *   n_q_heads    must be a multiple of n_kv_heads; G = n_q_heads / n_kv_heads <= 4.
+ *   head_dim     64 or 128.
+ *   ffn_dim      must be a multiple of 8 (bf16) or 4 (f32) elements.
+ *   max_seq      capacity of the KV cache in positions (steps may use positions 0..max_seq-1).
+ *   batch        sessions stepped together; this build supports batch == 1.
+ *   norm_eps     RMSNorm epsilon (inside the square root).
+ *   rope_base    RoPE base: pair (i, i + head_dim/2) turns by position * rope_base^(-2i/head_dim).
+ *   weight_dtype KD_DTYPE_BF16 or KD_DTYPE_F32; kv_dtype likewise (must match weight_dtype).
+ */
+typedef struct kd_config {
+  int32_t n_layers;
+  int32_t d_model;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t ffn_dim;
+  int32_t vocab;
+  int32_t max_seq;
+  int32_t batch;
+  float norm_eps;
+  float rope_base;
+  int32_t weight_dtype;
+  int32_t kv_dtype;
+} kd_config;
+
+/* Host pointers to one layer's tensors, row-major, in weight_dtype (bf16 = uint16 patterns). */
+typedef struct kd_layer_weights {
+  const void* attn_norm; /* [d_model] */
+  const void* wq;        /* [n_q_heads*head_dim, d_model] */
+  const void* wk;        /* [n_kv_heads*head_dim, d_model] */
+  const void* wv;        /* [n_kv_heads*head_dim, d_model] */
+  const void* wo;        /* [d_model, n_q_heads*head_dim] */
+  const void* ffn_norm;  /* [d_model] */
+  const void* w_gate;    /* [ffn_dim, d_model] */
+  const void* w_up;      /* [ffn_dim, d_model] */
+  const void* w_down;    /* [d_model, ffn_dim] */
+} kd_layer_weights;
+
+/* Host pointers to all weights.  layers points to n_layers entries. */
+typedef struct kd_weights {
+  const void* embed;              /* [vocab, d_model] */
+  const kd_layer_weights* layers; /* [n_layers] */
+  const void* final_norm;         /* [d_model] */
+  const void* lm_head;            /* [vocab, d_model] (separate from embed) */
+} kd_weights;
+
+typedef struct kd_handle kd_handle;
+
+/*
+ * Validate cfg, pack the weights into library-owned device memory on the
+ * current HIP device, and allocate every buffer a step needs.
+ * Host memory in w may be freed as soon as kd_init returns; it is only read.
+ * Synchronous. On success *out receives the handle. On error it returns a
+ * negative code, leaves *out NULL and keeps no device memory.
+ */
+int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out);
+
+/*
+ * Layout of the caller-owned KV cache for cfg.  The cache is one device buffer
+ * of kv_dtype values indexed [layer][slot][session][kv_head][position][dim]:
+ *   slot 0 holds K after RoPE, slot 1 holds V.
+ * strides[0..5] receive the element strides of those six indices (dim stride is 1);
+ * the position extent is max_seq + 7 rounded up to a multiple of 16.  *bytes receives the
+ * buffer size.  Host-only computation, no device needed.
+ */
+int kd_kv_layout(const kd_config* cfg, size_t* bytes, size_t strides[6]);
+
+/*
+ * Enqueue one decode step on `stream` (a hipStream_t; NULL = the null stream) and return.
+ *   tokens    device int32[batch], in/out: read as this step's input ids, overwritten with the
+ *             greedy next ids.
+ *   positions device int32[batch], in/out: read as the position p of each input token (the
+ *             step attends over cached positions 0..p and writes K,V at p), then incremented.
+ *   kv        device buffer laid out as kd_kv_layout reports; read and written.
+ *   logits    device float[batch, vocab] written with this step's logits, or NULL to skip.
+ * No allocation, no synchronisation and no host<->device copy happen here.  Device-detected
+ * input errors set sticky status bits (kd_device_status) and leave outputs unchanged.
+ */
+int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* logits, void* stream);
+
+/* Read (and optionally clear) the sticky KD_STATUS_* bits.  Synchronises with the device. */
+int kd_device_status(kd_handle* h, uint32_t* bits, int clear);
+
+/* Free everything the library owns. NULL is accepted. Caller buffers are never touched. */
+void kd_destroy(kd_handle* h);
+
+/* Static description of a status code. */
+const char* kd_strerror(int code);
+
+/*
+ * Facts about an initialised handle (for measurement and tests).
+ *   info[0] workgroups in the persistent grid      info[1] threads per workgroup
+ *   info[2] packed weight bytes on the device      info[3] LDS bytes per workgroup
+ *   info[4] ring depth (1 KB packets per compute wave)
+ */
+int kd_get_info(kd_handle* h, int64_t info[8]);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KD_H_ */

@@ -1,0 +1,204 @@
+"""Parity of the HIP decode step (through the C ABI) with the CPU oracle, on an MI355X.
+
+Every input is seeded and synthetic (``workloads``); every expected value comes from
+``oracle``. Tolerance: the largest logit error over the largest reference logit must stay
+within 2e-2 for bf16 weights with fp32 arithmetic. The greedy token of every step must equal
+the oracle's argmax (in float32), except at an exact tie-flip (see gpu_harness.compare_sequence).
+The fp32 tiny decoder is held to a much tighter bound, 1e-4, because there the only error
+sources are fp32 rounding and the hardware exp and sqrt.
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import decoder as ref
+
+from . import gpu_harness as gh
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+
+    assert t.cuda.is_available()
+    return t
+
+
+@pytest.fixture(scope="module")
+def kdm():
+    from bandwidth_bound_transformer_amd import kd
+
+    kd.library()  # fails loudly if the HIP library is missing
+    return kd
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    wl = workloads.get("tiny")
+    return wl, workloads.make_weights(wl.model, seed=wl.weight_seed)
+
+
+def _decoder(kdm, wl, w, max_seq=None):
+    return kdm.Decoder(wl.model, w, max_seq=max_seq or wl.max_seq)
+
+
+def test_tiny_generation_and_cache(torch, kdm, tiny):
+    """The tiny workload end to end: 32-token prompt, 64 greedy tokens, KV cache contents."""
+    wl, w = tiny
+    dec = _decoder(kdm, wl, w)
+    prompt = workloads.make_prompt(wl, 0)
+    toks, logits = gh.run_prompt(dec, prompt, wl.gen_tokens, torch)
+    assert dec.status() == 0
+    o = ref.Oracle(wl.model, w, batch=1, max_seq=wl.max_seq)
+    feed = list(prompt) + [int(t) for t in toks[len(prompt) - 1 : -1]]
+    want = np.stack([o.step_one(0, int(t), p) for p, t in enumerate(feed)])
+    worst, flips, defects = gh.compare_sequence(toks, logits, want, F32_TOL)
+    print(f"tiny: max rel logit err {worst:.3e}, tie-flips {flips}")
+    assert worst <= F32_TOL
+    assert not defects and flips == 0
+    # the cache holds K (after RoPE) and V of every fed position, as the oracle stored them
+    kv = dec.kv_view().float().cpu().numpy()
+    n = len(feed)
+    k_err = np.max(np.abs(kv[:, 0, 0, :, :n] - o.k_cache[0][:, :, :n]))
+    v_err = np.max(np.abs(kv[:, 1, 0, :, :n] - o.v_cache[0][:, :, :n]))
+    assert k_err < 1e-4 * max(1.0, np.max(np.abs(o.k_cache))) and v_err < 1e-4 * max(1.0, np.max(np.abs(o.v_cache)))
+    # positions advanced once per step
+    assert int(dec.positions.item()) == n
+    dec.close()
+
+
+def test_tiny_first_position_and_null_logits(torch, kdm, tiny):
+    """Position 0 (a single cached key) and a step that skips the logits write give the same token."""
+    wl, w = tiny
+    dec = _decoder(kdm, wl, w)
+    dec.tokens.fill_(7)
+    dec.positions.zero_()
+    dec.step(write_logits=True)
+    t_with = int(dec.tokens.item())
+    l0 = dec.logits[0].cpu().numpy()
+    want = ref.Oracle(wl.model, w, 1, wl.max_seq).step_one(0, 7, 0)
+    assert gh.inf_rel_err(l0, want) <= F32_TOL
+    dec.kv.zero_()
+    dec.tokens.fill_(7)
+    dec.positions.zero_()
+    dec.logits.fill_(123.0)
+    dec.step(write_logits=False)
+    torch.cuda.synchronize()
+    assert int(dec.tokens.item()) == t_with
+    assert bool(torch.all(dec.logits == 123.0))
+    dec.close()
+
+
+def test_tiny_bitwise_deterministic(torch, kdm, tiny):
+    """Two runs of the same inputs give identical bits (fixed reduction orders, no float atomics)."""
+    wl, w = tiny
+    runs = []
+    for _ in range(2):
+        dec = _decoder(kdm, wl, w)
+        toks, logits = gh.run_prompt(dec, workloads.make_prompt(wl, 0)[:8], 24, torch)
+        runs.append((toks, logits, dec.kv_view().float().cpu().numpy()))
+        dec.close()
+    assert np.array_equal(runs[0][0], runs[1][0])
+    assert np.array_equal(runs[0][1].view(np.uint32), runs[1][1].view(np.uint32))
+    assert np.array_equal(runs[0][2], runs[1][2])
+
+
+def test_input_errors_set_status_and_write_nothing(torch, kdm, tiny):
+    wl, w = tiny
+    dec = _decoder(kdm, wl, w)
+    for token, pos, bit in ((wl.model.vocab, 0, kdm.KD_STATUS_TOKEN_RANGE), (-1, 0, kdm.KD_STATUS_TOKEN_RANGE),
+                            (5, wl.max_seq, kdm.KD_STATUS_POS_OVERFLOW), (5, -3, kdm.KD_STATUS_POS_OVERFLOW)):
+        dec.tokens.fill_(token)
+        dec.positions.fill_(pos)
+        dec.logits.fill_(-7.0)
+        before = dec.kv.clone()
+        dec.step()
+        assert dec.status(clear=True) == bit
+        assert int(dec.tokens.item()) == token and int(dec.positions.item()) == pos
+        assert bool(torch.all(dec.logits == -7.0)) and bool(torch.equal(before, dec.kv))
+    # the handle keeps working afterwards
+    dec.tokens.fill_(3)
+    dec.positions.zero_()
+    dec.step()
+    assert dec.status() == 0
+    dec.close()
+
+
+def test_2b_prompt512_generation(torch, kdm):
+    """2B-class decoder at its real shape: the 512-token prompt, then 8 greedy tokens."""
+    wl = workloads.get("2b")
+    w = workloads.make_weights(wl.model, seed=wl.weight_seed)
+    dec = _decoder(kdm, wl, w)
+    prompt = workloads.make_prompt(wl, 0)
+    n_gen = 8
+    toks, logits = gh.run_prompt(dec, prompt, n_gen, torch)
+    assert dec.status() == 0
+    seq = list(prompt) + [int(t) for t in toks[len(prompt) - 1 : -1]]
+    want = ref.forward_full(wl.model, w, seq)
+    worst, flips, defects = gh.compare_sequence(toks, logits, want, BF16_TOL)
+    print(f"2b: max rel logit err {worst:.3e} over {len(seq)} steps, tie-flips {flips}")
+    assert worst <= BF16_TOL
+    assert not defects
+    dec.close()
+
+
+def test_8b_short_prompt(torch, kdm):
+    """Llama-3-8B shape at its real dimensions and launch configuration, 48-token prompt + 6 tokens."""
+    wl = workloads.get("8b")
+    w = workloads.make_weights(wl.model, seed=wl.weight_seed)
+    dec = _decoder(kdm, wl, w)
+    prompt = workloads.make_prompt(wl, 0)[:48]
+    toks, logits = gh.run_prompt(dec, prompt, 6, torch)
+    assert dec.status() == 0
+    seq = list(prompt) + [int(t) for t in toks[len(prompt) - 1 : -1]]
+    want = ref.forward_full(wl.model, w, seq)
+    worst, flips, defects = gh.compare_sequence(toks, logits, want, BF16_TOL)
+    print(f"8b: max rel logit err {worst:.3e} over {len(seq)} steps, tie-flips {flips}")
+    assert worst <= BF16_TOL
+    assert not defects
+    dec.close()
+
+
+def test_2b_long_context_prefilled(torch, kdm):
+    """2B decoder with the KV cache pre-filled to 32768 positions: two steps from the seeded first token."""
+    wl = workloads.get("2b_long")
+    m = wl.model
+    w = workloads.make_weights(m, seed=wl.weight_seed)
+    dec = _decoder(kdm, wl, w)
+    kv_host = np.zeros((m.n_layers, 2, 1, m.n_kv_heads, dec.s_alloc, m.head_dim), np.uint16)
+    workloads.fill_kv_prefill(wl, kv_host)
+    dec.kv.view(torch.int16).copy_(torch.from_numpy(kv_host.view(np.int16).reshape(-1)))
+    o = ref.Oracle(m, w, batch=1, max_seq=wl.max_seq)
+    for l in range(m.n_layers):
+        for g in range(m.n_kv_heads):
+            o.load_kv(0, l, g, workloads.f32_from_bf16_bits(kv_host[l, 0, 0, g, : wl.prefill_len]),
+                      workloads.f32_from_bf16_bits(kv_host[l, 1, 0, g, : wl.prefill_len]))
+    del kv_host
+    first = int(workloads.make_first_tokens(wl)[0])
+    dec.tokens.fill_(first)
+    dec.positions.fill_(wl.prefill_len)
+    tok = first
+    for i in range(2):
+        dec.step()
+        gl = dec.logits[0].cpu().numpy()
+        want = o.step_one(0, tok, wl.prefill_len + i)
+        err = gh.inf_rel_err(gl, want)
+        print(f"2b_long step {i}: rel logit err {err:.3e}")
+        assert err <= BF16_TOL
+        g_tok = int(dec.tokens.item())
+        if g_tok != int(ref.greedy_token(want[None])[0]):
+            assert gh.top2_margin(want) <= 2 * np.max(np.abs(gl - want))
+        tok = g_tok
+    assert dec.status() == 0
+    # the new positions were appended to the cache as the oracle stored them
+    kv = dec.kv_view()
+    for l in (0, m.n_layers - 1):
+        got = kv[l, 0, 0, :, wl.prefill_len : wl.prefill_len + 2].float().cpu().numpy()
+        assert np.max(np.abs(got - o.k_cache[0, l, :, wl.prefill_len : wl.prefill_len + 2])) <= 2e-2 * np.max(np.abs(got))
+    dec.close()
