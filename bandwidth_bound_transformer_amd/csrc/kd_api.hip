@@ -59,6 +59,7 @@ struct kd_handle {
   KernelFn kernel = nullptr;
   uint32_t seq = 0;
   int64_t lds_bytes = 0;
+  uint64_t* trace = nullptr;
 };
 
 namespace {
@@ -283,6 +284,7 @@ int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* 
   P.tokens = tokens;
   P.positions = positions;
   P.logits = logits;
+  P.trace = h->trace;
   P.status = h->buf.flags;
   P.abortf = h->buf.flags + 1;
   if (++h->seq == 0) ++h->seq;  // tag 0 never names a live vector
@@ -320,6 +322,19 @@ void kd_destroy(kd_handle* h) {
   free_buffers(h->buf);
   if (cur >= 0) (void)hipSetDevice(cur);
   delete h;
+}
+
+int kd_trace(kd_handle* h, uint64_t* dev_buf, int64_t words, int64_t* stride) {
+  if (!h) return KD_ERR_INVALID_ARG;
+  const int64_t st = kd::trace_stride(h->m.L);
+  if (stride) *stride = st;
+  if (!dev_buf) {
+    h->trace = nullptr;
+    return KD_OK;
+  }
+  if (words < st * h->m.nwg) return KD_ERR_INVALID_ARG;
+  h->trace = dev_buf;
+  return KD_OK;
 }
 
 int kd_get_info(kd_handle* h, int64_t info[8]) {

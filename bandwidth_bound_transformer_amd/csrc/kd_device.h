@@ -58,6 +58,7 @@ struct Params {
   float* logits;
   uint32_t* status;
   uint32_t* abortf;
+  uint64_t* trace;  // per-workgroup phase timestamps (100 MHz clock), or null
   uint32_t seq;
   int32_t max_seq;
   float eps;
@@ -622,6 +623,9 @@ struct Ctl {
 // LDS-DMA loads in flight across it; that is the point of the ring.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Timestamp slot of phase-boundary `ev` (layer < L) or of the final phases (layer == L).
+__device__ __forceinline__ int trace_slot(int L, int layer, int ev) { return 2 + kTraceLayerEvents * layer + ev; }
+
 // Phase protocol. Every phase runs as: control prepares the input in LDS; barrier B; compute
 // waves stream their packets into per-wave partial sums; barrier A; control reduces and
 // publishes. A failed wait sets the LDS abort flag before the next barrier B. All waves read the
@@ -724,6 +728,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   const int gD = nf / m.vpl;
   const int mc = max_chunks(m);
 
+  uint64_t* const tr = P.trace ? P.trace + (int64_t)w * trace_stride(m.L) : nullptr;
+  auto stamp = [&](int slot) {
+    if (tr && lane == 0) tr[slot] = now_ticks();
+  };
+  stamp(0);
   // RoPE angles of this step's position, in float64 then rounded to float32
   for (int i = lane; i < m.hd / 2; i += 64) {
     const double theta = pow((double)P.rope_base, -2.0 * (double)i / (double)m.hd);
@@ -735,19 +744,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   for (int i = lane; i < m.d; i += 64) sm.x[i] = load_w<WB>(P.embed, (int64_t)token * m.d + i);
 
   const float inv_sqrt_hd = 1.0f / sqrtf((float)m.hd);
+  stamp(1);
   for (int layer = 0; layer < m.L; ++layer) {
     const uint8_t* g_attn = P.norms + ((int64_t)layer * 2 + 0) * m.d * m.wbytes;
     const uint8_t* g_ffn = P.norms + ((int64_t)layer * 2 + 1) * m.d * m.wbytes;
     // ---- QKV rows ----
     if (layer > 0) ctl.gather_vec(ll_tag(m, P.seq, layer - 1, kX), P.lo.x, m.d, sm.x);
     if (!ctl.failed()) ctl.template rmsnorm<WB>(sm.x, g_attn, sm.act, m.d);
+    stamp(trace_slot(m.L, layer, 0));
     wg_barrier();
     if (sm.abort_flag) return;
     wg_barrier();
+    stamp(trace_slot(m.L, layer, 1));
     {
       const uint32_t tag = ll_tag(m, P.seq, layer, kQKV);
       for (int r = lane; r < n_qkv; r += 64) ll_store(P.ll, P.lo.qkv + r_qkv0 + r, ctl.row_total(kTileQKV, m.cd, r), tag);
     }
+    stamp(trace_slot(m.L, layer, 2));
     // ---- attention units: one chunk of positions of one kv head each ----
     for (int k = 0; k < si.nunits; ++k) {
       const Unit u = unit_of(si, w, k, m.nwg);
@@ -810,9 +823,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
           sm.u.att.vp[i] = vv;
         }
       }
+      if (k == 0) stamp(trace_slot(m.L, layer, 3));
       wg_barrier();
       if (sm.abort_flag) return;
       wg_barrier();
+      if (k == 0) stamp(trace_slot(m.L, layer, 4));
       // merge the compute waves' partial softmax sums, plus the current position in the last chunk
       if (!ctl.failed()) {
         const uint32_t tag = ll_tag(m, P.seq, layer, kATTP);
@@ -853,6 +868,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         }
       }
     }
+    stamp(trace_slot(m.L, layer, 5));
     // ---- merge units: one slice of one head's output, over all chunks ----
     for (int k = 0; k < nmerge_here && !ctl.failed(); ++k) {
       const int mu = mfirst + k * m.nwg;
@@ -894,31 +910,39 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         ll_store(P.ll, P.lo.o + (int64_t)hq * m.hd + (int64_t)sl * MS + i, a * invL, tag);
       }
     }
+    stamp(trace_slot(m.L, layer, 6));
     // ---- output projection rows + residual ----
     ctl.gather_vec(ll_tag(m, P.seq, layer, kO), P.lo.o, m.qdim, sm.act);
+    stamp(trace_slot(m.L, layer, 7));
     wg_barrier();
     if (sm.abort_flag) return;
     wg_barrier();
+    stamp(trace_slot(m.L, layer, 8));
     {
       const uint32_t tag = ll_tag(m, P.seq, layer, kXP);
       for (int r = lane; r < nrow_d; r += 64)
         ll_store(P.ll, P.lo.xp + rows_d0 + r, sm.x[rows_d0 + r] + ctl.row_total(kTileO, m.cq, r), tag);
     }
+    stamp(trace_slot(m.L, layer, 9));
     // ---- gate/up rows of this workgroup's FFN slice ----
     ctl.gather_vec(ll_tag(m, P.seq, layer, kXP), P.lo.xp, m.d, sm.x);
     if (!ctl.failed()) ctl.template rmsnorm<WB>(sm.x, g_ffn, sm.act, m.d);
+    stamp(trace_slot(m.L, layer, 10));
     wg_barrier();
     if (sm.abort_flag) return;
     wg_barrier();
+    stamp(trace_slot(m.L, layer, 11));
     for (int i = lane; i < nf; i += 64) {
       const float gt = ctl.row_total(kTileGU, m.cd, i);
       const float up = ctl.row_total(kTileGU, m.cd, nf + i);
       sm.act[i] = gt / (1.0f + __expf(-gt)) * up;
     }
+    stamp(trace_slot(m.L, layer, 12));
     // ---- down projection of the slice, for all d rows ----
     wg_barrier();
     if (sm.abort_flag) return;
     wg_barrier();
+    stamp(trace_slot(m.L, layer, 13));
     {
       const uint32_t tag = ll_tag(m, P.seq, layer, kDP);
       for (int b = 0; b < m.d / 64; ++b) {
@@ -929,6 +953,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         ll_store(P.ll, P.lo.dp + (int64_t)olo * m.nwg + (int64_t)w * (ohi - olo) + (i - olo), val, tag);
       }
     }
+    stamp(trace_slot(m.L, layer, 14));
     // ---- sum every slice's contribution to this workgroup's rows; residual add ----
     {
       float* st = sm.act;  // [nwg][nrow_d]
@@ -945,14 +970,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         if (lane < nrow_d) ll_store(P.ll, P.lo.x + rows_d0 + lane, sm.x[rows_d0 + lane] + tot, ll_tag(m, P.seq, layer, kX));
       }
     }
+    stamp(trace_slot(m.L, layer, 15));
   }
 
   // ---- final norm, LM head rows, argmax ----
   ctl.gather_vec(ll_tag(m, P.seq, m.L - 1, kX), P.lo.x, m.d, sm.x);
   if (!ctl.failed()) ctl.template rmsnorm<WB>(sm.x, P.norms + (int64_t)m.L * 2 * m.d * m.wbytes, sm.act, m.d);
+  stamp(trace_slot(m.L, m.L, 0));
   wg_barrier();
   if (sm.abort_flag) return;
   wg_barrier();
+  stamp(trace_slot(m.L, m.L, 1));
   {
     float best = -INFINITY;
     int32_t besti = 0x7fffffff;
@@ -975,6 +1003,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       ll_store_bits(P.ll, P.lo.lm + 2 * w + 1, (uint32_t)besti, tag);
     }
   }
+  stamp(trace_slot(m.L, m.L, 2));
   if (w == 0) {
     float best = -INFINITY;
     int32_t besti = 0x7fffffff;
@@ -993,6 +1022,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       P.tokens[0] = besti == 0x7fffffff ? 0 : besti;
       P.positions[0] = si.p + 1;
     }
+    stamp(trace_slot(m.L, m.L, 3));
   }
 }
 

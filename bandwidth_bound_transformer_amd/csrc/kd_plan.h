@@ -125,6 +125,11 @@ KD_HD LLLayout ll_layout(const Dims& m) {
   return l;
 }
 
+// Step trace: per workgroup, slots 0-1 (start, setup done), kTraceLayerEvents phase
+// boundaries per layer, then 4 for the final norm, LM head and argmax.
+constexpr int kTraceLayerEvents = 16;
+KD_HD int64_t trace_stride(int L) { return 2 + (int64_t)kTraceLayerEvents * L + 4; }
+
 // Tag of vector `kind` of layer `layer` (layer == L for the LM head) in step `seq`.
 KD_HD uint32_t ll_tag(const Dims& m, uint32_t seq, int layer, int kind) {
   return seq * (uint32_t)(8 * (m.L + 1)) + (uint32_t)(8 * layer + kind);

@@ -43,6 +43,7 @@ EXPORTS = (
     "kd_destroy",
     "kd_strerror",
     "kd_get_info",
+    "kd_trace",
 )
 
 
@@ -107,6 +108,8 @@ def library() -> ctypes.CDLL:
         lib.kd_strerror.restype = ctypes.c_char_p
         lib.kd_get_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
         lib.kd_get_info.restype = ctypes.c_int
+        lib.kd_trace.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
+        lib.kd_trace.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -197,6 +200,13 @@ def kd_get_info(handle: int) -> dict:
         "lds_bytes": info[3],
         "ring_packets": info[4],
     }
+
+
+def kd_trace(handle: int, dev_buf=None, words: int = 0) -> int:
+    """Turn step tracing on (device buffer of uint64 words) or off (None); returns the per-workgroup stride."""
+    stride = ctypes.c_int64()
+    _check(library().kd_trace(handle, _dev_ptr(dev_buf), int(words), ctypes.byref(stride)), "kd_trace")
+    return stride.value
 
 
 class Decoder:

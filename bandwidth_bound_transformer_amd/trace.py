@@ -1,0 +1,73 @@
+"""Decode the per-workgroup phase timestamps written by a traced kd_step.
+
+Layout (see kd_trace in include/kd.h): per workgroup, slot 0 = step start, slot 1 = setup
+done, then 16 phase boundaries per layer, then 4 final ones. The timestamps come from the
+GPU's 100 MHz constant clock (10 ns ticks). A boundary a workgroup did not reach (e.g. no
+attention unit assigned) holds 0 and is skipped.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+TICK_US = 0.01
+LAYER_EVENTS = (
+    "x gathered, RMSNorm",
+    "QKV rows streamed",
+    "QKV reduced, published",
+    "q/k/v gathered, RoPE, KV append",
+    "attention chunk streamed",
+    "chunk partials merged, published",
+    "head merges",
+    "o gathered",
+    "O rows streamed",
+    "O reduced, residual, published",
+    "x' gathered, RMSNorm",
+    "gate/up rows streamed",
+    "SiLU*up",
+    "down slice streamed",
+    "down partials published",
+    "reduce-scatter gathered, x published",
+)
+FINAL_EVENTS = ("x gathered, final norm", "LM head streamed", "argmax partial published", "argmax done")
+
+
+def stride(n_layers: int) -> int:
+    return 2 + len(LAYER_EVENTS) * n_layers + len(FINAL_EVENTS)
+
+
+def intervals(buf: np.ndarray, n_layers: int, n_wg: int):
+    """Per workgroup, the time (us) spent before each reached boundary; dict name -> [n_wg, n_layers] or [n_wg]."""
+    st = stride(n_layers)
+    t = np.asarray(buf, np.int64)[: n_wg * st].reshape(n_wg, st)
+    layer = t[:, 2 : 2 + len(LAYER_EVENTS) * n_layers].reshape(n_wg, n_layers, len(LAYER_EVENTS))
+    final = t[:, 2 + len(LAYER_EVENTS) * n_layers :]
+    # walk the boundaries in order, keeping the last reached stamp
+    seq = np.concatenate([t[:, 1:2], layer.reshape(n_wg, -1), final], axis=1)
+    prev = seq[:, 0].copy()
+    deltas = np.zeros(seq.shape, np.float64)
+    for j in range(1, seq.shape[1]):
+        reached = seq[:, j] > 0
+        deltas[:, j] = np.where(reached, (seq[:, j] - prev) * TICK_US, np.nan)
+        prev = np.where(reached, seq[:, j], prev)
+    lay = deltas[:, 1 : 1 + n_layers * len(LAYER_EVENTS)].reshape(n_wg, n_layers, len(LAYER_EVENTS))
+    fin = deltas[:, 1 + n_layers * len(LAYER_EVENTS) :]
+    out = {name: lay[:, :, i] for i, name in enumerate(LAYER_EVENTS)}
+    out.update({name: fin[:, i] for i, name in enumerate(FINAL_EVENTS)})
+    total = (np.max(np.where(seq > 0, seq, 0), axis=1) - t[:, 0]) * TICK_US
+    return out, total
+
+
+def summary(buf: np.ndarray, n_layers: int, n_wg: int) -> str:
+    """Median (over workgroups) time per step spent before each boundary, summed over layers."""
+    parts, total = intervals(buf, n_layers, n_wg)
+    lines = [f"step span per workgroup: median {np.median(total):.1f} us, max {np.max(total):.1f} us"]
+    acc = 0.0
+    for name, v in parts.items():
+        per_step = np.nansum(v, axis=1) if v.ndim == 2 else np.nan_to_num(v)
+        med = float(np.median(per_step))
+        acc += med
+        per_layer = float(np.nanmedian(v)) if v.ndim == 2 and np.isfinite(v).any() else float("nan")
+        lines.append(f"  {name:38s} {med:9.1f} us/step" + (f"   ({per_layer:6.2f} us/layer median)" if v.ndim == 2 else ""))
+    lines.append(f"  {'sum of medians':38s} {acc:9.1f} us/step")
+    return "\n".join(lines)

@@ -156,6 +156,17 @@ void kd_destroy(kd_handle* h);
 const char* kd_strerror(int code);
 
 /*
+ * Step tracing, for measurement.  With dev_buf non-NULL, every later kd_step writes 64-bit
+ * timestamps of the GPU's 100 MHz constant clock at its phase boundaries: workgroup w uses
+ * dev_buf[w * stride .. (w + 1) * stride).  Slot 0 is the step start, slot 1 the end of setup,
+ * slots 2 + 16*l + e (e < 16) the phase boundaries of layer l, and the last 4 slots the final
+ * norm, LM head and argmax.  dev_buf is device memory of at least stride * workgroups words,
+ * owned by the caller; NULL turns tracing off.  *stride (optional) receives the stride.
+ * Returns KD_ERR_INVALID_ARG if the buffer is too small.
+ */
+int kd_trace(kd_handle* h, uint64_t* dev_buf, int64_t words, int64_t* stride);
+
+/*
  * Facts about an initialised handle (for measurement and tests).
  *   info[0] workgroups in the persistent grid      info[1] threads per workgroup
  *   info[2] packed weight bytes on the device      info[3] LDS bytes per workgroup

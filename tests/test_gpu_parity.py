@@ -134,11 +134,13 @@ def test_2b_prompt512_generation(torch, kdm):
     """2B-class decoder at its real shape: the 512-token prompt, then 8 greedy tokens."""
     wl = workloads.get("2b")
     w = workloads.make_weights(wl.model, seed=wl.weight_seed)
+    print("2b: weights ready", flush=True)
     dec = _decoder(kdm, wl, w)
     prompt = workloads.make_prompt(wl, 0)
     n_gen = 8
     toks, logits = gh.run_prompt(dec, prompt, n_gen, torch)
     assert dec.status() == 0
+    print("2b: GPU run done; oracle ...", flush=True)
     seq = list(prompt) + [int(t) for t in toks[len(prompt) - 1 : -1]]
     want = ref.forward_full(wl.model, w, seq)
     worst, flips, defects = gh.compare_sequence(toks, logits, want, BF16_TOL)
@@ -152,10 +154,12 @@ def test_8b_short_prompt(torch, kdm):
     """Llama-3-8B shape at its real dimensions and launch configuration, 48-token prompt + 6 tokens."""
     wl = workloads.get("8b")
     w = workloads.make_weights(wl.model, seed=wl.weight_seed)
+    print("8b: weights ready", flush=True)
     dec = _decoder(kdm, wl, w)
     prompt = workloads.make_prompt(wl, 0)[:48]
     toks, logits = gh.run_prompt(dec, prompt, 6, torch)
     assert dec.status() == 0
+    print("8b: GPU run done; oracle ...", flush=True)
     seq = list(prompt) + [int(t) for t in toks[len(prompt) - 1 : -1]]
     want = ref.forward_full(wl.model, w, seq)
     worst, flips, defects = gh.compare_sequence(toks, logits, want, BF16_TOL)
@@ -180,6 +184,7 @@ def test_2b_long_context_prefilled(torch, kdm):
             o.load_kv(0, l, g, workloads.f32_from_bf16_bits(kv_host[l, 0, 0, g, : wl.prefill_len]),
                       workloads.f32_from_bf16_bits(kv_host[l, 1, 0, g, : wl.prefill_len]))
     del kv_host
+    print("2b_long: cache pre-filled on both sides", flush=True)
     first = int(workloads.make_first_tokens(wl)[0])
     dec.tokens.fill_(first)
     dec.positions.fill_(wl.prefill_len)
@@ -189,7 +194,7 @@ def test_2b_long_context_prefilled(torch, kdm):
         gl = dec.logits[0].cpu().numpy()
         want = o.step_one(0, tok, wl.prefill_len + i)
         err = gh.inf_rel_err(gl, want)
-        print(f"2b_long step {i}: rel logit err {err:.3e}")
+        print(f"2b_long step {i}: rel logit err {err:.3e}", flush=True)
         assert err <= BF16_TOL
         g_tok = int(dec.tokens.item())
         if g_tok != int(ref.greedy_token(want[None])[0]):
