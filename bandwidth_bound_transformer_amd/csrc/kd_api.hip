@@ -3,7 +3,7 @@
 // kd_init fixes everything ahead of the first step: the weight layout, the
 // work plan, and every device buffer ("Why is real-time AI inference 56x more
 // expensive?", section "decide everything ahead of time"). kd_step is then a
-// single cooperative launch on the caller's stream, with no allocation and no
+// single kernel launch on the caller's stream, with no allocation and no
 // synchronisation ("keep the work resident on the GPU": per step the host
 // only hands over the input and takes the output).
 #include <hip/hip_runtime.h>
@@ -145,7 +145,7 @@ const char* kd_strerror(int code) {
     case KD_ERR_NO_DEVICE: return "no HIP device available";
     case KD_ERR_OOM: return "device memory allocation failed";
     case KD_ERR_HIP: return "HIP runtime call failed";
-    case KD_ERR_LAUNCH: return "cooperative kernel launch rejected";
+    case KD_ERR_LAUNCH: return "kernel launch rejected";
     default: return "unknown error code";
   }
 }
@@ -184,8 +184,6 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return KD_ERR_HIP;
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return KD_ERR_UNSUPPORTED;
-  int coop = 0;
-  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return KD_ERR_UNSUPPORTED;
 
   const int wb = dtype_bytes(cfg->weight_dtype), kb = dtype_bytes(cfg->kv_dtype);
   const int nwg = prop.multiProcessorCount;
@@ -294,8 +292,11 @@ int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* 
   P.rope_base = h->cfg.rope_base;
   P.m = h->m;
   void* args[] = {&P};
-  const hipError_t e = hipLaunchCooperativeKernel((const void*)h->kernel, dim3(h->m.nwg), dim3(kd::kThreads), args, 0,
-                                                  (hipStream_t)stream);
+  // One workgroup per compute unit, and a workgroup needs most of a CU's LDS, so on an idle
+  // device the whole grid is resident at once. If another kernel holds CUs, the waits between
+  // workgroups time out and the step ends with KD_STATUS_SYNC_TIMEOUT instead of hanging.
+  const hipError_t e = hipLaunchKernel((const void*)h->kernel, dim3(h->m.nwg), dim3(kd::kThreads), args, 0,
+                                       (hipStream_t)stream);
   int rc = KD_OK;
   if (e != hipSuccess) rc = KD_ERR_LAUNCH;
   if (cur != h->device) (void)hipSetDevice(cur);

@@ -49,7 +49,7 @@ extern "C" {
 #define KD_ERR_NO_DEVICE (-3)   /* no HIP device visible */
 #define KD_ERR_OOM (-4)         /* device memory allocation failed */
 #define KD_ERR_HIP (-5)         /* a HIP runtime call failed */
-#define KD_ERR_LAUNCH (-6)      /* the cooperative launch was rejected (grid cannot be co-resident) */
+#define KD_ERR_LAUNCH (-6)      /* the kernel launch was rejected by the HIP runtime */
 
 /* ---- sticky device status bits (kd_device_status) ------------------------ */
 #define KD_STATUS_TOKEN_RANGE 0x1u     /* an input token was outside [0, vocab): that step wrote nothing */
