@@ -8,10 +8,12 @@
 // only hands over the input and takes the output).
 #include <hip/hip_runtime.h>
 
-#include <cstdio>
 #include <algorithm>
+#include <cmath>
+#include <cstdio>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "kd.h"
 #include "kd_device.h"
@@ -25,6 +27,7 @@ struct Buffers {
   uint8_t* blob = nullptr;
   uint8_t* embed = nullptr;
   uint8_t* norms = nullptr;
+  float2* rope = nullptr;     // [S][hd/2] (cos, sin)
   uint64_t* ll = nullptr;
   uint32_t* flags = nullptr;  // [0] sticky status bits, [1] abort flag
 };
@@ -33,6 +36,7 @@ void free_buffers(Buffers& b) {
   if (b.blob) (void)hipFree(b.blob);
   if (b.embed) (void)hipFree(b.embed);
   if (b.norms) (void)hipFree(b.norms);
+  if (b.rope) (void)hipFree(b.rope);
   if (b.ll) (void)hipFree(b.ll);
   if (b.flags) (void)hipFree(b.flags);
   b = Buffers{};
@@ -85,45 +89,43 @@ int check_supported(const kd_config* c, const kd::Dims& m) {
   if (c->batch != 1) return KD_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return KD_ERR_UNSUPPORTED;
   if (c->weight_dtype != c->kv_dtype) return KD_ERR_UNSUPPORTED;
-  if (m.G > kd::kMaxGroup) return KD_ERR_UNSUPPORTED;
+  if (m.G > kd::kMaxGroup || (int64_t)m.G * m.hd > kd::kThreads) return KD_ERR_UNSUPPORTED;
   if (m.d > kd::kMaxDim || m.qdim > kd::kMaxDim || m.d % 64 != 0) return KD_ERR_UNSUPPORTED;
   if ((int64_t)m.d * m.wbytes % kd::kPacketBytes || (int64_t)m.qdim * m.wbytes % kd::kPacketBytes) return KD_ERR_UNSUPPORTED;
-  if (m.F % m.vpl != 0) return KD_ERR_UNSUPPORTED;
-  if (m.nwg % 2 != 0) return KD_ERR_UNSUPPORTED;
-  // per-workgroup and per-wave bookkeeping must fit the LDS arrays
-  const int64_t nrow_max = kd::ceil_div(m.d, m.nwg);
-  if (nrow_max > 64 || (int64_t)m.nwg * nrow_max > kd::kMaxDim) return KD_ERR_UNSUPPORTED;
-  auto max_segs = [&](int64_t nrows_total, int64_t C) {
+  if (m.F % m.vpl != 0 || m.F / m.vpl < m.nwg) return KD_ERR_UNSUPPORTED;  // every workgroup owns an FFN slice
+  // per-workgroup shares must fit the LDS arrays and the thread count
+  const int64_t nrd_max = 2 * kd::ceil_div(m.d / 2, m.nwg);
+  const int64_t nq_max = kd::ceil_div(m.nqkv, m.nwg);
+  const int64_t nf_max = m.vpl * kd::ceil_div(m.F / m.vpl, m.nwg);
+  if (nrd_max > kd::kMaxRowsD || nq_max > kd::kThreads || nf_max > kd::kMaxSlice) return KD_ERR_UNSUPPORTED;
+  if ((int64_t)m.nwg * nrd_max > kd::kStageWords || 2 * (int64_t)m.nwg > kd::kStageWords) return KD_ERR_UNSUPPORTED;
+  // rows one wave's packet range can span, for every row-split tile of every workgroup
+  auto max_rows = [&](auto rows_of, int64_t C) {
     int64_t worst = 0;
     for (int64_t w = 0; w < m.nwg; ++w) {
-      const int64_t R = kd::part_lo(nrows_total, m.nwg, w + 1) - kd::part_lo(nrows_total, m.nwg, w);
-      const int64_t T = R * C;
-      for (int v = 0; v < kd::kComputeWaves; ++v) {
-        const int64_t lo = kd::part_lo(T, kd::kComputeWaves, v), hi = kd::part_lo(T, kd::kComputeWaves, v + 1);
+      const int64_t T = rows_of(w) * C;
+      for (int v = 0; v < kd::kWaves; ++v) {
+        const int64_t lo = kd::part_lo(T, kd::kWaves, v), hi = kd::part_lo(T, kd::kWaves, v + 1);
         if (hi > lo) worst = std::max(worst, (hi - 1) / C - lo / C + 1);
       }
     }
     return worst;
   };
-  if (max_segs(m.nqkv, m.cd) > kd::kSegR || max_segs(m.d, m.cq) > kd::kSegR || max_segs(m.V, m.cd) > kd::kSegR)
+  auto rows_qkv = [&](int64_t w) { return kd::part_lo(m.nqkv, m.nwg, w + 1) - kd::part_lo(m.nqkv, m.nwg, w); };
+  auto rows_o = [&](int64_t w) { return 2 * (kd::part_lo(m.d / 2, m.nwg, w + 1) - kd::part_lo(m.d / 2, m.nwg, w)); };
+  auto rows_gu = [&](int64_t w) { return 2 * (kd::ffn_lo(m, w + 1) - kd::ffn_lo(m, w)); };
+  auto rows_lm = [&](int64_t w) { return kd::part_lo(m.V, m.nwg, w + 1) - kd::part_lo(m.V, m.nwg, w); };
+  if (max_rows(rows_qkv, m.cd) > kd::kRowPart || max_rows(rows_o, m.cq) > kd::kRowPart ||
+      max_rows(rows_gu, m.cd) > kd::kRowPart || max_rows(rows_lm, m.cd) > kd::kRowPart)
     return KD_ERR_UNSUPPORTED;
-  for (int64_t w = 0; w < m.nwg; ++w) {
-    const int64_t nf = kd::ffn_lo(m, w + 1) - kd::ffn_lo(m, w);
-    const int64_t Tgu = 2 * nf * m.cd, g = nf / m.vpl, Td = (m.d / 64) * g;
-    for (int v = 0; v < kd::kComputeWaves; ++v) {
-      const int64_t lo = kd::part_lo(Tgu, kd::kComputeWaves, v), hi = kd::part_lo(Tgu, kd::kComputeWaves, v + 1);
-      if (hi > lo && (hi - 1) / m.cd - lo / m.cd + 1 > kd::kSegR) return KD_ERR_UNSUPPORTED;
-      const int64_t dlo = kd::part_lo(Td, kd::kComputeWaves, v), dhi = kd::part_lo(Td, kd::kComputeWaves, v + 1);
-      if (dhi > dlo && (dhi - 1) / g - dlo / g + 1 > kd::kSegC) return KD_ERR_UNSUPPORTED;
-    }
-  }
   // attention split at every position the cache can hold
   for (int32_t p = 0; p < c->max_seq; ++p) {
     const kd::AttPlan a = kd::att_plan(m, p);
     if (a.NC > kd::max_chunks(m)) return KD_ERR_UNSUPPORTED;
-    if ((int64_t)a.NC * (a.MS + 2) > kd::kMergeWords + 64) return KD_ERR_UNSUPPORTED;
-    const int64_t pk = kd::ceil_div(a.CH, m.ppp);
-    if (kd::ceil_div(pk, kd::kComputeWaves) * m.ppp > kd::kScorePos) return KD_ERR_UNSUPPORTED;
+    if (kd::ceil_div(a.units, m.nwg) > kd::kMaxUnits) return KD_ERR_UNSUPPORTED;
+    if ((int64_t)a.NC * (a.MS + 2) > kd::kStageWords || a.MS % 2 != 0) return KD_ERR_UNSUPPORTED;
+    const int64_t pk = kd::ceil_div(a.CH, m.ppp);  // packets of one chunk
+    if (kd::ceil_div(pk, kd::kWaves) * m.ppp > kd::kScorePos) return KD_ERR_UNSUPPORTED;
   }
   return KD_OK;
 }
@@ -216,6 +218,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
     if (hipMalloc(&h->buf.embed, (size_t)m.V * d * wb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     if (hipMalloc(&h->buf.norms, (size_t)(2 * m.L + 1) * d * wb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     if (hipMalloc(&h->buf.ll, (size_t)h->lo.total * 8) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
+    if (hipMalloc(&h->buf.rope, (size_t)m.S * (m.hd / 2) * sizeof(float2)) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     if (hipMalloc(&h->buf.flags, 256) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     if (hipMalloc(&tmp, (size_t)2 * m.F * d * wb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     KD_TRY(hipMemset(h->buf.ll, 0, (size_t)h->lo.total * 8));
@@ -253,6 +256,19 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
     KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * m.L) * row, w->final_norm, row, hipMemcpyHostToDevice));
     KD_TRY(hipMemcpy(h->buf.blob + (size_t)m.off_lm * wb, w->lm_head, (size_t)m.V * row, hipMemcpyHostToDevice));
     KD_TRY(hipMemcpy(h->buf.embed, w->embed, (size_t)m.V * row, hipMemcpyHostToDevice));
+    {
+      // RoPE: pair (i, i + hd/2) turns by position * base^(-2i/hd); angles, cos and sin in float64
+      const int half = m.hd / 2;
+      std::vector<float2> tab((size_t)m.S * half);
+      std::vector<double> theta(half);
+      for (int i = 0; i < half; ++i) theta[i] = std::pow((double)cfg->rope_base, -2.0 * (double)i / (double)m.hd);
+      for (int64_t pos = 0; pos < m.S; ++pos)
+        for (int i = 0; i < half; ++i) {
+          const double ang = (double)pos * theta[i];
+          tab[(size_t)pos * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+        }
+      KD_TRY(hipMemcpy(h->buf.rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice));
+    }
     KD_TRY(hipDeviceSynchronize());
     (void)hipFree(tmp);
     tmp = nullptr;
@@ -276,6 +292,7 @@ int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* 
   P.blob = h->buf.blob;
   P.embed = h->buf.embed;
   P.norms = h->buf.norms;
+  P.rope = h->buf.rope;
   P.ll = h->buf.ll;
   P.lo = h->lo;
   P.kv = (uint8_t*)kv;
@@ -289,7 +306,6 @@ int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* 
   P.seq = h->seq;
   P.max_seq = h->cfg.max_seq;
   P.eps = h->cfg.norm_eps;
-  P.rope_base = h->cfg.rope_base;
   P.m = h->m;
   void* args[] = {&P};
   // One workgroup per compute unit, and a workgroup needs most of a CU's LDS, so on an idle

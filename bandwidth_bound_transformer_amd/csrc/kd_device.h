@@ -2,43 +2,43 @@
 //
 // One launch runs a whole decode step: embedding, every layer, LM head and argmax.
 //
-// Grid. One workgroup per compute unit. Every workgroup stays resident for the
-// whole step, as in the single-kernel runtime of the Kog engine ("Real-time LLM
-// inference on standard data-centre GPUs (3,000 tokens/s single request)",
-// section "technical principles"). A workgroup has 8 waves:
+// Grid. One workgroup per compute unit, resident for the whole step, as in the
+// single-kernel runtime of the Kog engine ("Real-time LLM inference on standard
+// data-centre GPUs (3,000 tokens/s single request)", section "technical
+// principles"). A workgroup has 8 waves, and all of them do the same kind of work:
 //
-//  * Waves 1..7 are compute waves. Each streams a fixed, precomputed sequence
-//    of 1 KB packets: its share of every weight tile of the step, plus its
-//    share of the KV positions its workgroup attends over. Packets arrive
-//    through a private ring in LDS, filled by LDS-DMA loads
-//    (global_load_lds_dwordx4, non-temporal). The loads run RING packets
-//    ahead of the consumer, straight across phase boundaries. Weights do not
-//    depend on activations, so HBM keeps streaming while the workgroup waits
-//    for the previous phase's results. This is the single-GPU form of "keep
-//    computing and synchronise later" ("Kog 3000 tok/s real-time inference",
-//    section "KCCL").
-//  * Wave 0 is the control wave. It never has weight loads in flight, so its
-//    waits are short. It collects the vectors other workgroups produced, runs
-//    RMSNorm, RoPE and softmax merges, reduces the compute waves' partial
-//    sums, and publishes this workgroup's results.
+//  * Streaming. Each wave walks a fixed sequence of 1 KB packets: its share of
+//    every weight tile of the step, plus its share of the KV positions of its
+//    workgroup's attention units. Packets arrive through a private ring in LDS,
+//    filled by LDS-DMA loads (global_load_lds_dwordx4, non-temporal). The loads
+//    run up to RING packets ahead, straight across phase boundaries. Weights do
+//    not depend on activations, so HBM keeps streaming while the workgroup
+//    waits for the previous phase's results. This is the single-GPU form of
+//    "keep computing and synchronise later" ("Kog 3000 tok/s real-time
+//    inference", section "KCCL").
+//  * Exchange. Between phases every wave helps gather the vector the next
+//    phase needs. All 512 lanes poll at once, so one round of 16-byte loads
+//    covers up to 4096 values.
 //
-// Exchange between workgroups. Vectors travel as "LL words": 64-bit words with
-// a float in the low half and a tag in the high half. They are written with
-// device-scope relaxed atomic stores and read with device-scope loads (sc1).
+// Exchange between workgroups. Vectors travel as "exchange words": 64-bit words
+// with a float in the low half and a tag in the high half. They are written with
+// device-scope relaxed atomic stores and read with device-scope 16-byte loads.
 // A tag names the step, layer and vector kind, so a reader spins until every
-// word it needs carries the expected tag. One round trip therefore does both
-// the synchronisation and the data transfer, with no grid-wide barrier and no
-// L2 writeback or invalidate. Each word is one naturally aligned 64-bit
-// atomic, so a reader never accepts a stale or torn value.
+// word it needs carries the expected tag. One round trip therefore does both the
+// synchronisation and the data transfer, with no grid-wide barrier and no L2
+// writeback or invalidate. Each word is one naturally aligned 64-bit store, so a
+// reader never accepts a stale or torn value. Every producer writes its part of
+// a vector as one contiguous run.
 //
 // Layer dataflow (WG = workgroup; every WG does each step for its own slice):
-//   x --gather--> RMSNorm --> QKV rows (row-split)      --> LL qkv
-//   q,k,v --gather--> RoPE, KV append, attention over one chunk of positions --> LL partials
-//   partials --gather--> merge (log-sum-exp) of one head slice --> LL o
-//   o --gather--> O rows + residual (row-split)        --> LL x'
-//   x' --gather--> RMSNorm --> gate/up rows of this WG's FFN slice --> SiLU*up stays in LDS
-//   local FFN slice --> down projection of that slice for all d rows --> LL partial sums
-//   partial sums for this WG's rows --gather--> sum + residual --> LL x
+//   x --gather--> RMSNorm --> QKV rows (row split)           --> qkv words
+//   q,k,v of one kv head --gather--> RoPE, KV append, attention over a chunk of positions
+//                                                            --> partial (max, sum, acc) words
+//   partials of one head slice --gather--> log-sum-exp merge --> o words
+//   o --gather--> O rows + residual (row split)              --> x' words
+//   x' --gather--> RMSNorm --> gate/up rows of this WG's FFN slice; SiLU(gate)*up stays in LDS
+//   FFN slice --> down projection of the slice for all d rows --> partial words (per producer)
+//   partials of this WG's rows --gather--> fixed-order sum + residual --> x words
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -50,6 +50,7 @@ struct Params {
   const uint8_t* blob;   // packed layer weights and LM head, weight dtype
   const uint8_t* embed;  // [V][d], weight dtype
   const uint8_t* norms;  // [L][2][d] attention/FFN gains, then final gain [d], weight dtype
+  const float2* rope;    // [S][hd/2] (cos, sin) of position * theta_i
   uint64_t* ll;          // exchange words
   LLLayout lo;
   uint8_t* kv;           // caller's cache [L][2][B][hkv][S][hd]
@@ -62,12 +63,13 @@ struct Params {
   uint32_t seq;
   int32_t max_seq;
   float eps;
-  float rope_base;
   Dims m;
 };
 
 constexpr uint32_t kStatusTokenRange = 0x1u, kStatusPosOverflow = 0x2u, kStatusTimeout = 0x4u, kStatusNaN = 0x8u;
 constexpr uint64_t kSpinTicks = 200000000ull;  // 2 s of the 100 MHz realtime counter
+constexpr int kMaxRowsD = 64;                  // most d rows one workgroup owns
+constexpr int kMaxSlice = 128;                 // most FFN columns one workgroup owns
 
 // ----------------------------------------------------------------------------------------------
 // small helpers
@@ -86,6 +88,7 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
 }
 
+// Butterfly sums: every lane ends with the bitwise-same total.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -102,8 +105,12 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier that waits for LDS traffic only. Each wave's LDS-DMA loads stay in flight
+// across it; that is the point of the ring.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // 64 lanes x 16 bytes from per-lane global addresses into LDS [lds_addr, lds_addr + 1 KB).
-// Non-temporal: weights and KV are read once per step.  Waits for this wave's earlier LDS reads
+// Non-temporal: weights and KV are read once per step. Waits for this wave's earlier LDS reads
 // first, so a slot is never refilled while a read of it is still in flight.
 __device__ __forceinline__ void dma_packet(const void* lane_addr, uint32_t lds_addr) {
   uint32_t saved;
@@ -122,7 +129,7 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// device-scope (sc1) 16-byte load of two LL words, bounds-checked by the buffer descriptor
+// device-scope (sc1) 16-byte load of two exchange words, bounds-checked by the buffer descriptor
 __device__ __forceinline__ uint4 ll_load2(__amdgpu_buffer_rsrc_t r, int64_t word) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(word * 8), 0, 16));
 }
@@ -150,17 +157,16 @@ __device__ __forceinline__ float load_w(const uint8_t* base, int64_t i) {
 // 32-bit plan arithmetic for the device (every count here fits in 31 bits)
 // ----------------------------------------------------------------------------------------------
 __device__ __forceinline__ int p_lo(int n, int parts, int i) { return (int)(((uint32_t)n * (uint32_t)i) / (uint32_t)parts); }
-__device__ __forceinline__ int p_of(int n, int parts, int i) { return (int)(((uint32_t)parts * (uint32_t)i + (uint32_t)parts - 1u) / (uint32_t)n); }
 __device__ __forceinline__ int c_div(int a, int b) { return (a + b - 1) / b; }
 __device__ __forceinline__ int ffn_lo32(const Dims& m, int w) { return m.vpl * p_lo(m.F / m.vpl, m.nwg, w); }
+// d rows are owned in pairs, so every workgroup's run of exchange words starts 16-byte aligned
+__device__ __forceinline__ int drow_lo(const Dims& m, int w) { return 2 * p_lo(m.d / 2, m.nwg, w); }
 
 // ----------------------------------------------------------------------------------------------
-// shared memory
+// the packet sequence of each wave
 // ----------------------------------------------------------------------------------------------
-constexpr int kMaxUnits = 16;  // attention units one workgroup handles in one step
-
-// One contiguous run of packets in a compute wave's sequence. `base` is the address of packet 0
-// at layer 0; kind says how it moves with the layer.
+// One contiguous run of packets. `base` is the address of packet 0 at layer 0; kind says how it
+// moves with the layer.
 enum SegKind : int32_t { kSegWeight = 0, kSegKV = 1, kSegOnce = 2 };
 struct SegEntry {
   const uint8_t* base;
@@ -168,43 +174,43 @@ struct SegEntry {
   int32_t kind, pad;
 };
 
-// Per-layer order of a compute wave's segments: QKV, (K, V) of each attention unit, O, gate/up, down.
+// Per-layer order of a wave's segments: QKV, (K, V) of each attention unit, O, gate/up, down.
 __device__ __forceinline__ int seg_o(int nunits) { return 1 + 2 * nunits; }
 
 enum Tile : int { kTileQKV = 0, kTileO = 1, kTileGU = 2, kTileD = 3, kTileLM = 4, kTiles = 5 };
 
 template <int RING>
 struct Smem {
-  uint4 ring[kComputeWaves][RING][64];
-  float x[kMaxDim];    // residual stream x (or x') of the current layer
-  float act[kMaxDim];  // input of the current projection (normalised x, o, or the FFN slice)
+  uint4 ring[kWaves][RING][64];
+  float act[kMaxDim];  // input of the current projection; during attention: per-wave accumulators
   union {
-    float part_r[kComputeWaves][kSegR];      // per-wave row sums
-    float part_c[kComputeWaves][kSegC][64];  // per-wave 64-row block sums (down projection)
+    float stage[kStageWords];  // merge partials, down-projection partials of this WG's rows
     struct {
-      float q[kMaxGroup][kMaxHeadDim];       // rotated queries of this unit's kv head, times 1/sqrt(hd)
-      float kp[kMaxHeadDim];                 // K and V of the current position, as stored
+      float q[kMaxGroup][kMaxHeadDim];  // rotated queries of this unit's kv head, times 1/sqrt(hd)
+      float kp[kMaxHeadDim];            // K and V of the current position, as stored
       float vp[kMaxHeadDim];
-      float scores[kComputeWaves][kScorePos][kMaxGroup];
-      float acc[kComputeWaves][kMaxGroup][kMaxHeadDim];
-      float ml[kComputeWaves][kMaxGroup][2];
+      float scores[kWaves][kScorePos][kMaxGroup];
+      float ml[kWaves][kMaxGroup][2];
+      float sp[kMaxGroup];  // score of the current position
     } att;
-    float stage[kMergeWords + 64];
   } u;
-  SegEntry segs[kComputeWaves][4 + 2 * kMaxUnits];
-  SegEntry lm_seg[kComputeWaves];
-  int32_t split[kTiles][kComputeWaves + 1];  // wave boundaries of each tile (packets)
-  int32_t first[kTiles][kComputeWaves];      // first row / block of each wave's share
+  float rowpart[kWaves][kRowPart];  // per-wave row sums of the current tile
+  float xo[kMaxRowsD];              // this WG's rows of x (then x')
+  float a[kMaxSlice];               // SiLU(gate)*up of this WG's FFN slice
   float rope_c[kMaxHeadDim / 2];
   float rope_s[kMaxHeadDim / 2];
+  float red[kWaves];
+  int32_t redi[kWaves];
+  SegEntry segs[kWaves][4 + 2 * kMaxUnits];
+  SegEntry lm_seg[kWaves];
+  int32_t split[kTiles][kWaves + 1];  // wave boundaries of each tile (packets)
+  int32_t first[kTiles][kWaves];      // first row / block of each wave's share
   int abort_flag;
 };
 
-// ----------------------------------------------------------------------------------------------
-// step-level facts every wave derives from the inputs
-// ----------------------------------------------------------------------------------------------
+// step-level facts every workgroup derives from the inputs
 struct StepInfo {
-  int32_t p;       // position of the input token
+  int32_t p;  // position of the input token
   AttPlan ap;
   int32_t nunits;  // attention units of this workgroup
 };
@@ -229,44 +235,60 @@ __device__ __forceinline__ Unit unit_of(const StepInfo& si, int w, int k, int nw
 // Packets of each tile of workgroup w, and how many packets a row (or 64-row block) spans.
 __device__ __forceinline__ void tile_shape(const Dims& m, int w, int tile, int& T, int& C) {
   if (tile == kTileQKV) { C = m.cd; T = (p_lo(m.nqkv, m.nwg, w + 1) - p_lo(m.nqkv, m.nwg, w)) * C; }
-  else if (tile == kTileO) { C = m.cq; T = (p_lo(m.d, m.nwg, w + 1) - p_lo(m.d, m.nwg, w)) * C; }
+  else if (tile == kTileO) { C = m.cq; T = (drow_lo(m, w + 1) - drow_lo(m, w)) * C; }
   else if (tile == kTileGU) { C = m.cd; T = 2 * (ffn_lo32(m, w + 1) - ffn_lo32(m, w)) * C; }
   else if (tile == kTileD) { C = (ffn_lo32(m, w + 1) - ffn_lo32(m, w)) / m.vpl; T = (m.d / 64) * C; }
   else { C = m.cd; T = (p_lo(m.V, m.nwg, w + 1) - p_lo(m.V, m.nwg, w)) * C; }
 }
 
-// Fill compute wave v's segment table (done by the wave itself).
+// Packet range [lo, hi) of wave v in a tile. The down tile is cut at whole 64-row blocks, so each
+// block's sum is finished by one wave.
+__device__ __forceinline__ void wave_range(const Dims& m, int w, int tile, int v, int& lo, int& hi) {
+  int T, C;
+  tile_shape(m, w, tile, T, C);
+  if (tile == kTileD) {
+    const int nb = m.d / 64;
+    lo = p_lo(nb, kWaves, v) * C;
+    hi = p_lo(nb, kWaves, v + 1) * C;
+  } else {
+    lo = p_lo(T, kWaves, v);
+    hi = p_lo(T, kWaves, v + 1);
+  }
+}
+
+// Fill wave v's segment table (done by the wave itself).
 template <int RING>
 __device__ __forceinline__ void build_segments(const Params& P, const StepInfo& si, int w, int v, Smem<RING>& sm) {
   const Dims& m = P.m;
   if (lane_id() != 0) return;
-  auto put = [&](SegEntry& e, const uint8_t* base, int T, int kind) {
+  auto put = [&](SegEntry& e, const uint8_t* base, int lo, int hi, int kind) {
     e.base = base;
-    e.lo = p_lo(T, kComputeWaves, v);
-    e.hi = p_lo(T, kComputeWaves, v + 1);
+    e.lo = lo;
+    e.hi = hi;
     e.kind = kind;
+    e.pad = 0;
   };
   SegEntry* t = sm.segs[v];
-  int T, C;
-  tile_shape(m, w, kTileQKV, T, C);
-  put(t[0], P.blob + (m.off_qkv + (int64_t)p_lo(m.nqkv, m.nwg, w) * m.d) * m.wbytes, T, kSegWeight);
+  int lo, hi;
+  wave_range(m, w, kTileQKV, v, lo, hi);
+  put(t[0], P.blob + (m.off_qkv + (int64_t)p_lo(m.nqkv, m.nwg, w) * m.d) * m.wbytes, lo, hi, kSegWeight);
   for (int k = 0; k < si.nunits; ++k) {
     const Unit u = unit_of(si, w, k, m.nwg);
     const int n = u.j1 > u.j0 ? c_div(u.j1 - u.j0, m.ppp) : 0;
     const int64_t kbase = (((int64_t)0 * 2 + 0) * m.hkv + u.g) * m.S + u.j0;
     const int64_t vbase = (((int64_t)0 * 2 + 1) * m.hkv + u.g) * m.S + u.j0;
-    put(t[1 + 2 * k], P.kv + kbase * m.hd * m.kvbytes, n, kSegKV);
-    put(t[2 + 2 * k], P.kv + vbase * m.hd * m.kvbytes, n, kSegKV);
+    put(t[1 + 2 * k], P.kv + kbase * m.hd * m.kvbytes, p_lo(n, kWaves, v), p_lo(n, kWaves, v + 1), kSegKV);
+    put(t[2 + 2 * k], P.kv + vbase * m.hd * m.kvbytes, p_lo(n, kWaves, v), p_lo(n, kWaves, v + 1), kSegKV);
   }
   const int o = seg_o(si.nunits);
-  tile_shape(m, w, kTileO, T, C);
-  put(t[o], P.blob + (m.off_o + (int64_t)p_lo(m.d, m.nwg, w) * m.qdim) * m.wbytes, T, kSegWeight);
-  tile_shape(m, w, kTileGU, T, C);
-  put(t[o + 1], P.blob + (m.off_gu + (int64_t)2 * ffn_lo32(m, w) * m.d) * m.wbytes, T, kSegWeight);
-  tile_shape(m, w, kTileD, T, C);
-  put(t[o + 2], P.blob + (m.off_d + (int64_t)m.d * ffn_lo32(m, w)) * m.wbytes, T, kSegWeight);
-  tile_shape(m, w, kTileLM, T, C);
-  put(sm.lm_seg[v], P.blob + (m.off_lm + (int64_t)p_lo(m.V, m.nwg, w) * m.d) * m.wbytes, T, kSegOnce);
+  wave_range(m, w, kTileO, v, lo, hi);
+  put(t[o], P.blob + (m.off_o + (int64_t)drow_lo(m, w) * m.qdim) * m.wbytes, lo, hi, kSegWeight);
+  wave_range(m, w, kTileGU, v, lo, hi);
+  put(t[o + 1], P.blob + (m.off_gu + (int64_t)2 * ffn_lo32(m, w) * m.d) * m.wbytes, lo, hi, kSegWeight);
+  wave_range(m, w, kTileD, v, lo, hi);
+  put(t[o + 2], P.blob + (m.off_d + (int64_t)m.d * ffn_lo32(m, w)) * m.wbytes, lo, hi, kSegWeight);
+  wave_range(m, w, kTileLM, v, lo, hi);
+  put(sm.lm_seg[v], P.blob + (m.off_lm + (int64_t)p_lo(m.V, m.nwg, w) * m.d) * m.wbytes, lo, hi, kSegOnce);
 }
 
 // Walks this wave's packet sequence ahead of the consumer and issues the loads.
@@ -299,7 +321,8 @@ struct Issuer {
       next_entry();
     }
   }
-  // Issue the next packet of the sequence into an LDS slot; past the end, reload the last one.
+  // Issue the next packet of the sequence into an LDS slot; past the end, reload the last one,
+  // so that every slot is always covered by exactly one load in flight.
   __device__ __forceinline__ void issue(uint32_t slot_addr) {
     const uint8_t* a = last;
     if (layer <= L) {
@@ -319,6 +342,8 @@ struct Ring {
   uint32_t cnt;
   Issuer is;
   __device__ __forceinline__ uint4 take() const {
+    // RING loads were issued after the oldest one's slot was last refilled, minus nothing: any
+    // other memory operation issued since only makes this wait longer, never shorter.
     wait_vm<RING - 1>();
     return slots[(cnt % RING) * 64 + lane_id()];
   }
@@ -365,8 +390,9 @@ __device__ __forceinline__ void unpack16(const uint4 w, float* out) {
   }
 }
 
-// Row-split matrix-vector product: packets are row chunks of 64*vpl values; act is the input vector.
-// A row's lane sums are reduced across the wave when the row (or this wave's share of it) ends.
+// Row-split matrix-vector product over packets [s.lo, s.hi): packets are row chunks of 64*vpl
+// values; act is the input vector. A row's lane sums are reduced across the wave when the row (or
+// this wave's share of it) ends; part[r - first row] receives the wave's sum.
 template <int RING, int WB>
 __device__ __forceinline__ void consume_rows(Ring<RING>& rg, const SegEntry& s, int C, const float* act, float* part) {
   constexpr int VPL = 16 / WB;
@@ -389,22 +415,23 @@ __device__ __forceinline__ void consume_rows(Ring<RING>& rg, const SegEntry& s, 
   }
 }
 
-// Column-block product of the down projection: packets hold 64 rows x vpl columns of this
-// workgroup's FFN slice; every lane owns one row, and all lanes read the same slice values.
+// Down projection of this WG's FFN slice over the wave's whole 64-row blocks: packets hold 64 rows
+// x vpl columns; lane l owns row 64*b + l, and all lanes read the same slice values. Each finished
+// block is published at once as 64 contiguous exchange words.
 template <int RING, int WB>
-__device__ __forceinline__ void consume_cols(Ring<RING>& rg, const SegEntry& s, int g, const float* a, float* part /* [kSegC][64] */) {
+__device__ __forceinline__ void consume_down(Ring<RING>& rg, const SegEntry& s, int g, const float* a, uint64_t* ll,
+                                             int64_t dp_at, uint32_t tag) {
   constexpr int VPL = 16 / WB;
   const int lane = lane_id();
   int b = s.lo / g;
-  const int b_first = b;
-  int j = s.lo - b * g;
+  int j = 0;
   float acc = 0.f;
   for (int i = s.lo; i < s.hi; ++i) {
     const uint4 wv = rg.take();
     acc += dot16<WB>(wv, a + j * VPL);
     rg.give();
-    if (++j == g || i + 1 == s.hi) {
-      part[(b - b_first) * 64 + lane] = acc;
+    if (++j == g) {
+      ll_store(ll, dp_at + (int64_t)b * 64 + lane, acc, tag);
       acc = 0.f;
       j = 0;
       ++b;
@@ -414,9 +441,10 @@ __device__ __forceinline__ void consume_cols(Ring<RING>& rg, const SegEntry& s, 
 
 // Scores, then the exp-weighted V sum, of one attention unit over this wave's share of the
 // unit's cached positions. lpp lanes hold one position; each lane holds kv_vpl of its dims.
+// Leaves (max, sum) in ml[v] and the weighted V sums in accv[h][hd].
 template <int RING, int KB, int HD>
 __device__ __forceinline__ void consume_attention(Ring<RING>& rg, const SegEntry& sk, const Unit& u, int G, Smem<RING>& sm,
-                                                  int v) {
+                                                  int v, float* accv) {
   constexpr int KVPL = 16 / KB;
   constexpr int LPP = HD / KVPL;
   constexpr int PPP = 64 / LPP;
@@ -499,7 +527,7 @@ __device__ __forceinline__ void consume_attention(Ring<RING>& rg, const SegEntry
     if (h < G) {
       if (lane < LPP) {
 #pragma unroll
-        for (int k = 0; k < KVPL; ++k) sm.u.att.acc[v][h][dim0 + k] = acc[h][k];
+        for (int k = 0; k < KVPL; ++k) accv[h * HD + dim0 + k] = acc[h][k];
       }
       if (lane == 0) {
         sm.u.att.ml[v][h][0] = mh[h];
@@ -510,15 +538,13 @@ __device__ __forceinline__ void consume_attention(Ring<RING>& rg, const SegEntry
 }
 
 // ----------------------------------------------------------------------------------------------
-// control wave: exchange, normalisation, reductions
+// exchange
 // ----------------------------------------------------------------------------------------------
 template <int RING>
-struct Ctl {
+struct Xchg {
   const Params& P;
   __amdgpu_buffer_rsrc_t llr;
   Smem<RING>& sm;
-
-  __device__ __forceinline__ bool failed() const { return sm.abort_flag != 0; }
 
   __device__ __forceinline__ void fail(uint32_t bit) {
     if (lane_id() == 0) {
@@ -528,108 +554,98 @@ struct Ctl {
     sm.abort_flag = 1;
   }
 
-  // Collect npieces 16-byte pieces (two LL words each) at word offsets off(k), wait until both
-  // words of every piece carry `tag`, then hand the two floats of piece k to sink(k, a, b).
+  // All 512 threads: collect npieces 16-byte pieces (two exchange words each) at word offsets
+  // off(k); each wave waits until both words of each of its pieces carry `tag`, then hands the two
+  // floats of piece k to sink(k, a, b). Ends with a workgroup barrier; returns false if the step
+  // was abandoned (timeout here or elsewhere).
   template <class Off, class Sink>
-  __device__ __forceinline__ void gather(uint32_t tag, int npieces, Off off, Sink sink) {
-    constexpr int NB = 8;
-    const int lane = lane_id();
-    for (int base = 0; base < npieces; base += 64 * NB) {
-      if (failed()) return;
+  __device__ __forceinline__ bool gather(uint32_t tag, int npieces, Off off, Sink sink) {
+    constexpr int NB = 4;
+    const int tid = (int)threadIdx.x;
+    for (int base = 0; base < npieces; base += kThreads * NB) {
       uint4 val[NB];
       uint64_t t0 = 0;
       bool started = false;
-      while (true) {
+      bool dead = false;
+      for (int spin = 0;; ++spin) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-          const int k = base + lane + 64 * i;
+          const int k = base + tid + kThreads * i;
           if (k < npieces) val[i] = ll_load2(llr, off(k));
         }
         bool ok = true;
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-          const int k = base + lane + 64 * i;
+          const int k = base + tid + kThreads * i;
           if (k < npieces) ok = ok && val[i].y == tag && val[i].w == tag;
         }
         if (__all(ok)) break;
         if (!started) { t0 = now_ticks(); started = true; }
-        if (now_ticks() - t0 > kSpinTicks) { fail(kStatusTimeout); return; }
-        if (ld_flag(P.abortf)) { sm.abort_flag = 1; return; }
-        __builtin_amdgcn_s_sleep(1);
+        if ((spin & 15) == 15) {
+          if (now_ticks() - t0 > kSpinTicks) { fail(kStatusTimeout); dead = true; break; }
+          if (ld_flag(P.abortf) || sm.abort_flag) { sm.abort_flag = 1; dead = true; break; }
+        }
       }
+      if (dead) break;
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const int k = base + lane + 64 * i;
+        const int k = base + tid + kThreads * i;
         if (k < npieces) sink(k, __uint_as_float(val[i].x), __uint_as_float(val[i].z));
       }
     }
+    wg_barrier();
+    return sm.abort_flag == 0;
   }
 
-  // Gather n consecutive LL words (n even) starting at word `at` into dst[0..n).
-  __device__ __forceinline__ void gather_vec(uint32_t tag, int64_t at, int n, float* dst) {
-    gather(tag, n / 2, [&](int k) { return at + 2 * (int64_t)k; },
-           [&](int k, float a, float b) {
-             dst[2 * k] = a;
-             dst[2 * k + 1] = b;
-           });
-  }
-
-  template <int WB>
-  __device__ __forceinline__ void rmsnorm(const float* x, const uint8_t* gain, float* out, int d) {
-    const int lane = lane_id();
-    float ss = 0.f;
-    for (int i = lane; i < d; i += 64) ss = fmaf(x[i], x[i], ss);
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)d + P.eps);
-    for (int i = lane; i < d; i += 64) out[i] = x[i] * r * load_w<WB>(gain, i);
-  }
-
-  // Boundaries of every tile's wave shares, for the reductions below.
-  __device__ __forceinline__ void build_splits(int w) {
-    const int lane = lane_id();
-    if (lane < kTiles) {
-      int T, C;
-      tile_shape(P.m, w, lane, T, C);
-      for (int v = 0; v <= kComputeWaves; ++v) sm.split[lane][v] = p_lo(T, kComputeWaves, v);
-      for (int v = 0; v < kComputeWaves; ++v) sm.first[lane][v] = C > 0 ? sm.split[lane][v] / C : 0;
-    }
-  }
-
-  // Total of row r (C packets per row) of a tile over the compute waves that touched it.
-  __device__ __forceinline__ float row_total(int tile, int C, int r) const {
-    const int a = r * C, b = a + C;
-    float s = 0.f;
-    for (int v = 0; v < kComputeWaves; ++v) {
-      const int lo = sm.split[tile][v], hi = sm.split[tile][v + 1];
-      if (lo < hi && lo < b && hi > a) s += sm.u.part_r[v][r - sm.first[tile][v]];
-    }
-    return s;
-  }
-  __device__ __forceinline__ float block_total(int g, int blk, int lane) const {
-    const int a = blk * g, b = a + g;
-    float s = 0.f;
-    for (int v = 0; v < kComputeWaves; ++v) {
-      const int lo = sm.split[kTileD][v], hi = sm.split[kTileD][v + 1];
-      if (lo < hi && lo < b && hi > a) s += sm.u.part_c[v][blk - sm.first[kTileD][v]][lane];
-    }
-    return s;
+  // Gather n consecutive exchange words (n even) starting at word `at` into dst[0..n).
+  __device__ __forceinline__ bool gather_vec(uint32_t tag, int64_t at, int n, float* dst) {
+    return gather(tag, n / 2, [&](int k) { return at + 2 * (int64_t)k; },
+                  [&](int k, float a, float b) {
+                    dst[2 * k] = a;
+                    dst[2 * k + 1] = b;
+                  });
   }
 };
+
+// RMSNorm of act[0..d) in place, times the gain; all threads; fixed summation order.
+template <int RING, int WB>
+__device__ __forceinline__ void rmsnorm(Smem<RING>& sm, const uint8_t* gain, int d, float eps) {
+  const int tid = (int)threadIdx.x, lane = lane_id(), wave = wave_id();
+  float ss = 0.f;
+  for (int i = tid; i < d; i += kThreads) ss = fmaf(sm.act[i], sm.act[i], ss);
+  ss = wave_sum(ss);
+  if (lane == 0) sm.red[wave] = ss;
+  wg_barrier();
+  float tot = 0.f;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) tot += sm.red[v];
+  const float r = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int i = tid; i < d; i += kThreads) sm.act[i] = sm.act[i] * r * load_w<WB>(gain, i);
+  wg_barrier();
+}
+
+// Total of row r (C packets per row) of a tile over the waves that touched it, in wave order.
+template <int RING>
+__device__ __forceinline__ float row_total(const Smem<RING>& sm, int tile, int C, int r) {
+  const int a = r * C, b = a + C;
+  float s = 0.f;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    const int lo = sm.split[tile][v], hi = sm.split[tile][v + 1];
+    if (lo < hi && lo < b && hi > a) s += sm.rowpart[v][r - sm.first[tile][v]];
+  }
+  return s;
+}
+
+// Timestamp slot of phase-boundary `ev` (layer < L) or of the final phases (layer == L).
+__device__ __forceinline__ int trace_slot(int layer, int ev) { return 2 + kTraceLayerEvents * layer + ev; }
 
 // ----------------------------------------------------------------------------------------------
 // the kernel
 // ----------------------------------------------------------------------------------------------
-// Workgroup barrier that waits for this wave's LDS traffic only. Compute waves keep their
-// LDS-DMA loads in flight across it; that is the point of the ring.
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Timestamp slot of phase-boundary `ev` (layer < L) or of the final phases (layer == L).
-__device__ __forceinline__ int trace_slot(int L, int layer, int ev) { return 2 + kTraceLayerEvents * layer + ev; }
-
-// Phase protocol. Every phase runs as: control prepares the input in LDS; barrier B; compute
-// waves stream their packets into per-wave partial sums; barrier A; control reduces and
-// publishes. A failed wait sets the LDS abort flag before the next barrier B. All waves read the
-// flag right after B and leave together, so the barrier sequences of the waves always match.
+// Every wave executes the same sequence of workgroup barriers. A failed wait sets the LDS abort
+// flag before the barrier that ends its gather; all waves test the flag right after that barrier
+// and leave together, after their LDS-DMA loads have landed.
 template <int RING, int WB, int KB, int HD>
 __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P_arg) {
   __shared__ Smem<RING> sm;
@@ -637,15 +653,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   const Params P = P_arg;
   const Dims m = P.m;
   const int w = (int)blockIdx.x;
+  const int tid = (int)threadIdx.x;
   const int wave = wave_id();
   const int lane = lane_id();
 
-  // inputs of this step; every wave of every workgroup takes the same decision
+  // inputs of this step; every thread of every workgroup takes the same decision
   StepInfo si{};
   const int32_t token = P.tokens[0];
   si.p = P.positions[0];
   if (token < 0 || token >= m.V || si.p < 0 || si.p >= P.max_seq) {
-    if (w == 0 && threadIdx.x == 0) {
+    if (w == 0 && tid == 0) {
       uint32_t bit = (token < 0 || token >= m.V) ? kStatusTokenRange : 0u;
       if (si.p < 0 || si.p >= P.max_seq) bit |= kStatusPosOverflow;
       __hip_atomic_fetch_or(P.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -654,113 +671,80 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   }
   si.ap = att_plan(m, si.p);
   si.nunits = w < si.ap.units ? c_div(si.ap.units - w, m.nwg) : 0;
-  const int mfirst = m.nwg - 1 - w;
+  const int mfirst = m.nwg - 1 - w;  // merge units are dealt from the last workgroup down
   const int nmerge_here = mfirst < si.ap.nmerge ? c_div(si.ap.nmerge - mfirst, m.nwg) : 0;
   const int oseg = seg_o(si.nunits);
 
-  if (threadIdx.x == 0) sm.abort_flag = 0;
-
-  if (wave > 0) {
-    // ============================ compute waves ============================
-    const int v = wave - 1;
-    build_segments(P, si, w, v, sm);
-    const SegEntry* tab = sm.segs[v];
-    Ring<RING> rg;
-    rg.slots = &sm.ring[v][0][0];
-    rg.slot_lds = lds_addr_of(&sm.ring[v][0][0]);
-    rg.cnt = 0;
-    rg.is.tab = tab;
-    rg.is.lm = &sm.lm_seg[v];
-    rg.is.nseg = oseg + 3;
-    rg.is.L = m.L;
-    rg.is.wstride = m.layer_elems * m.wbytes;
-    rg.is.kvstride = (int64_t)2 * m.hkv * m.S * m.hd * m.kvbytes;
-    rg.is.layer = 0;
-    rg.is.e = 0;
-    rg.is.last = P.blob;
-    rg.is.load();
-    for (int s = 0; s < RING; ++s) rg.is.issue(rg.slot_lds + s * kPacketBytes);
-
-    int gD, T_unused;
-    tile_shape(m, w, kTileD, T_unused, gD);
-    for (int layer = 0; layer < m.L; ++layer) {
-      wg_barrier();
-      if (sm.abort_flag) goto drain;
-      consume_rows<RING, WB>(rg, tab[0], m.cd, sm.act, sm.u.part_r[v]);
-      wg_barrier();
-      for (int k = 0; k < si.nunits; ++k) {
-        wg_barrier();
-        if (sm.abort_flag) goto drain;
-        const Unit u = unit_of(si, w, k, m.nwg);
-        consume_attention<RING, KB, HD>(rg, tab[1 + 2 * k], u, m.G, sm, v);
-        wg_barrier();
-      }
-      wg_barrier();
-      if (sm.abort_flag) goto drain;
-      consume_rows<RING, WB>(rg, tab[oseg], m.cq, sm.act, sm.u.part_r[v]);
-      wg_barrier();
-      wg_barrier();
-      if (sm.abort_flag) goto drain;
-      consume_rows<RING, WB>(rg, tab[oseg + 1], m.cd, sm.act, sm.u.part_r[v]);
-      wg_barrier();
-      wg_barrier();
-      if (sm.abort_flag) goto drain;
-      consume_cols<RING, WB>(rg, tab[oseg + 2], gD, sm.act, &sm.u.part_c[v][0][0]);
-      wg_barrier();
-    }
-    wg_barrier();
-    if (sm.abort_flag) goto drain;
-    consume_rows<RING, WB>(rg, sm.lm_seg[v], m.cd, sm.act, sm.u.part_r[v]);
-    wg_barrier();
-  drain:
-    wait_vm<0>();
-    return;
-  }
-
-  // ============================ control wave ============================
-  Ctl<RING> ctl{P, __builtin_amdgcn_make_buffer_rsrc(P.ll, (short)0, (int)(P.lo.total * 8), 0x00020000), sm};
-  ctl.build_splits(w);
-  const int rows_d0 = p_lo(m.d, m.nwg, w);
-  const int nrow_d = p_lo(m.d, m.nwg, w + 1) - rows_d0;
-  const int nf = ffn_lo32(m, w + 1) - ffn_lo32(m, w);
-  const int r_qkv0 = p_lo(m.nqkv, m.nwg, w), n_qkv = p_lo(m.nqkv, m.nwg, w + 1) - r_qkv0;
-  const int r_lm0 = p_lo(m.V, m.nwg, w), n_lm = p_lo(m.V, m.nwg, w + 1) - r_lm0;
+  const int rd0 = drow_lo(m, w), nrd = drow_lo(m, w + 1) - rd0;  // this WG's d rows (O, x ownership)
+  const int f0 = ffn_lo32(m, w), nf = ffn_lo32(m, w + 1) - f0;     // this WG's FFN slice
+  const int rq0 = p_lo(m.nqkv, m.nwg, w), nq = p_lo(m.nqkv, m.nwg, w + 1) - rq0;
+  const int rl0 = p_lo(m.V, m.nwg, w), nl = p_lo(m.V, m.nwg, w + 1) - rl0;
   const int gD = nf / m.vpl;
   const int mc = max_chunks(m);
 
   uint64_t* const tr = P.trace ? P.trace + (int64_t)w * trace_stride(m.L) : nullptr;
   auto stamp = [&](int slot) {
-    if (tr && lane == 0) tr[slot] = now_ticks();
+    if (tr && tid == 0) tr[slot] = now_ticks();
   };
   stamp(0);
-  // RoPE angles of this step's position, in float64 then rounded to float32
-  for (int i = lane; i < m.hd / 2; i += 64) {
-    const double theta = pow((double)P.rope_base, -2.0 * (double)i / (double)m.hd);
-    const double ang = (double)si.p * theta;
-    sm.rope_c[i] = (float)cos(ang);
-    sm.rope_s[i] = (float)sin(ang);
-  }
-  // embedding row of the input token
-  for (int i = lane; i < m.d; i += 64) sm.x[i] = load_w<WB>(P.embed, (int64_t)token * m.d + i);
 
+  // ---- setup: segment tables, ring, split tables, RoPE row, embedding row ----
+  if (tid == 0) sm.abort_flag = 0;
+  build_segments(P, si, w, wave, sm);
+  if (tid < kTiles) {
+    for (int v = 0; v <= kWaves; ++v) {
+      int lo, hi;
+      wave_range(m, w, tid, v < kWaves ? v : kWaves - 1, lo, hi);
+      sm.split[tid][v] = v < kWaves ? lo : hi;
+    }
+    int T, C;
+    tile_shape(m, w, tid, T, C);
+    for (int v = 0; v < kWaves; ++v) sm.first[tid][v] = C > 0 ? sm.split[tid][v] / C : 0;
+  }
+  for (int i = tid; i < m.hd / 2; i += kThreads) {
+    const float2 cs = P.rope[(int64_t)si.p * (m.hd / 2) + i];
+    sm.rope_c[i] = cs.x;
+    sm.rope_s[i] = cs.y;
+  }
+  for (int i = tid; i < m.d; i += kThreads) sm.act[i] = load_w<WB>(P.embed, (int64_t)token * m.d + i);
+  wg_barrier();  // segment tables visible
+
+  Ring<RING> rg;
+  rg.slots = &sm.ring[wave][0][0];
+  rg.slot_lds = lds_addr_of(&sm.ring[wave][0][0]);
+  rg.cnt = 0;
+  rg.is.tab = sm.segs[wave];
+  rg.is.lm = &sm.lm_seg[wave];
+  rg.is.nseg = oseg + 3;
+  rg.is.L = m.L;
+  rg.is.wstride = m.layer_elems * m.wbytes;
+  rg.is.kvstride = (int64_t)2 * m.hkv * m.S * m.hd * m.kvbytes;
+  rg.is.layer = 0;
+  rg.is.e = 0;
+  rg.is.last = P.blob;
+  rg.is.load();
+  for (int s = 0; s < RING; ++s) rg.is.issue(rg.slot_lds + s * kPacketBytes);
+
+  Xchg<RING> xc{P, __builtin_amdgcn_make_buffer_rsrc(P.ll, (short)0, (int)(P.lo.total * 8), 0x00020000), sm};
   const float inv_sqrt_hd = 1.0f / sqrtf((float)m.hd);
+  const SegEntry* tab = sm.segs[wave];
   stamp(1);
+
   for (int layer = 0; layer < m.L; ++layer) {
     const uint8_t* g_attn = P.norms + ((int64_t)layer * 2 + 0) * m.d * m.wbytes;
     const uint8_t* g_ffn = P.norms + ((int64_t)layer * 2 + 1) * m.d * m.wbytes;
+    // ---- x, RMSNorm ----
+    if (layer > 0 && !xc.gather_vec(ll_tag(m, P.seq, layer - 1, kX), P.lo.x, m.d, sm.act)) goto drain;
+    stamp(trace_slot(layer, 0));
+    if (tid < nrd) sm.xo[tid] = sm.act[rd0 + tid];
+    rmsnorm<RING, WB>(sm, g_attn, m.d, P.eps);
+    stamp(trace_slot(layer, 1));
     // ---- QKV rows ----
-    if (layer > 0) ctl.gather_vec(ll_tag(m, P.seq, layer - 1, kX), P.lo.x, m.d, sm.x);
-    if (!ctl.failed()) ctl.template rmsnorm<WB>(sm.x, g_attn, sm.act, m.d);
-    stamp(trace_slot(m.L, layer, 0));
+    consume_rows<RING, WB>(rg, tab[0], m.cd, sm.act, sm.rowpart[wave]);
     wg_barrier();
-    if (sm.abort_flag) return;
-    wg_barrier();
-    stamp(trace_slot(m.L, layer, 1));
-    {
-      const uint32_t tag = ll_tag(m, P.seq, layer, kQKV);
-      for (int r = lane; r < n_qkv; r += 64) ll_store(P.ll, P.lo.qkv + r_qkv0 + r, ctl.row_total(kTileQKV, m.cd, r), tag);
-    }
-    stamp(trace_slot(m.L, layer, 2));
+    stamp(trace_slot(layer, 2));
+    if (tid < nq) ll_store(P.ll, P.lo.qkv + rq0 + tid, row_total(sm, kTileQKV, m.cd, tid), ll_tag(m, P.seq, layer, kQKV));
+    stamp(trace_slot(layer, 3));
     // ---- attention units: one chunk of positions of one kv head each ----
     for (int k = 0; k < si.nunits; ++k) {
       const Unit u = unit_of(si, w, k, m.nwg);
@@ -768,43 +752,46 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       const int64_t qoff = P.lo.qkv + (int64_t)u.g * G * m.hd;
       const int64_t koff = P.lo.qkv + m.qdim + (int64_t)u.g * m.hd;
       const int64_t voff = P.lo.qkv + m.qdim + m.kvdim + (int64_t)u.g * m.hd;
-      const int nq = G * m.hd / 2, nk = m.hd / 2;
-      ctl.gather(
-          ll_tag(m, P.seq, layer, kQKV), nq + 2 * nk,
+      const int nqp = G * m.hd / 2, nkp = m.hd / 2;
+      const bool ok = xc.gather(
+          ll_tag(m, P.seq, layer, kQKV), nqp + 2 * nkp,
           [&](int k2) -> int64_t {
-            return k2 < nq ? qoff + 2 * k2 : (k2 < nq + nk ? koff + 2 * (k2 - nq) : voff + 2 * (k2 - nq - nk));
+            return k2 < nqp ? qoff + 2 * k2 : (k2 < nqp + nkp ? koff + 2 * (k2 - nqp) : voff + 2 * (k2 - nqp - nkp));
           },
           [&](int k2, float a, float b) {
-            if (k2 < nq) {
+            if (k2 < nqp) {
               const int h = (2 * k2) / m.hd, e = (2 * k2) - h * m.hd;
               sm.u.att.q[h][e] = a;
               sm.u.att.q[h][e + 1] = b;
-            } else if (k2 < nq + nk) {
-              sm.u.att.kp[2 * (k2 - nq)] = a;
-              sm.u.att.kp[2 * (k2 - nq) + 1] = b;
+            } else if (k2 < nqp + nkp) {
+              sm.u.att.kp[2 * (k2 - nqp)] = a;
+              sm.u.att.kp[2 * (k2 - nqp) + 1] = b;
             } else {
-              sm.u.att.vp[2 * (k2 - nq - nk)] = a;
-              sm.u.att.vp[2 * (k2 - nq - nk) + 1] = b;
+              sm.u.att.vp[2 * (k2 - nqp - nkp)] = a;
+              sm.u.att.vp[2 * (k2 - nqp - nkp) + 1] = b;
             }
           });
-      if (!ctl.failed()) {
-        // RoPE on q (and the 1/sqrt(hd) score scale) and on k; K and V rounded to the cache type
+      if (!ok) goto drain;
+      if (k == 0) stamp(trace_slot(layer, 4));
+      {
+        // RoPE on the G queries (with the 1/sqrt(hd) score scale) and on k; K and V rounded to the
+        // cache type, and appended by the unit that holds the last chunk
         const int half = m.hd / 2;
-        for (int i = lane; i < half; i += 64) {
+        if (tid < (G + 1) * half) {
+          const int h = tid / half, i = tid - h * half;
           const float c = sm.rope_c[i], s = sm.rope_s[i];
-          for (int h = 0; h < G; ++h) {
-            const float a = sm.u.att.q[h][i], b = sm.u.att.q[h][i + half];
-            sm.u.att.q[h][i] = (a * c - b * s) * inv_sqrt_hd;
-            sm.u.att.q[h][i + half] = (a * s + b * c) * inv_sqrt_hd;
-          }
-          const float a = sm.u.att.kp[i], b = sm.u.att.kp[i + half];
-          sm.u.att.kp[i] = a * c - b * s;
-          sm.u.att.kp[i + half] = a * s + b * c;
+          float* vec = h < G ? sm.u.att.q[h] : sm.u.att.kp;
+          const float a = vec[i], b = vec[i + half];
+          const float sc = h < G ? inv_sqrt_hd : 1.0f;
+          vec[i] = (a * c - b * s) * sc;
+          vec[i + half] = (a * s + b * c) * sc;
         }
-        const int64_t kh = (((int64_t)layer * 2 + 0) * m.hkv + u.g) * m.S + si.p;
-        const int64_t vh = (((int64_t)layer * 2 + 1) * m.hkv + u.g) * m.S + si.p;
-        for (int i = lane; i < m.hd; i += 64) {
+        wg_barrier();
+        if (tid < m.hd) {
+          const int i = tid;
           float kk = sm.u.att.kp[i], vv = sm.u.att.vp[i];
+          const int64_t kh = (((int64_t)layer * 2 + 0) * m.hkv + u.g) * m.S + si.p;
+          const int64_t vh = (((int64_t)layer * 2 + 1) * m.hkv + u.g) * m.S + si.p;
           if constexpr (KB == 2) {
             const uint32_t kb = bf16_rne_bits(kk), vb = bf16_rne_bits(vv);
             kk = __uint_as_float(kb << 16);
@@ -822,55 +809,60 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
           sm.u.att.kp[i] = kk;
           sm.u.att.vp[i] = vv;
         }
+        wg_barrier();
       }
-      if (k == 0) stamp(trace_slot(m.L, layer, 3));
+      // score of the current position (last chunk only), one wave per query head
+      if (u.last && wave < G) {
+        float t = 0.f;
+        for (int i = lane; i < m.hd; i += 64) t = fmaf(sm.u.att.q[wave][i], sm.u.att.kp[i], t);
+        t = wave_sum(t);
+        if (lane == 0) sm.u.att.sp[wave] = t;
+      }
+      consume_attention<RING, KB, HD>(rg, tab[1 + 2 * k], u, G, sm, wave, sm.act + (int64_t)wave * kMaxGroup * HD);
       wg_barrier();
-      if (sm.abort_flag) return;
-      wg_barrier();
-      if (k == 0) stamp(trace_slot(m.L, layer, 4));
-      // merge the compute waves' partial softmax sums, plus the current position in the last chunk
-      if (!ctl.failed()) {
-        const uint32_t tag = ll_tag(m, P.seq, layer, kATTP);
-        for (int h = 0; h < G; ++h) {
-          float sp = -INFINITY;
-          if (u.last) {
-            float t = 0.f;
-            for (int i = lane; i < m.hd; i += 64) t = fmaf(sm.u.att.q[h][i], sm.u.att.kp[i], t);
-            sp = wave_sum(t);
-          }
-          float M = sp;
+      if (k == 0) stamp(trace_slot(layer, 5));
+      // combine the waves' partial softmax sums (plus the current position in the last chunk)
+      if (tid < G * m.hd) {
+        const int h = tid / m.hd, i = tid - h * m.hd;
+        const float sp = u.last ? sm.u.att.sp[h] : -INFINITY;
+        float M = sp;
 #pragma unroll
-          for (int vv = 0; vv < kComputeWaves; ++vv)
-            if (sm.u.att.ml[vv][h][1] > 0.f) M = fmaxf(M, sm.u.att.ml[vv][h][0]);
-          float Lsum = 0.f;
+        for (int v = 0; v < kWaves; ++v)
+          if (sm.u.att.ml[v][h][1] > 0.f) M = fmaxf(M, sm.u.att.ml[v][h][0]);
+        float Lsum = 0.f, acc = 0.f;
 #pragma unroll
-          for (int vv = 0; vv < kComputeWaves; ++vv) {
-            const float lv = sm.u.att.ml[vv][h][1];
-            if (lv > 0.f) Lsum = fmaf(__expf(sm.u.att.ml[vv][h][0] - M), lv, Lsum);
-          }
-          const float sp_w = u.last ? __expf(sp - M) : 0.f;
-          Lsum += sp_w;
-          const int hq = u.g * G + h;
-          const int64_t at = P.lo.attp + ((int64_t)hq * mc + u.c) * (m.hd + 2);
-          for (int i = lane; i < m.hd; i += 64) {
-            float a = sp_w * sm.u.att.vp[i];
-#pragma unroll
-            for (int vv = 0; vv < kComputeWaves; ++vv) {
-              const float lv = sm.u.att.ml[vv][h][1];
-              if (lv > 0.f) a = fmaf(__expf(sm.u.att.ml[vv][h][0] - M), sm.u.att.acc[vv][h][i], a);
-            }
-            ll_store(P.ll, at + 2 + i, a, tag);
-          }
-          if (lane == 0) {
-            ll_store(P.ll, at, M, tag);
-            ll_store(P.ll, at + 1, Lsum, tag);
+        for (int v = 0; v < kWaves; ++v) {
+          const float lv = sm.u.att.ml[v][h][1];
+          if (lv > 0.f) {
+            const float sc = __expf(sm.u.att.ml[v][h][0] - M);
+            Lsum = fmaf(sc, lv, Lsum);
+            acc = fmaf(sc, sm.act[((int64_t)v * kMaxGroup + h) * HD + i], acc);
           }
         }
+        if (u.last) {
+          const float e = __expf(sp - M);
+          Lsum += e;
+          acc = fmaf(e, sm.u.att.vp[i], acc);
+        }
+        const uint32_t tag = ll_tag(m, P.seq, layer, kATTP);
+        const int hq = u.g * G + h;
+        const int64_t at = P.lo.attp + ((int64_t)hq * mc + u.c) * (m.hd + 2);
+        ll_store(P.ll, at + 2 + i, acc, tag);
+        if (i == 0) {
+          ll_store(P.ll, at, M, tag);
+          ll_store(P.ll, at + 1, Lsum, tag);
+        }
       }
+      // the per-wave sums must stay readable until every thread has combined them: clear the
+      // unused wave slots of the next unit only after this barrier
+      wg_barrier();
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h)
+        if (lane == 0) sm.u.att.ml[wave][h][1] = 0.f;
     }
-    stamp(trace_slot(m.L, layer, 5));
+    stamp(trace_slot(layer, 6));
     // ---- merge units: one slice of one head's output, over all chunks ----
-    for (int k = 0; k < nmerge_here && !ctl.failed(); ++k) {
+    for (int k = 0; k < nmerge_here; ++k) {
       const int mu = mfirst + k * m.nwg;
       const int NC = si.ap.NC, MS = si.ap.MS;
       const int per_head = m.hd / MS;
@@ -878,7 +870,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       const int ppc = 1 + MS / 2;  // pieces per chunk: (m, l), then the slice
       const int64_t head_at = P.lo.attp + (int64_t)hq * mc * (m.hd + 2);
       float* st = sm.u.stage;  // [NC][2 + MS]
-      ctl.gather(
+      const bool ok = xc.gather(
           ll_tag(m, P.seq, layer, kATTP), NC * ppc,
           [&](int k2) -> int64_t {
             const int c = k2 / ppc, t = k2 - c * ppc;
@@ -890,106 +882,98 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
             st[c * (2 + MS) + 2 * t] = a;
             st[c * (2 + MS) + 2 * t + 1] = b;
           });
-      if (ctl.failed()) break;
-      float M = -INFINITY;
-      for (int c = lane; c < NC; c += 64) M = fmaxf(M, st[c * (2 + MS)]);
-      M = wave_max(M);
-      // chunk weights exp(m_c - M), stored over the m_c slots
-      float Ls = 0.f;
-      for (int c = lane; c < NC; c += 64) {
-        const float sc = __expf(st[c * (2 + MS)] - M);
-        Ls = fmaf(sc, st[c * (2 + MS) + 1], Ls);
-        st[c * (2 + MS)] = sc;
+      if (!ok) goto drain;
+      if (wave == 0) {
+        float M = -INFINITY;
+        for (int c = lane; c < NC; c += 64) M = fmaxf(M, st[c * (2 + MS)]);
+        M = wave_max(M);
+        float Ls = 0.f;
+        for (int c = lane; c < NC; c += 64) Ls = fmaf(__expf(st[c * (2 + MS)] - M), st[c * (2 + MS) + 1], Ls);
+        Ls = wave_sum(Ls);
+        const float invL = 1.0f / Ls;
+        const uint32_t tag = ll_tag(m, P.seq, layer, kO);
+        for (int i = lane; i < MS; i += 64) {
+          float a = 0.f;
+          for (int c = 0; c < NC; ++c) a = fmaf(__expf(st[c * (2 + MS)] - M), st[c * (2 + MS) + 2 + i], a);
+          ll_store(P.ll, P.lo.o + (int64_t)hq * m.hd + (int64_t)sl * MS + i, a * invL, tag);
+        }
       }
-      Ls = wave_sum(Ls);
-      const float invL = 1.0f / Ls;
-      const uint32_t tag = ll_tag(m, P.seq, layer, kO);
-      for (int i = lane; i < MS; i += 64) {
-        float a = 0.f;
-        for (int c = 0; c < NC; ++c) a = fmaf(st[c * (2 + MS)], st[c * (2 + MS) + 2 + i], a);
-        ll_store(P.ll, P.lo.o + (int64_t)hq * m.hd + (int64_t)sl * MS + i, a * invL, tag);
-      }
+      wg_barrier();
     }
-    stamp(trace_slot(m.L, layer, 6));
+    stamp(trace_slot(layer, 7));
     // ---- output projection rows + residual ----
-    ctl.gather_vec(ll_tag(m, P.seq, layer, kO), P.lo.o, m.qdim, sm.act);
-    stamp(trace_slot(m.L, layer, 7));
+    if (!xc.gather_vec(ll_tag(m, P.seq, layer, kO), P.lo.o, m.qdim, sm.act)) goto drain;
+    stamp(trace_slot(layer, 8));
+    consume_rows<RING, WB>(rg, tab[oseg], m.cq, sm.act, sm.rowpart[wave]);
     wg_barrier();
-    if (sm.abort_flag) return;
-    wg_barrier();
-    stamp(trace_slot(m.L, layer, 8));
-    {
-      const uint32_t tag = ll_tag(m, P.seq, layer, kXP);
-      for (int r = lane; r < nrow_d; r += 64)
-        ll_store(P.ll, P.lo.xp + rows_d0 + r, sm.x[rows_d0 + r] + ctl.row_total(kTileO, m.cq, r), tag);
+    stamp(trace_slot(layer, 9));
+    if (tid < nrd) {
+      const float xp = sm.xo[tid] + row_total(sm, kTileO, m.cq, tid);
+      sm.xo[tid] = xp;
+      ll_store(P.ll, P.lo.xp + rd0 + tid, xp, ll_tag(m, P.seq, layer, kXP));
     }
-    stamp(trace_slot(m.L, layer, 9));
+    stamp(trace_slot(layer, 10));
     // ---- gate/up rows of this workgroup's FFN slice ----
-    ctl.gather_vec(ll_tag(m, P.seq, layer, kXP), P.lo.xp, m.d, sm.x);
-    if (!ctl.failed()) ctl.template rmsnorm<WB>(sm.x, g_ffn, sm.act, m.d);
-    stamp(trace_slot(m.L, layer, 10));
+    if (!xc.gather_vec(ll_tag(m, P.seq, layer, kXP), P.lo.xp, m.d, sm.act)) goto drain;
+    stamp(trace_slot(layer, 11));
+    rmsnorm<RING, WB>(sm, g_ffn, m.d, P.eps);
+    consume_rows<RING, WB>(rg, tab[oseg + 1], m.cd, sm.act, sm.rowpart[wave]);
     wg_barrier();
-    if (sm.abort_flag) return;
-    wg_barrier();
-    stamp(trace_slot(m.L, layer, 11));
-    for (int i = lane; i < nf; i += 64) {
-      const float gt = ctl.row_total(kTileGU, m.cd, i);
-      const float up = ctl.row_total(kTileGU, m.cd, nf + i);
-      sm.act[i] = gt / (1.0f + __expf(-gt)) * up;
+    stamp(trace_slot(layer, 12));
+    if (tid < nf) {
+      const float gt = row_total(sm, kTileGU, m.cd, tid);
+      const float up = row_total(sm, kTileGU, m.cd, nf + tid);
+      sm.a[tid] = gt / (1.0f + __expf(-gt)) * up;
     }
-    stamp(trace_slot(m.L, layer, 12));
-    // ---- down projection of the slice, for all d rows ----
     wg_barrier();
-    if (sm.abort_flag) return;
-    wg_barrier();
-    stamp(trace_slot(m.L, layer, 13));
-    {
-      const uint32_t tag = ll_tag(m, P.seq, layer, kDP);
-      for (int b = 0; b < m.d / 64; ++b) {
-        const int i = b * 64 + lane;
-        const float val = gD > 0 ? ctl.block_total(gD, b, lane) : 0.f;
-        const int o = p_of(m.d, m.nwg, i);
-        const int olo = p_lo(m.d, m.nwg, o), ohi = p_lo(m.d, m.nwg, o + 1);
-        ll_store(P.ll, P.lo.dp + (int64_t)olo * m.nwg + (int64_t)w * (ohi - olo) + (i - olo), val, tag);
-      }
-    }
-    stamp(trace_slot(m.L, layer, 14));
+    // ---- down projection of the slice, for all d rows, published block by block ----
+    consume_down<RING, WB>(rg, tab[oseg + 2], gD, sm.a, P.ll, P.lo.dp + (int64_t)w * m.d, ll_tag(m, P.seq, layer, kDP));
+    stamp(trace_slot(layer, 13));
     // ---- sum every slice's contribution to this workgroup's rows; residual add ----
     {
-      float* st = sm.act;  // [nwg][nrow_d]
-      ctl.gather_vec(ll_tag(m, P.seq, layer, kDP), P.lo.dp + (int64_t)rows_d0 * m.nwg, m.nwg * nrow_d, st);
-      if (!ctl.failed() && nrow_d > 0) {
-        // lane = (row, group of producers); fixed summation order, so results are reproducible
-        const int groups = 64 / nrow_d;
-        const int r = lane % nrow_d, grp = lane / nrow_d;
+      float* st = sm.u.stage;  // [nwg][nrd]
+      const int hp = nrd / 2;  // pieces per producer
+      const bool ok = nrd == 0 ||
+                      xc.gather(
+                          ll_tag(m, P.seq, layer, kDP), m.nwg * hp,
+                          [&](int k2) -> int64_t {
+                            const int q = k2 / hp, j = k2 - q * hp;
+                            return P.lo.dp + (int64_t)q * m.d + rd0 + 2 * j;
+                          },
+                          [&](int k2, float a, float b) {
+                            st[2 * k2] = a;
+                            st[2 * k2 + 1] = b;
+                          });
+      if (!ok) goto drain;
+      stamp(trace_slot(layer, 14));
+      // one wave per row: lanes take producers lane, lane+64, ... in order, then a butterfly
+      for (int r = wave; r < nrd; r += kWaves) {
         float s = 0.f;
-        if (grp < groups)
-          for (int pr = grp; pr < m.nwg; pr += groups) s += st[pr * nrow_d + r];
-        float tot = 0.f;
-        for (int q2 = 0; q2 < groups; ++q2) tot += __shfl(s, q2 * nrow_d + r);
-        if (lane < nrow_d) ll_store(P.ll, P.lo.x + rows_d0 + lane, sm.x[rows_d0 + lane] + tot, ll_tag(m, P.seq, layer, kX));
+        for (int q = lane; q < m.nwg; q += 64) s += st[q * nrd + r];
+        s = wave_sum(s);
+        if (lane == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(m, P.seq, layer, kX));
       }
+      wg_barrier();  // the staging area is reused by the next layer's attention
     }
-    stamp(trace_slot(m.L, layer, 15));
+    stamp(trace_slot(layer, 15));
   }
 
   // ---- final norm, LM head rows, argmax ----
-  ctl.gather_vec(ll_tag(m, P.seq, m.L - 1, kX), P.lo.x, m.d, sm.x);
-  if (!ctl.failed()) ctl.template rmsnorm<WB>(sm.x, P.norms + (int64_t)m.L * 2 * m.d * m.wbytes, sm.act, m.d);
-  stamp(trace_slot(m.L, m.L, 0));
+  if (!xc.gather_vec(ll_tag(m, P.seq, m.L - 1, kX), P.lo.x, m.d, sm.act)) goto drain;
+  rmsnorm<RING, WB>(sm, P.norms + (int64_t)m.L * 2 * m.d * m.wbytes, m.d, P.eps);
+  stamp(trace_slot(m.L, 0));
+  consume_rows<RING, WB>(rg, sm.lm_seg[wave], m.cd, sm.act, sm.rowpart[wave]);
   wg_barrier();
-  if (sm.abort_flag) return;
-  wg_barrier();
-  stamp(trace_slot(m.L, m.L, 1));
+  stamp(trace_slot(m.L, 1));
   {
     float best = -INFINITY;
     int32_t besti = 0x7fffffff;
     bool nan = false;
-    for (int r = lane; r < n_lm; r += 64) {
-      const float val = ctl.row_total(kTileLM, m.cd, r);
-      if (P.logits) P.logits[r_lm0 + r] = val;
+    for (int r = tid; r < nl; r += kThreads) {
+      const float val = row_total(sm, kTileLM, m.cd, r);
+      if (P.logits) P.logits[rl0 + r] = val;
       if (val != val) { nan = true; continue; }
-      if (val > best || (val == best && r_lm0 + r < besti)) { best = val; besti = r_lm0 + r; }
+      if (val > best || (val == best && rl0 + r < besti)) { best = val; besti = rl0 + r; }
     }
     for (int o = 32; o > 0; o >>= 1) {
       const float ob = __shfl_xor(best, o);
@@ -998,32 +982,48 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     }
     if (__any(nan) && lane == 0) __hip_atomic_fetch_or(P.status, kStatusNaN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (lane == 0) {
+      sm.red[wave] = best;
+      sm.redi[wave] = besti;
+    }
+    wg_barrier();
+    if (tid == 0) {
+      for (int v = 1; v < kWaves; ++v)
+        if (sm.red[v] > best || (sm.red[v] == best && sm.redi[v] < besti)) { best = sm.red[v]; besti = sm.redi[v]; }
       const uint32_t tag = ll_tag(m, P.seq, m.L, kLM);
       ll_store_bits(P.ll, P.lo.lm + 2 * w, __float_as_uint(best), tag);
       ll_store_bits(P.ll, P.lo.lm + 2 * w + 1, (uint32_t)besti, tag);
     }
   }
-  stamp(trace_slot(m.L, m.L, 2));
+  stamp(trace_slot(m.L, 2));
   if (w == 0) {
-    float best = -INFINITY;
-    int32_t besti = 0x7fffffff;
-    ctl.gather(ll_tag(m, P.seq, m.L, kLM), m.nwg, [&](int k) -> int64_t { return P.lo.lm + 2 * (int64_t)k; },
-               [&](int k, float a, float b) {
-                 const int32_t idx = (int32_t)__float_as_uint(b);
-                 if (a > best || (a == best && idx < besti)) { best = a; besti = idx; }
-               });
-    if (ctl.failed() || ld_flag(P.abortf)) return;
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ob = __shfl_xor(best, o);
-      const int32_t oi = __shfl_xor(besti, o);
-      if (ob > best || (ob == best && oi < besti)) { best = ob; besti = oi; }
+    const bool ok = xc.gather(ll_tag(m, P.seq, m.L, kLM), m.nwg, [&](int k) -> int64_t { return P.lo.lm + 2 * (int64_t)k; },
+                              [&](int k, float a, float b) {
+                                sm.u.stage[2 * k] = a;
+                                sm.u.stage[2 * k + 1] = b;
+                              });
+    if (!ok || ld_flag(P.abortf)) goto drain;
+    if (wave == 0) {
+      float best = -INFINITY;
+      int32_t besti = 0x7fffffff;
+      for (int k = lane; k < m.nwg; k += 64) {
+        const float a = sm.u.stage[2 * k];
+        const int32_t idx = (int32_t)__float_as_uint(sm.u.stage[2 * k + 1]);
+        if (a > best || (a == best && idx < besti)) { best = a; besti = idx; }
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ob = __shfl_xor(best, o);
+        const int32_t oi = __shfl_xor(besti, o);
+        if (ob > best || (ob == best && oi < besti)) { best = ob; besti = oi; }
+      }
+      if (lane == 0) {
+        P.tokens[0] = besti == 0x7fffffff ? 0 : besti;
+        P.positions[0] = si.p + 1;
+      }
     }
-    if (lane == 0) {
-      P.tokens[0] = besti == 0x7fffffff ? 0 : besti;
-      P.positions[0] = si.p + 1;
-    }
-    stamp(trace_slot(m.L, m.L, 3));
+    stamp(trace_slot(m.L, 3));
   }
+drain:
+  wait_vm<0>();
 }
 
 }  // namespace kd

@@ -4,7 +4,7 @@
 // streams which weight rows, which KV positions each wave reads and where every
 // intermediate vector lives ("Why is real-time AI inference 56x more expensive?",
 // section "decide everything ahead of time"). Only the attention split depends
-// on the current position, and that is integer arithmetic every wave repeats.
+// on the current position, and that is integer arithmetic every workgroup repeats.
 #pragma once
 #include <stdint.h>
 
@@ -16,20 +16,20 @@
 
 namespace kd {
 
-constexpr int kThreads = 512;          // 8 waves of 64 lanes per workgroup
-constexpr int kComputeWaves = 7;       // waves 1..7 stream packets; wave 0 is the control wave
-constexpr int kPacketBytes = 1024;     // one 16-byte load by each of 64 lanes
-constexpr int kMaxDim = 4096;          // largest d_model and n_q_heads*head_dim held in LDS
-constexpr int kMaxGroup = 4;           // largest q heads per kv head
+constexpr int kThreads = 512;      // 8 waves of 64 lanes per workgroup
+constexpr int kWaves = 8;          // every wave streams packets and joins every exchange
+constexpr int kPacketBytes = 1024; // one 16-byte load by each of 64 lanes
+constexpr int kMaxDim = 4096;      // largest d_model and n_q_heads*head_dim held in LDS
+constexpr int kMaxGroup = 4;       // largest q heads per kv head
 constexpr int kMaxHeadDim = 128;
-constexpr int kChunkMin = 64;          // attention chunk bounds (positions per unit)
-constexpr int kChunkMax = 256;
-constexpr int kMergeWords = 2048;      // largest LL gather of one merge unit
-constexpr int kSegR = 96;              // row partials kept per compute wave
-constexpr int kSegC = 12;              // 64-row blocks kept per compute wave (down projection)
-constexpr int kScorePos = 48;          // attention scores kept per compute wave
+constexpr int kChunkMin = 32;      // fewest cached positions per attention unit
+constexpr int kMaxUnits = 4;       // attention units one workgroup may hold in one step
+constexpr int kMergeWords = 4096;  // largest gather of one merge unit
+constexpr int kRowPart = 96;       // row partial sums kept per wave
+constexpr int kScorePos = 64;      // attention scores kept per wave (positions)
+constexpr int kStageWords = 4096;  // staging area for gathers that are not the activation
 
-// Tag kinds of the vectors exchanged between workgroups (LL words carry value|tag).
+// Tag kinds of the vectors exchanged between workgroups (an exchange word carries value|tag).
 enum Kind : int { kQKV = 0, kATTP = 1, kO = 2, kXP = 3, kDP = 4, kX = 5, kLM = 6 };
 
 // Start of part i when n items are cut into `parts` contiguous parts.
@@ -77,35 +77,49 @@ KD_HD int64_t ffn_lo(const Dims& m, int64_t w) { return (int64_t)m.vpl * part_lo
 // Element offset of workgroup w's down-projection packets inside a layer's down block.
 KD_HD int64_t down_wg_off(const Dims& m, int64_t w) { return (int64_t)m.d * ffn_lo(m, w); }
 
-// Attention split of one step at position p (P = p+1 positions attended).
+// Attention split of one step at position p (P = p+1 positions attended, 0..p).
+//   NC chunks of CH positions per kv head -> units = NC * hkv, unit u = (head u / NC, chunk u % NC).
+//   The cached positions 0..p-1 are streamed; position p comes from this step's QKV and is
+//   added by the unit holding the last chunk.
+//   Merge units: q head h, dim slice s of MS dims -> nmerge = hq * (hd / MS).
 struct AttPlan {
   int32_t P, CH, NC, units, MS, nmerge;
 };
 
+// Chunks per kv head that one round of units (one per workgroup) covers.
+KD_HD int64_t chunk_round(const Dims& m) {
+  const int64_t r = m.nwg / m.hkv;
+  return r < 1 ? 1 : r;
+}
+
 KD_HD AttPlan att_plan(const Dims& m, int32_t p) {
   AttPlan a{};
   a.P = p + 1;
-  int64_t work = (int64_t)a.P * m.hkv;
-  int64_t k = ceil_div(work, (int64_t)m.nwg * kChunkMax);
-  if (k < 1) k = 1;
-  int64_t ch = ceil_div(work, k * m.nwg);
-  ch = ceil_div(ch, m.ppp) * m.ppp;
-  if (ch < kChunkMin) ch = kChunkMin;
-  if (ch > kChunkMax) ch = kChunkMax;
+  const int64_t cap = chunk_round(m);
+  int64_t nc = ceil_div(a.P, kChunkMin);
+  if (nc > cap) nc = cap;
+  int64_t ch = 0;
+  while (true) {
+    ch = ceil_div(ceil_div(a.P, nc), m.ppp) * m.ppp;
+    // a wave keeps the scores of its share of the chunk in LDS: add rounds of units until it fits
+    if (ceil_div(ceil_div(ch, m.ppp), kWaves) * m.ppp <= kScorePos || nc >= cap * kMaxUnits) break;
+    nc += cap;
+  }
   a.CH = (int32_t)ch;
   a.NC = (int32_t)ceil_div(a.P, ch);
   a.units = a.NC * m.hkv;
+  // merge slices: the most merge units that still fit one workgroup each, slices of >= 2 dims
   int32_t ms = m.hd;
-  while (ms > 2 && (int64_t)a.NC * (ms + 2) > kMergeWords) ms /= 2;
+  while (ms > 2 && ((int64_t)m.hq * (m.hd / (ms / 2)) <= m.nwg || (int64_t)a.NC * (ms + 2) > kMergeWords)) ms /= 2;
   a.MS = ms;
   a.nmerge = m.hq * (m.hd / ms);
   return a;
 }
 
-// Most chunks any step of a cache with S positions can use (sizes the partial buffer).
-KD_HD int32_t max_chunks(const Dims& m) { return (int32_t)ceil_div(m.S, kChunkMin); }
+// Most chunks any step can use (sizes the partial buffer).
+KD_HD int32_t max_chunks(const Dims& m) { return (int32_t)(chunk_round(m) * kMaxUnits); }
 
-// Word offsets of the exchange buffers (64-bit LL words) for one session.
+// Word offsets of the exchange buffers (64-bit words) for one session.
 struct LLLayout {
   int64_t qkv, attp, o, xp, dp, x, lm, total;
 };
@@ -118,7 +132,7 @@ KD_HD LLLayout ll_layout(const Dims& m) {
   l.attp = take((int64_t)m.hq * max_chunks(m) * (m.hd + 2));
   l.o = take(m.qdim);
   l.xp = take(m.d);
-  l.dp = take((int64_t)m.nwg * m.d);
+  l.dp = take((int64_t)m.nwg * m.d);  // [producer workgroup][d]: each producer's partial is contiguous
   l.x = take(m.d);
   l.lm = take((int64_t)m.nwg * 2);
   l.total = at;

@@ -12,22 +12,22 @@ import numpy as np
 
 TICK_US = 0.01
 LAYER_EVENTS = (
-    "x gathered, RMSNorm",
+    "x gathered",
+    "RMSNorm",
     "QKV rows streamed",
     "QKV reduced, published",
-    "q/k/v gathered, RoPE, KV append",
-    "attention chunk streamed",
-    "chunk partials merged, published",
+    "q/k/v gathered (first unit)",
+    "RoPE, KV append, chunk streamed",
+    "chunk partials published",
     "head merges",
     "o gathered",
     "O rows streamed",
     "O reduced, residual, published",
-    "x' gathered, RMSNorm",
-    "gate/up rows streamed",
-    "SiLU*up",
-    "down slice streamed",
-    "down partials published",
-    "reduce-scatter gathered, x published",
+    "x' gathered",
+    "RMSNorm, gate/up rows streamed",
+    "SiLU*up, down slice streamed+published",
+    "down partials gathered",
+    "x rows summed, published",
 )
 FINAL_EVENTS = ("x gathered, final norm", "LM head streamed", "argmax partial published", "argmax done")
 
