@@ -88,16 +88,119 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
 }
 
-// Butterfly sums: every lane ends with the bitwise-same total.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+// Cross-lane moves without LDS: DPP within 16-lane rows, and gfx950's permlane swaps across rows.
+// (ds_bpermute-based shuffles would queue behind the LDS-DMA writes of the weight stream.)
+constexpr int kDppQuad1 = 0xB1;       // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuad2 = 0x4E;       // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within each 16 lanes
+constexpr int kDppRor8 = 0x128;       // lane i <- (i + 8) mod 16 within each 16 lanes: lane ^ 8
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+// {a, b} = this lane's value and that of lane ^ 16 (or ^ 32), in an order that depends on the lane
+struct LanePair {
+  uint32_t a, b;
+};
+__device__ __forceinline__ LanePair swap16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return {r[0], r[1]};
+}
+__device__ __forceinline__ LanePair swap32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return {r[0], r[1]};
+}
+
+// Sums over groups of 8 / 16 lanes (every lane of a group ends with the bitwise-same value), and
+// butterfly steps that add lane ^ 8, ^ 16, ^ 32. Every step adds two identical operand values in
+// both partner lanes, so all lanes of a group always hold the same bits.
+__device__ __forceinline__ float sum_rows8(float v) {
+  v += dpp_f<kDppQuad1>(v);
+  v += dpp_f<kDppQuad2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
   return v;
 }
+__device__ __forceinline__ float sum_rows16(float v) {
+  const float t = sum_rows8(v);
+  return t + dpp_f<kDppMirror>(t);
+}
+__device__ __forceinline__ float xsum8(float v) { return v + dpp_f<kDppRor8>(v); }
+__device__ __forceinline__ float xsum16(float v) {
+  const LanePair p = swap16(__float_as_uint(v));
+  return __uint_as_float(p.a) + __uint_as_float(p.b);
+}
+__device__ __forceinline__ float xsum32(float v) {
+  const LanePair p = swap32(__float_as_uint(v));
+  return __uint_as_float(p.a) + __uint_as_float(p.b);
+}
+__device__ __forceinline__ float xmax8(float v) { return fmaxf(v, dpp_f<kDppRor8>(v)); }
+__device__ __forceinline__ float xmax16(float v) {
+  const LanePair p = swap16(__float_as_uint(v));
+  return fmaxf(__uint_as_float(p.a), __uint_as_float(p.b));
+}
+__device__ __forceinline__ float xmax32(float v) {
+  const LanePair p = swap32(__float_as_uint(v));
+  return fmaxf(__uint_as_float(p.a), __uint_as_float(p.b));
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return xsum32(xsum16(sum_rows16(v))); }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  v = fmaxf(v, dpp_f<kDppQuad1>(v));
+  v = fmaxf(v, dpp_f<kDppQuad2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return xmax32(xmax16(v));
+}
+
+// Sum over the N lanes that hold one KV position (N = 8, 16 or 32 consecutive lanes).
+template <int N>
+__device__ __forceinline__ float sum_lanes(float v) {
+  if constexpr (N == 8) return sum_rows8(v);
+  else if constexpr (N == 16) return sum_rows16(v);
+  else return xsum16(sum_rows16(v));
+}
+// Sum over the positions of a packet: lanes with the same index modulo N (N = 8, 16 or 32).
+template <int N>
+__device__ __forceinline__ float sum_positions(float v) {
+  v = xsum32(v);
+  if constexpr (N <= 16) v = xsum16(v);
+  if constexpr (N <= 8) v = xsum8(v);
   return v;
+}
+template <int N>
+__device__ __forceinline__ float max_positions(float v) {
+  v = xmax32(v);
+  if constexpr (N <= 16) v = xmax16(v);
+  if constexpr (N <= 8) v = xmax8(v);
+  return v;
+}
+
+// (value, index) maximum over the wave, ties to the lower index; every lane ends with the result.
+__device__ __forceinline__ bool better(float b, int32_t ib, float a, int32_t ia) { return b > a || (b == a && ib < ia); }
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& best, int32_t& besti) {
+  const float ob = dpp_f<CTRL>(best);
+  const int32_t oi = dpp_i<CTRL>(besti);
+  if (better(ob, oi, best, besti)) { best = ob; besti = oi; }
+}
+__device__ __forceinline__ void argmax_swap(LanePair vb, LanePair vi, float& best, int32_t& besti) {
+  const float a = __uint_as_float(vb.a), b = __uint_as_float(vb.b);
+  const int32_t ia = (int32_t)vi.a, ib = (int32_t)vi.b;
+  if (better(b, ib, a, ia)) { best = b; besti = ib; } else { best = a; besti = ia; }
+}
+__device__ __forceinline__ void wave_argmax(float& best, int32_t& besti) {
+  argmax_step<kDppQuad1>(best, besti);
+  argmax_step<kDppQuad2>(best, besti);
+  argmax_step<kDppHalfMirror>(best, besti);
+  argmax_step<kDppMirror>(best, besti);
+  argmax_swap(swap16(__float_as_uint(best)), swap16((uint32_t)besti), best, besti);
+  argmax_swap(swap32(__float_as_uint(best)), swap32((uint32_t)besti), best, besti);
 }
 
 template <int N>
@@ -473,8 +576,7 @@ __device__ __forceinline__ void consume_attention(Ring<RING>& rg, const SegEntry
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < KVPL; ++e) s = fmaf(qv[h][e], kf[e], s);
-#pragma unroll
-        for (int o = LPP / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+        s = sum_lanes<LPP>(s);
         if (valid) {
           mh[h] = fmaxf(mh[h], s);
           if (lane % LPP == 0) sm.u.att.scores[v][(i - sk.lo) * PPP + q_in][h] = s;
@@ -483,9 +585,7 @@ __device__ __forceinline__ void consume_attention(Ring<RING>& rg, const SegEntry
     }
   }
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
-#pragma unroll
-    for (int o = 32; o >= LPP; o >>= 1) mh[h] = fmaxf(mh[h], __shfl_xor(mh[h], o));
+  for (int h = 0; h < kMaxGroup; ++h) mh[h] = max_positions<LPP>(mh[h]);
   // pass 2: V weighted by exp(score - wave max)
   float acc[kMaxGroup][KVPL];
   float lsum[kMaxGroup];
@@ -515,11 +615,10 @@ __device__ __forceinline__ void consume_attention(Ring<RING>& rg, const SegEntry
   }
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
+    if (h < G) {
+      lsum[h] = sum_positions<LPP>(lsum[h]);
 #pragma unroll
-    for (int o = 32; o >= LPP; o >>= 1) {
-      lsum[h] += __shfl_xor(lsum[h], o);
-#pragma unroll
-      for (int k = 0; k < KVPL; ++k) acc[h][k] += __shfl_xor(acc[h][k], o);
+      for (int k = 0; k < KVPL; ++k) acc[h][k] = sum_positions<LPP>(acc[h][k]);
     }
   }
 #pragma unroll
@@ -607,12 +706,27 @@ struct Xchg {
   }
 };
 
+// Gains of the elements thread tid normalises (i = tid + kThreads * j), loaded into registers
+// before the gather that precedes the norm, so their latency hides behind the wait.
+constexpr int kGainRegs = kMaxDim / kThreads;
+template <int WB>
+__device__ __forceinline__ void load_gains(const uint8_t* gain, int d, float (&g)[kGainRegs]) {
+  const int tid = (int)threadIdx.x;
+  // no branches: loads issued back to back are waited for together, by the gather's first poll
+#pragma unroll
+  for (int j = 0; j < kGainRegs; ++j) g[j] = load_w<WB>(gain, min(tid + kThreads * j, d - 1));
+}
+
 // RMSNorm of act[0..d) in place, times the gain; all threads; fixed summation order.
-template <int RING, int WB>
-__device__ __forceinline__ void rmsnorm(Smem<RING>& sm, const uint8_t* gain, int d, float eps) {
+template <int RING>
+__device__ __forceinline__ void rmsnorm(Smem<RING>& sm, const float (&g)[kGainRegs], int d, float eps) {
   const int tid = (int)threadIdx.x, lane = lane_id(), wave = wave_id();
   float ss = 0.f;
-  for (int i = tid; i < d; i += kThreads) ss = fmaf(sm.act[i], sm.act[i], ss);
+#pragma unroll
+  for (int j = 0; j < kGainRegs; ++j) {
+    const int i = tid + kThreads * j;
+    if (i < d) ss = fmaf(sm.act[i], sm.act[i], ss);
+  }
   ss = wave_sum(ss);
   if (lane == 0) sm.red[wave] = ss;
   wg_barrier();
@@ -620,7 +734,11 @@ __device__ __forceinline__ void rmsnorm(Smem<RING>& sm, const uint8_t* gain, int
 #pragma unroll
   for (int v = 0; v < kWaves; ++v) tot += sm.red[v];
   const float r = 1.0f / sqrtf(tot / (float)d + eps);
-  for (int i = tid; i < d; i += kThreads) sm.act[i] = sm.act[i] * r * load_w<WB>(gain, i);
+#pragma unroll
+  for (int j = 0; j < kGainRegs; ++j) {
+    const int i = tid + kThreads * j;
+    if (i < d) sm.act[i] = sm.act[i] * r * g[j];
+  }
   wg_barrier();
 }
 
@@ -728,16 +846,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   Xchg<RING> xc{P, __builtin_amdgcn_make_buffer_rsrc(P.ll, (short)0, (int)(P.lo.total * 8), 0x00020000), sm};
   const float inv_sqrt_hd = 1.0f / sqrtf((float)m.hd);
   const SegEntry* tab = sm.segs[wave];
+  float gains[kGainRegs];
   stamp(1);
 
   for (int layer = 0; layer < m.L; ++layer) {
     const uint8_t* g_attn = P.norms + ((int64_t)layer * 2 + 0) * m.d * m.wbytes;
     const uint8_t* g_ffn = P.norms + ((int64_t)layer * 2 + 1) * m.d * m.wbytes;
     // ---- x, RMSNorm ----
+    load_gains<WB>(g_attn, m.d, gains);
     if (layer > 0 && !xc.gather_vec(ll_tag(m, P.seq, layer - 1, kX), P.lo.x, m.d, sm.act)) goto drain;
     stamp(trace_slot(layer, 0));
     if (tid < nrd) sm.xo[tid] = sm.act[rd0 + tid];
-    rmsnorm<RING, WB>(sm, g_attn, m.d, P.eps);
+    rmsnorm<RING>(sm, gains, m.d, P.eps);
     stamp(trace_slot(layer, 1));
     // ---- QKV rows ----
     consume_rows<RING, WB>(rg, tab[0], m.cd, sm.act, sm.rowpart[wave]);
@@ -787,6 +907,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
           vec[i + half] = (a * s + b * c) * sc;
         }
         wg_barrier();
+        if (k == 0) stamp(trace_slot(layer, 5));
         if (tid < m.hd) {
           const int i = tid;
           float kk = sm.u.att.kp[i], vv = sm.u.att.vp[i];
@@ -810,6 +931,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
           sm.u.att.vp[i] = vv;
         }
         wg_barrier();
+        if (k == 0) stamp(trace_slot(layer, 6));
       }
       // score of the current position (last chunk only), one wave per query head
       if (u.last && wave < G) {
@@ -819,8 +941,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         if (lane == 0) sm.u.att.sp[wave] = t;
       }
       consume_attention<RING, KB, HD>(rg, tab[1 + 2 * k], u, G, sm, wave, sm.act + (int64_t)wave * kMaxGroup * HD);
+      if (k == 0) stamp(trace_slot(layer, 7));
       wg_barrier();
-      if (k == 0) stamp(trace_slot(layer, 5));
+      if (k == 0) stamp(trace_slot(layer, 8));
       // combine the waves' partial softmax sums (plus the current position in the last chunk)
       if (tid < G * m.hd) {
         const int h = tid / m.hd, i = tid - h * m.hd;
@@ -853,6 +976,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
           ll_store(P.ll, at + 1, Lsum, tag);
         }
       }
+      if (k == 0) stamp(trace_slot(layer, 9));
       // the per-wave sums must stay readable until every thread has combined them: clear the
       // unused wave slots of the next unit only after this barrier
       wg_barrier();
@@ -860,7 +984,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       for (int h = 0; h < kMaxGroup; ++h)
         if (lane == 0) sm.u.att.ml[wave][h][1] = 0.f;
     }
-    stamp(trace_slot(layer, 6));
+    stamp(trace_slot(layer, 10));
     // ---- merge units: one slice of one head's output, over all chunks ----
     for (int k = 0; k < nmerge_here; ++k) {
       const int mu = mfirst + k * m.nwg;
@@ -883,6 +1007,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
             st[c * (2 + MS) + 2 * t + 1] = b;
           });
       if (!ok) goto drain;
+      if (k == 0) stamp(trace_slot(layer, 11));
       if (wave == 0) {
         float M = -INFINITY;
         for (int c = lane; c < NC; c += 64) M = fmaxf(M, st[c * (2 + MS)]);
@@ -900,35 +1025,38 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       }
       wg_barrier();
     }
-    stamp(trace_slot(layer, 7));
+    stamp(trace_slot(layer, 12));
     // ---- output projection rows + residual ----
     if (!xc.gather_vec(ll_tag(m, P.seq, layer, kO), P.lo.o, m.qdim, sm.act)) goto drain;
-    stamp(trace_slot(layer, 8));
+    stamp(trace_slot(layer, 13));
     consume_rows<RING, WB>(rg, tab[oseg], m.cq, sm.act, sm.rowpart[wave]);
     wg_barrier();
-    stamp(trace_slot(layer, 9));
+    stamp(trace_slot(layer, 14));
     if (tid < nrd) {
       const float xp = sm.xo[tid] + row_total(sm, kTileO, m.cq, tid);
       sm.xo[tid] = xp;
       ll_store(P.ll, P.lo.xp + rd0 + tid, xp, ll_tag(m, P.seq, layer, kXP));
     }
-    stamp(trace_slot(layer, 10));
+    stamp(trace_slot(layer, 15));
     // ---- gate/up rows of this workgroup's FFN slice ----
+    load_gains<WB>(g_ffn, m.d, gains);
     if (!xc.gather_vec(ll_tag(m, P.seq, layer, kXP), P.lo.xp, m.d, sm.act)) goto drain;
-    stamp(trace_slot(layer, 11));
-    rmsnorm<RING, WB>(sm, g_ffn, m.d, P.eps);
+    stamp(trace_slot(layer, 16));
+    rmsnorm<RING>(sm, gains, m.d, P.eps);
+    stamp(trace_slot(layer, 17));
     consume_rows<RING, WB>(rg, tab[oseg + 1], m.cd, sm.act, sm.rowpart[wave]);
     wg_barrier();
-    stamp(trace_slot(layer, 12));
+    stamp(trace_slot(layer, 18));
     if (tid < nf) {
       const float gt = row_total(sm, kTileGU, m.cd, tid);
       const float up = row_total(sm, kTileGU, m.cd, nf + tid);
       sm.a[tid] = gt / (1.0f + __expf(-gt)) * up;
     }
     wg_barrier();
+    stamp(trace_slot(layer, 19));
     // ---- down projection of the slice, for all d rows, published block by block ----
     consume_down<RING, WB>(rg, tab[oseg + 2], gD, sm.a, P.ll, P.lo.dp + (int64_t)w * m.d, ll_tag(m, P.seq, layer, kDP));
-    stamp(trace_slot(layer, 13));
+    stamp(trace_slot(layer, 20));
     // ---- sum every slice's contribution to this workgroup's rows; residual add ----
     {
       float* st = sm.u.stage;  // [nwg][nrd]
@@ -945,7 +1073,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
                             st[2 * k2 + 1] = b;
                           });
       if (!ok) goto drain;
-      stamp(trace_slot(layer, 14));
+      stamp(trace_slot(layer, 21));
       // one wave per row: lanes take producers lane, lane+64, ... in order, then a butterfly
       for (int r = wave; r < nrd; r += kWaves) {
         float s = 0.f;
@@ -955,12 +1083,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       }
       wg_barrier();  // the staging area is reused by the next layer's attention
     }
-    stamp(trace_slot(layer, 15));
+    stamp(trace_slot(layer, 22));
   }
 
   // ---- final norm, LM head rows, argmax ----
+  load_gains<WB>(P.norms + (int64_t)m.L * 2 * m.d * m.wbytes, m.d, gains);
   if (!xc.gather_vec(ll_tag(m, P.seq, m.L - 1, kX), P.lo.x, m.d, sm.act)) goto drain;
-  rmsnorm<RING, WB>(sm, P.norms + (int64_t)m.L * 2 * m.d * m.wbytes, m.d, P.eps);
+  rmsnorm<RING>(sm, gains, m.d, P.eps);
   stamp(trace_slot(m.L, 0));
   consume_rows<RING, WB>(rg, sm.lm_seg[wave], m.cd, sm.act, sm.rowpart[wave]);
   wg_barrier();
@@ -973,13 +1102,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       const float val = row_total(sm, kTileLM, m.cd, r);
       if (P.logits) P.logits[rl0 + r] = val;
       if (val != val) { nan = true; continue; }
-      if (val > best || (val == best && rl0 + r < besti)) { best = val; besti = rl0 + r; }
+      if (better(val, rl0 + r, best, besti)) { best = val; besti = rl0 + r; }
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ob = __shfl_xor(best, o);
-      const int32_t oi = __shfl_xor(besti, o);
-      if (ob > best || (ob == best && oi < besti)) { best = ob; besti = oi; }
-    }
+    wave_argmax(best, besti);
     if (__any(nan) && lane == 0) __hip_atomic_fetch_or(P.status, kStatusNaN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (lane == 0) {
       sm.red[wave] = best;
@@ -988,7 +1113,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     wg_barrier();
     if (tid == 0) {
       for (int v = 1; v < kWaves; ++v)
-        if (sm.red[v] > best || (sm.red[v] == best && sm.redi[v] < besti)) { best = sm.red[v]; besti = sm.redi[v]; }
+        if (better(sm.red[v], sm.redi[v], best, besti)) { best = sm.red[v]; besti = sm.redi[v]; }
       const uint32_t tag = ll_tag(m, P.seq, m.L, kLM);
       ll_store_bits(P.ll, P.lo.lm + 2 * w, __float_as_uint(best), tag);
       ll_store_bits(P.ll, P.lo.lm + 2 * w + 1, (uint32_t)besti, tag);
@@ -1008,13 +1133,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       for (int k = lane; k < m.nwg; k += 64) {
         const float a = sm.u.stage[2 * k];
         const int32_t idx = (int32_t)__float_as_uint(sm.u.stage[2 * k + 1]);
-        if (a > best || (a == best && idx < besti)) { best = a; besti = idx; }
+        if (better(a, idx, best, besti)) { best = a; besti = idx; }
       }
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ob = __shfl_xor(best, o);
-        const int32_t oi = __shfl_xor(besti, o);
-        if (ob > best || (ob == best && oi < besti)) { best = ob; besti = oi; }
-      }
+      wave_argmax(best, besti);
       if (lane == 0) {
         P.tokens[0] = besti == 0x7fffffff ? 0 : besti;
         P.positions[0] = si.p + 1;

@@ -141,7 +141,7 @@ KD_HD LLLayout ll_layout(const Dims& m) {
 
 // Step trace: per workgroup, slots 0-1 (start, setup done), kTraceLayerEvents phase
 // boundaries per layer, then 4 for the final norm, LM head and argmax.
-constexpr int kTraceLayerEvents = 16;
+constexpr int kTraceLayerEvents = 24;
 KD_HD int64_t trace_stride(int L) { return 2 + (int64_t)kTraceLayerEvents * L + 4; }
 
 // Tag of vector `kind` of layer `layer` (layer == L for the LM head) in step `seq`.

@@ -8,6 +8,8 @@ attention unit assigned) holds 0 and is skipped.
 
 from __future__ import annotations
 
+import warnings
+
 import numpy as np
 
 TICK_US = 0.01
@@ -17,17 +19,25 @@ LAYER_EVENTS = (
     "QKV rows streamed",
     "QKV reduced, published",
     "q/k/v gathered (first unit)",
-    "RoPE, KV append, chunk streamed",
+    "RoPE",
+    "K/V rounded, appended",
+    "chunk streamed",
+    "waves joined",
     "chunk partials published",
-    "head merges",
+    "attention units done",
+    "merge partials gathered",
+    "head merges done",
     "o gathered",
     "O rows streamed",
     "O reduced, residual, published",
     "x' gathered",
-    "RMSNorm, gate/up rows streamed",
-    "SiLU*up, down slice streamed+published",
+    "RMSNorm (FFN)",
+    "gate/up rows streamed",
+    "SiLU*up",
+    "down slice streamed, published",
     "down partials gathered",
     "x rows summed, published",
+    "(unused)",
 )
 FINAL_EVENTS = ("x gathered, final norm", "LM head streamed", "argmax partial published", "argmax done")
 
@@ -70,4 +80,35 @@ def summary(buf: np.ndarray, n_layers: int, n_wg: int) -> str:
         per_layer = float(np.nanmedian(v)) if v.ndim == 2 and np.isfinite(v).any() else float("nan")
         lines.append(f"  {name:38s} {med:9.1f} us/step" + (f"   ({per_layer:6.2f} us/layer median)" if v.ndim == 2 else ""))
     lines.append(f"  {'sum of medians':38s} {acc:9.1f} us/step")
+    return "\n".join(lines)
+
+
+def critical_path(buf: np.ndarray, n_layers: int, n_wg: int) -> str:
+    """When the last workgroup reached each boundary, as the median over layers of the time since
+    the last workgroup reached the previous boundary (the step's critical path, event by event)."""
+    st = stride(n_layers)
+    t = np.asarray(buf, np.int64)[: n_wg * st].reshape(n_wg, st).astype(np.float64)
+    t[t == 0] = np.nan
+    ev = len(LAYER_EVENTS)
+    lay = t[:, 2 : 2 + ev * n_layers].reshape(n_wg, n_layers, ev)
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore", RuntimeWarning)  # boundaries no workgroup reached
+        last = np.nanmax(lay, axis=0)  # [layer, event]
+        first = np.nanmin(lay, axis=0)
+    lines = ["critical path per layer (median over layers; last WG to reach each boundary):"]
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore", RuntimeWarning)
+        prev_end = np.nanmax(last, axis=1)  # latest boundary any workgroup reached in each layer
+    prev = np.concatenate([[np.nanmax(t[:, 1])], prev_end[:-1]])
+    acc = 0.0
+    for e in range(ev):
+        if np.all(np.isnan(last[:, e])):
+            continue
+        d = (last[:, e] - prev) * TICK_US
+        spread = (last[:, e] - first[:, e]) * TICK_US
+        med = float(np.nanmedian(d))
+        acc += med
+        lines.append(f"  {LAYER_EVENTS[e]:34s} +{med:7.2f} us   (first..last WG spread {float(np.nanmedian(spread)):6.2f} us)")
+        prev = np.where(np.isnan(last[:, e]), prev, last[:, e])
+    lines.append(f"  {'layer total':34s} {acc:8.2f} us")
     return "\n".join(lines)

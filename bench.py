@@ -97,6 +97,7 @@ def main() -> int:
     ap.add_argument("--workload", default="2b", choices=["tiny", "2b", "8b", "2b_long"])
     ap.add_argument("--cpu-steps", type=int, default=3, help="oracle decode steps timed for cpu_baseline (0: skip)")
     ap.add_argument("--trace", action="store_true", help="after timing, trace one step and print its phase breakdown")
+    ap.add_argument("--trace-out", default=None, help="with --trace: also save the raw timestamp buffer (.npy)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -193,7 +194,11 @@ def main() -> int:
             dec.step()
         torch.cuda.synchronize()
         kd.kd_trace(dec.handle, None, 0)
-        log("phase breakdown of one traced step:\n" + tr.summary(buf.cpu().numpy(), m.n_layers, info["workgroups"]))
+        raw = buf.cpu().numpy()
+        log("phase breakdown of one traced step:\n" + tr.summary(raw, m.n_layers, info["workgroups"]))
+        log(tr.critical_path(raw, m.n_layers, info["workgroups"]))
+        if args.trace_out:
+            np.save(args.trace_out, raw)
 
     cpu = None
     if args.cpu_steps > 0:

@@ -159,7 +159,7 @@ const char* kd_strerror(int code);
  * Step tracing, for measurement.  With dev_buf non-NULL, every later kd_step writes 64-bit
  * timestamps of the GPU's 100 MHz constant clock at its phase boundaries: workgroup w uses
  * dev_buf[w * stride .. (w + 1) * stride).  Slot 0 is the step start, slot 1 the end of setup,
- * slots 2 + 16*l + e (e < 16) the phase boundaries of layer l, and the last 4 slots the final
+ * slots 2 + 24*l + e (e < 24) the phase boundaries of layer l, and the last 4 slots the final
  * norm, LM head and argmax.  dev_buf is device memory of at least stride * workgroups words,
  * owned by the caller; NULL turns tracing off.  *stride (optional) receives the stride.
  * Returns KD_ERR_INVALID_ARG if the buffer is too small.

@@ -4,9 +4,12 @@ import numpy as np
 
 from bandwidth_bound_transformer_amd import trace
 
+EV = len(trace.LAYER_EVENTS)
 
-def test_intervals_of_a_synthetic_trace():
-    L, nwg = 2, 3
+
+def _synthetic(L, nwg, skip_wg=1, skip=(4, 5)):
+    """Workgroup w starts at 1000 + 10 w; boundary e of every layer comes 50 (e + 1) ticks after
+    the previous reached one; workgroup `skip_wg` never reaches the boundaries in `skip`."""
     st = trace.stride(L)
     buf = np.zeros(nwg * st, np.uint64)
     for w in range(nwg):
@@ -16,20 +19,40 @@ def test_intervals_of_a_synthetic_trace():
         row[1] = t + 100  # setup: 1 us
         tick = t + 100
         for l in range(L):
-            for e in range(len(trace.LAYER_EVENTS)):
-                if w == 1 and e in (4, 5):
+            for e in range(EV - 1):  # the last slot of a layer is not stamped
+                if w == skip_wg and e in skip:
                     continue  # this workgroup had no attention unit
                 tick += 50 * (e + 1)
-                row[2 + 16 * l + e] = tick
+                row[2 + EV * l + e] = tick
         for e in range(4):
             tick += 7
-            row[2 + 16 * L + e] = tick
+            row[2 + EV * L + e] = tick
+    return buf
+
+
+def test_layout_matches_kernel():
+    assert EV == 24 and trace.stride(3) == 2 + 24 * 3 + 4
+
+
+def test_intervals_of_a_synthetic_trace():
+    L, nwg = 2, 3
+    buf = _synthetic(L, nwg)
     parts, total = trace.intervals(buf, L, nwg)
-    assert np.allclose(parts["QKV rows streamed"], 1.5)  # 150 ticks
-    assert np.isnan(parts["RoPE, KV append, chunk streamed"][1]).all()
-    # the boundary after a skipped one measures from the last reached one
-    assert np.allclose(parts["chunk partials published"][1], 50 * 7 * 0.01)
+    assert np.allclose(parts[trace.LAYER_EVENTS[2]], 1.5)  # 150 ticks
+    assert np.isnan(parts[trace.LAYER_EVENTS[5]][1]).all()
+    # the boundary after skipped ones measures from the last reached one (boundary 3)
+    assert np.allclose(parts[trace.LAYER_EVENTS[6]][1], 50 * 7 * 0.01)
     assert np.allclose(parts["argmax done"], 0.07)
     assert total.shape == (nwg,) and np.all(total > 0)
     text = trace.summary(buf, L, nwg)
     assert "x gathered" in text and "sum of medians" in text
+
+
+def test_critical_path_follows_the_last_workgroup():
+    L, nwg = 2, 3
+    buf = _synthetic(L, nwg, skip_wg=-1)
+    text = trace.critical_path(buf, L, nwg)
+    # every boundary is 50 (e + 1) ticks after the previous one in every workgroup
+    for e in (0, 3, 10):
+        line = next(x for x in text.splitlines() if x.strip().startswith(trace.LAYER_EVENTS[e]))
+        assert f"+{0.5 * (e + 1):7.2f} us" in line
