@@ -98,6 +98,9 @@ def main() -> int:
     ap.add_argument("--cpu-steps", type=int, default=3, help="oracle decode steps timed for cpu_baseline (0: skip)")
     ap.add_argument("--trace", action="store_true", help="after timing, trace one step and print its phase breakdown")
     ap.add_argument("--trace-out", default=None, help="with --trace: also save the raw timestamp buffer (.npy)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before decoding, copy MIB MiB once with a plain device copy; HBM-traffic counters read on "
+                         "that copy calibrate the counters read on the decode kernel (profiling runs only)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -123,6 +126,15 @@ def main() -> int:
     weights = workloads.make_weights(m, seed=wl.weight_seed)
     log(f"weights generated in {time.perf_counter() - t0:.1f} s")
     torch.cuda.set_device(0)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
     dec = kd.Decoder(m, weights, max_seq=wl.max_seq, device="cuda:0")
     info = kd.kd_get_info(dec.handle)
     log(f"kd_init done: {info}")
