@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "kd.h"
+#include "kd_batch_host.h"
 #include "kd_device.h"
 #include "kd_pack.h"
 
@@ -64,6 +65,8 @@ struct kd_handle {
   uint32_t seq = 0;
   int64_t lds_bytes = 0;
   uint64_t* trace = nullptr;
+  bool batched = false;  // B > 1: the lockstep-sessions path (kd_batch.h)
+  kd::bt::BatchState bs;
 };
 
 namespace {
@@ -189,6 +192,28 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
 
   const int wb = dtype_bytes(cfg->weight_dtype), kb = dtype_bytes(cfg->kv_dtype);
   const int nwg = prop.multiProcessorCount;
+  if (cfg->batch > 1) {
+    rc = kd::bt::batch_check(cfg);
+    if (rc != KD_OK) return rc;
+    kd_handle* hb = new (std::nothrow) kd_handle();
+    if (!hb) return KD_ERR_OOM;
+    hb->device = dev;
+    hb->cfg = *cfg;
+    hb->batched = true;
+    if (hipMalloc(&hb->buf.flags, 256) != hipSuccess) {
+      delete hb;
+      return KD_ERR_OOM;
+    }
+    if (hipMemset(hb->buf.flags, 0, 256) != hipSuccess) rc = KD_ERR_HIP;
+    if (rc == KD_OK) rc = kd::bt::batch_init(cfg, w, nwg, hb->bs);
+    if (rc != KD_OK) {
+      free_buffers(hb->buf);
+      delete hb;
+      return rc;
+    }
+    *out = hb;
+    return KD_OK;
+  }
   const kd::Dims m = kd::make_dims(cfg->n_layers, cfg->d_model, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->ffn_dim,
                                    cfg->vocab, cfg->max_seq, nwg, wb, kb);
   rc = check_supported(cfg, m);
@@ -288,6 +313,11 @@ int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* 
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return KD_ERR_HIP;
   if (cur != h->device && hipSetDevice(h->device) != hipSuccess) return KD_ERR_HIP;
+  if (h->batched) {
+    const int rcb = kd::bt::batch_step(h->bs, tokens, positions, kv, logits, (hipStream_t)stream, h->buf.flags);
+    if (cur != h->device) (void)hipSetDevice(cur);
+    return rcb;
+  }
   kd::Params P{};
   P.blob = h->buf.blob;
   P.embed = h->buf.embed;
@@ -337,12 +367,14 @@ void kd_destroy(kd_handle* h) {
   (void)hipSetDevice(h->device);
   (void)hipDeviceSynchronize();
   free_buffers(h->buf);
+  if (h->batched) kd::bt::batch_free(h->bs);
   if (cur >= 0) (void)hipSetDevice(cur);
   delete h;
 }
 
 int kd_trace(kd_handle* h, uint64_t* dev_buf, int64_t words, int64_t* stride) {
   if (!h) return KD_ERR_INVALID_ARG;
+  if (h->batched) return KD_ERR_UNSUPPORTED;
   const int64_t st = kd::trace_stride(h->m.L);
   if (stride) *stride = st;
   if (!dev_buf) {
@@ -357,6 +389,16 @@ int kd_trace(kd_handle* h, uint64_t* dev_buf, int64_t words, int64_t* stride) {
 int kd_get_info(kd_handle* h, int64_t info[8]) {
   if (!h || !info) return KD_ERR_INVALID_ARG;
   for (int i = 0; i < 8; ++i) info[i] = 0;
+  if (h->batched) {
+    const kd::bt::BatchState& b = h->bs;
+    info[0] = 0;
+    info[1] = kd::bt::kGemmThreads;
+    info[2] = (int64_t)(b.w_lm + (size_t)b.V * b.d) * 2 + (int64_t)b.V * b.d * 2 + (int64_t)(2 * b.L + 1) * b.d * 2;
+    info[5] = kd::bt::batch_kernels_per_tick(b);
+    info[6] = b.g_qkv.KS | (b.g_o.KS << 8) | (b.g_gu.KS << 16) | (b.g_d.KS << 24);
+    info[7] = b.CH;
+    return KD_OK;
+  }
   info[0] = h->m.nwg;
   info[1] = kd::kThreads;
   info[2] = h->m.blob_elems * h->m.wbytes + (int64_t)h->m.V * h->m.d * h->m.wbytes + (int64_t)(2 * h->m.L + 1) * h->m.d * h->m.wbytes;

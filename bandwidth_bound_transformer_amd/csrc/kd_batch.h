@@ -1,0 +1,482 @@
+// kd_batch.h -- decode step of B > 1 sessions stepped in lockstep, for gfx950.
+//
+// All due sessions advance together, so each weight is read once per tick for the whole group
+// rather than once per session ("Why is real-time AI inference 56x more expensive? Continuous
+// inference and resident kernels", section "advance all active sessions in lockstep"). With
+// B sessions the projections become small-M GEMMs: B rows (padded to 64) times the weight matrix.
+// They run on the matrix cores (v_mfma_f32_16x16x32_bf16) so that they stay bound by the weight
+// stream instead of by fp32 vector arithmetic. Activations are fp32; each is fed to the matrix
+// cores as a bf16 pair (hi = bf16(x), lo = bf16(x - hi)), two products per weight, so the result
+// keeps about 16 significant bits of the activation instead of 8.
+//
+// One tick is a fixed sequence of kernels on the caller's stream (no host work between them):
+//   check --> embed+norm --> per layer:
+//     QKV GEMM --> reduce+RoPE+KV append --> attention chunks --> merge (o as hi/lo)
+//     --> O GEMM --> residual+norm --> gate/up GEMM --> SiLU*up (hi/lo) --> down GEMM
+//     --> residual+norm (next layer's norm, or the final one)
+//   --> LM-head GEMM (logits) --> argmax (next token, position + 1)
+// A GEMM writes split-K partial sums; the kernel after it adds them in a fixed order, so results
+// are bitwise reproducible.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace kd {
+namespace bt {
+
+constexpr int kM = 64;             // sessions padded to four 16-row MFMA tiles
+constexpr int kNB = 64;            // GEMM output columns per workgroup: 4 waves x 16
+constexpr int kKC = 128;           // K per LDS chunk of the activation block
+constexpr int kGemmThreads = 256;
+constexpr int kAttThreads = 256;   // 4 waves; 16 lanes per KV position (hd = 128, bf16)
+constexpr int kMaxG = 4;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// float32 -> bfloat16, round to nearest, ties to even; NaN -> quiet NaN.
+__device__ __forceinline__ uint16_t f_to_bf16(float x) {
+  uint32_t b = __float_as_uint(x);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+}
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ void split_hilo(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f_to_bf16(x);
+  lo = f_to_bf16(x - bf16_to_f(hi));
+}
+
+// Sum over each group of 16 lanes (every lane of the group gets the same bits), without LDS.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dppf<0xB1>(v);   // lane ^ 1
+  v += dppf<0x4E>(v);   // lane ^ 2
+  v += dppf<0x141>(v);  // half-row mirror: groups of 4 -> 8
+  v += dppf<0x140>(v);  // row mirror: groups of 8 -> 16
+  return v;
+}
+// {this lane, lane ^ 16} and {this lane, lane ^ 32} (order depends on the lane)
+__device__ __forceinline__ void swap16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float wsum(float v) {
+  float a, b;
+  v = sum16(v);
+  swap16(v, a, b);
+  v = a + b;
+  swap32(v, a, b);
+  return a + b;
+}
+
+// ---------------------------------------------------------------------------------------------
+// tick validation: every later kernel of the tick reads *skip and writes nothing when it is set
+// ---------------------------------------------------------------------------------------------
+__global__ void check_kernel(const int32_t* tokens, const int32_t* positions, int B, int V, int max_seq,
+                             uint32_t* status, uint32_t* skip) {
+  uint32_t bits = 0;
+  for (int b = 0; b < B; ++b) {
+    if (tokens[b] < 0 || tokens[b] >= V) bits |= 0x1u;
+    if (positions[b] < 0 || positions[b] >= max_seq) bits |= 0x2u;
+  }
+  if (bits) __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  *skip = bits ? 1u : 0u;
+}
+
+// ---------------------------------------------------------------------------------------------
+// small-M GEMM on MFMA: P[s][m][n] = sum over K-range s of (Ahi[m][k] + Alo[m][k]) * W[n][k]
+// ---------------------------------------------------------------------------------------------
+// Grid: (N / kNB) * KS workgroups; unit u covers columns [64 (u / KS), +64) and K range u % KS.
+// Wave w owns 16 output columns. Lane l streams weight row n = n0 + 16w + l % 16; for each 128-K
+// chunk it loads the 64 contiguous bytes k = 32 (l / 16) .. + 32. The matrix-core K order is
+// permuted to match (step t uses k = 32 (l / 16) + 8 t + j), and the activation fragments are
+// read from LDS in that same order, so the sum is unchanged. The activation block (64 rows x 128
+// K, hi and lo) is staged through LDS once per chunk and shared by the four waves.
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint16_t* __restrict__ W, int N, int K,
+                                                                const uint16_t* __restrict__ Ahi,
+                                                                const uint16_t* __restrict__ Alo, int lda,
+                                                                float* __restrict__ P, int KS, int B, const uint32_t* skip) {
+  if (*skip) return;
+  // [buffer][hi, lo][row][16-byte chunk of the 128-K slice, padded by one against bank conflicts]
+  __shared__ uint4 As[2][2][kM][kKC / 8 + 1];
+  const int unit = (int)blockIdx.x;
+  const int nb = unit / KS, s = unit - nb * KS;
+  const int Kr = K / KS, k0 = s * Kr, nchunks = Kr / kKC;
+  const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int q = lane >> 4;
+  const int n = nb * kNB + wave * 16 + (lane & 15);
+  const u32x4* wrow = (const u32x4*)(W + (size_t)n * K + k0 + q * 32);
+
+  // activation loader: 2 x 64 rows x 16 chunks of 16 bytes = 2048 pieces, 8 per thread
+  uint4 areg[8];
+  auto load_a = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = tid + kGemmThreads * j;
+      const int hl = idx >> 10, r = (idx >> 4) & 63, cc = idx & 15;
+      const uint16_t* src = (hl ? Alo : Ahi) + (size_t)r * lda + k0 + c * kKC + cc * 8;
+      areg[j] = *(const uint4*)src;
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = tid + kGemmThreads * j;
+      const int hl = idx >> 10, r = (idx >> 4) & 63, cc = idx & 15;
+      As[buf][hl][r][cc] = areg[j];
+    }
+  };
+  // weights are read once per tick: non-temporal loads
+  u32x4 wcur[4], wnext[4];
+  auto load_w = [&](int c, u32x4 (&dst)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dst[t] = __builtin_nontemporal_load(wrow + (size_t)c * (kKC / 8) + t);
+  };
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_a(0);
+  load_w(0, wcur);
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    store_a(buf);
+    __syncthreads();
+    if (c + 1 < nchunks) {
+      load_a(c + 1);
+      load_w(c + 1, wnext);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 bw = __builtin_bit_cast(bf16x8, wcur[t]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int r = mt * 16 + (lane & 15);
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, As[buf][0][r][q * 4 + t]);
+        const bf16x8 al = __builtin_bit_cast(bf16x8, As[buf][1][r][q * 4 + t]);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[mt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) wcur[t] = wnext[t];
+  }
+  // lane l holds rows 16 mt + 4 (l / 16) + i of column n
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mt * 16 + q * 4 + i;
+      if (m < B) P[((size_t)s * B + m) * N + n] = acc[mt][i];
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// residual + RMSNorm: X[b] (+)= sum of partials (or the embedding row), then H = RMSNorm(X) * g as hi/lo
+// ---------------------------------------------------------------------------------------------
+// Grid: B workgroups of 256 threads. mode 0: X[b] = E[tokens[b]]; mode 1: X[b] += sum_s P[s][b].
+__global__ __launch_bounds__(256) void residual_norm_kernel(int mode, const uint16_t* __restrict__ E,
+                                                             const int32_t* __restrict__ tokens,
+                                                             const float* __restrict__ P, int KS, float* __restrict__ X,
+                                                             const uint16_t* __restrict__ gain, int d, float eps,
+                                                             uint16_t* __restrict__ Ahi, uint16_t* __restrict__ Alo,
+                                                             int lda, int B, const uint32_t* skip) {
+  if (*skip) return;
+  __shared__ float red[4];
+  const int b = (int)blockIdx.x, tid = (int)threadIdx.x;
+  float* x = X + (size_t)b * d;
+  float ss = 0.f;
+  const int64_t tok = mode == 0 ? (int64_t)tokens[b] : 0;
+  for (int i = tid; i < d; i += 256) {
+    float v;
+    if (mode == 0) {
+      v = bf16_to_f(E[tok * d + i]);
+    } else {
+      v = x[i];
+      for (int s = 0; s < KS; ++s) v += P[((size_t)s * B + b) * d + i];
+    }
+    x[i] = v;
+    ss = fmaf(v, v, ss);
+  }
+  ss = wsum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float r = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int i = tid; i < d; i += 256) {
+    uint16_t hi, lo;
+    split_hilo(x[i] * r * bf16_to_f(gain[i]), hi, lo);
+    Ahi[(size_t)b * lda + i] = hi;
+    Alo[(size_t)b * lda + i] = lo;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// QKV: sum partials, RoPE on q and k, scale q by 1/sqrt(hd), append rounded K and V to the cache
+// ---------------------------------------------------------------------------------------------
+// Grid: (hq + 2 hkv, B) workgroups of hd threads; workgroup (head, b) owns one head vector.
+__global__ __launch_bounds__(128) void qkv_epilogue_kernel(const float* __restrict__ P, int KS, int nqkv, int hq, int hkv,
+                                                            int hd, const float2* __restrict__ rope,
+                                                            const int32_t* __restrict__ positions, float* __restrict__ Qs,
+                                                            uint16_t* __restrict__ kv, int64_t kv_slot, int64_t kv_sess,
+                                                            int64_t kv_head, int B, const uint32_t* skip) {
+  if (*skip) return;
+  __shared__ float v[128];
+  const int head = (int)blockIdx.x, b = (int)blockIdx.y, i = (int)threadIdx.x;
+  const int p = positions[b];
+  float x = 0.f;
+  for (int s = 0; s < KS; ++s) x += P[((size_t)s * B + b) * nqkv + head * hd + i];
+  const int half = hd / 2;
+  if (head < hq + hkv) {  // q or k: rotate pair (i, i + hd/2) by the angle of position p
+    v[i] = x;
+    __syncthreads();
+    const float2 cs = rope[(int64_t)p * half + (i % half)];
+    x = i < half ? v[i] * cs.x - v[i + half] * cs.y : v[i - half] * cs.y + v[i] * cs.x;
+  }
+  if (head < hq) {
+    Qs[(size_t)b * hq * hd + head * hd + i] = x * (1.0f / sqrtf((float)hd));
+  } else {
+    const int slot = head < hq + hkv ? 0 : 1;
+    const int g = head - hq - slot * hkv;
+    kv[kv_slot * slot + kv_sess * b + kv_head * g + (int64_t)p * hd + i] = f_to_bf16(x);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// attention over one chunk of positions of one (session, kv head), for its G query heads
+// ---------------------------------------------------------------------------------------------
+// Grid: (NCmax, hkv, B) workgroups of 4 waves. Chunk c covers positions [c CH, min((c+1) CH, p+1)),
+// where p is the session's current position (already appended). 16 lanes hold one position (8 dims
+// each, hd = 128); a wave reads 4 positions per 1 KB load, and waves take packets round-robin.
+// Each lane group keeps a running (max, sum, acc) per head; groups and waves are then merged.
+// Output: part[((b hq + h) NCmax + c) (hd + 2) + {0: max, 1: sum, 2 + i: acc_i}].
+__global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __restrict__ Qs,
+                                                                 const uint16_t* __restrict__ kv, int64_t kv_slot,
+                                                                 int64_t kv_sess, int64_t kv_head,
+                                                                 const int32_t* __restrict__ positions, int hq, int hkv,
+                                                                 int CH, int NCmax, float* __restrict__ part,
+                                                                 const uint32_t* skip) {
+  if (*skip) return;
+  constexpr int HD = 128;
+  __shared__ float sm[4][kMaxG][HD + 2];
+  const int c = (int)blockIdx.x, g = (int)blockIdx.y, b = (int)blockIdx.z;
+  const int G = hq / hkv;
+  const int P1 = positions[b] + 1;
+  const int j0 = c * CH;
+  if (j0 >= P1) return;
+  const int j1 = min(j0 + CH, P1);
+  const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = lane >> 4, dim0 = (lane & 15) * 8;
+  float qv[kMaxG][8];
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[h][e] = h < G ? Qs[((size_t)b * hq + g * G + h) * HD + dim0 + e] : 0.f;
+  float mx[kMaxG], ls[kMaxG], acc[kMaxG][8];
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    mx[h] = -INFINITY;
+    ls[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+  const uint16_t* kbase = kv + kv_sess * b + kv_head * g + dim0;
+  const uint16_t* vbase = kbase + kv_slot;
+  const int npk = (j1 - j0 + 3) / 4;
+  for (int k = wave; k < npk; k += 4) {
+    const int pos = j0 + 4 * k + grp;
+    const bool valid = pos < j1;
+    const int pl = valid ? pos : j0;  // stay inside the chunk's cached positions
+    const uint4 kw = *(const uint4*)(kbase + (int64_t)pl * HD);
+    const uint4 vw = *(const uint4*)(vbase + (int64_t)pl * HD);
+    float kf[8], vf[8];
+    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, vv[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kf[2 * e] = __uint_as_float(kk[e] << 16);
+      kf[2 * e + 1] = __uint_as_float(kk[e] & 0xffff0000u);
+      vf[2 * e] = __uint_as_float(vv[e] << 16);
+      vf[2 * e + 1] = __uint_as_float(vv[e] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+      if (h < G) {
+        float sc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc = fmaf(qv[h][e], kf[e], sc);
+        sc = sum16(sc);
+        if (valid) {
+          const float mn = fmaxf(mx[h], sc);
+          const float r = __expf(mx[h] - mn), w = __expf(sc - mn);
+          ls[h] = fmaf(ls[h], r, w);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], r, w * vf[e]);
+          mx[h] = mn;
+        }
+      }
+    }
+  }
+  // merge the four position groups of the wave (lane ^ 16, then lane ^ 32)
+  auto merge_pair = [&](int h, float m_a, float m_b, float l_a, float l_b, float* ea, float* eb) {
+    const float M = fmaxf(m_a, m_b);
+    const float ra = M == -INFINITY ? 0.f : __expf(m_a - M), rb = M == -INFINITY ? 0.f : __expf(m_b - M);
+    mx[h] = M;
+    ls[h] = l_a * ra + l_b * rb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = ea[e] * ra + eb[e] * rb;
+  };
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    if (h < G) {
+#pragma unroll
+      for (int step = 0; step < 2; ++step) {
+        float ma, mb, la, lb, ea[8], eb[8];
+        if (step == 0) {
+          swap16(mx[h], ma, mb);
+          swap16(ls[h], la, lb);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) swap16(acc[h][e], ea[e], eb[e]);
+        } else {
+          swap32(mx[h], ma, mb);
+          swap32(ls[h], la, lb);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) swap32(acc[h][e], ea[e], eb[e]);
+        }
+        merge_pair(h, ma, mb, la, lb, ea, eb);
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm[wave][h][2 + dim0 + e] = acc[h][e];
+        if (lane == 0) {
+          sm[wave][h][0] = mx[h];
+          sm[wave][h][1] = ls[h];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // merge the four waves; thread t handles (head t / 64, dims 2 (t % 64) .. + 2)
+  for (int t = tid; t < G * (HD / 2); t += kAttThreads) {
+    const int h = t / (HD / 2), i0 = 2 * (t % (HD / 2));
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][h][0]);
+    float L = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float r = M == -INFINITY ? 0.f : __expf(sm[w][h][0] - M);
+      L = fmaf(sm[w][h][1], r, L);
+      a0 = fmaf(sm[w][h][2 + i0], r, a0);
+      a1 = fmaf(sm[w][h][2 + i0 + 1], r, a1);
+    }
+    float* out = part + (((size_t)b * hq + g * G + h) * NCmax + c) * (HD + 2);
+    out[2 + i0] = a0;
+    out[2 + i0 + 1] = a1;
+    if (i0 == 0) {
+      out[0] = M;
+      out[1] = L;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// merge the chunks of one (session, q head) and hand o to the O GEMM as hi/lo
+// ---------------------------------------------------------------------------------------------
+// Grid: (hq, B) workgroups of hd threads.
+__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part, const int32_t* __restrict__ positions,
+                                                     int hq, int hd, int CH, int NCmax, uint16_t* __restrict__ Ahi,
+                                                     uint16_t* __restrict__ Alo, int lda, const uint32_t* skip) {
+  if (*skip) return;
+  const int h = (int)blockIdx.x, b = (int)blockIdx.y, i = (int)threadIdx.x;
+  const int NC = (positions[b] + 1 + CH - 1) / CH;
+  const float* base = part + ((size_t)b * hq + h) * NCmax * (hd + 2);
+  float M = -INFINITY;
+  for (int c = 0; c < NC; ++c) M = fmaxf(M, base[(size_t)c * (hd + 2)]);
+  float L = 0.f, a = 0.f;
+  for (int c = 0; c < NC; ++c) {
+    const float* pc = base + (size_t)c * (hd + 2);
+    const float r = __expf(pc[0] - M);
+    L = fmaf(pc[1], r, L);
+    a = fmaf(pc[2 + i], r, a);
+  }
+  uint16_t hi, lo;
+  split_hilo(a / L, hi, lo);
+  Ahi[(size_t)b * lda + h * hd + i] = hi;
+  Alo[(size_t)b * lda + h * hd + i] = lo;
+}
+
+// ---------------------------------------------------------------------------------------------
+// SiLU(gate) * up of every FFN column, as hi/lo for the down GEMM
+// ---------------------------------------------------------------------------------------------
+// The gate/up GEMM's columns come in blocks of 64: 32 gate rows, then the 32 matching up rows.
+// Grid: (F / 256, B) workgroups of 256 threads.
+__global__ __launch_bounds__(256) void silu_kernel(const float* __restrict__ P, int KS, int F, uint16_t* __restrict__ Ahi,
+                                                    uint16_t* __restrict__ Alo, int lda, int B, const uint32_t* skip) {
+  if (*skip) return;
+  const int f = (int)(blockIdx.x * 256 + threadIdx.x), b = (int)blockIdx.y;
+  const int N = 2 * F;
+  const int col = 64 * (f / 32) + (f % 32);
+  float gt = 0.f, up = 0.f;
+  for (int s = 0; s < KS; ++s) {
+    gt += P[((size_t)s * B + b) * N + col];
+    up += P[((size_t)s * B + b) * N + col + 32];
+  }
+  uint16_t hi, lo;
+  split_hilo(gt / (1.0f + __expf(-gt)) * up, hi, lo);
+  Ahi[(size_t)b * lda + f] = hi;
+  Alo[(size_t)b * lda + f] = lo;
+}
+
+// ---------------------------------------------------------------------------------------------
+// greedy argmax of every session: lowest index of the maximum; NaN logits are skipped and flagged
+// ---------------------------------------------------------------------------------------------
+// Grid: B workgroups of 1024 threads.
+__global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ logits, int V, int32_t* tokens,
+                                                      int32_t* positions, uint32_t* status, const uint32_t* skip) {
+  if (*skip) return;
+  __shared__ float bv[16];
+  __shared__ int32_t bi[16];
+  const int b = (int)blockIdx.x, tid = (int)threadIdx.x;
+  const float* l = logits + (size_t)b * V;
+  float best = -INFINITY;
+  int32_t besti = 0x7fffffff;
+  bool nan = false;
+  for (int i = tid; i < V; i += 1024) {
+    const float v = l[i];
+    if (v != v) { nan = true; continue; }
+    if (v > best || (v == best && i < besti)) { best = v; besti = i; }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ob = __shfl_xor(best, o);
+    const int32_t oi = __shfl_xor(besti, o);
+    if (ob > best || (ob == best && oi < besti)) { best = ob; besti = oi; }
+  }
+  if (__any(nan) && (tid & 63) == 0) __hip_atomic_fetch_or(status, 0x8u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((tid & 63) == 0) {
+    bv[tid >> 6] = best;
+    bi[tid >> 6] = besti;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 16; ++w)
+      if (bv[w] > best || (bv[w] == best && bi[w] < besti)) { best = bv[w]; besti = bi[w]; }
+    tokens[b] = besti == 0x7fffffff ? 0 : besti;
+    positions[b] = positions[b] + 1;
+  }
+}
+
+}  // namespace bt
+}  // namespace kd

@@ -1,0 +1,223 @@
+// kd_batch_host.h -- host side of the B > 1 (lockstep sessions) path behind kd_init / kd_step.
+//
+// Everything is fixed at init: weight layout, split-K factors, attention chunking and every
+// buffer ("Why is real-time AI inference 56x more expensive?", section "decide everything ahead
+// of time"). A tick then only enqueues the fixed kernel sequence of kd_batch.h on the caller's
+// stream: no allocation, no synchronisation, no host-side decision that depends on device data.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "kd.h"
+#include "kd_batch.h"
+
+namespace kd {
+namespace bt {
+
+// One projection: W[N][K] (bf16, row-major) times the activation block, split over KS K-ranges.
+struct Gemm {
+  int N = 0, K = 0, KS = 1;
+};
+
+struct BatchState {
+  int B = 0, L = 0, d = 0, hq = 0, hkv = 0, hd = 0, F = 0, V = 0, S = 0, max_seq = 0;
+  int nqkv = 0, qdim = 0, lda = 0;  // lda: row stride of the hi/lo activation blocks
+  int CH = 0, NCmax = 0;            // attention chunk length and most chunks per (session, kv head)
+  float eps = 0.f;
+  Gemm g_qkv, g_o, g_gu, g_d, g_lm;
+  size_t layer_elems = 0;           // per-layer weight elements: qkv, o, gate/up (interleaved), down
+  uint16_t* w = nullptr;            // L layers, then the LM head
+  uint16_t* embed = nullptr;        // [V][d]
+  uint16_t* norms = nullptr;        // [L][2][d] then [d]
+  float2* rope = nullptr;           // [S][hd/2]
+  float* X = nullptr;               // [B][d] residual stream
+  uint16_t* Ahi = nullptr;          // [64][lda] activation block, hi halves (rows >= B stay zero)
+  uint16_t* Alo = nullptr;          // [64][lda] lo halves
+  float* P = nullptr;               // split-K partial sums [KS][B][N]
+  float* Qs = nullptr;              // [B][hq * hd] rotated, scaled queries
+  float* part = nullptr;            // attention chunk partials [B][hq][NCmax][hd + 2]
+  float* logits = nullptr;          // [B][V] when the caller passes none
+  size_t w_qkv = 0, w_o = 0, w_gu = 0, w_d = 0, w_lm = 0;  // element offsets inside a layer / the blob
+};
+
+// Smallest power-of-two split with enough workgroups to fill the device (about 2 per CU), each
+// K range a whole number of 128-K chunks.
+inline int pick_ks(int N, int K, int nwg) {
+  int ks = 1;
+  while ((int64_t)(N / kNB) * ks < 2 * nwg && ks < 16 && K % (2 * ks * kKC) == 0) ks *= 2;
+  return ks;
+}
+
+inline int batch_check(const kd_config* c) {
+  if (c->batch < 2 || c->batch > kM) return KD_ERR_UNSUPPORTED;
+  if (c->weight_dtype != KD_DTYPE_BF16 || c->kv_dtype != KD_DTYPE_BF16) return KD_ERR_UNSUPPORTED;
+  if (c->head_dim != 128) return KD_ERR_UNSUPPORTED;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G > kMaxG) return KD_ERR_UNSUPPORTED;
+  const int64_t qdim = (int64_t)c->n_q_heads * c->head_dim, nqkv = qdim + 2LL * c->n_kv_heads * c->head_dim;
+  if (c->d_model % kKC || qdim % kKC || c->ffn_dim % 256) return KD_ERR_UNSUPPORTED;
+  if (nqkv % kNB || c->d_model % kNB || c->vocab % kNB) return KD_ERR_UNSUPPORTED;
+  return KD_OK;
+}
+
+inline void batch_free(BatchState& st) {
+  void* ptrs[] = {st.w, st.embed, st.norms, st.rope, st.X, st.Ahi, st.Alo, st.P, st.Qs, st.part, st.logits};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+  st = BatchState{};
+}
+
+#define KD_BT_TRY(expr)             \
+  do {                              \
+    if ((expr) != hipSuccess) {     \
+      batch_free(st);               \
+      return KD_ERR_HIP;            \
+    }                               \
+  } while (0)
+#define KD_BT_ALLOC(ptr, bytes)                                        \
+  do {                                                                 \
+    if (hipMalloc(&(ptr), (bytes)) != hipSuccess) {                    \
+      batch_free(st);                                                  \
+      return KD_ERR_OOM;                                               \
+    }                                                                  \
+  } while (0)
+
+inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, BatchState& st) {
+  st = BatchState{};
+  st.B = c->batch; st.L = c->n_layers; st.d = c->d_model; st.hq = c->n_q_heads; st.hkv = c->n_kv_heads;
+  st.hd = c->head_dim; st.F = c->ffn_dim; st.V = c->vocab; st.max_seq = c->max_seq; st.eps = c->norm_eps;
+  st.S = (int)((((int64_t)c->max_seq + 7 + 15) / 16) * 16);
+  st.qdim = st.hq * st.hd;
+  st.nqkv = st.qdim + 2 * st.hkv * st.hd;
+  st.lda = std::max({st.d, st.qdim, st.F});
+  st.g_qkv = {st.nqkv, st.d, pick_ks(st.nqkv, st.d, nwg)};
+  st.g_o = {st.d, st.qdim, pick_ks(st.d, st.qdim, nwg)};
+  st.g_gu = {2 * st.F, st.d, pick_ks(2 * st.F, st.d, nwg)};
+  st.g_d = {st.d, st.F, pick_ks(st.d, st.F, nwg)};
+  st.g_lm = {st.V, st.d, 1};
+  // attention: chunks of 512 positions (enough units to fill the device for any session count here)
+  st.CH = 512;
+  st.NCmax = (st.max_seq + st.CH - 1) / st.CH;
+
+  const size_t d = st.d;
+  st.w_qkv = 0;
+  st.w_o = st.w_qkv + (size_t)st.nqkv * d;
+  st.w_gu = st.w_o + d * st.qdim;
+  st.w_d = st.w_gu + 2 * (size_t)st.F * d;
+  st.layer_elems = st.w_d + d * st.F;
+  st.w_lm = (size_t)st.L * st.layer_elems;
+  const size_t blob = st.w_lm + (size_t)st.V * d;
+  size_t p_elems = 0;
+  for (const Gemm* g : {&st.g_qkv, &st.g_o, &st.g_gu, &st.g_d})
+    p_elems = std::max(p_elems, (size_t)g->KS * st.B * g->N);
+
+  KD_BT_ALLOC(st.w, blob * 2);
+  KD_BT_ALLOC(st.embed, (size_t)st.V * d * 2);
+  KD_BT_ALLOC(st.norms, (size_t)(2 * st.L + 1) * d * 2);
+  KD_BT_ALLOC(st.rope, (size_t)st.S * (st.hd / 2) * sizeof(float2));
+  KD_BT_ALLOC(st.X, (size_t)st.B * d * 4);
+  KD_BT_ALLOC(st.Ahi, (size_t)kM * st.lda * 2);
+  KD_BT_ALLOC(st.Alo, (size_t)kM * st.lda * 2);
+  KD_BT_ALLOC(st.P, p_elems * 4);
+  KD_BT_ALLOC(st.Qs, (size_t)st.B * st.qdim * 4);
+  KD_BT_ALLOC(st.part, (size_t)st.B * st.hq * st.NCmax * (st.hd + 2) * 4);
+  KD_BT_ALLOC(st.logits, (size_t)st.B * st.V * 4);
+  KD_BT_TRY(hipMemset(st.Ahi, 0, (size_t)kM * st.lda * 2));  // padding rows stay zero for good
+  KD_BT_TRY(hipMemset(st.Alo, 0, (size_t)kM * st.lda * 2));
+
+  const size_t row = d * 2;
+  for (int l = 0; l < st.L; ++l) {
+    const kd_layer_weights& lw = w->layers[l];
+    uint16_t* lay = st.w + (size_t)l * st.layer_elems;
+    KD_BT_TRY(hipMemcpy(lay + st.w_qkv, lw.wq, (size_t)st.qdim * row, hipMemcpyHostToDevice));
+    KD_BT_TRY(hipMemcpy(lay + st.w_qkv + (size_t)st.qdim * d, lw.wk, (size_t)st.hkv * st.hd * row, hipMemcpyHostToDevice));
+    KD_BT_TRY(hipMemcpy(lay + st.w_qkv + (size_t)(st.qdim + st.hkv * st.hd) * d, lw.wv, (size_t)st.hkv * st.hd * row,
+                        hipMemcpyHostToDevice));
+    KD_BT_TRY(hipMemcpy(lay + st.w_o, lw.wo, d * st.qdim * 2, hipMemcpyHostToDevice));
+    // gate/up interleaved in blocks of 32 rows: rows [64j, 64j+32) = gate rows [32j, 32j+32),
+    // rows [64j+32, 64j+64) = the matching up rows, so one 64-column GEMM tile holds both halves
+    KD_BT_TRY(hipMemcpy2D(lay + st.w_gu, 64 * row, lw.w_gate, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
+    KD_BT_TRY(hipMemcpy2D(lay + st.w_gu + 32 * d, 64 * row, lw.w_up, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
+    KD_BT_TRY(hipMemcpy(lay + st.w_d, lw.w_down, d * st.F * 2, hipMemcpyHostToDevice));
+    KD_BT_TRY(hipMemcpy(st.norms + (size_t)(2 * l) * d, lw.attn_norm, row, hipMemcpyHostToDevice));
+    KD_BT_TRY(hipMemcpy(st.norms + (size_t)(2 * l + 1) * d, lw.ffn_norm, row, hipMemcpyHostToDevice));
+  }
+  KD_BT_TRY(hipMemcpy(st.norms + (size_t)(2 * st.L) * d, w->final_norm, row, hipMemcpyHostToDevice));
+  KD_BT_TRY(hipMemcpy(st.w + st.w_lm, w->lm_head, (size_t)st.V * row, hipMemcpyHostToDevice));
+  KD_BT_TRY(hipMemcpy(st.embed, w->embed, (size_t)st.V * row, hipMemcpyHostToDevice));
+  {
+    // RoPE: pair (i, i + hd/2) turns by position * base^(-2i/hd); angles, cos and sin in float64
+    const int half = st.hd / 2;
+    std::vector<double> theta(half);
+    for (int i = 0; i < half; ++i) theta[i] = std::pow((double)c->rope_base, -2.0 * (double)i / (double)st.hd);
+    std::vector<float2> tab((size_t)st.S * half);
+    for (int64_t pos = 0; pos < st.S; ++pos)
+      for (int i = 0; i < half; ++i) {
+        const double ang = (double)pos * theta[i];
+        tab[(size_t)pos * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+      }
+    KD_BT_TRY(hipMemcpy(st.rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice));
+  }
+  KD_BT_TRY(hipDeviceSynchronize());
+  return KD_OK;
+}
+
+// Kernels one tick enqueues: check, embed+norm, 10 per layer, LM head, argmax.
+inline int batch_kernels_per_tick(const BatchState& st) { return 2 + 10 * st.L + 2; }
+
+// Enqueue one tick. flags: [0] sticky status bits, [2] this tick's skip flag.
+inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions, void* kvp, float* logits,
+                      hipStream_t s, uint32_t* flags) {
+  uint32_t* status = flags;
+  const uint32_t* skip = flags + 2;
+  uint16_t* kv = (uint16_t*)kvp;
+  const int64_t kv_head = (int64_t)st.S * st.hd, kv_sess = st.hkv * kv_head, kv_slot = st.B * kv_sess,
+                kv_layer = 2 * kv_slot;
+  float* lg = logits ? logits : st.logits;
+  auto gemm = [&](const uint16_t* W, const Gemm& g, float* out) {
+    hipLaunchKernelGGL(gemm_kernel, dim3((g.N / kNB) * g.KS), dim3(kGemmThreads), 0, s, W, g.N, g.K,
+                       (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, out, g.KS, st.B, skip);
+  };
+  auto norm = [&](int mode, const Gemm* g, int gain_index) {
+    hipLaunchKernelGGL(residual_norm_kernel, dim3(st.B), dim3(256), 0, s, mode, (const uint16_t*)st.embed,
+                       (const int32_t*)tokens, (const float*)st.P, g ? g->KS : 0, st.X,
+                       (const uint16_t*)(st.norms + (size_t)gain_index * st.d), st.d, st.eps, st.Ahi, st.Alo, st.lda,
+                       st.B, skip);
+  };
+  hipLaunchKernelGGL(check_kernel, dim3(1), dim3(1), 0, s, (const int32_t*)tokens, (const int32_t*)positions, st.B, st.V,
+                     st.max_seq, status, flags + 2);
+  norm(0, nullptr, 0);
+  for (int l = 0; l < st.L; ++l) {
+    const uint16_t* lay = st.w + (size_t)l * st.layer_elems;
+    uint16_t* kvl = kv + (int64_t)l * kv_layer;
+    gemm(lay + st.w_qkv, st.g_qkv, st.P);
+    hipLaunchKernelGGL(qkv_epilogue_kernel, dim3(st.hq + 2 * st.hkv, st.B), dim3(st.hd), 0, s, (const float*)st.P,
+                       st.g_qkv.KS, st.nqkv, st.hq, st.hkv, st.hd, (const float2*)st.rope, (const int32_t*)positions,
+                       st.Qs, kvl, kv_slot, kv_sess, kv_head, st.B, skip);
+    hipLaunchKernelGGL(attention_kernel, dim3(st.NCmax, st.hkv, st.B), dim3(kAttThreads), 0, s, (const float*)st.Qs,
+                       (const uint16_t*)kvl, kv_slot, kv_sess, kv_head, (const int32_t*)positions, st.hq, st.hkv, st.CH,
+                       st.NCmax, st.part, skip);
+    hipLaunchKernelGGL(merge_kernel, dim3(st.hq, st.B), dim3(st.hd), 0, s, (const float*)st.part,
+                       (const int32_t*)positions, st.hq, st.hd, st.CH, st.NCmax, st.Ahi, st.Alo, st.lda, skip);
+    gemm(lay + st.w_o, st.g_o, st.P);
+    norm(1, &st.g_o, 2 * l + 1);
+    gemm(lay + st.w_gu, st.g_gu, st.P);
+    hipLaunchKernelGGL(silu_kernel, dim3(st.F / 256, st.B), dim3(256), 0, s, (const float*)st.P, st.g_gu.KS, st.F, st.Ahi,
+                       st.Alo, st.lda, st.B, skip);
+    gemm(lay + st.w_d, st.g_d, st.P);
+    norm(1, &st.g_d, l + 1 < st.L ? 2 * (l + 1) : 2 * st.L);
+  }
+  gemm(st.w + st.w_lm, st.g_lm, lg);
+  hipLaunchKernelGGL(argmax_kernel, dim3(st.B), dim3(1024), 0, s, (const float*)lg, st.V, tokens, positions, status, skip);
+  return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+#undef KD_BT_TRY
+#undef KD_BT_ALLOC
+
+}  // namespace bt
+}  // namespace kd

@@ -199,6 +199,9 @@ def kd_get_info(handle: int) -> dict:
         "packed_weight_bytes": info[2],
         "lds_bytes": info[3],
         "ring_packets": info[4],
+        "kernels_per_step": info[5],
+        "split_k": [(info[6] >> (8 * i)) & 0xFF for i in range(4)],
+        "attention_chunk": info[7],
     }
 
 

@@ -1,14 +1,16 @@
 """Decode-step benchmark: tokens/s on one MI355X and the fraction of the HBM roofline.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2b|8b|2b_long|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2b|8b|2b_long|tiny|11b_x56]
 
-One "step" is one kd_step: a whole decode step of the batch-1 decoder, run as one persistent
-kernel launch. The default workload is the 2B-class decoder. Its 512-token prompt is fed one
-token per step to fill the KV cache; this is untimed. Then W warm-up decode steps and K timed
-decode steps follow, each feeding back the greedy token of the step before.
+One "step" is one kd_step: a whole decode step of every session. At batch 1 it is one persistent
+kernel launch; for the 56 lockstep sessions it is one tick, a fixed kernel sequence on one stream.
+The default workload is the 2B-class decoder at batch 1. Its 512-token prompt is fed one token per
+step to fill the KV cache; this is untimed. Pre-filled workloads write the seeded cache contents
+instead. Then W warm-up steps and K timed steps follow, each feeding back the greedy tokens of
+the step before.
 
 Printed on stdout, as one JSON line:
-  value          tokens/s over the timed steps (batch 1: one token per step), inputs resident in HBM
+  value          tokens/s over the timed steps (B tokens per step, all sessions), inputs resident in HBM
   roofline       algorithmic bytes per step (every weight, the KV cache over 0..p, the KV write,
                  the logits) divided by the kernel's mean duration. The duration comes from HIP
                  events on the launch stream; the peak is the HBM spec of 8 TB/s.
@@ -33,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "batch-1 decode tokens/sec on 1 MI355X + % of HBM bytes/token roofline"
+METRIC_SESSIONS = "aggregate decode tokens/sec of lockstep sessions on 1 MI355X + p99 tick latency"
 KERNEL_SOURCES = ("kd_device.h", "kd_plan.h", "kd_api.hip")
 
 
@@ -62,15 +65,16 @@ def measured_traffic(workload: str):
 
 
 def cpu_baseline(wl, weights, dec, torch, n_steps: int, first_pos: int, first_token: int):
-    """Time the oracle on decode steps of the same workload, starting from the GPU's KV cache."""
+    """Time the oracle on decode steps of session 0 of the same workload, from the GPU's KV cache."""
     from oracle import decoder as ref
     from threadpoolctl import threadpool_info
 
     m = wl.model
     o = ref.Oracle(m, weights, batch=1, max_seq=first_pos + n_steps + 1)
-    kv = dec.kv_view()[:, :, 0, :, :first_pos].float().cpu().numpy()
-    o.k_cache[0, :, :, :first_pos] = kv[:, 0]
-    o.v_cache[0, :, :, :first_pos] = kv[:, 1]
+    for l in range(m.n_layers):
+        kv = dec.kv_view()[l, :, 0, :, :first_pos].float().cpu().numpy()
+        o.k_cache[0, l, :, :first_pos] = kv[0]
+        o.v_cache[0, l, :, :first_pos] = kv[1]
     del kv
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     tok = first_token
@@ -84,9 +88,40 @@ def cpu_baseline(wl, weights, dec, torch, n_steps: int, first_pos: int, first_to
         "unit": "tok/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{n_steps} decode steps of workload {wl.name} at positions {first_pos}..{first_pos + n_steps - 1}, "
-                  f"float64 numpy oracle, {dt:.1f} s",
+        "sample": f"{n_steps} decode steps of session 0 of workload {wl.name} at positions "
+                  f"{first_pos}..{first_pos + n_steps - 1}, float64 numpy oracle, {dt:.1f} s",
     }
+
+
+def nearest_rank(values, q: float) -> float:
+    """Nearest-rank percentile: the ceil(q n)-th smallest value."""
+    v = np.sort(np.asarray(values, np.float64))
+    return float(v[max(0, int(np.ceil(q * len(v))) - 1)])
+
+
+def fill_prefilled_cache(wl, dec, torch) -> None:
+    """Write the seeded pre-filled K/V values of every session, one layer at a time."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import workloads
+
+    m = wl.model
+    storage = np.uint16 if m.kv_dtype == "bf16" else np.float32
+    view_dtype = torch.int16 if m.kv_dtype == "bf16" else torch.float32
+    host = np.zeros((2, wl.batch, m.n_kv_heads, wl.prefill_len, m.head_dim), storage)
+    kv = dec.kv_view().view(view_dtype)
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for l in range(m.n_layers):
+            def work(job, l=l):
+                s, b, g = job
+                host[s, b, g] = workloads.kv_prefill_block(wl, l, s, b, g)
+
+            list(pool.map(work, [(s, b, g) for s in range(2) for b in range(wl.batch) for g in range(m.n_kv_heads)]))
+            kv[l, :, :, :, : wl.prefill_len] = torch.from_numpy(host.view(np.int16 if m.kv_dtype == "bf16" else np.float32))
+            if (l + 1) % 8 == 0 or l + 1 == m.n_layers:
+                log(f"pre-filled cache: {l + 1}/{m.n_layers} layers ({time.perf_counter() - t0:.1f} s)")
 
 
 def main() -> int:
@@ -94,8 +129,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="2b", choices=["tiny", "2b", "8b", "2b_long"])
-    ap.add_argument("--cpu-steps", type=int, default=3, help="oracle decode steps timed for cpu_baseline (0: skip)")
+    ap.add_argument("--workload", default="2b", choices=["tiny", "2b", "8b", "2b_long", "11b_x56"])
+    ap.add_argument("--cpu-steps", type=int, default=None,
+                    help="oracle decode steps (of one session) timed for cpu_baseline; 0 skips it "
+                         "(default: 3 at batch 1, 1 for the lockstep sessions)")
     ap.add_argument("--trace", action="store_true", help="after timing, trace one step and print its phase breakdown")
     ap.add_argument("--trace-out", default=None, help="with --trace: also save the raw timestamp buffer (.npy)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -116,6 +153,9 @@ def main() -> int:
 
     wl = workloads.get(args.workload)
     m = wl.model
+    B = wl.batch
+    if args.cpu_steps is None:
+        args.cpu_steps = 3 if B == 1 else 1
     decode_steps = wl.decode_steps
     if args.warmup + args.steps > decode_steps:
         args.steps = decode_steps - args.warmup
@@ -135,20 +175,15 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"calibration copy: {n} bytes read, {n} bytes written")
         del src, dst
-    dec = kd.Decoder(m, weights, max_seq=wl.max_seq, device="cuda:0")
+    dec = kd.Decoder(m, weights, max_seq=wl.max_seq, batch=B, device="cuda:0")
     info = kd.kd_get_info(dec.handle)
     log(f"kd_init done: {info}")
     stream = torch.cuda.current_stream()
 
     # fill the KV cache: the prompt fed one token per step, or the seeded pre-filled values
     if wl.prefill_len > 0:
-        kv_host = np.zeros((m.n_layers, 2, 1, m.n_kv_heads, dec.s_alloc, m.head_dim),
-                           np.uint16 if m.kv_dtype == "bf16" else np.float32)
-        workloads.fill_kv_prefill(wl, kv_host)
-        flat = torch.from_numpy(kv_host.reshape(-1).view(np.int16 if m.kv_dtype == "bf16" else np.float32))
-        dec.kv.view(torch.int16 if m.kv_dtype == "bf16" else torch.float32).copy_(flat)
-        del kv_host, flat
-        dec.tokens.fill_(int(workloads.make_first_tokens(wl)[0]))
+        fill_prefilled_cache(wl, dec, torch)
+        dec.tokens.copy_(torch.from_numpy(workloads.make_first_tokens(wl)))
         dec.positions.fill_(wl.prefill_len)
     else:
         prompt = torch.as_tensor(workloads.make_prompt(wl, 0), device=dec.device)
@@ -164,8 +199,8 @@ def main() -> int:
     for _ in range(args.warmup):
         dec.step()
     torch.cuda.synchronize()
-    first_pos = int(dec.positions.item())
-    first_token = int(dec.tokens.item())
+    first_pos = int(dec.positions[0].item())
+    first_token = int(dec.tokens[0].item())
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     whole0, whole1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -187,16 +222,16 @@ def main() -> int:
     elapsed_ms = whole0.elapsed_time(whole1)
     per_step_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
     positions = range(first_pos, first_pos + args.steps)
-    alg_bytes = np.array([roofline.step_bytes(m, 1, p).total for p in positions], np.float64)
+    alg_bytes = np.array([roofline.step_bytes(m, B, p).total for p in positions], np.float64)
     achieved_gbps = float(alg_bytes.mean() / (per_step_us.mean() * 1e-6) / 1e9)
-    tok_s = args.steps / (elapsed_ms * 1e-3)
-    bound_tok_s = roofline.tokens_per_s_bound(PEAK_HBM_GBPS * 1e9, float(alg_bytes.mean()))
-    log(f"{args.steps} steps in {elapsed_ms:.2f} ms (wall {t_wall * 1e3:.1f} ms): {tok_s:.1f} tok/s, "
-        f"kernel mean {per_step_us.mean():.1f} us (p50 {np.percentile(per_step_us, 50):.1f}, "
-        f"p99 {np.percentile(per_step_us, 99):.1f}), {achieved_gbps:.0f} GB/s algorithmic, "
-        f"roofline {bound_tok_s:.0f} tok/s")
+    tok_s = args.steps * B / (elapsed_ms * 1e-3)
+    bound_tok_s = roofline.tokens_per_s_bound(PEAK_HBM_GBPS * 1e9, float(alg_bytes.mean()), B)
+    p99 = nearest_rank(per_step_us, 0.99)
+    log(f"{args.steps} steps x {B} sessions in {elapsed_ms:.2f} ms (wall {t_wall * 1e3:.1f} ms): {tok_s:.1f} tok/s, "
+        f"step mean {per_step_us.mean():.1f} us (p50 {np.percentile(per_step_us, 50):.1f}, "
+        f"p99 {p99:.1f}), {achieved_gbps:.0f} GB/s algorithmic, roofline {bound_tok_s:.0f} tok/s")
 
-    if args.trace:
+    if args.trace and B == 1:
         from bandwidth_bound_transformer_amd import trace as tr
 
         stride = kd.kd_trace(dec.handle, None, 0)
@@ -220,7 +255,7 @@ def main() -> int:
 
     traffic = measured_traffic(wl.name)
     out = {
-        "metric": METRIC,
+        "metric": METRIC if B == 1 else METRIC_SESSIONS,
         "value": round(tok_s, 2),
         "unit": "tok/s",
         "n_gpus": 1,
@@ -237,7 +272,7 @@ def main() -> int:
             "description": wl.description,
             "layers": m.n_layers, "d_model": m.d_model, "q_heads": m.n_q_heads, "kv_heads": m.n_kv_heads,
             "head_dim": m.head_dim, "ffn": m.ffn_dim, "vocab": m.vocab, "weight_dtype": m.weight_dtype,
-            "kv_dtype": m.kv_dtype, "batch": 1, "positions": [first_pos, first_pos + args.steps - 1],
+            "kv_dtype": m.kv_dtype, "batch": B, "positions": [first_pos, first_pos + args.steps - 1],
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
@@ -247,15 +282,18 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
-            "kernel": "decode_step_kernel",
+            "kernel": "decode_step_kernel" if B == 1 else "one tick (the kd_step kernel sequence)",
             "algorithmic_bytes_per_launch": round(float(alg_bytes.mean())),
             "kernel_mean_us": round(float(per_step_us.mean()), 2),
         },
         "roofline_tok_s": round(bound_tok_s, 1),
         "frac_of_roofline_tok_s": round(tok_s / bound_tok_s, 4),
-        "itl_us": {"p50": round(float(np.percentile(per_step_us, 50)), 2), "p99": round(float(np.percentile(per_step_us, 99)), 2)},
+        "itl_us": {"p50": round(float(np.percentile(per_step_us, 50)), 2), "p99": round(p99, 2)},
         "cpu_baseline": cpu,
     }
+    if B > 1:
+        out["tick_latency_ms"] = {"p50": round(float(np.percentile(per_step_us, 50)) / 1e3, 4), "p99": round(p99 / 1e3, 4),
+                                  "max": round(float(per_step_us.max()) / 1e3, 4)}
     print(json.dumps(out), flush=True)
     dec.close()
     return 0

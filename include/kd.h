@@ -70,7 +70,11 @@ extern "C" {
  *   head_dim     64 or 128.
  *   ffn_dim      must be a multiple of 8 (bf16) or 4 (f32) elements.
  *   max_seq      capacity of the KV cache in positions (steps may use positions 0..max_seq-1).
- *   batch        sessions stepped together; this build supports batch == 1.
+ *   batch        sessions stepped together in lockstep. batch == 1 runs the single persistent
+ *                kernel. 2 <= batch <= 64 runs the lockstep-sessions path: the projections become
+ *                small-M GEMMs on the matrix cores. That path needs bf16 weights and cache,
+ *                head_dim 128, d_model, n_q_heads*head_dim and (n_q_heads+2*n_kv_heads)*head_dim
+ *                multiples of 128 (the last of 64), ffn_dim a multiple of 256 and vocab of 64.
  *   norm_eps     RMSNorm epsilon (inside the square root).
  *   rope_base    RoPE base: pair (i, i + head_dim/2) turns by position * rope_base^(-2i/head_dim).
  *   weight_dtype KD_DTYPE_BF16 or KD_DTYPE_F32; kv_dtype likewise (must match weight_dtype).
@@ -156,7 +160,7 @@ void kd_destroy(kd_handle* h);
 const char* kd_strerror(int code);
 
 /*
- * Step tracing, for measurement.  With dev_buf non-NULL, every later kd_step writes 64-bit
+ * Step tracing, for measurement (batch 1 only; KD_ERR_UNSUPPORTED for batch > 1).  With dev_buf non-NULL, every later kd_step writes 64-bit
  * timestamps of the GPU's 100 MHz constant clock at its phase boundaries: workgroup w uses
  * dev_buf[w * stride .. (w + 1) * stride).  Slot 0 is the step start, slot 1 the end of setup,
  * slots 2 + 24*l + e (e < 24) the phase boundaries of layer l, and the last 4 slots the final
@@ -171,6 +175,10 @@ int kd_trace(kd_handle* h, uint64_t* dev_buf, int64_t words, int64_t* stride);
  *   info[0] workgroups in the persistent grid      info[1] threads per workgroup
  *   info[2] packed weight bytes on the device      info[3] LDS bytes per workgroup
  *   info[4] ring depth (1 KB packets per compute wave)
+ * For batch > 1: info[0] = 0 (no persistent grid), info[1] threads per GEMM workgroup,
+ *   info[2] weight bytes on the device, info[5] kernels one kd_step enqueues,
+ *   info[6] split-K factors of the QKV / O / gate-up / down GEMMs (one byte each, low first),
+ *   info[7] attention chunk length in positions.
  */
 int kd_get_info(kd_handle* h, int64_t info[8]);
 

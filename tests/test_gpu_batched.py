@@ -1,0 +1,194 @@
+"""Parity of the lockstep-sessions path (B > 1: small-M GEMMs on MFMA) with the CPU oracle.
+
+Every input is seeded and synthetic (``workloads``); every expected value comes from ``oracle``.
+Logits must stay within 2e-2 of the largest reference logit, per session and tick (bf16 weights,
+activations fed to the matrix cores as bf16 hi/lo pairs, fp32 accumulation). Each session's
+greedy token must equal the oracle's argmax, except at a tie-flip: a step whose top-2 margin is
+within twice that step's measured logit error. The oracle is teacher-forced with the GPU's
+tokens, so one flip does not desynchronise the rest of the run.
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import decoder as ref
+from workloads.presets import ModelShape, Workload
+
+from . import gpu_harness as gh
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+
+    assert t.cuda.is_available()
+    return t
+
+
+@pytest.fixture(scope="module")
+def kdm():
+    from bandwidth_bound_transformer_amd import kd
+
+    kd.library()  # fails loudly if the HIP library is missing
+    return kd
+
+
+def _clone():
+    """A shrunk clone of the 56-session workload that runs the same kernels: head_dim 128, four
+    query heads per kv head, 56 sessions, a pre-filled cache, and every GEMM shape a multiple of
+    the tiles (several split-K ranges for QKV, O and down)."""
+    shape = ModelShape(2, 256, 4, 1, 128, 512, 1024, rope_base=500000.0)
+    return Workload("clone_x56", shape, batch=56, prefill_len=48, gen_tokens=16, weight_seed=11, kv_seed=12,
+                    first_token_seed=13)
+
+
+def _fill_sessions(dec, wl, sessions, torch):
+    """Write the recipe's pre-filled K/V of `sessions` into the device cache, block by block."""
+    m = wl.model
+    kv = dec.kv_view().view(torch.int16)
+    for l in range(m.n_layers):
+        for s in range(2):
+            for b in sessions:
+                for g in range(m.n_kv_heads):
+                    blk = workloads.kv_prefill_block(wl, l, s, b, g)
+                    kv[l, s, b, g, : wl.prefill_len] = torch.from_numpy(blk.view(np.int16))
+
+
+def _oracle_with_prefill(wl, w, sessions):
+    m = wl.model
+    o = ref.Oracle(m, w, batch=len(sessions), max_seq=wl.max_seq)
+    for i, b in enumerate(sessions):
+        for l in range(m.n_layers):
+            for g in range(m.n_kv_heads):
+                o.load_kv(i, l, g, workloads.f32_from_bf16_bits(workloads.kv_prefill_block(wl, l, 0, b, g)),
+                          workloads.f32_from_bf16_bits(workloads.kv_prefill_block(wl, l, 1, b, g)))
+    return o
+
+
+def _check_tick(gl, g_tok, want, tag):
+    """Logit error and greedy choice of one tick of one session; returns (error, tie-flip?)."""
+    err = gh.inf_rel_err(gl, want)
+    assert err <= BF16_TOL, (tag, err)
+    ref_tok = int(ref.greedy_token(want[None])[0])
+    if int(g_tok) != ref_tok:
+        abs_err = float(np.max(np.abs(np.asarray(gl, np.float64) - want)))
+        assert gh.top2_margin(want) <= 2 * abs_err, (tag, int(g_tok), ref_tok, gh.top2_margin(want), abs_err)
+        return err, True
+    return err, False
+
+
+def test_clone_x56_every_session(torch, kdm):
+    """56 sessions, 16 ticks from a 48-position pre-filled cache: logits, tokens, positions and the
+    K/V each tick appends, for every session."""
+    wl = _clone()
+    m = wl.model
+    w = workloads.make_weights(m, seed=wl.weight_seed)
+    dec = kdm.Decoder(m, w, max_seq=wl.max_seq, batch=wl.batch)
+    assert kdm.kd_get_info(dec.handle)["workgroups"] == 0  # the batched path, not the batch-1 kernel
+    sessions = list(range(wl.batch))
+    _fill_sessions(dec, wl, sessions, torch)
+    o = _oracle_with_prefill(wl, w, sessions)
+    first = workloads.make_first_tokens(wl)
+    dec.tokens.copy_(torch.from_numpy(first))
+    dec.positions.fill_(wl.prefill_len)
+    tok = first.astype(np.int64)
+    worst, flips = 0.0, 0
+    for t in range(wl.gen_tokens):
+        p = wl.prefill_len + t
+        dec.step()
+        gl = dec.logits.cpu().numpy()
+        g_tok = dec.tokens.cpu().numpy()
+        want = o.step(tok, [p] * wl.batch)
+        for b in range(wl.batch):
+            err, flip = _check_tick(gl[b], g_tok[b], want[b], (t, b))
+            worst = max(worst, err)
+            flips += flip
+        tok = g_tok.astype(np.int64)
+    print(f"clone_x56: max rel logit err {worst:.3e} over {wl.gen_tokens} ticks x {wl.batch} sessions, tie-flips {flips}")
+    assert flips <= 2
+    assert dec.status() == 0
+    assert np.all(dec.positions.cpu().numpy() == wl.prefill_len + wl.gen_tokens)
+    # the appended positions hold K (after RoPE) and V as the oracle stored them
+    kv = dec.kv_view()
+    n0, n1 = wl.prefill_len, wl.prefill_len + wl.gen_tokens
+    k_gpu = kv[:, 0, :, :, n0:n1].float().cpu().numpy()  # [L][B][hkv][n][hd]
+    k_ref = o.k_cache[:, :, :, n0:n1].transpose(1, 0, 2, 3, 4)
+    assert np.max(np.abs(k_gpu - k_ref)) <= BF16_TOL * np.max(np.abs(k_ref))
+    dec.close()
+
+
+def test_clone_x56_bitwise_deterministic(torch, kdm):
+    """Fixed reduction orders everywhere (split-K partials summed in order): identical bits."""
+    wl = _clone()
+    m = wl.model
+    w = workloads.make_weights(m, seed=wl.weight_seed)
+    runs = []
+    for _ in range(2):
+        dec = kdm.Decoder(m, w, max_seq=wl.max_seq, batch=wl.batch)
+        _fill_sessions(dec, wl, range(wl.batch), torch)
+        dec.tokens.copy_(torch.from_numpy(workloads.make_first_tokens(wl)))
+        dec.positions.fill_(wl.prefill_len)
+        out = []
+        for _ in range(4):
+            dec.step()
+            out.append(dec.logits.clone())
+        torch.cuda.synchronize()
+        runs.append(torch.stack(out).cpu().numpy())
+        dec.close()
+    assert np.array_equal(runs[0].view(np.uint32), runs[1].view(np.uint32))
+
+
+def test_clone_x56_bad_input_writes_nothing(torch, kdm):
+    """One session with an out-of-range token: status bit set, no session's state changes."""
+    wl = _clone()
+    m = wl.model
+    w = workloads.make_weights(m, seed=wl.weight_seed)
+    dec = kdm.Decoder(m, w, max_seq=wl.max_seq, batch=wl.batch)
+    dec.tokens.fill_(3)
+    dec.tokens[17] = m.vocab
+    dec.positions.fill_(5)
+    dec.logits.fill_(-7.0)
+    before = dec.kv.clone()
+    dec.step()
+    assert dec.status(clear=True) == kdm.KD_STATUS_TOKEN_RANGE
+    assert bool(torch.all(dec.positions == 5)) and int(dec.tokens[17].item()) == m.vocab
+    assert bool(torch.all(dec.logits == -7.0)) and bool(torch.equal(before, dec.kv))
+    dec.tokens[17] = 4
+    dec.step()
+    assert dec.status() == 0 and bool(torch.all(dec.positions == 6))
+    dec.close()
+
+
+def test_11b_x56_sampled_sessions(torch, kdm):
+    """The 11B-class decoder at its real shape and launch configuration (56 sessions, KV cache
+    pre-filled to 4096 positions): two ticks, logits of sessions 0 and 55 against the oracle."""
+    wl = workloads.get("11b_x56")
+    m = wl.model
+    w = workloads.make_weights(m, seed=wl.weight_seed)
+    print("11b: weights ready", flush=True)
+    dec = kdm.Decoder(m, w, max_seq=wl.max_seq, batch=wl.batch)
+    sessions = [0, 55]
+    _fill_sessions(dec, wl, sessions, torch)
+    o = _oracle_with_prefill(wl, w, sessions)
+    print("11b: caches filled", flush=True)
+    first = workloads.make_first_tokens(wl)
+    dec.tokens.copy_(torch.from_numpy(first))
+    dec.positions.fill_(wl.prefill_len)
+    tok = first.astype(np.int64)
+    for t in range(2):
+        p = wl.prefill_len + t
+        dec.step()
+        gl = dec.logits.cpu().numpy()
+        g_tok = dec.tokens.cpu().numpy()
+        for i, b in enumerate(sessions):
+            want = o.step_one(i, int(tok[b]), p)
+            err, _ = _check_tick(gl[b], g_tok[b], want, (t, b))
+            print(f"11b tick {t} session {b}: rel logit err {err:.3e}", flush=True)
+        tok = g_tok.astype(np.int64)
+    assert dec.status() == 0
+    dec.close()
