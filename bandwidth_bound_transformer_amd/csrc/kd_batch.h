@@ -26,9 +26,9 @@ namespace kd {
 namespace bt {
 
 constexpr int kM = 64;             // sessions padded to four 16-row MFMA tiles
-constexpr int kNB = 64;            // GEMM output columns per workgroup: 4 waves x 16
+constexpr int kNB = 128;           // GEMM output columns per workgroup: 8 waves x 16
 constexpr int kKC = 128;           // K per LDS chunk of the activation block
-constexpr int kGemmThreads = 256;
+constexpr int kGemmThreads = 512;
 constexpr int kAttThreads = 256;   // 4 waves; 16 lanes per KV position (hd = 128, bf16)
 constexpr int kMaxG = 4;
 
@@ -98,70 +98,71 @@ __global__ void check_kernel(const int32_t* tokens, const int32_t* positions, in
 // ---------------------------------------------------------------------------------------------
 // small-M GEMM on MFMA: P[s][m][n] = sum over K-range s of (Ahi[m][k] + Alo[m][k]) * W[n][k]
 // ---------------------------------------------------------------------------------------------
-// Grid: (N / kNB) * KS workgroups; unit u covers columns [64 (u / KS), +64) and K range u % KS.
-// Wave w owns 16 output columns. Lane l streams weight row n = n0 + 16w + l % 16; for each 128-K
-// chunk it loads the 64 contiguous bytes k = 32 (l / 16) .. + 32. The matrix-core K order is
-// permuted to match (step t uses k = 32 (l / 16) + 8 t + j), and the activation fragments are
-// read from LDS in that same order, so the sum is unchanged. The activation block (64 rows x 128
-// K, hi and lo) is staged through LDS once per chunk and shared by the four waves.
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint16_t* __restrict__ W, int N, int K,
+// Grid: (N / kNB) * KS workgroups of 8 waves; unit u covers columns [kNB (u / KS), + kNB) and K range
+// u % KS, in chunks of 128 K. Wave w owns 16 output columns. Lane l streams weight row
+// n = n0 + 16 w + l % 16; per chunk it loads the 64 contiguous bytes k = 32 (l / 16) .. + 32. The
+// matrix-core K order is permuted to match (step t uses k = 32 (l / 16) + 8 t + j), and the
+// activation fragments are read from LDS in that same order, so the sum is unchanged.
+//
+// Both the weights (HBM) and the activation block (64 rows x 128 K, hi and lo; it stays in L2)
+// are loaded into registers kPF chunks ahead, in the same order, so a wait for one never holds up
+// the other: the compiler sees every load and a wave's loads complete in issue order. The
+// activation chunk then goes through a double-buffered LDS tile that the eight waves share.
+constexpr int kPF = 4;  // chunks in flight per wave
+// NCH chunks per K range, fully unrolled: with no loop back-edge the compiler places every wait
+// exactly (at a back-edge it would drain all loads in flight).
+template <int NCH>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint16_t* __restrict__ W, int N, int K,
                                                                 const uint16_t* __restrict__ Ahi,
                                                                 const uint16_t* __restrict__ Alo, int lda,
                                                                 float* __restrict__ P, int KS, int B, const uint32_t* skip) {
   if (*skip) return;
   // [buffer][hi, lo][row][16-byte chunk of the 128-K slice, padded by one against bank conflicts]
-  __shared__ uint4 As[2][2][kM][kKC / 8 + 1];
+  __shared__ u32x4 As[2][2][kM][kKC / 8 + 1];
   const int unit = (int)blockIdx.x;
   const int nb = unit / KS, s = unit - nb * KS;
-  const int Kr = K / KS, k0 = s * Kr, nchunks = Kr / kKC;
+  const int k0 = s * (NCH * kKC);
   const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q = lane >> 4;
   const int n = nb * kNB + wave * 16 + (lane & 15);
   const u32x4* wrow = (const u32x4*)(W + (size_t)n * K + k0 + q * 32);
 
-  // activation loader: 2 x 64 rows x 16 chunks of 16 bytes = 2048 pieces, 8 per thread
-  uint4 areg[8];
-  auto load_a = [&](int c) {
+  // activation chunk: 2 x 64 rows x 16 pieces of 16 bytes = 2048 pieces, 4 per thread
+  constexpr int kAPer = 2 * kM * (kKC / 8) / kGemmThreads;
+  // ext_vector_type registers (HIP's uint4 is a struct with a union, which the compiler keeps in
+  // scratch memory when it sits in an array)
+  struct Slot {
+    u32x4 a[kAPer];
+    u32x4 w[4];
+  };
+  auto load_chunk = [&](int c, Slot& sl) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kAPer; ++j) {
       const int idx = tid + kGemmThreads * j;
       const int hl = idx >> 10, r = (idx >> 4) & 63, cc = idx & 15;
-      const uint16_t* src = (hl ? Alo : Ahi) + (size_t)r * lda + k0 + c * kKC + cc * 8;
-      areg[j] = *(const uint4*)src;
+      sl.a[j] = *(const u32x4*)((hl ? Alo : Ahi) + (size_t)r * lda + k0 + c * kKC + cc * 8);
     }
-  };
-  auto store_a = [&](int buf) {
+    // weights are read once per tick: non-temporal loads
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = tid + kGemmThreads * j;
-      const int hl = idx >> 10, r = (idx >> 4) & 63, cc = idx & 15;
-      As[buf][hl][r][cc] = areg[j];
-    }
-  };
-  // weights are read once per tick: non-temporal loads
-  u32x4 wcur[4], wnext[4];
-  auto load_w = [&](int c, u32x4 (&dst)[4]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) dst[t] = __builtin_nontemporal_load(wrow + (size_t)c * (kKC / 8) + t);
+    for (int t = 0; t < 4; ++t) sl.w[t] = __builtin_nontemporal_load(wrow + (size_t)c * (kKC / 8) + t);
   };
 
   f32x4 acc[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  load_a(0);
-  load_w(0, wcur);
-  for (int c = 0; c < nchunks; ++c) {
+  // one chunk: activation slot -> LDS buffer, barrier, 32 MFMAs, then refill the slot kPF ahead
+  auto step = [&](int c, Slot& sl) __attribute__((always_inline)) {
     const int buf = c & 1;
-    store_a(buf);
-    __syncthreads();
-    if (c + 1 < nchunks) {
-      load_a(c + 1);
-      load_w(c + 1, wnext);
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) {
+      const int idx = tid + kGemmThreads * j;
+      const int hl = idx >> 10, r = (idx >> 4) & 63, cc = idx & 15;
+      As[buf][hl][r][cc] = sl.a[j];
     }
+    __syncthreads();
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bf16x8 bw = __builtin_bit_cast(bf16x8, wcur[t]);
+      const bf16x8 bw = __builtin_bit_cast(bf16x8, sl.w[t]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int r = mt * 16 + (lane & 15);
@@ -171,9 +172,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint16_t* _
         acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[mt], 0, 0, 0);
       }
     }
+    if (c + kPF < NCH) load_chunk(c + kPF, sl);
+  };
+  Slot ring[kPF];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) wcur[t] = wnext[t];
-  }
+  for (int c = 0; c < kPF && c < NCH; ++c) load_chunk(c, ring[c]);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) step(c, ring[c % kPF]);
   // lane l holds rows 16 mt + 4 (l / 16) + i of column n
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -187,40 +192,65 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint16_t* _
 // ---------------------------------------------------------------------------------------------
 // residual + RMSNorm: X[b] (+)= sum of partials (or the embedding row), then H = RMSNorm(X) * g as hi/lo
 // ---------------------------------------------------------------------------------------------
-// Grid: B workgroups of 256 threads. mode 0: X[b] = E[tokens[b]]; mode 1: X[b] += sum_s P[s][b].
-__global__ __launch_bounds__(256) void residual_norm_kernel(int mode, const uint16_t* __restrict__ E,
-                                                             const int32_t* __restrict__ tokens,
-                                                             const float* __restrict__ P, int KS, float* __restrict__ X,
-                                                             const uint16_t* __restrict__ gain, int d, float eps,
-                                                             uint16_t* __restrict__ Ahi, uint16_t* __restrict__ Alo,
-                                                             int lda, int B, const uint32_t* skip) {
+// Grid: B workgroups of 1024 threads; thread t owns columns 4t .. 4t+3 (d <= 4096).
+// mode 0: X[b] = E[tokens[b]]; mode 1: X[b] += sum_s P[s][b], partials added in order s = 0, 1, ...
+__global__ __launch_bounds__(1024) void residual_norm_kernel(int mode, const uint16_t* __restrict__ E,
+                                                              const int32_t* __restrict__ tokens,
+                                                              const float* __restrict__ P, int KS, float* __restrict__ X,
+                                                              const uint16_t* __restrict__ gain, int d, float eps,
+                                                              uint16_t* __restrict__ Ahi, uint16_t* __restrict__ Alo,
+                                                              int lda, int B, const uint32_t* skip) {
   if (*skip) return;
-  __shared__ float red[4];
+  __shared__ float red[16];
   const int b = (int)blockIdx.x, tid = (int)threadIdx.x;
-  float* x = X + (size_t)b * d;
-  float ss = 0.f;
-  const int64_t tok = mode == 0 ? (int64_t)tokens[b] : 0;
-  for (int i = tid; i < d; i += 256) {
-    float v;
+  const int i0 = 4 * tid;
+  const bool mine = i0 < d;
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (mine) {
     if (mode == 0) {
-      v = bf16_to_f(E[tok * d + i]);
+      const uint2 e = *(const uint2*)(E + (int64_t)tokens[b] * d + i0);
+      x = make_float4(__uint_as_float(e.x << 16), __uint_as_float(e.x & 0xffff0000u), __uint_as_float(e.y << 16),
+                      __uint_as_float(e.y & 0xffff0000u));
     } else {
-      v = x[i];
-      for (int s = 0; s < KS; ++s) v += P[((size_t)s * B + b) * d + i];
+      x = *(const float4*)(X + (size_t)b * d + i0);
+      int s = 0;
+      for (; s + 4 <= KS; s += 4) {  // four partials in flight at a time, added in order
+        float4 p[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) p[u] = *(const float4*)(P + ((size_t)(s + u) * B + b) * d + i0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          x.x += p[u].x; x.y += p[u].y; x.z += p[u].z; x.w += p[u].w;
+        }
+      }
+      for (; s < KS; ++s) {
+        const float4 p = *(const float4*)(P + ((size_t)s * B + b) * d + i0);
+        x.x += p.x; x.y += p.y; x.z += p.z; x.w += p.w;
+      }
     }
-    x[i] = v;
-    ss = fmaf(v, v, ss);
+    *(float4*)(X + (size_t)b * d + i0) = x;
   }
+  float ss = x.x * x.x;
+  ss = fmaf(x.y, x.y, ss);
+  ss = fmaf(x.z, x.z, ss);
+  ss = fmaf(x.w, x.w, ss);
   ss = wsum(ss);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
-  const float tot = red[0] + red[1] + red[2] + red[3];
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) tot += red[w];
   const float r = 1.0f / sqrtf(tot / (float)d + eps);
-  for (int i = tid; i < d; i += 256) {
-    uint16_t hi, lo;
-    split_hilo(x[i] * r * bf16_to_f(gain[i]), hi, lo);
-    Ahi[(size_t)b * lda + i] = hi;
-    Alo[(size_t)b * lda + i] = lo;
+  if (mine) {
+    const uint2 g = *(const uint2*)(gain + i0);
+    const float gv[4] = {__uint_as_float(g.x << 16), __uint_as_float(g.x & 0xffff0000u), __uint_as_float(g.y << 16),
+                         __uint_as_float(g.y & 0xffff0000u)};
+    const float xv[4] = {x.x, x.y, x.z, x.w};
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) split_hilo(xv[u] * r * gv[u], hi[u], lo[u]);
+    *(uint2*)(Ahi + (size_t)b * lda + i0) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+    *(uint2*)(Alo + (size_t)b * lda + i0) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
   }
 }
 
@@ -296,35 +326,44 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __r
   const uint16_t* kbase = kv + kv_sess * b + kv_head * g + dim0;
   const uint16_t* vbase = kbase + kv_slot;
   const int npk = (j1 - j0 + 3) / 4;
-  for (int k = wave; k < npk; k += 4) {
-    const int pos = j0 + 4 * k + grp;
-    const bool valid = pos < j1;
-    const int pl = valid ? pos : j0;  // stay inside the chunk's cached positions
-    const uint4 kw = *(const uint4*)(kbase + (int64_t)pl * HD);
-    const uint4 vw = *(const uint4*)(vbase + (int64_t)pl * HD);
-    float kf[8], vf[8];
-    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, vv[4] = {vw.x, vw.y, vw.z, vw.w};
+  constexpr int U = 4;  // packets of K and V in flight per wave
+  for (int k0 = wave; k0 < npk; k0 += 4 * U) {
+    uint4 kw[U], vw[U];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kf[2 * e] = __uint_as_float(kk[e] << 16);
-      kf[2 * e + 1] = __uint_as_float(kk[e] & 0xffff0000u);
-      vf[2 * e] = __uint_as_float(vv[e] << 16);
-      vf[2 * e + 1] = __uint_as_float(vv[e] & 0xffff0000u);
+    for (int u = 0; u < U; ++u) {
+      const int pos = j0 + 4 * (k0 + 4 * u) + grp;
+      const int pl = pos < j1 ? pos : j0;  // stay inside the chunk's cached positions
+      kw[u] = *(const uint4*)(kbase + (int64_t)pl * HD);
+      vw[u] = *(const uint4*)(vbase + (int64_t)pl * HD);
     }
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
-      if (h < G) {
-        float sc = 0.f;
+    for (int u = 0; u < U; ++u) {
+      const int pos = j0 + 4 * (k0 + 4 * u) + grp;
+      const bool valid = pos < j1;
+      float kf[8], vf[8];
+      const uint32_t kk[4] = {kw[u].x, kw[u].y, kw[u].z, kw[u].w}, vv[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sc = fmaf(qv[h][e], kf[e], sc);
-        sc = sum16(sc);
-        if (valid) {
-          const float mn = fmaxf(mx[h], sc);
-          const float r = __expf(mx[h] - mn), w = __expf(sc - mn);
-          ls[h] = fmaf(ls[h], r, w);
+      for (int e = 0; e < 4; ++e) {
+        kf[2 * e] = __uint_as_float(kk[e] << 16);
+        kf[2 * e + 1] = __uint_as_float(kk[e] & 0xffff0000u);
+        vf[2 * e] = __uint_as_float(vv[e] << 16);
+        vf[2 * e + 1] = __uint_as_float(vv[e] & 0xffff0000u);
+      }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], r, w * vf[e]);
-          mx[h] = mn;
+      for (int h = 0; h < kMaxG; ++h) {
+        if (h < G) {
+          float sc = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc = fmaf(qv[h][e], kf[e], sc);
+          sc = sum16(sc);
+          if (valid) {
+            const float mn = fmaxf(mx[h], sc);
+            const float r = __expf(mx[h] - mn), w = __expf(sc - mn);
+            ls[h] = fmaf(ls[h], r, w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], r, w * vf[e]);
+            mx[h] = mn;
+          }
         }
       }
     }

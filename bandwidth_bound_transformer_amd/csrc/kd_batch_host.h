@@ -44,12 +44,24 @@ struct BatchState {
   size_t w_qkv = 0, w_o = 0, w_gu = 0, w_d = 0, w_lm = 0;  // element offsets inside a layer / the blob
 };
 
-// Smallest power-of-two split with enough workgroups to fill the device (about 2 per CU), each
-// K range a whole number of 128-K chunks.
+// Smallest power-of-two split with enough workgroups to fill the device (one per CU), each K
+// range 4, 8, 16 or 32 chunks of 128 K (the unrolled kernel variants).
+inline bool chunks_ok(int nch) { return nch == 4 || nch == 8 || nch == 16 || nch == 32; }
 inline int pick_ks(int N, int K, int nwg) {
   int ks = 1;
-  while ((int64_t)(N / kNB) * ks < 2 * nwg && ks < 16 && K % (2 * ks * kKC) == 0) ks *= 2;
+  while (!chunks_ok(K / (ks * kKC)) && K % (2 * ks * kKC) == 0) ks *= 2;  // too long a range
+  while ((int64_t)(N / kNB) * ks < nwg && K % (2 * ks * kKC) == 0 && chunks_ok(K / (2 * ks * kKC))) ks *= 2;
   return ks;
+}
+typedef void (*GemmFn)(const uint16_t*, int, int, const uint16_t*, const uint16_t*, int, float*, int, int, const uint32_t*);
+inline GemmFn gemm_for(int nch) {
+  switch (nch) {
+    case 4: return gemm_kernel<4>;
+    case 8: return gemm_kernel<8>;
+    case 16: return gemm_kernel<16>;
+    case 32: return gemm_kernel<32>;
+    default: return nullptr;
+  }
 }
 
 inline int batch_check(const kd_config* c) {
@@ -59,8 +71,15 @@ inline int batch_check(const kd_config* c) {
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G > kMaxG) return KD_ERR_UNSUPPORTED;
   const int64_t qdim = (int64_t)c->n_q_heads * c->head_dim, nqkv = qdim + 2LL * c->n_kv_heads * c->head_dim;
-  if (c->d_model % kKC || qdim % kKC || c->ffn_dim % 256) return KD_ERR_UNSUPPORTED;
-  if (nqkv % kNB || c->d_model % kNB || c->vocab % kNB) return KD_ERR_UNSUPPORTED;
+  if (c->d_model % (kKC * kPF) || qdim % (kKC * kPF) || c->ffn_dim % (kKC * kPF)) return KD_ERR_UNSUPPORTED;
+  // every GEMM's K must split into ranges of 4, 8, 16 or 32 chunks
+  for (int64_t K : {(int64_t)c->d_model, qdim, (int64_t)c->ffn_dim}) {
+    int64_t nch = K / kKC;
+    while (nch > 32 && nch % 2 == 0) nch /= 2;
+    if (!chunks_ok((int)nch)) return KD_ERR_UNSUPPORTED;
+  }
+  if (!chunks_ok(c->d_model / kKC)) return KD_ERR_UNSUPPORTED;  // the LM head runs unsplit; d <= 4096
+  if (nqkv % kNB || c->d_model % kNB || c->vocab % kNB || (2LL * c->ffn_dim) % kNB) return KD_ERR_UNSUPPORTED;
   return KD_OK;
 }
 
@@ -98,7 +117,7 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, BatchSta
   st.g_o = {st.d, st.qdim, pick_ks(st.d, st.qdim, nwg)};
   st.g_gu = {2 * st.F, st.d, pick_ks(2 * st.F, st.d, nwg)};
   st.g_d = {st.d, st.F, pick_ks(st.d, st.F, nwg)};
-  st.g_lm = {st.V, st.d, 1};
+  st.g_lm = {st.V, st.d, 1};  // written straight into the logits: no split
   // attention: chunks of 512 positions (enough units to fill the device for any session count here)
   st.CH = 512;
   st.NCmax = (st.max_seq + st.CH - 1) / st.CH;
@@ -139,7 +158,7 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, BatchSta
                         hipMemcpyHostToDevice));
     KD_BT_TRY(hipMemcpy(lay + st.w_o, lw.wo, d * st.qdim * 2, hipMemcpyHostToDevice));
     // gate/up interleaved in blocks of 32 rows: rows [64j, 64j+32) = gate rows [32j, 32j+32),
-    // rows [64j+32, 64j+64) = the matching up rows, so one 64-column GEMM tile holds both halves
+    // rows [64j+32, 64j+64) = the matching up rows, so every GEMM tile holds whole pairs
     KD_BT_TRY(hipMemcpy2D(lay + st.w_gu, 64 * row, lw.w_gate, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
     KD_BT_TRY(hipMemcpy2D(lay + st.w_gu + 32 * d, 64 * row, lw.w_up, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
     KD_BT_TRY(hipMemcpy(lay + st.w_d, lw.w_down, d * st.F * 2, hipMemcpyHostToDevice));
@@ -179,11 +198,11 @@ inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions,
                 kv_layer = 2 * kv_slot;
   float* lg = logits ? logits : st.logits;
   auto gemm = [&](const uint16_t* W, const Gemm& g, float* out) {
-    hipLaunchKernelGGL(gemm_kernel, dim3((g.N / kNB) * g.KS), dim3(kGemmThreads), 0, s, W, g.N, g.K,
+    hipLaunchKernelGGL(gemm_for(g.K / (g.KS * kKC)), dim3((g.N / kNB) * g.KS), dim3(kGemmThreads), 0, s, W, g.N, g.K,
                        (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, out, g.KS, st.B, skip);
   };
   auto norm = [&](int mode, const Gemm* g, int gain_index) {
-    hipLaunchKernelGGL(residual_norm_kernel, dim3(st.B), dim3(256), 0, s, mode, (const uint16_t*)st.embed,
+    hipLaunchKernelGGL(residual_norm_kernel, dim3(st.B), dim3(1024), 0, s, mode, (const uint16_t*)st.embed,
                        (const int32_t*)tokens, (const float*)st.P, g ? g->KS : 0, st.X,
                        (const uint16_t*)(st.norms + (size_t)gain_index * st.d), st.d, st.eps, st.Ahi, st.Alo, st.lda,
                        st.B, skip);

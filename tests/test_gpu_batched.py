@@ -41,8 +41,8 @@ def kdm():
 def _clone():
     """A shrunk clone of the 56-session workload that runs the same kernels: head_dim 128, four
     query heads per kv head, 56 sessions, a pre-filled cache, and every GEMM shape a multiple of
-    the tiles (several split-K ranges for QKV, O and down)."""
-    shape = ModelShape(2, 256, 4, 1, 128, 512, 1024, rope_base=500000.0)
+    the tiles (two split-K ranges for QKV and down)."""
+    shape = ModelShape(2, 1024, 4, 1, 128, 1024, 1024, rope_base=500000.0)
     return Workload("clone_x56", shape, batch=56, prefill_len=48, gen_tokens=16, weight_seed=11, kv_seed=12,
                     first_token_seed=13)
 
