@@ -26,10 +26,11 @@ namespace kd {
 namespace bt {
 
 constexpr int kM = 64;             // sessions padded to four 16-row MFMA tiles
-constexpr int kNB = 128;           // GEMM output columns per workgroup: 8 waves x 16
+constexpr int kNB = 256;           // GEMM output columns per workgroup: 8 waves x 32
 constexpr int kKC = 128;           // K per LDS chunk of the activation block
 constexpr int kGemmThreads = 512;
 constexpr int kAttThreads = 256;   // 4 waves; 16 lanes per KV position (hd = 128, bf16)
+constexpr int kChunk = 512;        // KV positions per attention workgroup
 constexpr int kMaxG = 4;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -96,19 +97,38 @@ __global__ void check_kernel(const int32_t* tokens, const int32_t* positions, in
 }
 
 // ---------------------------------------------------------------------------------------------
+// weight tiles: the layout the GEMM streams
+// ---------------------------------------------------------------------------------------------
+// A weight matrix W[N][K] is stored as tiles of 16 rows x 32 K (1 KB), tile (r, t) at index
+// r * (K / 32) + t, each in the lane order of the matrix-core B operand: the 16 bytes of lane l
+// are W[16 r + l % 16][32 t + 8 (l / 16) .. + 8]. One 64-lane load then reads one whole tile,
+// 1 KB contiguous, and a wave walks its 16 rows as one contiguous run.
+// Grid: one thread per 16-byte piece (N * K / 8 of them).
+__global__ void tile_pack_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int N, int K) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)N * K / 8) return;
+  const int lane = (int)(i & 63);
+  const int64_t tile = i >> 6;
+  const int64_t per_row_block = K / 32;
+  const int64_t rb = tile / per_row_block, t = tile - rb * per_row_block;
+  const int64_t row = rb * 16 + (lane & 15), k = t * 32 + (lane >> 4) * 8;
+  ((u32x4*)dst)[i] = *(const u32x4*)(src + row * K + k);
+}
+
+// ---------------------------------------------------------------------------------------------
 // small-M GEMM on MFMA: P[s][m][n] = sum over K-range s of (Ahi[m][k] + Alo[m][k]) * W[n][k]
 // ---------------------------------------------------------------------------------------------
 // Grid: (N / kNB) * KS workgroups of 8 waves; unit u covers columns [kNB (u / KS), + kNB) and K range
-// u % KS, in chunks of 128 K. Wave w owns 16 output columns. Lane l streams weight row
-// n = n0 + 16 w + l % 16; per chunk it loads the 64 contiguous bytes k = 32 (l / 16) .. + 32. The
-// matrix-core K order is permuted to match (step t uses k = 32 (l / 16) + 8 t + j), and the
-// activation fragments are read from LDS in that same order, so the sum is unchanged.
+// u % KS, in chunks of 128 K. Wave w owns two 16-row tiles of W (32 output columns), so every
+// activation fragment it reads from LDS feeds two products. Per chunk a lane loads four 1 KB
+// tiles of each of its row blocks (W in the tile layout above), straight into registers in the
+// B-operand layout.
 //
-// Both the weights (HBM) and the activation block (64 rows x 128 K, hi and lo; it stays in L2)
-// are loaded into registers kPF chunks ahead, in the same order, so a wait for one never holds up
-// the other: the compiler sees every load and a wave's loads complete in issue order. The
-// activation chunk then goes through a double-buffered LDS tile that the eight waves share.
-constexpr int kPF = 4;  // chunks in flight per wave
+// The weights (HBM) and the activation block (64 rows x 128 K, hi and lo; it stays in L2) are
+// loaded into registers kPF chunks ahead, in the same order, so a wait for one never holds up
+// the other. The activation chunk then goes through a double-buffered LDS tile that the eight
+// waves share.
+constexpr int kPF = 2;  // chunks in flight per wave
 // NCH chunks per K range, fully unrolled: with no loop back-edge the compiler places every wait
 // exactly (at a back-edge it would drain all loads in flight).
 template <int NCH>
@@ -117,15 +137,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint16_t* _
                                                                 const uint16_t* __restrict__ Alo, int lda,
                                                                 float* __restrict__ P, int KS, int B, const uint32_t* skip) {
   if (*skip) return;
-  // [buffer][hi, lo][row][16-byte chunk of the 128-K slice, padded by one against bank conflicts]
+  // [buffer][hi, lo][row][16-byte piece of the 128-K chunk, padded by one against bank conflicts]
   __shared__ u32x4 As[2][2][kM][kKC / 8 + 1];
   const int unit = (int)blockIdx.x;
   const int nb = unit / KS, s = unit - nb * KS;
   const int k0 = s * (NCH * kKC);
   const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q = lane >> 4;
-  const int n = nb * kNB + wave * 16 + (lane & 15);
-  const u32x4* wrow = (const u32x4*)(W + (size_t)n * K + k0 + q * 32);
+  const int rb0 = nb * (kNB / 16) + 2 * wave;  // this wave's two 16-row blocks
+  const u32x4* wt[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) wt[j] = (const u32x4*)W + ((size_t)(rb0 + j) * (K / 32) + k0 / 32) * 64 + lane;
 
   // activation chunk: 2 x 64 rows x 16 pieces of 16 bytes = 2048 pieces, 4 per thread
   constexpr int kAPer = 2 * kM * (kKC / 8) / kGemmThreads;
@@ -133,7 +155,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint16_t* _
   // scratch memory when it sits in an array)
   struct Slot {
     u32x4 a[kAPer];
-    u32x4 w[4];
+    u32x4 w[2][4];
   };
   auto load_chunk = [&](int c, Slot& sl) __attribute__((always_inline)) {
 #pragma unroll
@@ -144,13 +166,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint16_t* _
     }
     // weights are read once per tick: non-temporal loads
 #pragma unroll
-    for (int t = 0; t < 4; ++t) sl.w[t] = __builtin_nontemporal_load(wrow + (size_t)c * (kKC / 8) + t);
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sl.w[j][t] = __builtin_nontemporal_load(wt[j] + (size_t)(c * 4 + t) * 64);
   };
 
-  f32x4 acc[4];
+  f32x4 acc[2][4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // one chunk: activation slot -> LDS buffer, barrier, 32 MFMAs, then refill the slot kPF ahead
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // one chunk: activation slot -> LDS buffer, barrier, 64 MFMAs, then refill the slot kPF ahead
   auto step = [&](int c, Slot& sl) __attribute__((always_inline)) {
     const int buf = c & 1;
 #pragma unroll
@@ -162,14 +188,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint16_t* _
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bf16x8 bw = __builtin_bit_cast(bf16x8, sl.w[t]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
+        // lane l supplies K = 32 t + 8 (l / 16) .. + 8 of row 16 mt + l % 16: piece 4 t + l / 16
         const int r = mt * 16 + (lane & 15);
-        const bf16x8 ah = __builtin_bit_cast(bf16x8, As[buf][0][r][q * 4 + t]);
-        const bf16x8 al = __builtin_bit_cast(bf16x8, As[buf][1][r][q * 4 + t]);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[mt], 0, 0, 0);
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, As[buf][0][r][t * 4 + q]);
+        const bf16x8 al = __builtin_bit_cast(bf16x8, As[buf][1][r][t * 4 + q]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8 bw = __builtin_bit_cast(bf16x8, sl.w[j][t]);
+          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[j][mt], 0, 0, 0);
+          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[j][mt], 0, 0, 0);
+        }
       }
     }
     if (c + kPF < NCH) load_chunk(c + kPF, sl);
@@ -179,14 +209,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint16_t* _
   for (int c = 0; c < kPF && c < NCH; ++c) load_chunk(c, ring[c]);
 #pragma unroll
   for (int c = 0; c < NCH; ++c) step(c, ring[c % kPF]);
-  // lane l holds rows 16 mt + 4 (l / 16) + i of column n
+  // lane l holds rows 16 mt + 4 (l / 16) + i of column 16 (rb0 + j) + l % 16
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int j = 0; j < 2; ++j) {
+    const int n = (rb0 + j) * 16 + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = mt * 16 + q * 4 + i;
-      if (m < B) P[((size_t)s * B + m) * N + n] = acc[mt][i];
-    }
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + q * 4 + i;
+        if (m < B) P[((size_t)s * B + m) * N + n] = acc[j][mt][i];
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -288,7 +322,7 @@ __global__ __launch_bounds__(128) void qkv_epilogue_kernel(const float* __restri
 // ---------------------------------------------------------------------------------------------
 // attention over one chunk of positions of one (session, kv head), for its G query heads
 // ---------------------------------------------------------------------------------------------
-// Grid: (NCmax, hkv, B) workgroups of 4 waves. Chunk c covers positions [c CH, min((c+1) CH, p+1)),
+// Grid: (NCmax, hkv, B) workgroups of 4 waves. Chunk c covers positions [c kChunk, min((c+1) kChunk, p+1)),
 // where p is the session's current position (already appended). 16 lanes hold one position (8 dims
 // each, hd = 128); a wave reads 4 positions per 1 KB load, and waves take packets round-robin.
 // Each lane group keeps a running (max, sum, acc) per head; groups and waves are then merged.
@@ -297,7 +331,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __r
                                                                  const uint16_t* __restrict__ kv, int64_t kv_slot,
                                                                  int64_t kv_sess, int64_t kv_head,
                                                                  const int32_t* __restrict__ positions, int hq, int hkv,
-                                                                 int CH, int NCmax, float* __restrict__ part,
+                                                                 int NCmax, float* __restrict__ part,
                                                                  const uint32_t* skip) {
   if (*skip) return;
   constexpr int HD = 128;
@@ -305,9 +339,9 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __r
   const int c = (int)blockIdx.x, g = (int)blockIdx.y, b = (int)blockIdx.z;
   const int G = hq / hkv;
   const int P1 = positions[b] + 1;
-  const int j0 = c * CH;
+  const int j0 = c * kChunk;
   if (j0 >= P1) return;
-  const int j1 = min(j0 + CH, P1);
+  const int j1 = min(j0 + kChunk, P1);
   const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = lane >> 4, dim0 = (lane & 15) * 8;
   float qv[kMaxG][8];
@@ -325,29 +359,36 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __r
   }
   const uint16_t* kbase = kv + kv_sess * b + kv_head * g + dim0;
   const uint16_t* vbase = kbase + kv_slot;
-  const int npk = (j1 - j0 + 3) / 4;
-  constexpr int U = 4;  // packets of K and V in flight per wave
-  for (int k0 = wave; k0 < npk; k0 += 4 * U) {
-    uint4 kw[U], vw[U];
+  // Wave w reads packets w, w + 4, ... of the chunk (4 positions each), U at a time; the loop is
+  // fully unrolled and loads the next U packets before working on the current ones. Positions
+  // past the current one are masked out; their loads re-read the chunk's first position.
+  constexpr int U = 4;
+  constexpr int kIt = kChunk / (16 * U);
+  auto load = [&](int it, u32x4 (&kw)[U], u32x4 (&vw)[U]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int pos = j0 + 4 * (k0 + 4 * u) + grp;
-      const int pl = pos < j1 ? pos : j0;  // stay inside the chunk's cached positions
-      kw[u] = *(const uint4*)(kbase + (int64_t)pl * HD);
-      vw[u] = *(const uint4*)(vbase + (int64_t)pl * HD);
+      const int pos = j0 + 4 * (wave + 4 * (it * U + u)) + grp;
+      const int pl = pos < j1 ? pos : j0;
+      kw[u] = *(const u32x4*)(kbase + (int64_t)pl * HD);
+      vw[u] = *(const u32x4*)(vbase + (int64_t)pl * HD);
     }
+  };
+  u32x4 kb[2][U], vb[2][U];
+  load(0, kb[0], vb[0]);
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    if (it + 1 < kIt) load(it + 1, kb[(it + 1) & 1], vb[(it + 1) & 1]);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int pos = j0 + 4 * (k0 + 4 * u) + grp;
+      const int pos = j0 + 4 * (wave + 4 * (it * U + u)) + grp;
       const bool valid = pos < j1;
       float kf[8], vf[8];
-      const uint32_t kk[4] = {kw[u].x, kw[u].y, kw[u].z, kw[u].w}, vv[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = __uint_as_float(kk[e] << 16);
-        kf[2 * e + 1] = __uint_as_float(kk[e] & 0xffff0000u);
-        vf[2 * e] = __uint_as_float(vv[e] << 16);
-        vf[2 * e + 1] = __uint_as_float(vv[e] & 0xffff0000u);
+        kf[2 * e] = __uint_as_float(kb[it & 1][u][e] << 16);
+        kf[2 * e + 1] = __uint_as_float(kb[it & 1][u][e] & 0xffff0000u);
+        vf[2 * e] = __uint_as_float(vb[it & 1][u][e] << 16);
+        vf[2 * e + 1] = __uint_as_float(vb[it & 1][u][e] & 0xffff0000u);
       }
 #pragma unroll
       for (int h = 0; h < kMaxG; ++h) {

@@ -18,7 +18,7 @@
 namespace kd {
 namespace bt {
 
-// One projection: W[N][K] (bf16, row-major) times the activation block, split over KS K-ranges.
+// One projection: W[N][K] (bf16, in the tile layout of tile_pack_kernel) times the activation block, split over KS K-ranges.
 struct Gemm {
   int N = 0, K = 0, KS = 1;
 };
@@ -44,18 +44,35 @@ struct BatchState {
   size_t w_qkv = 0, w_o = 0, w_gu = 0, w_d = 0, w_lm = 0;  // element offsets inside a layer / the blob
 };
 
-// Smallest power-of-two split with enough workgroups to fill the device (one per CU), each K
-// range 4, 8, 16 or 32 chunks of 128 K (the unrolled kernel variants).
-inline bool chunks_ok(int nch) { return nch == 4 || nch == 8 || nch == 16 || nch == 32; }
-inline int pick_ks(int N, int K, int nwg) {
-  int ks = 1;
-  while (!chunks_ok(K / (ks * kKC)) && K % (2 * ks * kKC) == 0) ks *= 2;  // too long a range
-  while ((int64_t)(N / kNB) * ks < nwg && K % (2 * ks * kKC) == 0 && chunks_ok(K / (2 * ks * kKC))) ks *= 2;
-  return ks;
+// Split-K factor of a GEMM: the power of two whose estimated time is least, over K ranges of
+// 2, 4, 8, 16 or 32 chunks of 128 K (the unrolled kernel variants). The estimate: the weight
+// stream at about 6.5 TB/s, or, when there are too few workgroups for that, rounds of one
+// workgroup per CU each paying a fixed start-up latency and streaming at a single CU's rate;
+// plus writing and reading back the fp32 partial sums. Returns -1 if no split is valid.
+inline bool chunks_ok(int nch) { return nch == 2 || nch == 4 || nch == 8 || nch == 16 || nch == 32; }
+inline int pick_ks(int N, int K, int B, int nwg) {
+  const double bw = 6.5e12, bw_cu = 50e9, start = 3e-6;
+  const int nch_all = K / kKC;
+  int best = -1;
+  double best_t = 1e30;
+  for (int ks = 1; ks <= nch_all && nch_all % ks == 0; ks *= 2) {
+    const int nch = nch_all / ks;
+    if (!chunks_ok(nch)) continue;
+    const int64_t units = (int64_t)(N / kNB) * ks;
+    const double rounds = (double)((units + nwg - 1) / nwg);
+    const double per_unit = start + nch * (double)kNB * kKC * 2.0 / bw_cu;
+    const double t = std::max(2.0 * N * K / bw, rounds * per_unit) + 2.0 * ks * B * (double)N * 4.0 / bw;
+    if (t < best_t) {
+      best_t = t;
+      best = ks;
+    }
+  }
+  return best;
 }
 typedef void (*GemmFn)(const uint16_t*, int, int, const uint16_t*, const uint16_t*, int, float*, int, int, const uint32_t*);
 inline GemmFn gemm_for(int nch) {
   switch (nch) {
+    case 2: return gemm_kernel<2>;
     case 4: return gemm_kernel<4>;
     case 8: return gemm_kernel<8>;
     case 16: return gemm_kernel<16>;
@@ -71,9 +88,9 @@ inline int batch_check(const kd_config* c) {
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G > kMaxG) return KD_ERR_UNSUPPORTED;
   const int64_t qdim = (int64_t)c->n_q_heads * c->head_dim, nqkv = qdim + 2LL * c->n_kv_heads * c->head_dim;
-  if (c->d_model % (kKC * kPF) || qdim % (kKC * kPF) || c->ffn_dim % (kKC * kPF)) return KD_ERR_UNSUPPORTED;
-  // every GEMM's K must split into ranges of 4, 8, 16 or 32 chunks
+  // every GEMM's K must split into ranges of 2, 4, 8, 16 or 32 chunks of 128
   for (int64_t K : {(int64_t)c->d_model, qdim, (int64_t)c->ffn_dim}) {
+    if (K % kKC) return KD_ERR_UNSUPPORTED;
     int64_t nch = K / kKC;
     while (nch > 32 && nch % 2 == 0) nch /= 2;
     if (!chunks_ok((int)nch)) return KD_ERR_UNSUPPORTED;
@@ -113,13 +130,15 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, BatchSta
   st.qdim = st.hq * st.hd;
   st.nqkv = st.qdim + 2 * st.hkv * st.hd;
   st.lda = std::max({st.d, st.qdim, st.F});
-  st.g_qkv = {st.nqkv, st.d, pick_ks(st.nqkv, st.d, nwg)};
-  st.g_o = {st.d, st.qdim, pick_ks(st.d, st.qdim, nwg)};
-  st.g_gu = {2 * st.F, st.d, pick_ks(2 * st.F, st.d, nwg)};
-  st.g_d = {st.d, st.F, pick_ks(st.d, st.F, nwg)};
+  st.g_qkv = {st.nqkv, st.d, pick_ks(st.nqkv, st.d, st.B, nwg)};
+  st.g_o = {st.d, st.qdim, pick_ks(st.d, st.qdim, st.B, nwg)};
+  st.g_gu = {2 * st.F, st.d, pick_ks(2 * st.F, st.d, st.B, nwg)};
+  st.g_d = {st.d, st.F, pick_ks(st.d, st.F, st.B, nwg)};
+  for (const Gemm* g : {&st.g_qkv, &st.g_o, &st.g_gu, &st.g_d})
+    if (g->KS < 1) return KD_ERR_UNSUPPORTED;
   st.g_lm = {st.V, st.d, 1};  // written straight into the logits: no split
   // attention: chunks of 512 positions (enough units to fill the device for any session count here)
-  st.CH = 512;
+  st.CH = kChunk;
   st.NCmax = (st.max_seq + st.CH - 1) / st.CH;
 
   const size_t d = st.d;
@@ -148,25 +167,56 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, BatchSta
   KD_BT_TRY(hipMemset(st.Ahi, 0, (size_t)kM * st.lda * 2));  // padding rows stay zero for good
   KD_BT_TRY(hipMemset(st.Alo, 0, (size_t)kM * st.lda * 2));
 
+  // Every matrix goes row-major into a staging buffer, then tile_pack_kernel writes it into the
+  // blob in the tile layout the GEMM streams.
   const size_t row = d * 2;
+  uint16_t* stage = nullptr;
+  {
+    size_t most = std::max({(size_t)st.nqkv * d, d * st.qdim, 2 * (size_t)st.F * d, (size_t)st.V * d});
+    if (hipMalloc(&stage, most * 2) != hipSuccess) {
+      batch_free(st);
+      return KD_ERR_OOM;
+    }
+  }
+#define KD_BT_STAGE_TRY(expr)   \
+  do {                          \
+    if ((expr) != hipSuccess) { \
+      (void)hipFree(stage);     \
+      batch_free(st);           \
+      return KD_ERR_HIP;        \
+    }                           \
+  } while (0)
+  auto pack = [&](uint16_t* dst, int N, int K) {
+    const int64_t pieces = (int64_t)N * K / 8;
+    hipLaunchKernelGGL(tile_pack_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, 0, (const uint16_t*)stage,
+                       dst, N, K);
+    return hipDeviceSynchronize();  // the next copy reuses the staging buffer
+  };
   for (int l = 0; l < st.L; ++l) {
     const kd_layer_weights& lw = w->layers[l];
     uint16_t* lay = st.w + (size_t)l * st.layer_elems;
-    KD_BT_TRY(hipMemcpy(lay + st.w_qkv, lw.wq, (size_t)st.qdim * row, hipMemcpyHostToDevice));
-    KD_BT_TRY(hipMemcpy(lay + st.w_qkv + (size_t)st.qdim * d, lw.wk, (size_t)st.hkv * st.hd * row, hipMemcpyHostToDevice));
-    KD_BT_TRY(hipMemcpy(lay + st.w_qkv + (size_t)(st.qdim + st.hkv * st.hd) * d, lw.wv, (size_t)st.hkv * st.hd * row,
-                        hipMemcpyHostToDevice));
-    KD_BT_TRY(hipMemcpy(lay + st.w_o, lw.wo, d * st.qdim * 2, hipMemcpyHostToDevice));
+    KD_BT_STAGE_TRY(hipMemcpy(stage, lw.wq, (size_t)st.qdim * row, hipMemcpyHostToDevice));
+    KD_BT_STAGE_TRY(hipMemcpy(stage + (size_t)st.qdim * d, lw.wk, (size_t)st.hkv * st.hd * row, hipMemcpyHostToDevice));
+    KD_BT_STAGE_TRY(hipMemcpy(stage + (size_t)(st.qdim + st.hkv * st.hd) * d, lw.wv, (size_t)st.hkv * st.hd * row,
+                              hipMemcpyHostToDevice));
+    KD_BT_STAGE_TRY(pack(lay + st.w_qkv, st.nqkv, st.d));
+    KD_BT_STAGE_TRY(hipMemcpy(stage, lw.wo, d * st.qdim * 2, hipMemcpyHostToDevice));
+    KD_BT_STAGE_TRY(pack(lay + st.w_o, st.d, st.qdim));
     // gate/up interleaved in blocks of 32 rows: rows [64j, 64j+32) = gate rows [32j, 32j+32),
     // rows [64j+32, 64j+64) = the matching up rows, so every GEMM tile holds whole pairs
-    KD_BT_TRY(hipMemcpy2D(lay + st.w_gu, 64 * row, lw.w_gate, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
-    KD_BT_TRY(hipMemcpy2D(lay + st.w_gu + 32 * d, 64 * row, lw.w_up, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
-    KD_BT_TRY(hipMemcpy(lay + st.w_d, lw.w_down, d * st.F * 2, hipMemcpyHostToDevice));
-    KD_BT_TRY(hipMemcpy(st.norms + (size_t)(2 * l) * d, lw.attn_norm, row, hipMemcpyHostToDevice));
-    KD_BT_TRY(hipMemcpy(st.norms + (size_t)(2 * l + 1) * d, lw.ffn_norm, row, hipMemcpyHostToDevice));
+    KD_BT_STAGE_TRY(hipMemcpy2D(stage, 64 * row, lw.w_gate, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
+    KD_BT_STAGE_TRY(hipMemcpy2D(stage + 32 * d, 64 * row, lw.w_up, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
+    KD_BT_STAGE_TRY(pack(lay + st.w_gu, 2 * st.F, st.d));
+    KD_BT_STAGE_TRY(hipMemcpy(stage, lw.w_down, d * st.F * 2, hipMemcpyHostToDevice));
+    KD_BT_STAGE_TRY(pack(lay + st.w_d, st.d, st.F));
+    KD_BT_STAGE_TRY(hipMemcpy(st.norms + (size_t)(2 * l) * d, lw.attn_norm, row, hipMemcpyHostToDevice));
+    KD_BT_STAGE_TRY(hipMemcpy(st.norms + (size_t)(2 * l + 1) * d, lw.ffn_norm, row, hipMemcpyHostToDevice));
   }
+  KD_BT_STAGE_TRY(hipMemcpy(stage, w->lm_head, (size_t)st.V * row, hipMemcpyHostToDevice));
+  KD_BT_STAGE_TRY(pack(st.w + st.w_lm, st.V, st.d));
+#undef KD_BT_STAGE_TRY
+  (void)hipFree(stage);
   KD_BT_TRY(hipMemcpy(st.norms + (size_t)(2 * st.L) * d, w->final_norm, row, hipMemcpyHostToDevice));
-  KD_BT_TRY(hipMemcpy(st.w + st.w_lm, w->lm_head, (size_t)st.V * row, hipMemcpyHostToDevice));
   KD_BT_TRY(hipMemcpy(st.embed, w->embed, (size_t)st.V * row, hipMemcpyHostToDevice));
   {
     // RoPE: pair (i, i + hd/2) turns by position * base^(-2i/hd); angles, cos and sin in float64
@@ -218,7 +268,7 @@ inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions,
                        st.g_qkv.KS, st.nqkv, st.hq, st.hkv, st.hd, (const float2*)st.rope, (const int32_t*)positions,
                        st.Qs, kvl, kv_slot, kv_sess, kv_head, st.B, skip);
     hipLaunchKernelGGL(attention_kernel, dim3(st.NCmax, st.hkv, st.B), dim3(kAttThreads), 0, s, (const float*)st.Qs,
-                       (const uint16_t*)kvl, kv_slot, kv_sess, kv_head, (const int32_t*)positions, st.hq, st.hkv, st.CH,
+                       (const uint16_t*)kvl, kv_slot, kv_sess, kv_head, (const int32_t*)positions, st.hq, st.hkv,
                        st.NCmax, st.part, skip);
     hipLaunchKernelGGL(merge_kernel, dim3(st.hq, st.B), dim3(st.hd), 0, s, (const float*)st.part,
                        (const int32_t*)positions, st.hq, st.hd, st.CH, st.NCmax, st.Ahi, st.Alo, st.lda, skip);

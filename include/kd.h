@@ -73,9 +73,9 @@ extern "C" {
  *   batch        sessions stepped together in lockstep. batch == 1 runs the single persistent
  *                kernel. 2 <= batch <= 64 runs the lockstep-sessions path: the projections become
  *                small-M GEMMs on the matrix cores. That path needs bf16 weights and cache,
- *                head_dim 128, d_model one of 512, 1024, 2048 or 4096, n_q_heads*head_dim and
- *                ffn_dim multiples of 512 (up to 32768), and (n_q_heads+2*n_kv_heads)*head_dim
- *                and vocab multiples of 128.
+ *                head_dim 128, d_model one of 256, 512, 1024, 2048 or 4096, n_q_heads*head_dim
+ *                and ffn_dim each 256 times a power of two, and d_model, 2*ffn_dim,
+ *                (n_q_heads+2*n_kv_heads)*head_dim and vocab multiples of 256.
  *   norm_eps     RMSNorm epsilon (inside the square root).
  *   rope_base    RoPE base: pair (i, i + head_dim/2) turns by position * rope_base^(-2i/head_dim).
  *   weight_dtype KD_DTYPE_BF16 or KD_DTYPE_F32; kv_dtype likewise (must match weight_dtype).
