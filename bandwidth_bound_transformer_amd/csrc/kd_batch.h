@@ -327,6 +327,9 @@ __global__ __launch_bounds__(128) void qkv_epilogue_kernel(const float* __restri
 // each, hd = 128); a wave reads 4 positions per 1 KB load, and waves take packets round-robin.
 // Each lane group keeps a running (max, sum, acc) per head; groups and waves are then merged.
 // Output: part[((b hq + h) NCmax + c) (hd + 2) + {0: max, 1: sum, 2 + i: acc_i}].
+// G = q heads per kv head. Weights are exp2 of base-2 scores on the hardware exp2 (a result below
+// 2^-126 may flush to zero; such a weight is far below the sum's rounding).
+template <int G>
 __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __restrict__ Qs,
                                                                  const uint16_t* __restrict__ kv, int64_t kv_slot,
                                                                  int64_t kv_sess, int64_t kv_head,
@@ -335,23 +338,24 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __r
                                                                  const uint32_t* skip) {
   if (*skip) return;
   constexpr int HD = 128;
-  __shared__ float sm[4][kMaxG][HD + 2];
+  __shared__ float sm[4][G][HD + 2];
   const int c = (int)blockIdx.x, g = (int)blockIdx.y, b = (int)blockIdx.z;
-  const int G = hq / hkv;
   const int P1 = positions[b] + 1;
   const int j0 = c * kChunk;
   if (j0 >= P1) return;
   const int j1 = min(j0 + kChunk, P1);
   const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = lane >> 4, dim0 = (lane & 15) * 8;
-  float qv[kMaxG][8];
+  // scores in base-2 units: q carries 1/sqrt(hd) and log2(e), so exp(s - m) = exp2(s2 - m2)
+  constexpr float kLog2e = 1.4426950408889634f;
+  float qv[G][8];
 #pragma unroll
-  for (int h = 0; h < kMaxG; ++h)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[h][e] = h < G ? Qs[((size_t)b * hq + g * G + h) * HD + dim0 + e] : 0.f;
-  float mx[kMaxG], ls[kMaxG], acc[kMaxG][8];
+    for (int e = 0; e < 8; ++e) qv[h][e] = Qs[((size_t)b * hq + g * G + h) * HD + dim0 + e] * kLog2e;
+  float mx[G], ls[G], acc[G][8];
 #pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
+  for (int h = 0; h < G; ++h) {
     mx[h] = -INFINITY;
     ls[h] = 0.f;
 #pragma unroll
@@ -361,7 +365,8 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __r
   const uint16_t* vbase = kbase + kv_slot;
   // Wave w reads packets w, w + 4, ... of the chunk (4 positions each), U at a time; the loop is
   // fully unrolled and loads the next U packets before working on the current ones. Positions
-  // past the current one are masked out; their loads re-read the chunk's first position.
+  // past the current one are masked out; their loads re-read the chunk's first position. K and V
+  // are read once per tick: non-temporal loads.
   constexpr int U = 4;
   constexpr int kIt = kChunk / (16 * U);
   auto load = [&](int it, u32x4 (&kw)[U], u32x4 (&vw)[U]) __attribute__((always_inline)) {
@@ -369,58 +374,98 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __r
     for (int u = 0; u < U; ++u) {
       const int pos = j0 + 4 * (wave + 4 * (it * U + u)) + grp;
       const int pl = pos < j1 ? pos : j0;
-      kw[u] = *(const u32x4*)(kbase + (int64_t)pl * HD);
-      vw[u] = *(const u32x4*)(vbase + (int64_t)pl * HD);
+      kw[u] = __builtin_nontemporal_load((const u32x4*)(kbase + (int64_t)pl * HD));
+      vw[u] = __builtin_nontemporal_load((const u32x4*)(vbase + (int64_t)pl * HD));
     }
   };
   u32x4 kb[2][U], vb[2][U];
   load(0, kb[0], vb[0]);
 #pragma unroll
   for (int it = 0; it < kIt; ++it) {
+    // keep each iteration's loads where they are (hoisting them all would need registers for the
+    // whole chunk)
+    __builtin_amdgcn_sched_barrier(0);
     if (it + 1 < kIt) load(it + 1, kb[(it + 1) & 1], vb[(it + 1) & 1]);
+    const u32x4(&kc)[U] = kb[it & 1];
+    const u32x4(&vc)[U] = vb[it & 1];
+    // the U positions of this lane group: scores of every head (masked past the current position)
+    float sc[G][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int pos = j0 + 4 * (wave + 4 * (it * U + u)) + grp;
-      const bool valid = pos < j1;
-      float kf[8], vf[8];
+      const bool valid = j0 + 4 * (wave + 4 * (it * U + u)) + grp < j1;
+      float kf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = __uint_as_float(kb[it & 1][u][e] << 16);
-        kf[2 * e + 1] = __uint_as_float(kb[it & 1][u][e] & 0xffff0000u);
-        vf[2 * e] = __uint_as_float(vb[it & 1][u][e] << 16);
-        vf[2 * e + 1] = __uint_as_float(vb[it & 1][u][e] & 0xffff0000u);
+        kf[2 * e] = __uint_as_float(kc[u][e] << 16);
+        kf[2 * e + 1] = __uint_as_float(kc[u][e] & 0xffff0000u);
       }
 #pragma unroll
-      for (int h = 0; h < kMaxG; ++h) {
-        if (h < G) {
-          float sc = 0.f;
+      for (int h = 0; h < G; ++h) {
+        {
+          float s2 = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sc = fmaf(qv[h][e], kf[e], sc);
-          sc = sum16(sc);
-          if (valid) {
-            const float mn = fmaxf(mx[h], sc);
-            const float r = __expf(mx[h] - mn), w = __expf(sc - mn);
-            ls[h] = fmaf(ls[h], r, w);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], r, w * vf[e]);
-            mx[h] = mn;
-          }
+          for (int e = 0; e < 8; ++e) s2 = fmaf(qv[h][e], kf[e], s2);
+          s2 = sum16(s2);
+          sc[h][u] = valid ? s2 : -INFINITY;
         }
       }
+    }
+    // one rescale per block of U positions: new running max, then the block's weights
+    float mb[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      {
+        float mn = mx[h];
+#pragma unroll
+        for (int u = 0; u < U; ++u) mn = fmaxf(mn, sc[h][u]);
+        mb[h] = mn == -INFINITY ? 0.f : mn;  // nothing valid yet: every weight below is exp2(-inf) = 0
+        const float r = __builtin_amdgcn_exp2f(mx[h] - mb[h]);
+        mx[h] = mn;
+        ls[h] *= r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= r;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[2 * e] = __uint_as_float(vc[u][e] << 16);
+        vf[2 * e + 1] = __uint_as_float(vc[u][e] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        {
+          const float w = __builtin_amdgcn_exp2f(sc[h][u] - mb[h]);
+          ls[h] += w;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
+        }
+      }
+    }
+    // Make this iteration's running state an opaque input of the next one, so the compiler
+    // cannot defer a head's updates to the end of the chunk (which keeps every iteration's K
+    // and V in registers).
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      asm volatile("" : "+v"(mx[h]), "+v"(ls[h]));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(acc[h][e]));
     }
   }
   // merge the four position groups of the wave (lane ^ 16, then lane ^ 32)
   auto merge_pair = [&](int h, float m_a, float m_b, float l_a, float l_b, float* ea, float* eb) {
     const float M = fmaxf(m_a, m_b);
-    const float ra = M == -INFINITY ? 0.f : __expf(m_a - M), rb = M == -INFINITY ? 0.f : __expf(m_b - M);
+    const float ra = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_a - M), rb = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_b - M);
     mx[h] = M;
     ls[h] = l_a * ra + l_b * rb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = ea[e] * ra + eb[e] * rb;
   };
 #pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
-    if (h < G) {
+  for (int h = 0; h < G; ++h) {
+    {
 #pragma unroll
       for (int step = 0; step < 2; ++step) {
         float ma, mb, la, lb, ea[8], eb[8];
@@ -457,7 +502,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __r
     float L = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float r = M == -INFINITY ? 0.f : __expf(sm[w][h][0] - M);
+      const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[w][h][0] - M);
       L = fmaf(sm[w][h][1], r, L);
       a0 = fmaf(sm[w][h][2 + i0], r, a0);
       a1 = fmaf(sm[w][h][2 + i0 + 1], r, a1);
@@ -466,7 +511,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __r
     out[2 + i0] = a0;
     out[2 + i0 + 1] = a1;
     if (i0 == 0) {
-      out[0] = M;
+      out[0] = M * 0.6931471805599453f;  // back to natural-log units for the merge
       out[1] = L;
     }
   }

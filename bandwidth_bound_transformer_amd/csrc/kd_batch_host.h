@@ -81,6 +81,18 @@ inline GemmFn gemm_for(int nch) {
   }
 }
 
+typedef void (*AttFn)(const float*, const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, int, int, int, float*,
+                      const uint32_t*);
+inline AttFn att_for(int G) {
+  switch (G) {
+    case 1: return attention_kernel<1>;
+    case 2: return attention_kernel<2>;
+    case 3: return attention_kernel<3>;
+    case 4: return attention_kernel<4>;
+    default: return nullptr;
+  }
+}
+
 inline int batch_check(const kd_config* c) {
   if (c->batch < 2 || c->batch > kM) return KD_ERR_UNSUPPORTED;
   if (c->weight_dtype != KD_DTYPE_BF16 || c->kv_dtype != KD_DTYPE_BF16) return KD_ERR_UNSUPPORTED;
@@ -267,7 +279,7 @@ inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions,
     hipLaunchKernelGGL(qkv_epilogue_kernel, dim3(st.hq + 2 * st.hkv, st.B), dim3(st.hd), 0, s, (const float*)st.P,
                        st.g_qkv.KS, st.nqkv, st.hq, st.hkv, st.hd, (const float2*)st.rope, (const int32_t*)positions,
                        st.Qs, kvl, kv_slot, kv_sess, kv_head, st.B, skip);
-    hipLaunchKernelGGL(attention_kernel, dim3(st.NCmax, st.hkv, st.B), dim3(kAttThreads), 0, s, (const float*)st.Qs,
+    hipLaunchKernelGGL(att_for(st.hq / st.hkv), dim3(st.NCmax, st.hkv, st.B), dim3(kAttThreads), 0, s, (const float*)st.Qs,
                        (const uint16_t*)kvl, kv_slot, kv_sess, kv_head, (const int32_t*)positions, st.hq, st.hkv,
                        st.NCmax, st.part, skip);
     hipLaunchKernelGGL(merge_kernel, dim3(st.hq, st.B), dim3(st.hd), 0, s, (const float*)st.part,
