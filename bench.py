@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 METRIC = "batch-1 decode tokens/sec on 1 MI355X + % of HBM bytes/token roofline"
 METRIC_SESSIONS = "aggregate decode tokens/sec of lockstep sessions on 1 MI355X + p99 tick latency"
-KERNEL_SOURCES = ("kd_device.h", "kd_plan.h", "kd_api.hip")
+KERNEL_SOURCES = ("kd_device.h", "kd_plan.h", "kd_pack.h")  # what defines the batch-1 step kernel and its weight layout
 
 
 def log(*a):
