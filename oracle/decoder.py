@@ -177,9 +177,17 @@ class Oracle:
         # cached values are exact in float32 (they are float32 or bf16 numbers)
         self.k_cache = np.zeros((batch, m.n_layers, m.n_kv_heads, max_seq, m.head_dim), np.float32)
         self.v_cache = np.zeros_like(self.k_cache)
+        # For a small model, the float64 value of each stored matrix is made once instead of at
+        # every use (the same values; large models convert per use to bound host memory). The
+        # dict holds the stored arrays' ids, which stay unique while self.w keeps them alive.
+        self._f64 = {}
+        stored = [lw[k] for lw in weights["layers"] for k in lw] + [weights["final_norm"], weights["lm_head"]]
+        if sum(a.size for a in stored) * 8 <= (1 << 30):
+            self._f64 = {id(a): weight_f64(a, self.wdt) for a in stored}
 
     def mat(self, t: np.ndarray) -> np.ndarray:
-        return weight_f64(t, self.wdt)
+        cached = self._f64.get(id(t))
+        return cached if cached is not None else weight_f64(t, self.wdt)
 
     def load_kv(self, session: int, layer: int, kv_head: int, keys: np.ndarray, values: np.ndarray) -> None:
         """Put pre-filled cache contents (already in storage precision) at positions 0..n-1."""

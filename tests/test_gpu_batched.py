@@ -43,7 +43,7 @@ def _clone():
     query heads per kv head, 56 sessions, a pre-filled cache, and every GEMM shape a multiple of
     the tiles (two split-K ranges for QKV and down)."""
     shape = ModelShape(2, 1024, 4, 1, 128, 1024, 1024, rope_base=500000.0)
-    return Workload("clone_x56", shape, batch=56, prefill_len=48, gen_tokens=16, weight_seed=11, kv_seed=12,
+    return Workload("clone_x56", shape, batch=56, prefill_len=48, gen_tokens=200, weight_seed=11, kv_seed=12,
                     first_token_seed=13)
 
 
@@ -83,8 +83,8 @@ def _check_tick(gl, g_tok, want, tag):
 
 
 def test_clone_x56_every_session(torch, kdm):
-    """56 sessions, 16 ticks from a 48-position pre-filled cache: logits, tokens, positions and the
-    K/V each tick appends, for every session."""
+    """56 sessions, 200 ticks from a 48-position pre-filled cache: logits, tokens, positions and the
+    K/V each tick appends, for every session. Tie-flips may touch at most 1% of the tokens."""
     wl = _clone()
     m = wl.model
     w = workloads.make_weights(m, seed=wl.weight_seed)
@@ -110,7 +110,7 @@ def test_clone_x56_every_session(torch, kdm):
             flips += flip
         tok = g_tok.astype(np.int64)
     print(f"clone_x56: max rel logit err {worst:.3e} over {wl.gen_tokens} ticks x {wl.batch} sessions, tie-flips {flips}")
-    assert flips <= 2
+    assert flips <= max(2, wl.gen_tokens * wl.batch // 100)
     assert dec.status() == 0
     assert np.all(dec.positions.cpu().numpy() == wl.prefill_len + wl.gen_tokens)
     # the appended positions hold K (after RoPE) and V as the oracle stored them
@@ -166,13 +166,14 @@ def test_clone_x56_bad_input_writes_nothing(torch, kdm):
 
 def test_11b_x56_sampled_sessions(torch, kdm):
     """The 11B-class decoder at its real shape and launch configuration (56 sessions, KV cache
-    pre-filled to 4096 positions): two ticks, logits of sessions 0 and 55 against the oracle."""
+    pre-filled to 4096 positions): four ticks, logits and tokens of sessions 0, 27 and 55 against
+    the oracle (which carries only those sessions' caches)."""
     wl = workloads.get("11b_x56")
     m = wl.model
     w = workloads.make_weights(m, seed=wl.weight_seed)
     print("11b: weights ready", flush=True)
     dec = kdm.Decoder(m, w, max_seq=wl.max_seq, batch=wl.batch)
-    sessions = [0, 55]
+    sessions = [0, 27, 55]
     _fill_sessions(dec, wl, sessions, torch)
     o = _oracle_with_prefill(wl, w, sessions)
     print("11b: caches filled", flush=True)
@@ -180,7 +181,7 @@ def test_11b_x56_sampled_sessions(torch, kdm):
     dec.tokens.copy_(torch.from_numpy(first))
     dec.positions.fill_(wl.prefill_len)
     tok = first.astype(np.int64)
-    for t in range(2):
+    for t in range(4):
         p = wl.prefill_len + t
         dec.step()
         gl = dec.logits.cpu().numpy()
