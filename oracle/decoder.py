@@ -200,38 +200,55 @@ class Oracle:
     def _store(self, x: np.ndarray) -> np.ndarray:
         return to_storage(x, self.shape.kv_dtype).astype(np.float32)
 
+    def step_sessions(self, sessions, tokens, positions) -> np.ndarray:
+        """Feed ``tokens[i]`` of session ``sessions[i]`` at ``positions[i]``; return logits [n, V] (float64).
+
+        Sessions are independent: each goes through exactly the operations of a step of its own.
+        The loop is layer-major only so that a layer's weights are converted to float64 once per
+        call rather than once per session.
+        """
+        m, w = self.shape, self.w
+        hd, hq, hkv = m.head_dim, m.n_q_heads, m.n_kv_heads
+        for token, position in zip(tokens, positions):
+            if not 0 <= token < m.vocab:
+                raise ValueError(f"token {token} out of range")
+            if not 0 <= position < self.max_seq:
+                raise ValueError(f"position {position} out of range")
+        rope = [rope_cos_sin(int(p), hd, m.rope_base) for p in positions]
+        xs = [self.mat(w["embed"][int(t)]) for t in tokens]
+        for l, lw in enumerate(w["layers"]):
+            W = {k: self.mat(lw[k]) for k in lw}
+            for i, session in enumerate(sessions):
+                position = int(positions[i])
+                cos, sin = rope[i]
+                x = xs[i]
+                h = rms_norm(x, W["attn_norm"], m.norm_eps)
+                q = (W["wq"] @ h).reshape(hq, hd)
+                k = (W["wk"] @ h).reshape(hkv, hd)
+                v = (W["wv"] @ h).reshape(hkv, hd)
+                q = apply_rope(q, cos, sin)
+                k = apply_rope(k, cos, sin)
+                self.k_cache[session, l, :, position] = self._store(k)
+                self.v_cache[session, l, :, position] = self._store(v)
+                kc = self.k_cache[session, l, :, : position + 1].astype(np.float64)
+                vc = self.v_cache[session, l, :, : position + 1].astype(np.float64)
+                o = attend(q, kc, vc).reshape(hq * hd)
+                x = x + W["wo"] @ o
+                h2 = rms_norm(x, W["ffn_norm"], m.norm_eps)
+                a = silu(W["w_gate"] @ h2) * (W["w_up"] @ h2)
+                xs[i] = x + W["w_down"] @ a
+            del W
+        g_final = self.mat(w["final_norm"])
+        lm = self.mat(w["lm_head"])
+        return np.stack([lm @ rms_norm(x, g_final, m.norm_eps) for x in xs])
+
     def step_one(self, session: int, token: int, position: int) -> np.ndarray:
         """Feed one token of one session at ``position``; return its logits [V] (float64)."""
-        m, w = self.shape, self.w
-        if not 0 <= token < m.vocab:
-            raise ValueError(f"token {token} out of range")
-        if not 0 <= position < self.max_seq:
-            raise ValueError(f"position {position} out of range")
-        hd, hq, hkv = m.head_dim, m.n_q_heads, m.n_kv_heads
-        cos, sin = rope_cos_sin(position, hd, m.rope_base)
-        x = self.mat(w["embed"][token])
-        for l, lw in enumerate(w["layers"]):
-            h = rms_norm(x, self.mat(lw["attn_norm"]), m.norm_eps)
-            q = (self.mat(lw["wq"]) @ h).reshape(hq, hd)
-            k = (self.mat(lw["wk"]) @ h).reshape(hkv, hd)
-            v = (self.mat(lw["wv"]) @ h).reshape(hkv, hd)
-            q = apply_rope(q, cos, sin)
-            k = apply_rope(k, cos, sin)
-            self.k_cache[session, l, :, position] = self._store(k)
-            self.v_cache[session, l, :, position] = self._store(v)
-            kc = self.k_cache[session, l, :, : position + 1].astype(np.float64)
-            vc = self.v_cache[session, l, :, : position + 1].astype(np.float64)
-            o = attend(q, kc, vc).reshape(hq * hd)
-            x = x + self.mat(lw["wo"]) @ o
-            h2 = rms_norm(x, self.mat(lw["ffn_norm"]), m.norm_eps)
-            a = silu(self.mat(lw["w_gate"]) @ h2) * (self.mat(lw["w_up"]) @ h2)
-            x = x + self.mat(lw["w_down"]) @ a
-        hf = rms_norm(x, self.mat(w["final_norm"]), m.norm_eps)
-        return self.mat(w["lm_head"]) @ hf
+        return self.step_sessions([session], [token], [position])[0]
 
     def step(self, tokens, positions) -> np.ndarray:
         """One step of every session: ``tokens[b]`` at ``positions[b]``; logits [B, V]."""
-        return np.stack([self.step_one(b, int(tokens[b]), int(positions[b])) for b in range(self.batch)])
+        return self.step_sessions(range(self.batch), [int(t) for t in tokens], [int(p) for p in positions])
 
     def generate(self, prompt, n_tokens: int, session: int = 0):
         """Feed ``prompt`` from position 0, then greedily generate ``n_tokens`` tokens.

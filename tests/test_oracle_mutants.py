@@ -28,26 +28,29 @@ MUTANTS = {
         "kc = self.k_cache[session, l, :, : position + 1]",
         "kc = self.k_cache[session, l, :, : position]",
     ),
-    "attention_residual_dropped": ('x = x + self.mat(lw["wo"]) @ o', 'x = self.mat(lw["wo"]) @ o'),
-    "ffn_residual_dropped": ('x = x + self.mat(lw["w_down"]) @ a', 'x = self.mat(lw["w_down"]) @ a'),
+    "attention_residual_dropped": ('x = x + W["wo"] @ o', 'x = W["wo"] @ o'),
+    "ffn_residual_dropped": ('xs[i] = x + W["w_down"] @ a', 'xs[i] = W["w_down"] @ a'),
     "silu_on_up_branch": (
-        'a = silu(self.mat(lw["w_gate"]) @ h2) * (self.mat(lw["w_up"]) @ h2)',
-        'a = (self.mat(lw["w_gate"]) @ h2) * silu(self.mat(lw["w_up"]) @ h2)',
+        'a = silu(W["w_gate"] @ h2) * (W["w_up"] @ h2)',
+        'a = (W["w_gate"] @ h2) * silu(W["w_up"] @ h2)',
     ),
     "rmsnorm_eps_outside_sqrt": ("x / np.sqrt(ms + eps) * gain", "x / (np.sqrt(ms) + eps) * gain"),
     "rmsnorm_sum_not_mean": ("ms = np.mean(x * x, axis=-1, keepdims=True)", "ms = np.sum(x * x, axis=-1, keepdims=True)"),
     "k_cached_before_rope": (
-        "            k = apply_rope(k, cos, sin)\n            self.k_cache[session, l, :, position] = self._store(k)",
-        "            self.k_cache[session, l, :, position] = self._store(k)\n            k = apply_rope(k, cos, sin)",
+        "                k = apply_rope(k, cos, sin)\n                self.k_cache[session, l, :, position] = self._store(k)",
+        "                self.k_cache[session, l, :, position] = self._store(k)\n                k = apply_rope(k, cos, sin)",
     ),
-    "ffn_uses_attention_gain": ('h2 = rms_norm(x, self.mat(lw["ffn_norm"])', 'h2 = rms_norm(x, self.mat(lw["attn_norm"])'),
-    "final_norm_skipped": ('hf = rms_norm(x, self.mat(w["final_norm"]), m.norm_eps)\n        return', "hf = x\n        return"),
-    "lm_head_tied_to_embedding": ('return self.mat(w["lm_head"]) @ hf', 'return self.mat(w["embed"]) @ hf'),
+    "ffn_uses_attention_gain": ('h2 = rms_norm(x, W["ffn_norm"]', 'h2 = rms_norm(x, W["attn_norm"]'),
+    "final_norm_skipped": (
+        "return np.stack([lm @ rms_norm(x, g_final, m.norm_eps) for x in xs])",
+        "return np.stack([lm @ x for x in xs])",
+    ),
+    "lm_head_tied_to_embedding": ('lm = self.mat(w["lm_head"])', 'lm = self.mat(w["embed"])'),
     "wk_wv_swapped": (
-        'k = (self.mat(lw["wk"]) @ h).reshape(hkv, hd)\n            v = (self.mat(lw["wv"]) @ h)',
-        'k = (self.mat(lw["wv"]) @ h).reshape(hkv, hd)\n            v = (self.mat(lw["wk"]) @ h)',
+        'k = (W["wk"] @ h).reshape(hkv, hd)\n                v = (W["wv"] @ h)',
+        'k = (W["wv"] @ h).reshape(hkv, hd)\n                v = (W["wk"] @ h)',
     ),
-    "wo_transposed": ('x = x + self.mat(lw["wo"]) @ o', 'x = x + self.mat(lw["wo"]).T @ o'),
+    "wo_transposed": ('x = x + W["wo"] @ o', 'x = x + W["wo"].T @ o'),
     "argmax_ties_to_last": (
         "return np.argmax(l32, axis=-1).astype(np.int32)",
         "return (l32.shape[-1] - 1 - np.argmax(l32[..., ::-1], axis=-1)).astype(np.int32)",
