@@ -64,13 +64,14 @@ def measured_traffic(workload: str):
     return float(val.group(1))
 
 
-def cpu_baseline(wl, weights, dec, torch, n_steps: int, first_pos: int, first_token: int):
-    """Time the oracle on decode steps of session 0 of the same workload, from the GPU's KV cache."""
+def cpu_baseline(wl, weights, dec, torch, max_steps: int, min_seconds: float, first_pos: int, first_token: int):
+    """Time the oracle on decode steps of session 0 of the same workload, from the GPU's KV cache:
+    steps until ``min_seconds`` have passed, or ``max_steps`` of them."""
     from oracle import decoder as ref
     from threadpoolctl import threadpool_info
 
     m = wl.model
-    o = ref.Oracle(m, weights, batch=1, max_seq=first_pos + n_steps + 1)
+    o = ref.Oracle(m, weights, batch=1, max_seq=first_pos + max_steps + 1)
     for l in range(m.n_layers):
         kv = dec.kv_view()[l, :, 0, :, :first_pos].float().cpu().numpy()
         o.k_cache[0, l, :, :first_pos] = kv[0]
@@ -78,10 +79,14 @@ def cpu_baseline(wl, weights, dec, torch, n_steps: int, first_pos: int, first_to
     del kv
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     tok = first_token
+    n_steps = 0
     t0 = time.perf_counter()
-    for i in range(n_steps):
-        logits = o.step_one(0, tok, first_pos + i)
+    while n_steps < max_steps:
+        logits = o.step_one(0, tok, first_pos + n_steps)
         tok = int(ref.greedy_token(logits[None])[0])
+        n_steps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     dt = time.perf_counter() - t0
     return {
         "value": n_steps / dt,
@@ -130,9 +135,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="2b", choices=["tiny", "2b", "8b", "2b_long", "11b_x56"])
-    ap.add_argument("--cpu-steps", type=int, default=None,
-                    help="oracle decode steps (of one session) timed for cpu_baseline; 0 skips it "
-                         "(default: 3 at batch 1, 1 for the lockstep sessions)")
+    ap.add_argument("--cpu-steps", type=int, default=30,
+                    help="most oracle decode steps (of one session) timed for cpu_baseline; 0 skips it")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="cpu_baseline stops stepping the oracle once this much time has passed")
     ap.add_argument("--trace", action="store_true", help="after timing, trace one step and print its phase breakdown")
     ap.add_argument("--trace-out", default=None, help="with --trace: also save the raw timestamp buffer (.npy)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -154,8 +160,6 @@ def main() -> int:
     wl = workloads.get(args.workload)
     m = wl.model
     B = wl.batch
-    if args.cpu_steps is None:
-        args.cpu_steps = 3 if B == 1 else 1
     decode_steps = wl.decode_steps
     if args.warmup + args.steps > decode_steps:
         args.steps = decode_steps - args.warmup
@@ -250,7 +254,7 @@ def main() -> int:
     cpu = None
     if args.cpu_steps > 0:
         log("timing the CPU oracle ...")
-        cpu = cpu_baseline(wl, weights, dec, torch, args.cpu_steps, first_pos, first_token)
+        cpu = cpu_baseline(wl, weights, dec, torch, args.cpu_steps, args.cpu_seconds, first_pos, first_token)
         log(f"cpu oracle: {cpu['value']:.3f} tok/s on {cpu['cores']} threads")
 
     traffic = measured_traffic(wl.name)
