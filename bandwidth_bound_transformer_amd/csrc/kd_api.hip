@@ -374,7 +374,7 @@ void kd_destroy(kd_handle* h) {
 
 int kd_trace(kd_handle* h, uint64_t* dev_buf, int64_t words, int64_t* stride) {
   if (!h) return KD_ERR_INVALID_ARG;
-  if (h->batched) return KD_ERR_UNSUPPORTED;
+  if (h->batched || h->m.L > kd::kTraceMaxLayers) return KD_ERR_UNSUPPORTED;
   const int64_t st = kd::trace_stride(h->m.L);
   if (stride) *stride = st;
   if (!dev_buf) {

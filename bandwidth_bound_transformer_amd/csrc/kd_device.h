@@ -706,51 +706,83 @@ struct Xchg {
   }
 };
 
-// Gains of the elements thread tid normalises (i = tid + kThreads * j), loaded into registers
-// before the gather that precedes the norm, so their latency hides behind the wait.
-constexpr int kGainRegs = kMaxDim / kThreads;
+// Gains of the elements thread tid normalises: 16-byte chunks tid, tid + kThreads, ... of four
+// consecutive elements each. Loaded into registers before the gather that precedes the norm, so
+// their latency hides behind the wait.
+constexpr int kNormVec = kMaxDim / (4 * kThreads);
 template <int WB>
-__device__ __forceinline__ void load_gains(const uint8_t* gain, int d, float (&g)[kGainRegs]) {
+__device__ __forceinline__ void load_gains(const uint8_t* gain, int d, float4 (&g)[kNormVec]) {
   const int tid = (int)threadIdx.x;
   // no branches: loads issued back to back are waited for together, by the gather's first poll
 #pragma unroll
-  for (int j = 0; j < kGainRegs; ++j) g[j] = load_w<WB>(gain, min(tid + kThreads * j, d - 1));
+  for (int c = 0; c < kNormVec; ++c) {
+    const int i0 = min(4 * (tid + kThreads * c), d - 4);
+    if constexpr (WB == 2) {
+      const uint2 u = *(const uint2*)((const uint16_t*)gain + i0);
+      g[c] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+    } else {
+      g[c] = *(const float4*)((const float*)gain + i0);
+    }
+  }
 }
 
-// RMSNorm of act[0..d) in place, times the gain; all threads; fixed summation order.
+// RMSNorm of act[0..d) in place, times the gain; all threads; fixed summation order. Every LDS
+// read is issued before the first wait (branch-free), so the norm costs two LDS round trips and
+// two barriers.
 template <int RING>
-__device__ __forceinline__ void rmsnorm(Smem<RING>& sm, const float (&g)[kGainRegs], int d, float eps) {
+__device__ __forceinline__ void rmsnorm(Smem<RING>& sm, const float4 (&g)[kNormVec], int d, float eps) {
   const int tid = (int)threadIdx.x, lane = lane_id(), wave = wave_id();
+  float4 v[kNormVec];
+#pragma unroll
+  for (int c = 0; c < kNormVec; ++c) {
+    const int i0 = 4 * (tid + kThreads * c);
+    const float4 x = *(const float4*)(sm.act + min(i0, d - 4));
+    const bool in = i0 < d;
+    v[c] = make_float4(in ? x.x : 0.f, in ? x.y : 0.f, in ? x.z : 0.f, in ? x.w : 0.f);
+  }
   float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < kGainRegs; ++j) {
-    const int i = tid + kThreads * j;
-    if (i < d) ss = fmaf(sm.act[i], sm.act[i], ss);
+  for (int c = 0; c < kNormVec; ++c) {
+    ss = fmaf(v[c].x, v[c].x, ss);
+    ss = fmaf(v[c].y, v[c].y, ss);
+    ss = fmaf(v[c].z, v[c].z, ss);
+    ss = fmaf(v[c].w, v[c].w, ss);
   }
   ss = wave_sum(ss);
   if (lane == 0) sm.red[wave] = ss;
   wg_barrier();
   float tot = 0.f;
 #pragma unroll
-  for (int v = 0; v < kWaves; ++v) tot += sm.red[v];
+  for (int w = 0; w < kWaves; ++w) tot += sm.red[w];
   const float r = 1.0f / sqrtf(tot / (float)d + eps);
 #pragma unroll
-  for (int j = 0; j < kGainRegs; ++j) {
-    const int i = tid + kThreads * j;
-    if (i < d) sm.act[i] = sm.act[i] * r * g[j];
+  for (int c = 0; c < kNormVec; ++c) {
+    const int i0 = 4 * (tid + kThreads * c);
+    if (i0 < d)
+      *(float4*)(sm.act + i0) =
+          make_float4(v[c].x * r * g[c].x, v[c].y * r * g[c].y, v[c].z * r * g[c].z, v[c].w * r * g[c].w);
   }
   wg_barrier();
 }
 
 // Total of row r (C packets per row) of a tile over the waves that touched it, in wave order.
+// Branch-free: all the wave bounds, then all the candidate partial sums, are read before use.
 template <int RING>
 __device__ __forceinline__ float row_total(const Smem<RING>& sm, int tile, int C, int r) {
   const int a = r * C, b = a + C;
+  int lo[kWaves + 1], fi[kWaves];
+#pragma unroll
+  for (int v = 0; v <= kWaves; ++v) lo[v] = sm.split[tile][v];
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) fi[v] = sm.first[tile][v];
+  float p[kWaves];
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) p[v] = sm.rowpart[v][min(max(r - fi[v], 0), kRowPart - 1)];
   float s = 0.f;
 #pragma unroll
   for (int v = 0; v < kWaves; ++v) {
-    const int lo = sm.split[tile][v], hi = sm.split[tile][v + 1];
-    if (lo < hi && lo < b && hi > a) s += sm.rowpart[v][r - sm.first[tile][v]];
+    const bool touched = lo[v] < lo[v + 1] && lo[v] < b && lo[v + 1] > a;
+    s = touched ? s + p[v] : s;
   }
   return s;
 }
@@ -800,9 +832,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   const int gD = nf / m.vpl;
   const int mc = max_chunks(m);
 
+  // Phase timestamps go to LDS and are copied out at the end of the step: a global store here
+  // would hold up the next memory wait of wave 0 (stores share the in-order vector memory
+  // counter with the loads).
   uint64_t* const tr = P.trace ? P.trace + (int64_t)w * trace_stride(m.L) : nullptr;
+  __shared__ uint64_t trl[kTraceMaxSlots];
+  const int trn = (int)trace_stride(m.L);
+  if (tr)
+    for (int i = tid; i < trn; i += kThreads) trl[i] = 0;
   auto stamp = [&](int slot) {
-    if (tr && tid == 0) tr[slot] = now_ticks();
+    if (tr && tid == 0) trl[slot] = now_ticks();
   };
   stamp(0);
 
@@ -846,7 +885,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   Xchg<RING> xc{P, __builtin_amdgcn_make_buffer_rsrc(P.ll, (short)0, (int)(P.lo.total * 8), 0x00020000), sm};
   const float inv_sqrt_hd = 1.0f / sqrtf((float)m.hd);
   const SegEntry* tab = sm.segs[wave];
-  float gains[kGainRegs];
+  float4 gains[kNormVec];
   stamp(1);
 
   for (int layer = 0; layer < m.L; ++layer) {
@@ -948,19 +987,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       if (tid < G * m.hd) {
         const int h = tid / m.hd, i = tid - h * m.hd;
         const float sp = u.last ? sm.u.att.sp[h] : -INFINITY;
+        float mv[kWaves], lv[kWaves], av[kWaves];
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+          mv[v] = sm.u.att.ml[v][h][0];
+          lv[v] = sm.u.att.ml[v][h][1];
+          av[v] = sm.act[((int64_t)v * kMaxGroup + h) * HD + i];
+        }
         float M = sp;
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v)
-          if (sm.u.att.ml[v][h][1] > 0.f) M = fmaxf(M, sm.u.att.ml[v][h][0]);
+        for (int v = 0; v < kWaves; ++v) M = lv[v] > 0.f ? fmaxf(M, mv[v]) : M;
         float Lsum = 0.f, acc = 0.f;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
-          const float lv = sm.u.att.ml[v][h][1];
-          if (lv > 0.f) {
-            const float sc = __expf(sm.u.att.ml[v][h][0] - M);
-            Lsum = fmaf(sc, lv, Lsum);
-            acc = fmaf(sc, sm.act[((int64_t)v * kMaxGroup + h) * HD + i], acc);
-          }
+          // a wave with no positions here contributes nothing (its slots may hold stale values)
+          const float sc = __expf(mv[v] - M);
+          Lsum = lv[v] > 0.f ? fmaf(sc, lv[v], Lsum) : Lsum;
+          acc = lv[v] > 0.f ? fmaf(sc, av[v], acc) : acc;
         }
         if (u.last) {
           const float e = __expf(sp - M);
@@ -1017,9 +1060,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         Ls = wave_sum(Ls);
         const float invL = 1.0f / Ls;
         const uint32_t tag = ll_tag(m, P.seq, layer, kO);
+        // the chunk weights once (act is free between the attention units and the o gather)
+        float* wts = sm.act;
+        for (int c = lane; c < NC; c += 64) wts[c] = __expf(st[c * (2 + MS)] - M);
         for (int i = lane; i < MS; i += 64) {
           float a = 0.f;
-          for (int c = 0; c < NC; ++c) a = fmaf(__expf(st[c * (2 + MS)] - M), st[c * (2 + MS) + 2 + i], a);
+#pragma unroll 8
+          for (int c = 0; c < NC; ++c) a = fmaf(wts[c], st[c * (2 + MS) + 2 + i], a);
           ll_store(P.ll, P.lo.o + (int64_t)hq * m.hd + (int64_t)sl * MS + i, a * invL, tag);
         }
       }
@@ -1077,6 +1124,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       // one wave per row: lanes take producers lane, lane+64, ... in order, then a butterfly
       for (int r = wave; r < nrd; r += kWaves) {
         float s = 0.f;
+#pragma unroll 4
         for (int q = lane; q < m.nwg; q += 64) s += st[q * nrd + r];
         s = wave_sum(s);
         if (lane == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(m, P.seq, layer, kX));
@@ -1145,6 +1193,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   }
 drain:
   wait_vm<0>();
+  if (tr) {
+    wg_barrier();
+    for (int i = tid; i < trn; i += kThreads) tr[i] = trl[i];
+  }
 }
 
 }  // namespace kd

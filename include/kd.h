@@ -161,8 +161,10 @@ void kd_destroy(kd_handle* h);
 const char* kd_strerror(int code);
 
 /*
- * Step tracing, for measurement (batch 1 only; KD_ERR_UNSUPPORTED for batch > 1).  With dev_buf non-NULL, every later kd_step writes 64-bit
- * timestamps of the GPU's 100 MHz constant clock at its phase boundaries: workgroup w uses
+ * Step tracing, for measurement (batch 1 and at most 48 layers; KD_ERR_UNSUPPORTED otherwise).
+ * With dev_buf non-NULL, every later kd_step records 64-bit timestamps of the GPU's 100 MHz
+ * constant clock at its phase boundaries (held in LDS during the step, written out at its end,
+ * so recording them does not delay the step's memory waits): workgroup w uses
  * dev_buf[w * stride .. (w + 1) * stride).  Slot 0 is the step start, slot 1 the end of setup,
  * slots 2 + 24*l + e (e < 24) the phase boundaries of layer l, and the last 4 slots the final
  * norm, LM head and argmax.  dev_buf is device memory of at least stride * workgroups words,
