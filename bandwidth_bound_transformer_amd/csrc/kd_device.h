@@ -542,55 +542,74 @@ __device__ __forceinline__ void consume_down(Ring<RING>& rg, const SegEntry& s, 
   }
 }
 
+// Lanes 0-31 get the sum of x over lanes l and l ^ 32, lanes 32-63 the sum of y (gfx950's
+// permlane32 swap exchanges the upper half of its first operand with the lower half of its
+// second). halve16 does the same one level down: even 16-lane rows get x, odd rows get y.
+__device__ __forceinline__ float halve32(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float halve16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Scores, then the exp-weighted V sum, of one attention unit over this wave's share of the
 // unit's cached positions. lpp lanes hold one position; each lane holds kv_vpl of its dims.
 // Leaves (max, sum) in ml[v] and the weighted V sums in accv[h][hd].
+//
+// Branch-free: all kMaxGroup head slots are computed (slots h >= G get q = 0 and are never read
+// back), and positions past the unit's end are masked by selects, so the LDS reads of a packet
+// are issued together rather than one per branch.
 template <int RING, int KB, int HD>
 __device__ __forceinline__ void consume_attention(Ring<RING>& rg, const SegEntry& sk, const Unit& u, int G, Smem<RING>& sm,
                                                   int v, float* accv) {
   constexpr int KVPL = 16 / KB;
   constexpr int LPP = HD / KVPL;
   constexpr int PPP = 64 / LPP;
+  constexpr int H = kMaxGroup;
+  static_assert(H == 4, "scores are stored as one float4 per position");
   const int lane = lane_id();
   const int q_in = lane / LPP;  // position inside a packet
   const int dim0 = (lane % LPP) * KVPL;
-  float qv[kMaxGroup][KVPL];
+  float qv[H][KVPL];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
+  for (int h = 0; h < H; ++h)
 #pragma unroll
-    for (int e = 0; e < KVPL; ++e) qv[h][e] = h < G ? sm.u.att.q[h][dim0 + e] : 0.f;
-  float mh[kMaxGroup];
+    for (int e = 0; e < KVPL; ++e) {
+      const float t = sm.u.att.q[h][dim0 + e];
+      qv[h][e] = h < G ? t : 0.f;
+    }
+  float mh[H];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) mh[h] = -INFINITY;
+  for (int h = 0; h < H; ++h) mh[h] = -INFINITY;
   // pass 1: scores (q already carries 1/sqrt(hd))
   for (int i = sk.lo; i < sk.hi; ++i) {
     const uint4 kw = rg.take();
     float kf[KVPL];
     unpack16<KB>(kw, kf);
     rg.give();
-    const int pos = u.j0 + i * PPP + q_in;
-    const bool valid = pos < u.j1;
+    const bool valid = u.j0 + i * PPP + q_in < u.j1;
+    float sc[H];
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h < G) {
-        float s = 0.f;
+    for (int h = 0; h < H; ++h) {
+      float t = 0.f;
 #pragma unroll
-        for (int e = 0; e < KVPL; ++e) s = fmaf(qv[h][e], kf[e], s);
-        s = sum_lanes<LPP>(s);
-        if (valid) {
-          mh[h] = fmaxf(mh[h], s);
-          if (lane % LPP == 0) sm.u.att.scores[v][(i - sk.lo) * PPP + q_in][h] = s;
-        }
-      }
+      for (int e = 0; e < KVPL; ++e) t = fmaf(qv[h][e], kf[e], t);
+      sc[h] = sum_lanes<LPP>(t);
+      mh[h] = valid ? fmaxf(mh[h], sc[h]) : mh[h];
     }
+    if (lane % LPP == 0)
+      *(float4*)&sm.u.att.scores[v][(i - sk.lo) * PPP + q_in][0] = make_float4(sc[0], sc[1], sc[2], sc[3]);
   }
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) mh[h] = max_positions<LPP>(mh[h]);
-  // pass 2: V weighted by exp(score - wave max)
-  float acc[kMaxGroup][KVPL];
-  float lsum[kMaxGroup];
+  for (int h = 0; h < H; ++h) mh[h] = max_positions<LPP>(mh[h]);
+  // pass 2: V weighted by exp(score - wave max); masked positions add nothing (their cache
+  // slots may hold anything, so the sums are selected rather than multiplied by zero)
+  float acc[H][KVPL];
+  float lsum[H];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
+  for (int h = 0; h < H; ++h) {
     lsum[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < KVPL; ++e) acc[h][e] = 0.f;
@@ -600,38 +619,52 @@ __device__ __forceinline__ void consume_attention(Ring<RING>& rg, const SegEntry
     float vf[KVPL];
     unpack16<KB>(vw, vf);
     rg.give();
-    const int pos = u.j0 + i * PPP + q_in;
-    if (pos < u.j1) {
+    const bool valid = u.j0 + i * PPP + q_in < u.j1;
+    const float4 s4 = *(const float4*)&sm.u.att.scores[v][(i - sk.lo) * PPP + q_in][0];
+    const float s[H] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        if (h < G) {
-          const float e = __expf(sm.u.att.scores[v][(i - sk.lo) * PPP + q_in][h] - mh[h]);
-          lsum[h] += e;
+    for (int h = 0; h < H; ++h) {
+      const float e = __expf(s[h] - mh[h]);
+      lsum[h] = valid ? lsum[h] + e : lsum[h];
 #pragma unroll
-          for (int k = 0; k < KVPL; ++k) acc[h][k] = fmaf(e, vf[k], acc[h][k]);
-        }
-      }
+      for (int k = 0; k < KVPL; ++k) acc[h][k] = valid ? fmaf(e, vf[k], acc[h][k]) : acc[h][k];
     }
   }
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    if (h < G) {
-      lsum[h] = sum_positions<LPP>(lsum[h]);
+  for (int h = 0; h < H; ++h) lsum[h] = sum_positions<LPP>(lsum[h]);
+  // Sum acc over the PPP position groups by halving: each level pairs value j with value
+  // j + n/2 and keeps one of them per half, so lane l ends with the totals of a block of values
+  // (block l >> 4 of four when PPP >= 4, l >> 5 of two when PPP == 2).
+  constexpr int NV = H * KVPL;
+  float a[NV];
 #pragma unroll
-      for (int k = 0; k < KVPL; ++k) acc[h][k] = sum_positions<LPP>(acc[h][k]);
+  for (int h = 0; h < H; ++h)
+#pragma unroll
+    for (int k = 0; k < KVPL; ++k) a[h * KVPL + k] = acc[h][k];
+#pragma unroll
+  for (int j = 0; j < NV / 2; ++j) a[j] = halve32(a[j], a[j + NV / 2]);
+  if constexpr (PPP >= 4) {
+#pragma unroll
+    for (int j = 0; j < NV / 4; ++j) a[j] = halve16(a[j], a[j + NV / 4]);
+  }
+  if constexpr (PPP >= 8) {
+#pragma unroll
+    for (int j = 0; j < NV / 4; ++j) a[j] = xsum8(a[j]);
+  }
+  constexpr int NR = PPP == 2 ? NV / 2 : NV / 4;  // values each lane ends with
+  const int blk = PPP == 2 ? (lane >> 5) : (lane >> 4);
+  if (PPP < 8 || (lane & 8) == 0) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const int vi = blk * NR + j, h = vi / KVPL, k = vi - h * KVPL;
+      accv[h * HD + dim0 + k] = a[j];
     }
   }
+  if (lane == 0) {
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    if (h < G) {
-      if (lane < LPP) {
-#pragma unroll
-        for (int k = 0; k < KVPL; ++k) accv[h * HD + dim0 + k] = acc[h][k];
-      }
-      if (lane == 0) {
-        sm.u.att.ml[v][h][0] = mh[h];
-        sm.u.att.ml[v][h][1] = lsum[h];
-      }
+    for (int h = 0; h < H; ++h) {
+      sm.u.att.ml[v][h][0] = mh[h];
+      sm.u.att.ml[v][h][1] = lsum[h];
     }
   }
 }
