@@ -692,6 +692,11 @@ struct Xchg {
   // was abandoned (timeout here or elsewhere).
   template <class Off, class Sink>
   __device__ __forceinline__ bool gather(uint32_t tag, int npieces, Off off, Sink sink) {
+    return gather(tag, npieces, off, sink, [] {});
+  }
+  // As above; fin() runs on every thread after its last sink call, before the closing barrier.
+  template <class Off, class Sink, class Fin>
+  __device__ __forceinline__ bool gather(uint32_t tag, int npieces, Off off, Sink sink, Fin fin) {
     constexpr int NB = 4;
     const int tid = (int)threadIdx.x;
     for (int base = 0; base < npieces; base += kThreads * NB) {
@@ -725,6 +730,7 @@ struct Xchg {
         if (k < npieces) sink(k, __uint_as_float(val[i].x), __uint_as_float(val[i].z));
       }
     }
+    fin();
     wg_barrier();
     return sm.abort_flag == 0;
   }
@@ -739,63 +745,62 @@ struct Xchg {
   }
 };
 
-// Gains of the elements thread tid normalises: 16-byte chunks tid, tid + kThreads, ... of four
-// consecutive elements each. Loaded into registers before the gather that precedes the norm, so
-// their latency hides behind the wait.
-constexpr int kNormVec = kMaxDim / (4 * kThreads);
+// RMSNorm folded into the gather of the vector it normalises. The projection after a norm is
+// linear, so W (x r g) = r W (x g) with r = 1 / sqrt(mean(x^2) + eps): the gather stores x g and
+// sums x^2 as the pieces arrive, and the projection's outputs are scaled by r when they are
+// published. No separate pass over the vector and no extra barrier.
+//
+// A full-vector gather hands thread tid the pieces tid + kThreads i (elements 2 (tid + kThreads i)
+// and + 1), in order of i; the gains of those elements are loaded into registers first, so their
+// latency hides behind the wait.
+constexpr int kPieceRegs = kMaxDim / (2 * kThreads);
 template <int WB>
-__device__ __forceinline__ void load_gains(const uint8_t* gain, int d, float4 (&g)[kNormVec]) {
+__device__ __forceinline__ void load_piece_gains(const uint8_t* gain, int d, float2 (&g)[kPieceRegs]) {
   const int tid = (int)threadIdx.x;
   // no branches: loads issued back to back are waited for together, by the gather's first poll
 #pragma unroll
-  for (int c = 0; c < kNormVec; ++c) {
-    const int i0 = min(4 * (tid + kThreads * c), d - 4);
+  for (int i = 0; i < kPieceRegs; ++i) {
+    const int e = min(2 * (tid + kThreads * i), d - 2);
     if constexpr (WB == 2) {
-      const uint2 u = *(const uint2*)((const uint16_t*)gain + i0);
-      g[c] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+      const uint32_t u = ((const uint32_t*)gain)[e / 2];
+      g[i] = make_float2(bf16_lo(u), bf16_hi(u));
     } else {
-      g[c] = *(const float4*)((const float*)gain + i0);
+      g[i] = *(const float2*)((const float*)gain + e);
     }
   }
 }
 
-// RMSNorm of act[0..d) in place, times the gain; all threads; fixed summation order. Every LDS
-// read is issued before the first wait (branch-free), so the norm costs two LDS round trips and
-// two barriers.
+// Per-thread state of a folded norm: the gains of the thread's pieces and its sum of squares.
+struct NormFold {
+  float2 g[kPieceRegs];
+  float ss;
+  // piece k (= tid + kThreads i) holds x[2k], x[2k+1]: store them times their gains, add squares
+  __device__ __forceinline__ void put(float* act, int k, float a, float b) {
+    const int i = (k - (int)threadIdx.x) / kThreads;
+    // select rather than index, so the gains stay in registers
+    float2 gi = g[0];
+#pragma unroll
+    for (int j = 1; j < kPieceRegs; ++j) gi = i == j ? g[j] : gi;
+    act[2 * k] = a * gi.x;
+    act[2 * k + 1] = b * gi.y;
+    ss = fmaf(a, a, ss);
+    ss = fmaf(b, b, ss);
+  }
+  // this wave's sum of squares into red[wave] (before the barrier that ends the gather)
+  template <class S>
+  __device__ __forceinline__ void finish(S& sm) {
+    const float t = wave_sum(ss);
+    if (lane_id() == 0) sm.red[wave_id()] = t;
+  }
+};
+
+// The norm's scale r from the waves' sums of squares (after the barrier), summed in wave order.
 template <int RING>
-__device__ __forceinline__ void rmsnorm(Smem<RING>& sm, const float4 (&g)[kNormVec], int d, float eps) {
-  const int tid = (int)threadIdx.x, lane = lane_id(), wave = wave_id();
-  float4 v[kNormVec];
-#pragma unroll
-  for (int c = 0; c < kNormVec; ++c) {
-    const int i0 = 4 * (tid + kThreads * c);
-    const float4 x = *(const float4*)(sm.act + min(i0, d - 4));
-    const bool in = i0 < d;
-    v[c] = make_float4(in ? x.x : 0.f, in ? x.y : 0.f, in ? x.z : 0.f, in ? x.w : 0.f);
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int c = 0; c < kNormVec; ++c) {
-    ss = fmaf(v[c].x, v[c].x, ss);
-    ss = fmaf(v[c].y, v[c].y, ss);
-    ss = fmaf(v[c].z, v[c].z, ss);
-    ss = fmaf(v[c].w, v[c].w, ss);
-  }
-  ss = wave_sum(ss);
-  if (lane == 0) sm.red[wave] = ss;
-  wg_barrier();
+__device__ __forceinline__ float norm_scale(const Smem<RING>& sm, int d, float eps) {
   float tot = 0.f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) tot += sm.red[w];
-  const float r = 1.0f / sqrtf(tot / (float)d + eps);
-#pragma unroll
-  for (int c = 0; c < kNormVec; ++c) {
-    const int i0 = 4 * (tid + kThreads * c);
-    if (i0 < d)
-      *(float4*)(sm.act + i0) =
-          make_float4(v[c].x * r * g[c].x, v[c].y * r * g[c].y, v[c].z * r * g[c].z, v[c].w * r * g[c].w);
-  }
-  wg_barrier();
+  return 1.0f / sqrtf(tot / (float)d + eps);
 }
 
 // Total of row r (C packets per row) of a tile over the waves that touched it, in wave order.
@@ -918,24 +923,49 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   Xchg<RING> xc{P, __builtin_amdgcn_make_buffer_rsrc(P.ll, (short)0, (int)(P.lo.total * 8), 0x00020000), sm};
   const float inv_sqrt_hd = 1.0f / sqrtf((float)m.hd);
   const SegEntry* tab = sm.segs[wave];
-  float4 gains[kNormVec];
+  NormFold fold;
+  float r_attn = 1.f, r_ffn = 1.f, r_final = 1.f;  // scales of the folded norms
   stamp(1);
 
   for (int layer = 0; layer < m.L; ++layer) {
     const uint8_t* g_attn = P.norms + ((int64_t)layer * 2 + 0) * m.d * m.wbytes;
     const uint8_t* g_ffn = P.norms + ((int64_t)layer * 2 + 1) * m.d * m.wbytes;
-    // ---- x, RMSNorm ----
-    load_gains<WB>(g_attn, m.d, gains);
-    if (layer > 0 && !xc.gather_vec(ll_tag(m, P.seq, layer - 1, kX), P.lo.x, m.d, sm.act)) goto drain;
+    // ---- x (this WG's rows kept raw for the residual), RMSNorm folded into the gather ----
+    load_piece_gains<WB>(g_attn, m.d, fold.g);
+    fold.ss = 0.f;
+    {
+      auto put_x = [&](int k, float a, float b) {
+        fold.put(sm.act, k, a, b);
+        const int e = 2 * k - rd0;  // rd0 and nrd are even
+        if (e >= 0 && e < nrd) {
+          sm.xo[e] = a;
+          sm.xo[e + 1] = b;
+        }
+      };
+      if (layer > 0) {
+        if (!xc.gather(ll_tag(m, P.seq, layer - 1, kX), m.d / 2, [&](int k) -> int64_t { return P.lo.x + 2 * (int64_t)k; },
+                       put_x, [&] { fold.finish(sm); }))
+          goto drain;
+      } else {
+        // the embedding row is already in act: fold it in place
+#pragma unroll
+        for (int i = 0; i < kPieceRegs; ++i) {
+          const int k = tid + kThreads * i;
+          if (2 * k < m.d) put_x(k, sm.act[2 * k], sm.act[2 * k + 1]);
+        }
+        fold.finish(sm);
+        wg_barrier();
+      }
+    }
+    r_attn = norm_scale(sm, m.d, P.eps);
     stamp(trace_slot(layer, 0));
-    if (tid < nrd) sm.xo[tid] = sm.act[rd0 + tid];
-    rmsnorm<RING>(sm, gains, m.d, P.eps);
     stamp(trace_slot(layer, 1));
     // ---- QKV rows ----
     consume_rows<RING, WB>(rg, tab[0], m.cd, sm.act, sm.rowpart[wave]);
     wg_barrier();
     stamp(trace_slot(layer, 2));
-    if (tid < nq) ll_store(P.ll, P.lo.qkv + rq0 + tid, row_total(sm, kTileQKV, m.cd, tid), ll_tag(m, P.seq, layer, kQKV));
+    if (tid < nq)
+      ll_store(P.ll, P.lo.qkv + rq0 + tid, row_total(sm, kTileQKV, m.cd, tid) * r_attn, ll_tag(m, P.seq, layer, kQKV));
     stamp(trace_slot(layer, 3));
     // ---- attention units: one chunk of positions of one kv head each ----
     for (int k = 0; k < si.nunits; ++k) {
@@ -1088,19 +1118,35 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         float M = -INFINITY;
         for (int c = lane; c < NC; c += 64) M = fmaxf(M, st[c * (2 + MS)]);
         M = wave_max(M);
+        // each chunk's weight once (act is free between the attention units and the o gather)
+        float* wts = sm.act;
         float Ls = 0.f;
-        for (int c = lane; c < NC; c += 64) Ls = fmaf(__expf(st[c * (2 + MS)] - M), st[c * (2 + MS) + 1], Ls);
+        for (int c = lane; c < NC; c += 64) {
+          const float e = __expf(st[c * (2 + MS)] - M);
+          wts[c] = e;
+          Ls = fmaf(e, st[c * (2 + MS) + 1], Ls);
+        }
         Ls = wave_sum(Ls);
         const float invL = 1.0f / Ls;
         const uint32_t tag = ll_tag(m, P.seq, layer, kO);
-        // the chunk weights once (act is free between the attention units and the o gather)
-        float* wts = sm.act;
-        for (int c = lane; c < NC; c += 64) wts[c] = __expf(st[c * (2 + MS)] - M);
-        for (int i = lane; i < MS; i += 64) {
+        if (MS >= 8 && MS <= 64) {
+          // lane = (chunk group cg, element i): cg sums chunks cg, cg + CG, ...; then a fixed
+          // butterfly over the chunk groups (lanes i + MS, i + 2 MS, ...)
+          const int CG = 64 / MS, i = lane % MS, cg = lane / MS;
           float a = 0.f;
+#pragma unroll 4
+          for (int c = cg; c < NC; c += CG) a = fmaf(wts[c], st[c * (2 + MS) + 2 + i], a);
+          if (MS <= 8) a = xsum8(a);
+          if (MS <= 16) a = xsum16(a);
+          if (MS <= 32) a = xsum32(a);
+          if (cg == 0) ll_store(P.ll, P.lo.o + (int64_t)hq * m.hd + (int64_t)sl * MS + i, a * invL, tag);
+        } else {
+          for (int i = lane; i < MS; i += 64) {
+            float a = 0.f;
 #pragma unroll 8
-          for (int c = 0; c < NC; ++c) a = fmaf(wts[c], st[c * (2 + MS) + 2 + i], a);
-          ll_store(P.ll, P.lo.o + (int64_t)hq * m.hd + (int64_t)sl * MS + i, a * invL, tag);
+            for (int c = 0; c < NC; ++c) a = fmaf(wts[c], st[c * (2 + MS) + 2 + i], a);
+            ll_store(P.ll, P.lo.o + (int64_t)hq * m.hd + (int64_t)sl * MS + i, a * invL, tag);
+          }
         }
       }
       wg_barrier();
@@ -1119,17 +1165,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     }
     stamp(trace_slot(layer, 15));
     // ---- gate/up rows of this workgroup's FFN slice ----
-    load_gains<WB>(g_ffn, m.d, gains);
-    if (!xc.gather_vec(ll_tag(m, P.seq, layer, kXP), P.lo.xp, m.d, sm.act)) goto drain;
+    load_piece_gains<WB>(g_ffn, m.d, fold.g);
+    fold.ss = 0.f;
+    if (!xc.gather(ll_tag(m, P.seq, layer, kXP), m.d / 2, [&](int k) -> int64_t { return P.lo.xp + 2 * (int64_t)k; },
+                   [&](int k, float a, float b) { fold.put(sm.act, k, a, b); }, [&] { fold.finish(sm); }))
+      goto drain;
+    r_ffn = norm_scale(sm, m.d, P.eps);
     stamp(trace_slot(layer, 16));
-    rmsnorm<RING>(sm, gains, m.d, P.eps);
     stamp(trace_slot(layer, 17));
     consume_rows<RING, WB>(rg, tab[oseg + 1], m.cd, sm.act, sm.rowpart[wave]);
     wg_barrier();
     stamp(trace_slot(layer, 18));
     if (tid < nf) {
-      const float gt = row_total(sm, kTileGU, m.cd, tid);
-      const float up = row_total(sm, kTileGU, m.cd, nf + tid);
+      const float gt = row_total(sm, kTileGU, m.cd, tid) * r_ffn;
+      const float up = row_total(sm, kTileGU, m.cd, nf + tid) * r_ffn;
       sm.a[tid] = gt / (1.0f + __expf(-gt)) * up;
     }
     wg_barrier();
@@ -1162,15 +1211,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         s = wave_sum(s);
         if (lane == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(m, P.seq, layer, kX));
       }
-      wg_barrier();  // the staging area is reused by the next layer's attention
+      // no barrier: the staging area is next written after the next layer's x gather, which
+      // ends with a workgroup barrier
     }
     stamp(trace_slot(layer, 22));
   }
 
   // ---- final norm, LM head rows, argmax ----
-  load_gains<WB>(P.norms + (int64_t)m.L * 2 * m.d * m.wbytes, m.d, gains);
-  if (!xc.gather_vec(ll_tag(m, P.seq, m.L - 1, kX), P.lo.x, m.d, sm.act)) goto drain;
-  rmsnorm<RING>(sm, gains, m.d, P.eps);
+  load_piece_gains<WB>(P.norms + (int64_t)m.L * 2 * m.d * m.wbytes, m.d, fold.g);
+  fold.ss = 0.f;
+  if (!xc.gather(ll_tag(m, P.seq, m.L - 1, kX), m.d / 2, [&](int k) -> int64_t { return P.lo.x + 2 * (int64_t)k; },
+                 [&](int k, float a, float b) { fold.put(sm.act, k, a, b); }, [&] { fold.finish(sm); }))
+    goto drain;
+  r_final = norm_scale(sm, m.d, P.eps);
   stamp(trace_slot(m.L, 0));
   consume_rows<RING, WB>(rg, sm.lm_seg[wave], m.cd, sm.act, sm.rowpart[wave]);
   wg_barrier();
@@ -1180,7 +1233,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     int32_t besti = 0x7fffffff;
     bool nan = false;
     for (int r = tid; r < nl; r += kThreads) {
-      const float val = row_total(sm, kTileLM, m.cd, r);
+      const float val = row_total(sm, kTileLM, m.cd, r) * r_final;
       if (P.logits) P.logits[rl0 + r] = val;
       if (val != val) { nan = true; continue; }
       if (better(val, rl0 + r, best, besti)) { best = val; besti = rl0 + r; }
