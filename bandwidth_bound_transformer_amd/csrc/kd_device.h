@@ -1179,7 +1179,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     if (tid < nf) {
       const float gt = row_total(sm, kTileGU, m.cd, tid) * r_ffn;
       const float up = row_total(sm, kTileGU, m.cd, nf + tid) * r_ffn;
-      sm.a[tid] = gt / (1.0f + __expf(-gt)) * up;
+      sm.a[tid] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;  // hardware reciprocal (1 ulp)
     }
     wg_barrier();
     stamp(trace_slot(layer, 19));
@@ -1203,13 +1203,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
                           });
       if (!ok) goto drain;
       stamp(trace_slot(layer, 21));
-      // one wave per row: lanes take producers lane, lane+64, ... in order, then a butterfly
-      for (int r = wave; r < nrd; r += kWaves) {
+      // T = kThreads / nrd threads per row when nrd is a power of two from 8 to 64: thread j of a
+      // row adds producers j, j + T, ... in order, then a fixed butterfly over the T lanes;
+      // otherwise one wave per row
+      if (nrd >= 8 && nrd <= 64 && (nrd & (nrd - 1)) == 0) {
+        const int T = kThreads / nrd, r = tid / T, j = tid - r * T;
         float s = 0.f;
-#pragma unroll 4
-        for (int q = lane; q < m.nwg; q += 64) s += st[q * nrd + r];
-        s = wave_sum(s);
-        if (lane == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(m, P.seq, layer, kX));
+#pragma unroll 8
+        for (int q = j; q < m.nwg; q += T) s += st[q * nrd + r];
+        if (T >= 64) s = wave_sum(s);
+        else if (T == 32) s = xsum16(sum_rows16(s));
+        else if (T == 16) s = sum_rows16(s);
+        else s = sum_rows8(s);
+        if (j == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(m, P.seq, layer, kX));
+      } else {
+        for (int r = wave; r < nrd; r += kWaves) {
+          float s = 0.f;
+          for (int q = lane; q < m.nwg; q += 64) s += st[q * nrd + r];
+          s = wave_sum(s);
+          if (lane == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(m, P.seq, layer, kX));
+        }
       }
       // no barrier: the staging area is next written after the next layer's x gather, which
       // ends with a workgroup barrier
