@@ -1188,7 +1188,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     stamp(trace_slot(layer, 20));
     // ---- sum every slice's contribution to this workgroup's rows; residual add ----
     {
-      float* st = sm.u.stage;  // [nwg][nrd]
+      float* st = sm.u.stage;  // [nrd][nwg]: each row's partials contiguous (conflict-free reads)
       const int hp = nrd / 2;  // pieces per producer
       const bool ok = nrd == 0 ||
                       xc.gather(
@@ -1198,8 +1198,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
                             return P.lo.dp + (int64_t)q * m.d + rd0 + 2 * j;
                           },
                           [&](int k2, float a, float b) {
-                            st[2 * k2] = a;
-                            st[2 * k2 + 1] = b;
+                            const int q = k2 / hp, j = k2 - q * hp;
+                            st[(2 * j) * m.nwg + q] = a;
+                            st[(2 * j + 1) * m.nwg + q] = b;
                           });
       if (!ok) goto drain;
       stamp(trace_slot(layer, 21));
@@ -1210,7 +1211,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         const int T = kThreads / nrd, r = tid / T, j = tid - r * T;
         float s = 0.f;
 #pragma unroll 8
-        for (int q = j; q < m.nwg; q += T) s += st[q * nrd + r];
+        for (int q = j; q < m.nwg; q += T) s += st[r * m.nwg + q];
         if (T >= 64) s = wave_sum(s);
         else if (T == 32) s = xsum16(sum_rows16(s));
         else if (T == 16) s = sum_rows16(s);
@@ -1219,7 +1220,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       } else {
         for (int r = wave; r < nrd; r += kWaves) {
           float s = 0.f;
-          for (int q = lane; q < m.nwg; q += 64) s += st[q * nrd + r];
+          for (int q = lane; q < m.nwg; q += 64) s += st[r * m.nwg + q];
           s = wave_sum(s);
           if (lane == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(m, P.seq, layer, kX));
         }
