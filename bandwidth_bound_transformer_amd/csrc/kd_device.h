@@ -497,7 +497,9 @@ __device__ __forceinline__ void unpack16(const uint4 w, float* out) {
 // values; act is the input vector. A row's lane sums are reduced across the wave when the row (or
 // this wave's share of it) ends; part[r - first row] receives the wave's sum.
 template <int RING, int WB>
-__device__ __forceinline__ void consume_rows(Ring<RING>& rg, const SegEntry& s, int C, const float* act, float* part) {
+// (The segment is taken by value: a copy in registers is not reloaded from LDS after every
+// LDS-DMA refill, whose asm clobbers memory.)
+__device__ __forceinline__ void consume_rows(Ring<RING>& rg, const SegEntry s, int C, const float* act, float* part) {
   constexpr int VPL = 16 / WB;
   const int lane = lane_id();
   int r = s.lo / C;
@@ -522,7 +524,7 @@ __device__ __forceinline__ void consume_rows(Ring<RING>& rg, const SegEntry& s, 
 // x vpl columns; lane l owns row 64*b + l, and all lanes read the same slice values. Each finished
 // block is published at once as 64 contiguous exchange words.
 template <int RING, int WB>
-__device__ __forceinline__ void consume_down(Ring<RING>& rg, const SegEntry& s, int g, const float* a, uint64_t* ll,
+__device__ __forceinline__ void consume_down(Ring<RING>& rg, const SegEntry s, int g, const float* a, uint64_t* ll,
                                              int64_t dp_at, uint32_t tag) {
   constexpr int VPL = 16 / WB;
   const int lane = lane_id();
@@ -562,7 +564,7 @@ __device__ __forceinline__ float halve16(float x, float y) {
 // back), and positions past the unit's end are masked by selects, so the LDS reads of a packet
 // are issued together rather than one per branch.
 template <int RING, int KB, int HD>
-__device__ __forceinline__ void consume_attention(Ring<RING>& rg, const SegEntry& sk, const Unit& u, int G, Smem<RING>& sm,
+__device__ __forceinline__ void consume_attention(Ring<RING>& rg, const SegEntry sk, const Unit& u, int G, Smem<RING>& sm,
                                                   int v, float* accv) {
   constexpr int KVPL = 16 / KB;
   constexpr int LPP = HD / KVPL;
