@@ -169,6 +169,55 @@ def test_8b_short_prompt(torch, kdm):
     dec.close()
 
 
+def test_8b_full_prompt_sampled_steps(torch, kdm):
+    """Llama-3-8B shape at the benchmark's positions: the 1024-token prompt runs on the GPU, then
+    the steps at positions 1023 and 1024 are checked against the oracle, which starts from the
+    GPU's cache of positions 0..1022 (sampled outputs at full size; the prompt path itself is
+    checked from position 0 by the 2B and short 8B tests). The K/V appended at 1023 and 1024 must
+    match what the oracle stored."""
+    wl = workloads.get("8b")
+    m = wl.model
+    w = workloads.make_weights(m, seed=wl.weight_seed)
+    print("8b full: weights ready", flush=True)
+    dec = _decoder(kdm, wl, w)
+    prompt = workloads.make_prompt(wl, 0)
+    P = len(prompt)
+    prompt_d = torch.as_tensor(np.asarray(prompt, np.int32), device=dec.device)
+    dec.positions.zero_()
+    for p in range(P - 1):
+        dec.tokens.copy_(prompt_d[p : p + 1])
+        dec.step()
+    torch.cuda.synchronize()
+    assert dec.status() == 0 and int(dec.positions.item()) == P - 1
+    print(f"8b full: GPU prompt 0..{P - 2} done", flush=True)
+    o = ref.Oracle(m, w, batch=1, max_seq=P + 2)
+    kv = dec.kv_view()
+    for l in range(m.n_layers):
+        c = kv[l, :, 0, :, : P - 1].float().cpu().numpy()  # [K/V][kv head][position][dim]
+        for g in range(m.n_kv_heads):
+            o.load_kv(0, l, g, c[0, g], c[1, g])
+    tok = int(prompt[P - 1])
+    dec.tokens.fill_(tok)
+    for i in range(2):
+        dec.step()
+        gl = dec.logits[0].cpu().numpy()
+        want = o.step_one(0, tok, P - 1 + i)
+        err = gh.inf_rel_err(gl, want)
+        print(f"8b full: position {P - 1 + i}: rel logit err {err:.3e}", flush=True)
+        assert err <= BF16_TOL
+        g_tok = int(dec.tokens.item())
+        if g_tok != int(ref.greedy_token(want[None])[0]):
+            assert gh.top2_margin(want) <= 2 * np.max(np.abs(gl - want))
+        tok = g_tok
+    assert dec.status() == 0
+    for l in (0, m.n_layers - 1):
+        got = kv[l, :, 0, :, P - 1 : P + 1].float().cpu().numpy()
+        for s, ref_cache in ((0, o.k_cache), (1, o.v_cache)):
+            exp = ref_cache[0, l, :, P - 1 : P + 1]
+            assert np.max(np.abs(got[s] - exp)) <= 2e-2 * np.max(np.abs(exp))
+    dec.close()
+
+
 def test_2b_long_context_prefilled(torch, kdm):
     """2B decoder with the KV cache pre-filled to 32768 positions: two steps from the seeded first token."""
     wl = workloads.get("2b_long")
