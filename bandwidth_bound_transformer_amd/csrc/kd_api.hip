@@ -22,7 +22,7 @@
 
 namespace {
 
-constexpr int kRing = 12;
+constexpr int kRing = 13;
 
 struct Buffers {
   uint8_t* blob = nullptr;

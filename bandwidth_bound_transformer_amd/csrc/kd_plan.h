@@ -143,7 +143,7 @@ KD_HD LLLayout ll_layout(const Dims& m) {
 // boundaries per layer, then 4 for the final norm, LM head and argmax.
 constexpr int kTraceLayerEvents = 24;
 KD_HD int64_t trace_stride(int L) { return 2 + (int64_t)kTraceLayerEvents * L + 4; }
-constexpr int kTraceMaxLayers = 48;  // step tracing covers models of up to this many layers
+constexpr int kTraceMaxLayers = 40;  // step tracing covers models of up to this many layers
 constexpr int kTraceMaxSlots = 2 + kTraceLayerEvents * kTraceMaxLayers + 4;
 
 // Tag of vector `kind` of layer `layer` (layer == L for the LM head) in step `seq`.

@@ -161,7 +161,7 @@ void kd_destroy(kd_handle* h);
 const char* kd_strerror(int code);
 
 /*
- * Step tracing, for measurement (batch 1 and at most 48 layers; KD_ERR_UNSUPPORTED otherwise).
+ * Step tracing, for measurement (batch 1 and at most 40 layers; KD_ERR_UNSUPPORTED otherwise).
  * With dev_buf non-NULL, every later kd_step records 64-bit timestamps of the GPU's 100 MHz
  * constant clock at its phase boundaries (held in LDS during the step, written out at its end,
  * so recording them does not delay the step's memory waits): workgroup w uses
