@@ -108,7 +108,7 @@ int check_supported(const kd_config* c, const kd::Dims& m) {
     for (int64_t w = 0; w < m.nwg; ++w) {
       const int64_t T = rows_of(w) * C;
       for (int v = 0; v < kd::kWaves; ++v) {
-        const int64_t lo = kd::part_lo(T, kd::kWaves, v), hi = kd::part_lo(T, kd::kWaves, v + 1);
+        const int64_t lo = kd::wave_lo(T, v), hi = kd::wave_lo(T, v + 1);
         if (hi > lo) worst = std::max(worst, (hi - 1) / C - lo / C + 1);
       }
     }

@@ -351,11 +351,11 @@ __device__ __forceinline__ void wave_range(const Dims& m, int w, int tile, int v
   tile_shape(m, w, tile, T, C);
   if (tile == kTileD) {
     const int nb = m.d / 64;
-    lo = p_lo(nb, kWaves, v) * C;
-    hi = p_lo(nb, kWaves, v + 1) * C;
+    lo = (int)wave_lo(nb, v) * C;
+    hi = (int)wave_lo(nb, v + 1) * C;
   } else {
-    lo = p_lo(T, kWaves, v);
-    hi = p_lo(T, kWaves, v + 1);
+    lo = (int)wave_lo(T, v);
+    hi = (int)wave_lo(T, v + 1);
   }
 }
 
