@@ -141,3 +141,77 @@ def test_batch1_last_cache_slot(torch, kdm):
     assert dec.status(clear=True) == kdm.KD_STATUS_POS_OVERFLOW
     assert bool(torch.equal(before, dec.kv))
     dec.close()
+
+
+def _tiny_run(kdm, wl, w, n_steps, torch, stream=None, trace=False, other=None):
+    """Steps of the tiny decoder from position 0 on `stream`; with `other` (a second decoder), the
+    two handles step alternately. Returns the logits of every step (and the trace buffer)."""
+    m = wl.model
+    dec = kdm.Decoder(m, w, max_seq=wl.max_seq)
+    buf = None
+    if trace:
+        info = kdm.kd_get_info(dec.handle)
+        stride = kdm.kd_trace(dec.handle, None, 0)
+        buf = torch.zeros(stride * info["workgroups"], dtype=torch.int64, device=dec.device)
+        kdm.kd_trace(dec.handle, buf, buf.numel())
+    prompt = workloads.make_prompt(wl, 0)
+    out = []
+    # every fill, step and copy goes on one stream (the current one inside the block)
+    with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+        for p in range(n_steps):
+            dec.tokens.fill_(int(prompt[p]))
+            dec.positions.fill_(p)
+            dec.step()
+            if other is not None:
+                other.tokens.fill_(int(prompt[-1 - p]))
+                other.positions.fill_(p)
+                other.step()
+            out.append(dec.logits.clone())
+    torch.cuda.synchronize()
+    assert dec.status() == 0
+    logits = torch.stack(out).cpu().numpy()
+    raw = buf.cpu().numpy() if buf is not None else None
+    if trace:
+        kdm.kd_trace(dec.handle, None, 0)
+    dec.close()
+    return logits, raw
+
+
+def test_trace_stream_and_second_handle_leave_results_bitwise_equal(torch, kdm):
+    """Tracing a step, launching on a non-default stream, and stepping a second handle in between
+    change no bit of the logits; the trace holds one increasing run of timestamps per workgroup."""
+    from bandwidth_bound_transformer_amd import trace as tr
+
+    wl = workloads.get("tiny")
+    m = wl.model
+    w = workloads.make_weights(m, seed=wl.weight_seed)
+    w2 = workloads.make_weights(m, seed=wl.weight_seed + 100)
+    n = 6
+    base, _ = _tiny_run(kdm, wl, w, n, torch)
+    traced, raw = _tiny_run(kdm, wl, w, n, torch, trace=True)
+    assert np.array_equal(base.view(np.uint32), traced.view(np.uint32))
+    side = torch.cuda.Stream()  # default priority
+    on_side, _ = _tiny_run(kdm, wl, w, n, torch, stream=side)
+    assert np.array_equal(base.view(np.uint32), on_side.view(np.uint32))
+    other = kdm.Decoder(m, w2, max_seq=wl.max_seq)
+    mixed, _ = _tiny_run(kdm, wl, w, n, torch, other=other)
+    assert other.status() == 0
+    other.close()
+    assert np.array_equal(base.view(np.uint32), mixed.view(np.uint32))
+    # the traced buffer holds the last step: every workgroup stamped its start, setup and final
+    # phases, and the stamps it reached never go backwards
+    nwg = 256
+    st = tr.stride(m.n_layers)
+    t = raw[: nwg * st].reshape(nwg, st)
+    assert np.all(t[:, 0] > 0) and np.all(t[:, 1] >= t[:, 0])
+    for row in t:
+        reached = row[row > 0]
+        assert np.all(np.diff(reached) >= 0)
+    parts, total = tr.intervals(raw, m.n_layers, nwg)
+    assert np.all(total > 0) and np.all(total < 1e5)  # microseconds
+    # the oracle agrees with the untraced run
+    o = ref.Oracle(m, w, batch=1, max_seq=wl.max_seq)
+    prompt = workloads.make_prompt(wl, 0)
+    for p in range(n):
+        want = o.step_one(0, int(prompt[p]), p)
+        assert gh.inf_rel_err(base[p, 0], want) <= F32_TOL, p
