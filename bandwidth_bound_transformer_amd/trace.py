@@ -112,3 +112,35 @@ def critical_path(buf: np.ndarray, n_layers: int, n_wg: int) -> str:
         prev = np.where(np.isnan(last[:, e]), prev, last[:, e])
     lines.append(f"  {'layer total':34s} {acc:8.2f} us")
     return "\n".join(lines)
+
+
+def to_chrome_trace(buf: np.ndarray, n_layers: int, n_wg: int) -> dict:
+    """The step as Chrome trace-event JSON (loadable in Perfetto or chrome://tracing).
+
+    One track per workgroup (tid = workgroup index); every reached boundary closes a complete
+    event ("ph": "X") named after it, which spans the time since the workgroup's previous reached
+    boundary. Timestamps are microseconds from the earliest step start.
+    """
+    st = stride(n_layers)
+    t = np.asarray(buf, np.int64)[: n_wg * st].reshape(n_wg, st)
+    names = ["setup"]
+    for l in range(n_layers):
+        names += [f"L{l} {e}" for e in LAYER_EVENTS]
+    names += list(FINAL_EVENTS)
+    started = t[:, 0] > 0
+    t0 = int(t[started, 0].min()) if started.any() else 0
+    events = []
+    for w in range(n_wg):
+        if t[w, 0] <= 0:
+            continue
+        prev = int(t[w, 0])
+        for j in range(1, st):
+            cur = int(t[w, j])
+            if cur <= 0:
+                continue
+            events.append({"name": names[j - 1], "ph": "X", "pid": 0, "tid": w,
+                           "ts": (prev - t0) * TICK_US, "dur": (cur - prev) * TICK_US})
+            prev = cur
+    meta = [{"name": "thread_name", "ph": "M", "pid": 0, "tid": w, "args": {"name": f"workgroup {w}"}}
+            for w in range(n_wg) if t[w, 0] > 0]
+    return {"traceEvents": meta + events, "displayTimeUnit": "ns"}

@@ -141,6 +141,8 @@ def main() -> int:
                     help="cpu_baseline stops stepping the oracle once this much time has passed")
     ap.add_argument("--trace", action="store_true", help="after timing, trace one step and print its phase breakdown")
     ap.add_argument("--trace-out", default=None, help="with --trace: also save the raw timestamp buffer (.npy)")
+    ap.add_argument("--trace-json", default=None,
+                    help="with --trace: also write the traced step as Chrome trace-event JSON (Perfetto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before decoding, copy MIB MiB once with a plain device copy; HBM-traffic counters read on "
                          "that copy calibrate the counters read on the decode kernel (profiling runs only)")
@@ -250,6 +252,9 @@ def main() -> int:
         log(tr.critical_path(raw, m.n_layers, info["workgroups"]))
         if args.trace_out:
             np.save(args.trace_out, raw)
+        if args.trace_json:
+            with open(args.trace_json, "w") as f:
+                json.dump(tr.to_chrome_trace(raw, m.n_layers, info["workgroups"]), f)
 
     cpu = None
     if args.cpu_steps > 0:

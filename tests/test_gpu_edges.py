@@ -215,3 +215,77 @@ def test_trace_stream_and_second_handle_leave_results_bitwise_equal(torch, kdm):
     for p in range(n):
         want = o.step_one(0, int(prompt[p]), p)
         assert gh.inf_rel_err(base[p, 0], want) <= F32_TOL, p
+
+
+def _snapshot(dec):
+    """Session state is the caller's buffers: cache, positions and tokens (device copies)."""
+    return dec.kv.clone(), dec.positions.clone(), dec.tokens.clone()
+
+
+def _restore(dec, snap):
+    kv, pos, tok = snap
+    dec.kv.copy_(kv)
+    dec.positions.copy_(pos)
+    dec.tokens.copy_(tok)
+
+
+@pytest.mark.parametrize("kind", ["batch1", "lockstep"])
+def test_checkpoint_resume_is_bitwise_exact(torch, kdm, kind):
+    """Decoding N + M steps on one handle equals decoding N, snapshotting the caller-owned state,
+    destroying the handle, restoring into a new one and decoding M: the same bits of logits,
+    tokens, positions and cache."""
+    if kind == "batch1":
+        wl = workloads.get("tiny").with_(prompt_len=12, gen_tokens=12)
+        B = 1
+    else:
+        shape = ModelShape(2, 512, 4, 2, 128, 512, 1024, rope_base=500000.0)
+        wl = Workload("resume_x17", shape, batch=17, prefill_len=40, gen_tokens=12, weight_seed=31, kv_seed=32,
+                      first_token_seed=33)
+        B = 17
+    m = wl.model
+    w = workloads.make_weights(m, seed=wl.weight_seed)
+    N, M = 7, 5
+
+    def start(dec):
+        if wl.prefill_len > 0:
+            kv = dec.kv_view().view(torch.int16)
+            for l in range(m.n_layers):
+                for s in range(2):
+                    for b in range(B):
+                        for g in range(m.n_kv_heads):
+                            blk = workloads.kv_prefill_block(wl, l, s, b, g)
+                            kv[l, s, b, g, : wl.prefill_len] = torch.from_numpy(blk.view(np.int16))
+            dec.tokens.copy_(torch.from_numpy(workloads.make_first_tokens(wl)))
+            dec.positions.fill_(wl.prefill_len)
+        else:
+            # the prompt's first token at position 0; every later step feeds back the greedy token
+            dec.tokens.fill_(int(workloads.make_prompt(wl, 0)[0]))
+            dec.positions.zero_()
+
+    def run(dec, n):
+        out = []
+        for _ in range(n):
+            dec.step()
+            out.append(torch.cat([dec.logits.flatten(), dec.tokens.float(), dec.positions.float()]))
+        torch.cuda.synchronize()
+        return torch.stack(out).cpu().numpy()
+
+    a = kdm.Decoder(m, w, max_seq=wl.max_seq, batch=B)
+    start(a)
+    whole = run(a, N + M)
+    kv_whole = a.kv.clone()
+    assert a.status() == 0
+    a.close()
+
+    b = kdm.Decoder(m, w, max_seq=wl.max_seq, batch=B)
+    start(b)
+    first = run(b, N)
+    snap = _snapshot(b)
+    b.close()
+    c = kdm.Decoder(m, w, max_seq=wl.max_seq, batch=B)
+    _restore(c, snap)
+    second = run(c, M)
+    assert c.status() == 0
+    assert np.array_equal(np.concatenate([first, second]).view(np.uint32), whole.view(np.uint32))
+    assert bool(torch.equal(c.kv, kv_whole))
+    c.close()

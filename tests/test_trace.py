@@ -56,3 +56,27 @@ def test_critical_path_follows_the_last_workgroup():
     for e in (0, 3, 10):
         line = next(x for x in text.splitlines() if x.strip().startswith(trace.LAYER_EVENTS[e]))
         assert f"+{0.5 * (e + 1):7.2f} us" in line
+
+
+def test_chrome_trace_export():
+    """Every reached boundary becomes one complete event on its workgroup's track; events of a
+    track tile its timeline without gaps or overlaps, and the whole is valid JSON."""
+    import json
+
+    L, nwg = 2, 3
+    buf = _synthetic(L, nwg)
+    doc = trace.to_chrome_trace(buf, L, nwg)
+    json.loads(json.dumps(doc))
+    ev = [e for e in doc["traceEvents"] if e["ph"] == "X"]
+    st = trace.stride(L)
+    reached = (buf.reshape(nwg, st)[:, 1:] > 0).sum()
+    assert len(ev) == reached
+    for w in range(nwg):
+        mine = sorted((e for e in ev if e["tid"] == w), key=lambda e: e["ts"])
+        assert mine[0]["name"] == "setup" and np.isclose(mine[0]["dur"], 1.0)
+        assert np.isclose(mine[0]["ts"], 0.1 * w)  # workgroup w starts 10 w ticks after the first
+        for a, b in zip(mine, mine[1:]):
+            assert np.isclose(a["ts"] + a["dur"], b["ts"])
+    # the skipped boundaries of workgroup 1 leave no events
+    names1 = {e["name"] for e in ev if e["tid"] == 1}
+    assert f"L0 {trace.LAYER_EVENTS[4]}" not in names1 and f"L0 {trace.LAYER_EVENTS[6]}" in names1
