@@ -26,9 +26,12 @@ namespace kd {
 namespace bt {
 
 constexpr int kM = 64;             // sessions padded to four 16-row MFMA tiles
-constexpr int kNB = 256;           // GEMM output columns per workgroup: 8 waves x 32
+// Four waves per GEMM workgroup, so two workgroups share a CU (registers and LDS allow two):
+// one's start-up and barrier waits overlap the other's streaming.
+constexpr int kGemmWaves = 4;
+constexpr int kNB = 32 * kGemmWaves;  // GEMM output columns per workgroup: 32 per wave
 constexpr int kKC = 128;           // K per LDS chunk of the activation block
-constexpr int kGemmThreads = 512;
+constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kAttThreads = 256;   // 4 waves; 16 lanes per KV position (hd = 128, bf16)
 constexpr int kChunk = 512;        // KV positions per attention workgroup
 constexpr int kMaxG = 4;
@@ -118,7 +121,7 @@ __global__ void tile_pack_kernel(const uint16_t* __restrict__ src, uint16_t* __r
 // ---------------------------------------------------------------------------------------------
 // small-M GEMM on MFMA: P[s][m][n] = sum over K-range s of (Ahi[m][k] + Alo[m][k]) * W[n][k]
 // ---------------------------------------------------------------------------------------------
-// Grid: (N / kNB) * KS workgroups of 8 waves; unit u covers columns [kNB (u / KS), + kNB) and K range
+// Grid: (N / kNB) * KS workgroups of kGemmWaves waves; unit u covers columns [kNB (u / KS), + kNB) and K range
 // u % KS, in chunks of 128 K. Wave w owns two 16-row tiles of W (32 output columns), so every
 // activation fragment it reads from LDS feeds two products. Per chunk a lane loads four 1 KB
 // tiles of each of its row blocks (W in the tile layout above), straight into registers in the
@@ -126,13 +129,13 @@ __global__ void tile_pack_kernel(const uint16_t* __restrict__ src, uint16_t* __r
 //
 // The weights (HBM) and the activation block (64 rows x 128 K, hi and lo; it stays in L2) are
 // loaded into registers kPF chunks ahead, in the same order, so a wait for one never holds up
-// the other. The activation chunk then goes through a double-buffered LDS tile that the eight
-// waves share.
+// the other. The activation chunk then goes through a double-buffered LDS tile that the
+// workgroup's waves share.
 constexpr int kPF = 2;  // chunks in flight per wave
 // NCH chunks per K range, fully unrolled: with no loop back-edge the compiler places every wait
 // exactly (at a back-edge it would drain all loads in flight).
 template <int NCH>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint16_t* __restrict__ W, int N, int K,
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __restrict__ W, int N, int K,
                                                                 const uint16_t* __restrict__ Ahi,
                                                                 const uint16_t* __restrict__ Alo, int lda,
                                                                 float* __restrict__ P, int KS, int B, const uint32_t* skip) {
