@@ -37,21 +37,22 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "batch-1 decode tokens/sec on 1 MI355X + % of HBM bytes/token roofline"
 METRIC_SESSIONS = "aggregate decode tokens/sec of lockstep sessions on 1 MI355X + p99 tick latency"
 KERNEL_SOURCES = ("kd_device.h", "kd_plan.h", "kd_pack.h")  # what defines the batch-1 step kernel and its weight layout
+BATCH_SOURCES = ("kd_batch.h", "kd_batch_host.h")  # the lockstep-sessions kernels and their launch plan
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "bandwidth_bound_transformer_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches this kernel."""
     path = os.path.join(ROOT, "profiles", f"decode_step_{workload}_hbm_traffic.md")
     if not os.path.exists(path):
@@ -59,7 +60,7 @@ def measured_traffic(workload: str):
     text = open(path).read()
     src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not src or not val or src.group(1) != kernel_source_hash():
+    if not src or not val or src.group(1) != kernel_source_hash(sources):
         return None
     return float(val.group(1))
 
@@ -262,7 +263,7 @@ def main() -> int:
         cpu = cpu_baseline(wl, weights, dec, torch, args.cpu_steps, args.cpu_seconds, first_pos, first_token)
         log(f"cpu oracle: {cpu['value']:.3f} tok/s on {cpu['cores']} threads")
 
-    traffic = measured_traffic(wl.name)
+    traffic = measured_traffic(wl.name, KERNEL_SOURCES if B == 1 else BATCH_SOURCES)
     out = {
         "metric": METRIC if B == 1 else METRIC_SESSIONS,
         "value": round(tok_s, 2),
