@@ -134,11 +134,16 @@ __global__ void tile_pack_kernel(const uint16_t* __restrict__ src, uint16_t* __r
 constexpr int kPF = 2;  // chunks in flight per wave
 // NCH chunks per K range, fully unrolled: with no loop back-edge the compiler places every wait
 // exactly (at a back-edge it would drain all loads in flight).
-template <int NCH>
+//
+// SILU (gate/up without a K split only): instead of partial sums, the workgroup writes
+// SiLU(gate) * up of its 64 FFN columns as the hi/lo activation block Ohi/Olo of the down
+// projection. Its 128 rows are two groups of [32 gate rows; the 32 up rows of the same columns].
+template <int NCH, bool SILU>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __restrict__ W, int N, int K,
                                                                 const uint16_t* __restrict__ Ahi,
                                                                 const uint16_t* __restrict__ Alo, int lda,
-                                                                float* __restrict__ P, int KS, int B, const uint32_t* skip) {
+                                                                float* __restrict__ P, int KS, int B, const uint32_t* skip,
+                                                                uint16_t* __restrict__ Ohi, uint16_t* __restrict__ Olo) {
   if (*skip) return;
   // [buffer][hi, lo][row][16-byte piece of the 128-K chunk, padded by one against bank conflicts]
   __shared__ u32x4 As[2][2][kM][kKC / 8 + 1];
@@ -212,6 +217,30 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
   for (int c = 0; c < kPF && c < NCH; ++c) load_chunk(c, ring[c]);
 #pragma unroll
   for (int c = 0; c < NCH; ++c) step(c, ring[c % kPF]);
+  if constexpr (SILU) {
+    // the workgroup's 128 rows x B sessions through LDS (As is free once every wave is past its
+    // last chunk), then SiLU(gate) * up for 64 columns
+    constexpr int LDC = kNB + 1;
+    static_assert(sizeof(As) >= sizeof(float) * kM * LDC, "the SiLU staging must fit in the activation tile");
+    float* Cs = reinterpret_cast<float*>(&As[0][0][0][0]);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Cs[(mt * 16 + q * 4 + i) * LDC + 32 * wave + 16 * j + (lane & 15)] = acc[j][mt][i];
+    __syncthreads();
+    for (int e = tid; e < B * (kNB / 2); e += kGemmThreads) {
+      const int m = e / (kNB / 2), c = e - m * (kNB / 2), grp = c / 32, ci = c - 32 * grp;
+      const float gt = Cs[m * LDC + 64 * grp + ci], up = Cs[m * LDC + 64 * grp + 32 + ci];
+      uint16_t hi, lo;
+      split_hilo(gt / (1.0f + __expf(-gt)) * up, hi, lo);
+      Ohi[(size_t)m * lda + nb * (kNB / 2) + c] = hi;
+      Olo[(size_t)m * lda + nb * (kNB / 2) + c] = lo;
+    }
+    return;
+  }
   // lane l holds rows 16 mt + 4 (l / 16) + i of column 16 (rb0 + j) + l % 16
 #pragma unroll
   for (int j = 0; j < 2; ++j) {

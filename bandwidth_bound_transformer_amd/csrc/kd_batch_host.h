@@ -37,6 +37,8 @@ struct BatchState {
   float* X = nullptr;               // [B][d] residual stream
   uint16_t* Ahi = nullptr;          // [64][lda] activation block, hi halves (rows >= B stay zero)
   uint16_t* Alo = nullptr;          // [64][lda] lo halves
+  uint16_t* A2hi = nullptr;         // [64][lda] input of the down projection when gate/up writes SiLU*up itself
+  uint16_t* A2lo = nullptr;
   float* P = nullptr;               // split-K partial sums [KS][B][N]
   float* Qs = nullptr;              // [B][hq * hd] rotated, scaled queries
   float* part = nullptr;            // attention chunk partials [B][hq][NCmax][hd + 2]
@@ -69,17 +71,21 @@ inline int pick_ks(int N, int K, int B, int nwg) {
   }
   return best;
 }
-typedef void (*GemmFn)(const uint16_t*, int, int, const uint16_t*, const uint16_t*, int, float*, int, int, const uint32_t*);
+typedef void (*GemmFn)(const uint16_t*, int, int, const uint16_t*, const uint16_t*, int, float*, int, int, const uint32_t*,
+                       uint16_t*, uint16_t*);
+template <bool SILU>
 inline GemmFn gemm_for(int nch) {
   switch (nch) {
-    case 2: return gemm_kernel<2>;
-    case 4: return gemm_kernel<4>;
-    case 8: return gemm_kernel<8>;
-    case 16: return gemm_kernel<16>;
-    case 32: return gemm_kernel<32>;
+    case 2: return gemm_kernel<2, SILU>;
+    case 4: return gemm_kernel<4, SILU>;
+    case 8: return gemm_kernel<8, SILU>;
+    case 16: return gemm_kernel<16, SILU>;
+    case 32: return gemm_kernel<32, SILU>;
     default: return nullptr;
   }
 }
+// gate/up without a K split writes SiLU(gate) * up itself (no silu_kernel launch)
+inline bool fused_silu(const BatchState& st) { return st.g_gu.KS == 1; }
 
 typedef void (*AttFn)(const float*, const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, int, int, int, float*,
                       const uint32_t*);
@@ -113,7 +119,7 @@ inline int batch_check(const kd_config* c) {
 }
 
 inline void batch_free(BatchState& st) {
-  void* ptrs[] = {st.w, st.embed, st.norms, st.rope, st.X, st.Ahi, st.Alo, st.P, st.Qs, st.part, st.logits};
+  void* ptrs[] = {st.w, st.embed, st.norms, st.rope, st.X, st.Ahi, st.Alo, st.A2hi, st.A2lo, st.P, st.Qs, st.part, st.logits};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   st = BatchState{};
@@ -172,12 +178,16 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, BatchSta
   KD_BT_ALLOC(st.X, (size_t)st.B * d * 4);
   KD_BT_ALLOC(st.Ahi, (size_t)kM * st.lda * 2);
   KD_BT_ALLOC(st.Alo, (size_t)kM * st.lda * 2);
+  KD_BT_ALLOC(st.A2hi, (size_t)kM * st.lda * 2);
+  KD_BT_ALLOC(st.A2lo, (size_t)kM * st.lda * 2);
   KD_BT_ALLOC(st.P, p_elems * 4);
   KD_BT_ALLOC(st.Qs, (size_t)st.B * st.qdim * 4);
   KD_BT_ALLOC(st.part, (size_t)st.B * st.hq * st.NCmax * (st.hd + 2) * 4);
   KD_BT_ALLOC(st.logits, (size_t)st.B * st.V * 4);
   KD_BT_TRY(hipMemset(st.Ahi, 0, (size_t)kM * st.lda * 2));  // padding rows stay zero for good
   KD_BT_TRY(hipMemset(st.Alo, 0, (size_t)kM * st.lda * 2));
+  KD_BT_TRY(hipMemset(st.A2hi, 0, (size_t)kM * st.lda * 2));
+  KD_BT_TRY(hipMemset(st.A2lo, 0, (size_t)kM * st.lda * 2));
 
   // Every matrix goes row-major into a staging buffer, then tile_pack_kernel writes it into the
   // blob in the tile layout the GEMM streams.
@@ -248,7 +258,7 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, BatchSta
 }
 
 // Kernels one tick enqueues: check, embed+norm, 10 per layer, LM head, argmax.
-inline int batch_kernels_per_tick(const BatchState& st) { return 2 + 10 * st.L + 2; }
+inline int batch_kernels_per_tick(const BatchState& st) { return 2 + (fused_silu(st) ? 9 : 10) * st.L + 2; }
 
 // Enqueue one tick. flags: [0] sticky status bits, [2] this tick's skip flag.
 inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions, void* kvp, float* logits,
@@ -260,8 +270,9 @@ inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions,
                 kv_layer = 2 * kv_slot;
   float* lg = logits ? logits : st.logits;
   auto gemm = [&](const uint16_t* W, const Gemm& g, float* out) {
-    hipLaunchKernelGGL(gemm_for(g.K / (g.KS * kKC)), dim3((g.N / kNB) * g.KS), dim3(kGemmThreads), 0, s, W, g.N, g.K,
-                       (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, out, g.KS, st.B, skip);
+    hipLaunchKernelGGL(gemm_for<false>(g.K / (g.KS * kKC)), dim3((g.N / kNB) * g.KS), dim3(kGemmThreads), 0, s, W, g.N,
+                       g.K, (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, out, g.KS, st.B, skip,
+                       (uint16_t*)nullptr, (uint16_t*)nullptr);
   };
   auto norm = [&](int mode, const Gemm* g, int gain_index) {
     hipLaunchKernelGGL(residual_norm_kernel, dim3(st.B), dim3(1024), 0, s, mode, (const uint16_t*)st.embed,
@@ -286,10 +297,22 @@ inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions,
                        (const int32_t*)positions, st.hq, st.hd, st.CH, st.NCmax, st.Ahi, st.Alo, st.lda, skip);
     gemm(lay + st.w_o, st.g_o, st.P);
     norm(1, &st.g_o, 2 * l + 1);
-    gemm(lay + st.w_gu, st.g_gu, st.P);
-    hipLaunchKernelGGL(silu_kernel, dim3(st.F / 256, st.B), dim3(256), 0, s, (const float*)st.P, st.g_gu.KS, st.F, st.Ahi,
-                       st.Alo, st.lda, st.B, skip);
-    gemm(lay + st.w_d, st.g_d, st.P);
+    if (fused_silu(st)) {
+      // gate/up writes SiLU(gate) * up into the second activation block, which the down
+      // projection reads (the first is still being read while gate/up runs)
+      const Gemm& g = st.g_gu;
+      hipLaunchKernelGGL(gemm_for<true>(g.K / kKC), dim3(g.N / kNB), dim3(kGemmThreads), 0, s, lay + st.w_gu, g.N, g.K,
+                         (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, st.P, 1, st.B, skip, st.A2hi, st.A2lo);
+      const Gemm& gd = st.g_d;
+      hipLaunchKernelGGL(gemm_for<false>(gd.K / (gd.KS * kKC)), dim3((gd.N / kNB) * gd.KS), dim3(kGemmThreads), 0, s,
+                         lay + st.w_d, gd.N, gd.K, (const uint16_t*)st.A2hi, (const uint16_t*)st.A2lo, st.lda, st.P, gd.KS,
+                         st.B, skip, (uint16_t*)nullptr, (uint16_t*)nullptr);
+    } else {
+      gemm(lay + st.w_gu, st.g_gu, st.P);
+      hipLaunchKernelGGL(silu_kernel, dim3(st.F / 256, st.B), dim3(256), 0, s, (const float*)st.P, st.g_gu.KS, st.F, st.Ahi,
+                         st.Alo, st.lda, st.B, skip);
+      gemm(lay + st.w_d, st.g_d, st.P);
+    }
     norm(1, &st.g_d, l + 1 < st.L ? 2 * (l + 1) : 2 * st.L);
   }
   gemm(st.w + st.w_lm, st.g_lm, lg);

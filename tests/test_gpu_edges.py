@@ -49,19 +49,20 @@ def _check(gl, g_tok, want, tol, tag):
     return err, 0
 
 
-# (sessions, q heads, kv heads): the smallest batch with plain multi-head attention, an odd batch
-# (a partly filled 16-row MFMA tile) with two query heads per kv head, and the largest batch with
-# four. Every GEMM of these shapes meets the lockstep path's tile and split constraints.
-RAGGED_CASES = [(2, 2, 2), (17, 4, 2), (64, 8, 2)]
+# (sessions, q heads, kv heads, d_model): the smallest batch with plain multi-head attention, an
+# odd batch (a partly filled 16-row MFMA tile) with two query heads per kv head, the largest batch
+# with four, and a d_model of 256, whose gate/up GEMM runs unsplit and so writes SiLU(gate) * up
+# itself. Every GEMM of these shapes meets the lockstep path's tile and split constraints.
+RAGGED_CASES = [(2, 2, 2, 512), (17, 4, 2, 512), (64, 8, 2, 512), (17, 2, 1, 256)]
 
 
-@pytest.mark.parametrize("B,hq,hkv", RAGGED_CASES)
-def test_lockstep_ragged_positions(torch, kdm, B, hq, hkv):
+@pytest.mark.parametrize("B,hq,hkv,d", RAGGED_CASES)
+def test_lockstep_ragged_positions(torch, kdm, B, hq, hkv, d):
     """Sessions at different positions in one tick: from position 0 (a single cached key) through
     both sides of the 512-position attention chunk boundaries, to the last slot of the cache on
     the final tick. Logits, tokens and positions of every session, every tick."""
     ticks = 5
-    shape = ModelShape(2, 512, hq, hkv, 128, 512, 1024, rope_base=500000.0)
+    shape = ModelShape(2, d, hq, hkv, 128, 512, 1024, rope_base=500000.0)
     start = np.array([(b * 389) % 1090 for b in range(B)], np.int64)
     start[0] = 0
     start[-1] = 1090  # reaches max_seq - 1 on the last tick
@@ -72,7 +73,10 @@ def test_lockstep_ragged_positions(torch, kdm, B, hq, hkv):
     assert wl.max_seq == prefill + ticks
     w = workloads.make_weights(shape, seed=wl.weight_seed)
     dec = kdm.Decoder(shape, w, max_seq=wl.max_seq, batch=B)
-    assert kdm.kd_get_info(dec.handle)["workgroups"] == 0  # the lockstep path
+    info = kdm.kd_get_info(dec.handle)
+    assert info["workgroups"] == 0  # the lockstep path
+    if d == 256:  # one K chunk pair: gate/up unsplit, SiLU fused into it (9 launches per layer)
+        assert info["split_k"][2] == 1 and info["kernels_per_step"] == 2 + 9 * shape.n_layers + 2
     o = ref.Oracle(shape, w, batch=B, max_seq=wl.max_seq)
     kv = dec.kv_view().view(torch.int16)
     for l in range(shape.n_layers):
@@ -98,7 +102,7 @@ def test_lockstep_ragged_positions(torch, kdm, B, hq, hkv):
             worst = max(worst, err)
             flips += f
         tok = g_tok.astype(np.int64)
-    print(f"ragged B={B} G={hq // hkv}: max rel logit err {worst:.3e}, tie-flips {flips}", flush=True)
+    print(f"ragged B={B} G={hq // hkv} d={d}: max rel logit err {worst:.3e}, tie-flips {flips}", flush=True)
     assert flips <= 1
     assert dec.status() == 0
     assert np.array_equal(dec.positions.cpu().numpy(), start + ticks)
