@@ -222,6 +222,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
     // last chunk), then SiLU(gate) * up for 64 columns
     constexpr int LDC = kNB + 1;
     static_assert(sizeof(As) >= sizeof(float) * kM * LDC, "the SiLU staging must fit in the activation tile");
+    static_assert(kNB % 64 == 0, "a workgroup's rows must be whole [32 gate; 32 up] groups");
     float* Cs = reinterpret_cast<float*>(&As[0][0][0][0]);
     __syncthreads();
 #pragma unroll
