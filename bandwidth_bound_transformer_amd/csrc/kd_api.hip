@@ -146,7 +146,7 @@ const char* kd_strerror(int code) {
   switch (code) {
     case KD_OK: return "success";
     case KD_ERR_INVALID_ARG: return "invalid argument";
-    case KD_ERR_UNSUPPORTED: return "configuration not supported by this build";
+    case KD_ERR_UNSUPPORTED: return "configuration not supported by this library";
     case KD_ERR_NO_DEVICE: return "no HIP device available";
     case KD_ERR_OOM: return "device memory allocation failed";
     case KD_ERR_HIP: return "HIP runtime call failed";

@@ -151,7 +151,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for {max(args.gpus, world)}).",
+        print(f"bench.py runs on exactly one GPU: the library has no multi-GPU path (asked for {max(args.gpus, world)}).",
               file=sys.stderr)
         return 2
 
