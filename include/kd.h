@@ -75,7 +75,7 @@ extern "C" {
  *                small-M GEMMs on the matrix cores. That path needs bf16 weights and cache,
  *                head_dim 128, d_model one of 256, 512, 1024, 2048 or 4096, n_q_heads*head_dim
  *                and ffn_dim each 256 times a power of two, and d_model, 2*ffn_dim,
- *                (n_q_heads+2*n_kv_heads)*head_dim and vocab multiples of 256.
+ *                (n_q_heads+2*n_kv_heads)*head_dim and vocab multiples of 128.
  *   norm_eps     RMSNorm epsilon (inside the square root).
  *   rope_base    RoPE base: pair (i, i + head_dim/2) turns by position * rope_base^(-2i/head_dim).
  *   weight_dtype KD_DTYPE_BF16 or KD_DTYPE_F32; kv_dtype likewise (must match weight_dtype).
