@@ -612,7 +612,20 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
   float best = -INFINITY;
   int32_t besti = 0x7fffffff;
   bool nan = false;
-  for (int i = tid; i < V; i += 1024) {
+  // eight loads in flight per thread, then the compares (ties resolve by index in any order)
+  int i = tid;
+  for (; i + 7 * 1024 < V; i += 8 * 1024) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = l[i + u * 1024];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = i + u * 1024;
+      if (v[u] != v[u]) nan = true;
+      else if (v[u] > best || (v[u] == best && j < besti)) { best = v[u]; besti = j; }
+    }
+  }
+  for (; i < V; i += 1024) {
     const float v = l[i];
     if (v != v) { nan = true; continue; }
     if (v > best || (v == best && i < besti)) { best = v; besti = i; }
