@@ -279,6 +279,41 @@ def pin_identity_layers(mod):
         assert _rel(got, want) < 1e-12
 
 
+def pin_sessions_independent(mod):
+    """Sessions stepped together are independent: a multi-session step of sessions in a scrambled
+    order, at ragged positions with distinct tokens, gives each session bit for bit what a
+    one-session oracle fed the same history gives, and what the brute force gives."""
+    shape = MICRO_GQA
+    w = micro_weights(shape, seed=31)
+    # per session: its own token history (session s has its own length and ids)
+    hist = {0: [5, 11, 2, 37], 1: [23, 8], 2: [1, 14, 39, 6, 20, 9]}
+    multi = mod.Oracle(shape, w, batch=3, max_seq=8)
+    single = {s: mod.Oracle(shape, w, batch=1, max_seq=8) for s in hist}
+    brute = {s: brute_force.decode(shape, w, [(t, p) for p, t in enumerate(seq)]) for s, seq in hist.items()}
+    got = {s: [] for s in hist}
+    # ticks: each names the sessions stepped together, in the order passed
+    ticks = [[2, 0, 1], [0, 2], [2, 1, 0], [0, 2], [2], [2]]
+    pos = {s: 0 for s in hist}
+    for tick in ticks:
+        toks = [hist[s][pos[s]] for s in tick]
+        ps = [pos[s] for s in tick]
+        out = multi.step_sessions(tick, toks, ps)
+        for i, s in enumerate(tick):
+            got[s].append(out[i])
+            pos[s] += 1
+    for s, seq in hist.items():
+        assert pos[s] == len(seq)
+        want = [single[s].step_one(0, t, p) for p, t in enumerate(seq)]
+        for p in range(len(seq)):
+            assert np.array_equal(np.asarray(got[s][p]).view(np.uint64), np.asarray(want[p]).view(np.uint64)), (s, p)
+            assert _rel(got[s][p], brute[s][p]) < 1e-9, (s, p)
+        # the cache rows of the session hold exactly its own history
+        n = len(seq)
+        assert np.array_equal(multi.k_cache[s, :, :, :n], single[s].k_cache[0, :, :, :n])
+        assert np.array_equal(multi.v_cache[s, :, :, :n], single[s].v_cache[0, :, :, :n])
+        assert not np.any(multi.k_cache[s, :, :, n:])
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_brute_force_prefilled,
@@ -292,4 +327,5 @@ ALL_PINS = [
     pin_argmax,
     pin_bf16,
     pin_identity_layers,
+    pin_sessions_independent,
 ]

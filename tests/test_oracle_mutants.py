@@ -60,6 +60,17 @@ MUTANTS = {
     "kv_not_rounded_to_cache_type": ('if dtype == "bf16":\n        f32 = round_f32_to_bf16(f32)', "if False:\n        pass"),
     "softmax_no_max_shift": ("e = np.exp(s - m)", "e = np.exp(s)"),
     "rope_position_off_by_one": ("angle = np.float64(position) * theta", "angle = np.float64(position + 1) * theta"),
+    # multi-session steps: every session must use its own angles, residual stream and cache rows
+    "sessions_share_first_rope": ("cos, sin = rope[i]", "cos, sin = rope[0]"),
+    "sessions_share_one_x": ("x = xs[i]", "x = xs[0]"),
+    "k_cache_indexed_by_call_slot": (
+        "self.k_cache[session, l, :, position] = self._store(k)",
+        "self.k_cache[i, l, :, position] = self._store(k)",
+    ),
+    "v_cache_read_by_call_slot": (
+        "vc = self.v_cache[session, l, :, : position + 1]",
+        "vc = self.v_cache[i, l, :, : position + 1]",
+    ),
 }
 
 # cheapest pins first: a mutant stops at its first failing pin
@@ -75,6 +86,7 @@ PIN_ORDER = [
     oracle_pins.pin_brute_force_prefilled,
     oracle_pins.pin_incremental_equals_full,
     oracle_pins.pin_silu,
+    oracle_pins.pin_sessions_independent,
     lambda mod: oracle_pins.pin_bf16(mod, n_random=1 << 14),
 ]
 
