@@ -23,6 +23,13 @@
 namespace {
 
 constexpr int kRing = 13;
+constexpr uint64_t kDefaultSpinTicks = 200000000ull;  // 2 s of the 100 MHz realtime counter
+constexpr int kFlagStatus = 0, kFlagAbort = 1, kFlagSkip = 2, kFlagCancel = 3;
+
+// Zero n 64-bit words (a kernel rather than a memset, so that a captured graph replays it reliably).
+__global__ void clear_words_kernel(uint64_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
 
 struct Buffers {
   uint8_t* blob = nullptr;
@@ -30,7 +37,7 @@ struct Buffers {
   uint8_t* norms = nullptr;
   float2* rope = nullptr;     // [S][hd/2] (cos, sin)
   uint64_t* ll = nullptr;
-  uint32_t* flags = nullptr;  // [0] sticky status bits, [1] abort flag
+  uint32_t* flags = nullptr;  // [0] sticky status bits, [1] abort word, [2] tick skip flag (B > 1), [3] cancel word
 };
 
 void free_buffers(Buffers& b) {
@@ -62,9 +69,11 @@ struct kd_handle {
   kd::LLLayout lo{};
   Buffers buf;
   KernelFn kernel = nullptr;
-  uint32_t seq = 0;
+  uint32_t next_tag = 0;  // tag base of the next launch (advances by steps * tag_stride)
+  uint64_t spin_ticks = kDefaultSpinTicks;
   int64_t lds_bytes = 0;
   uint64_t* trace = nullptr;
+  hipStream_t ctl = nullptr;  // private non-blocking stream for cancel-word writes
   bool batched = false;  // B > 1: the lockstep-sessions path (kd_batch.h)
   kd::bt::BatchState bs;
 };
@@ -205,8 +214,10 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
       return KD_ERR_OOM;
     }
     if (hipMemset(hb->buf.flags, 0, 256) != hipSuccess) rc = KD_ERR_HIP;
+    if (rc == KD_OK && hipStreamCreateWithFlags(&hb->ctl, hipStreamNonBlocking) != hipSuccess) rc = KD_ERR_HIP;
     if (rc == KD_OK) rc = kd::bt::batch_init(cfg, w, nwg, hb->bs);
     if (rc != KD_OK) {
+      if (hb->ctl) (void)hipStreamDestroy(hb->ctl);
       free_buffers(hb->buf);
       delete hb;
       return rc;
@@ -234,6 +245,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
   h->lo = kd::ll_layout(m);
   h->kernel = kern;
   h->lds_bytes = (int64_t)fattr.sharedSizeBytes;
+  h->next_tag = kd::tag_stride(m);
 
   uint8_t* tmp = nullptr;
   {
@@ -248,6 +260,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
     if (hipMalloc(&tmp, (size_t)2 * m.F * d * wb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     KD_TRY(hipMemset(h->buf.ll, 0, (size_t)h->lo.total * 8));
     KD_TRY(hipMemset(h->buf.flags, 0, 256));
+    KD_TRY(hipStreamCreateWithFlags(&h->ctl, hipStreamNonBlocking));
     const size_t row = (size_t)d * wb;
     for (int l = 0; l < m.L; ++l) {
       const kd_layer_weights& lw = w->layers[l];
@@ -303,72 +316,161 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
 
 fail:
   if (tmp) (void)hipFree(tmp);
+  if (h->ctl) (void)hipStreamDestroy(h->ctl);
   free_buffers(h->buf);
   delete h;
   return rc;
 }
 
-int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* logits, void* stream) {
-  if (!h || !tokens || !positions || !kv) return KD_ERR_INVALID_ARG;
-  int cur = -1;
-  if (hipGetDevice(&cur) != hipSuccess) return KD_ERR_HIP;
-  if (cur != h->device && hipSetDevice(h->device) != hipSuccess) return KD_ERR_HIP;
-  if (h->batched) {
-    const int rcb = kd::bt::batch_step(h->bs, tokens, positions, kv, logits, (hipStream_t)stream, h->buf.flags);
-    if (cur != h->device) (void)hipSetDevice(cur);
-    return rcb;
+}  // extern "C"
+
+namespace {
+
+// Tag bases for a launch of n steps from the counter *next (advanced past them). A range never
+// wraps past zero: when it would, the counter restarts and *clear is set, and the caller clears
+// the exchange words first, so no word left from before can carry a tag of the new range.
+uint32_t take_tags(uint32_t* next, uint32_t stride, int n, bool* clear) {
+  const uint64_t need = (uint64_t)stride * (uint64_t)n;
+  *clear = false;
+  if ((uint64_t)*next + need >= (1ull << 32)) {
+    *next = stride;
+    *clear = true;
+  }
+  const uint32_t t = *next;
+  *next = (uint32_t)(t + need);
+  return t;
+}
+
+// Launch n steps of the batch-1 kernel with the exchange words at ll and the abort word at abortf.
+int launch_steps(kd_handle* h, uint64_t* ll, uint32_t* abortf, uint32_t* next_tag, int n, int32_t* tokens,
+                 int32_t* positions, void* kv, float* logits, int32_t* out_tokens, uint32_t* progress, hipStream_t stream) {
+  bool clear = false;
+  const uint32_t tag0 = take_tags(next_tag, kd::tag_stride(h->m), n, &clear);
+  if (clear) {
+    hipLaunchKernelGGL(clear_words_kernel, dim3(256), dim3(256), 0, stream, ll, (int64_t)h->lo.total);
+    if (hipGetLastError() != hipSuccess) return KD_ERR_LAUNCH;
   }
   kd::Params P{};
   P.blob = h->buf.blob;
   P.embed = h->buf.embed;
   P.norms = h->buf.norms;
   P.rope = h->buf.rope;
-  P.ll = h->buf.ll;
+  P.ll = ll;
   P.lo = h->lo;
   P.kv = (uint8_t*)kv;
   P.tokens = tokens;
   P.positions = positions;
   P.logits = logits;
+  P.status = h->buf.flags + kFlagStatus;
+  P.abortf = abortf;
+  P.cancel = h->buf.flags + kFlagCancel;
   P.trace = h->trace;
-  P.status = h->buf.flags;
-  P.abortf = h->buf.flags + 1;
-  if (++h->seq == 0) ++h->seq;  // tag 0 never names a live vector
-  P.seq = h->seq;
+  P.out_tokens = out_tokens;
+  P.progress = progress;
+  P.spin_ticks = h->spin_ticks;
+  P.tag0 = tag0;
+  P.n_steps = n;
   P.max_seq = h->cfg.max_seq;
   P.eps = h->cfg.norm_eps;
   P.m = h->m;
   void* args[] = {&P};
   // One workgroup per compute unit, and a workgroup needs most of a CU's LDS, so on an idle
   // device the whole grid is resident at once. If another kernel holds CUs, the waits between
-  // workgroups time out and the step ends with KD_STATUS_SYNC_TIMEOUT instead of hanging.
-  const hipError_t e = hipLaunchKernel((const void*)h->kernel, dim3(h->m.nwg), dim3(kd::kThreads), args, 0,
-                                       (hipStream_t)stream);
-  int rc = KD_OK;
-  if (e != hipSuccess) rc = KD_ERR_LAUNCH;
-  if (cur != h->device) (void)hipSetDevice(cur);
-  return rc;
+  // workgroups time out and the launch ends with KD_STATUS_SYNC_TIMEOUT instead of hanging.
+  const hipError_t e = hipLaunchKernel((const void*)h->kernel, dim3(h->m.nwg), dim3(kd::kThreads), args, 0, stream);
+  return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+// Makes h's device current for the lifetime of the guard, then restores the caller's.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) return;
+    ok = prev == dev || hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* logits, void* stream) {
+  if (!h || !tokens || !positions || !kv) return KD_ERR_INVALID_ARG;
+  DeviceGuard g(h->device);
+  if (!g.ok) return KD_ERR_HIP;
+  if (h->batched)
+    return kd::bt::batch_step(h->bs, tokens, positions, kv, logits, (hipStream_t)stream, h->buf.flags, nullptr, nullptr, 0);
+  return launch_steps(h, h->buf.ll, h->buf.flags + kFlagAbort, &h->next_tag, 1, tokens, positions, kv, logits, nullptr,
+                      nullptr, (hipStream_t)stream);
+}
+
+int kd_generate(kd_handle* h, int32_t n_steps, int32_t* tokens, int32_t* positions, void* kv, int32_t* out_tokens,
+                float* logits, uint32_t* progress, void* stream) {
+  if (!h || !tokens || !positions || !kv || n_steps < 1) return KD_ERR_INVALID_ARG;
+  DeviceGuard g(h->device);
+  if (!g.ok) return KD_ERR_HIP;
+  if (h->batched) {
+    // B > 1: the ticks' kernel sequences back to back on the stream, tokens fed back on the device
+    const size_t per = (size_t)h->bs.B * h->bs.V;
+    for (int s = 0; s < n_steps; ++s) {
+      const int rc = kd::bt::batch_step(h->bs, tokens, positions, kv, logits ? logits + s * per : nullptr,
+                                        (hipStream_t)stream, h->buf.flags, out_tokens ? out_tokens + (size_t)s * h->bs.B : nullptr,
+                                        progress, (uint32_t)(s + 1));
+      if (rc != KD_OK) return rc;
+    }
+    return KD_OK;
+  }
+  return launch_steps(h, h->buf.ll, h->buf.flags + kFlagAbort, &h->next_tag, n_steps, tokens, positions, kv, logits,
+                      out_tokens, progress, (hipStream_t)stream);
+}
+
+int kd_control(kd_handle* h, int32_t op, int64_t value) {
+  if (!h) return KD_ERR_INVALID_ARG;
+  DeviceGuard g(h->device);
+  if (!g.ok) return KD_ERR_HIP;
+  switch (op) {
+    case KD_CTRL_CANCEL: {
+      // written on the handle's own non-blocking stream, so it lands while a launch runs
+      static const uint32_t kOne = 1, kZero = 0;
+      if (hipMemcpyAsync(h->buf.flags + kFlagCancel, value ? &kOne : &kZero, 4, hipMemcpyHostToDevice, h->ctl) != hipSuccess)
+        return KD_ERR_HIP;
+      return hipStreamSynchronize(h->ctl) == hipSuccess ? KD_OK : KD_ERR_HIP;
+    }
+    case KD_CTRL_WAIT_LIMIT_US:
+      if (value < 0 || value > 60000000) return KD_ERR_INVALID_ARG;
+      h->spin_ticks = (uint64_t)value * 100u;  // 100 MHz counter
+      return KD_OK;
+    default:
+      return KD_ERR_INVALID_ARG;
+  }
 }
 
 int kd_device_status(kd_handle* h, uint32_t* bits, int clear) {
   if (!h || !bits) return KD_ERR_INVALID_ARG;
-  if (hipSetDevice(h->device) != hipSuccess) return KD_ERR_HIP;
+  DeviceGuard g(h->device);
+  if (!g.ok) return KD_ERR_HIP;
   if (hipDeviceSynchronize() != hipSuccess) return KD_ERR_HIP;
-  uint32_t f[2] = {0, 0};
-  if (hipMemcpy(f, h->buf.flags, sizeof(f), hipMemcpyDeviceToHost) != hipSuccess) return KD_ERR_HIP;
-  *bits = f[0];
-  if (clear && hipMemset(h->buf.flags, 0, sizeof(f)) != hipSuccess) return KD_ERR_HIP;
+  uint32_t f = 0;
+  if (hipMemcpy(&f, h->buf.flags + kFlagStatus, sizeof(f), hipMemcpyDeviceToHost) != hipSuccess) return KD_ERR_HIP;
+  *bits = f;
+  if (clear && hipMemset(h->buf.flags + kFlagStatus, 0, sizeof(f)) != hipSuccess) return KD_ERR_HIP;
   return KD_OK;
 }
 
 void kd_destroy(kd_handle* h) {
   if (!h) return;
-  int cur = -1;
-  (void)hipGetDevice(&cur);
-  (void)hipSetDevice(h->device);
-  (void)hipDeviceSynchronize();
-  free_buffers(h->buf);
-  if (h->batched) kd::bt::batch_free(h->bs);
-  if (cur >= 0) (void)hipSetDevice(cur);
+  {
+    DeviceGuard g(h->device);
+    (void)hipDeviceSynchronize();
+    if (h->ctl) (void)hipStreamDestroy(h->ctl);
+    free_buffers(h->buf);
+    if (h->batched) kd::bt::batch_free(h->bs);
+  }
   delete h;
 }
 

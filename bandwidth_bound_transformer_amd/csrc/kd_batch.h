@@ -88,13 +88,15 @@ __device__ __forceinline__ float wsum(float v) {
 // ---------------------------------------------------------------------------------------------
 // tick validation: every later kernel of the tick reads *skip and writes nothing when it is set
 // ---------------------------------------------------------------------------------------------
+// A nonzero cancel word skips the tick too (status bit 0x10).
 __global__ void check_kernel(const int32_t* tokens, const int32_t* positions, int B, int V, int max_seq,
-                             uint32_t* status, uint32_t* skip) {
+                             uint32_t* status, uint32_t* skip, const uint32_t* cancel) {
   uint32_t bits = 0;
   for (int b = 0; b < B; ++b) {
     if (tokens[b] < 0 || tokens[b] >= V) bits |= 0x1u;
     if (positions[b] < 0 || positions[b] >= max_seq) bits |= 0x2u;
   }
+  if (__hip_atomic_load(cancel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) bits |= 0x10u;
   if (bits) __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   *skip = bits ? 1u : 0u;
 }
@@ -602,8 +604,10 @@ __global__ __launch_bounds__(256) void silu_kernel(const float* __restrict__ P, 
 // greedy argmax of every session: lowest index of the maximum; NaN logits are skipped and flagged
 // ---------------------------------------------------------------------------------------------
 // Grid: B workgroups of 1024 threads.
+// out (optional): the tick's row of the caller's token record.
 __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ logits, int V, int32_t* tokens,
-                                                      int32_t* positions, uint32_t* status, const uint32_t* skip) {
+                                                      int32_t* positions, uint32_t* status, const uint32_t* skip,
+                                                      int32_t* out) {
   if (*skip) return;
   __shared__ float bv[16];
   __shared__ int32_t bi[16];
@@ -646,7 +650,15 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
       if (bv[w] > best || (bv[w] == best && bi[w] < besti)) { best = bv[w]; besti = bi[w]; }
     tokens[b] = besti == 0x7fffffff ? 0 : besti;
     positions[b] = positions[b] + 1;
+    if (out) out[b] = tokens[b];
   }
+}
+
+// After a tick of a multi-tick call: the count of completed ticks, written through to memory (the
+// tick's outputs were written by the kernels before this one on the stream).
+__global__ void progress_kernel(uint32_t* progress, uint32_t value, const uint32_t* skip) {
+  if (*skip) return;
+  __hip_atomic_store(progress, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 }  // namespace bt

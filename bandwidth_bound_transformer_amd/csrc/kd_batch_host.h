@@ -260,9 +260,10 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, BatchSta
 // Kernels one tick enqueues: check, embed+norm, 10 per layer, LM head, argmax.
 inline int batch_kernels_per_tick(const BatchState& st) { return 2 + (fused_silu(st) ? 9 : 10) * st.L + 2; }
 
-// Enqueue one tick. flags: [0] sticky status bits, [2] this tick's skip flag.
+// Enqueue one tick. flags: [0] sticky status bits, [2] this tick's skip flag, [3] the cancel word.
+// out (optional) receives the tick's B tokens; progress (optional) is set to progress_value after it.
 inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions, void* kvp, float* logits,
-                      hipStream_t s, uint32_t* flags) {
+                      hipStream_t s, uint32_t* flags, int32_t* out, uint32_t* progress, uint32_t progress_value) {
   uint32_t* status = flags;
   const uint32_t* skip = flags + 2;
   uint16_t* kv = (uint16_t*)kvp;
@@ -281,7 +282,7 @@ inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions,
                        st.B, skip);
   };
   hipLaunchKernelGGL(check_kernel, dim3(1), dim3(1), 0, s, (const int32_t*)tokens, (const int32_t*)positions, st.B, st.V,
-                     st.max_seq, status, flags + 2);
+                     st.max_seq, status, flags + 2, (const uint32_t*)(flags + 3));
   norm(0, nullptr, 0);
   for (int l = 0; l < st.L; ++l) {
     const uint16_t* lay = st.w + (size_t)l * st.layer_elems;
@@ -316,7 +317,9 @@ inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions,
     norm(1, &st.g_d, l + 1 < st.L ? 2 * (l + 1) : 2 * st.L);
   }
   gemm(st.w + st.w_lm, st.g_lm, lg);
-  hipLaunchKernelGGL(argmax_kernel, dim3(st.B), dim3(1024), 0, s, (const float*)lg, st.V, tokens, positions, status, skip);
+  hipLaunchKernelGGL(argmax_kernel, dim3(st.B), dim3(1024), 0, s, (const float*)lg, st.V, tokens, positions, status, skip,
+                     out);
+  if (progress) hipLaunchKernelGGL(progress_kernel, dim3(1), dim3(1), 0, s, progress, progress_value, skip);
   return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
 

@@ -57,17 +57,22 @@ struct Params {
   int32_t* tokens;
   int32_t* positions;
   float* logits;
-  uint32_t* status;
-  uint32_t* abortf;
-  uint64_t* trace;  // per-workgroup phase timestamps (100 MHz clock), or null
-  uint32_t seq;
+  uint32_t* status;          // sticky status bits
+  uint32_t* abortf;          // tag base of the last call a workgroup gave up on
+  const uint32_t* cancel;    // nonzero: abandon the call (set by the host between or during calls)
+  uint64_t* trace;           // per-workgroup phase timestamps (100 MHz clock), or null
+  int32_t* out_tokens;       // [n_steps] greedy token of every step, or null
+  uint32_t* progress;        // steps completed so far (system-scope store after each step), or null
+  uint64_t spin_ticks;       // longest wait for another workgroup, in 100 MHz ticks
+  uint32_t tag0;             // tag base of step 0; step s uses tag0 + s * tag_stride
+  int32_t n_steps;           // decode steps this launch runs, each fed the previous step's token
   int32_t max_seq;
   float eps;
   Dims m;
 };
 
-constexpr uint32_t kStatusTokenRange = 0x1u, kStatusPosOverflow = 0x2u, kStatusTimeout = 0x4u, kStatusNaN = 0x8u;
-constexpr uint64_t kSpinTicks = 200000000ull;  // 2 s of the 100 MHz realtime counter
+constexpr uint32_t kStatusTokenRange = 0x1u, kStatusPosOverflow = 0x2u, kStatusTimeout = 0x4u, kStatusNaN = 0x8u,
+                   kStatusCancelled = 0x10u;
 constexpr int kMaxRowsD = 64;                  // most d rows one workgroup owns
 constexpr int kMaxSlice = 128;                 // most FFN columns one workgroup owns
 
@@ -228,6 +233,22 @@ __device__ __forceinline__ void dma_packet(const void* lane_addr, uint32_t lds_a
       : "memory");
 }
 
+// The same load with device-scope coherence (sc1): it sees values another workgroup of the same
+// launch stored with device-scope stores, where the plain load could hit a stale line of this
+// compute unit's L2. Used for K/V positions appended earlier in the same launch.
+__device__ __forceinline__ void dma_packet_coherent(const void* lane_addr, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off sc1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(lane_addr)
+      : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -274,8 +295,10 @@ enum SegKind : int32_t { kSegWeight = 0, kSegKV = 1, kSegOnce = 2 };
 struct SegEntry {
   const uint8_t* base;
   int32_t lo, hi;
-  int32_t kind, pad;
+  int32_t kind;
+  int32_t coh;  // packets from this index on are loaded with device-scope coherence
 };
+constexpr int32_t kNoCoherent = 0x7fffffff;
 
 // Per-layer order of a wave's segments: QKV, (K, V) of each attention unit, O, gate/up, down.
 __device__ __forceinline__ int seg_o(int nunits) { return 1 + 2 * nunits; }
@@ -309,6 +332,8 @@ struct Smem {
   int32_t split[kTiles][kWaves + 1];  // wave boundaries of each tile (packets)
   int32_t first[kTiles][kWaves];      // first row / block of each wave's share
   int abort_flag;
+  uint32_t cancel;                    // the cancel word as read at the start of the step
+  int32_t next_token;                 // the step's greedy token, for the next step of the launch
 };
 
 // step-level facts every workgroup derives from the inputs
@@ -360,16 +385,19 @@ __device__ __forceinline__ void wave_range(const Dims& m, int w, int tile, int v
 }
 
 // Fill wave v's segment table (done by the wave itself).
+// K/V positions from p_new on were appended earlier in this launch (by a multi-step launch), so
+// their packets are loaded coherently; p_new = max_seq when no such position exists.
 template <int RING>
-__device__ __forceinline__ void build_segments(const Params& P, const StepInfo& si, int w, int v, Smem<RING>& sm) {
+__device__ __forceinline__ void build_segments(const Params& P, const StepInfo& si, int w, int v, Smem<RING>& sm,
+                                               int p_new) {
   const Dims& m = P.m;
   if (lane_id() != 0) return;
-  auto put = [&](SegEntry& e, const uint8_t* base, int lo, int hi, int kind) {
+  auto put = [&](SegEntry& e, const uint8_t* base, int lo, int hi, int kind, int coh = kNoCoherent) {
     e.base = base;
     e.lo = lo;
     e.hi = hi;
     e.kind = kind;
-    e.pad = 0;
+    e.coh = coh;
   };
   SegEntry* t = sm.segs[v];
   int lo, hi;
@@ -380,8 +408,9 @@ __device__ __forceinline__ void build_segments(const Params& P, const StepInfo& 
     const int n = u.j1 > u.j0 ? c_div(u.j1 - u.j0, m.ppp) : 0;
     const int64_t kbase = (((int64_t)0 * 2 + 0) * m.hkv + u.g) * m.S + u.j0;
     const int64_t vbase = (((int64_t)0 * 2 + 1) * m.hkv + u.g) * m.S + u.j0;
-    put(t[1 + 2 * k], P.kv + kbase * m.hd * m.kvbytes, p_lo(n, kWaves, v), p_lo(n, kWaves, v + 1), kSegKV);
-    put(t[2 + 2 * k], P.kv + vbase * m.hd * m.kvbytes, p_lo(n, kWaves, v), p_lo(n, kWaves, v + 1), kSegKV);
+    const int coh = p_new < u.j1 ? max(p_new - u.j0, 0) / m.ppp : kNoCoherent;  // packet holding p_new
+    put(t[1 + 2 * k], P.kv + kbase * m.hd * m.kvbytes, p_lo(n, kWaves, v), p_lo(n, kWaves, v + 1), kSegKV, coh);
+    put(t[2 + 2 * k], P.kv + vbase * m.hd * m.kvbytes, p_lo(n, kWaves, v), p_lo(n, kWaves, v + 1), kSegKV, coh);
   }
   const int o = seg_o(si.nunits);
   wave_range(m, w, kTileO, v, lo, hi);
@@ -402,7 +431,7 @@ struct Issuer {
   int64_t wstride, kvstride;
   int layer, e;  // layer == L: the LM head; layer > L: past the end
   const uint8_t* base;
-  int32_t idx, hi;
+  int32_t idx, hi, coh;
   const uint8_t* last;
 
   __device__ __forceinline__ void next_entry() {
@@ -419,6 +448,7 @@ struct Issuer {
         base = s.base + (s.kind == kSegWeight ? layer * wstride : (s.kind == kSegKV ? layer * kvstride : 0));
         idx = s.lo;
         hi = s.hi;
+        coh = s.coh;
         return;
       }
       next_entry();
@@ -428,12 +458,15 @@ struct Issuer {
   // so that every slot is always covered by exactly one load in flight.
   __device__ __forceinline__ void issue(uint32_t slot_addr) {
     const uint8_t* a = last;
+    bool c = false;
     if (layer <= L) {
       a = base + (int64_t)idx * kPacketBytes;
+      c = idx >= coh;
       last = a;
       if (++idx == hi) { next_entry(); load(); }
     }
-    dma_packet(a + lane_id() * 16, slot_addr);
+    if (c) dma_packet_coherent(a + lane_id() * 16, slot_addr);
+    else dma_packet(a + lane_id() * 16, slot_addr);
   }
 };
 
@@ -680,10 +713,12 @@ struct Xchg {
   __amdgpu_buffer_rsrc_t llr;
   Smem<RING>& sm;
 
+  // Give up on this launch: record why, and name it (by its tag base) in the abort word, which
+  // only the workgroups of this launch compare against. A later launch runs normally.
   __device__ __forceinline__ void fail(uint32_t bit) {
     if (lane_id() == 0) {
       __hip_atomic_fetch_or(P.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(P.abortf, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(P.abortf, P.tag0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     sm.abort_flag = 1;
   }
@@ -721,8 +756,9 @@ struct Xchg {
         if (__all(ok)) break;
         if (!started) { t0 = now_ticks(); started = true; }
         if ((spin & 15) == 15) {
-          if (now_ticks() - t0 > kSpinTicks) { fail(kStatusTimeout); dead = true; break; }
-          if (ld_flag(P.abortf) || sm.abort_flag) { sm.abort_flag = 1; dead = true; break; }
+          if (now_ticks() - t0 > P.spin_ticks) { fail(kStatusTimeout); dead = true; break; }
+          if (ld_flag(P.cancel)) { fail(kStatusCancelled); dead = true; break; }
+          if (ld_flag(P.abortf) == P.tag0 || sm.abort_flag) { sm.abort_flag = 1; dead = true; break; }
         }
       }
       if (dead) break;
@@ -847,23 +883,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   const int wave = wave_id();
   const int lane = lane_id();
 
-  // inputs of this step; every thread of every workgroup takes the same decision
-  StepInfo si{};
-  const int32_t token = P.tokens[0];
-  si.p = P.positions[0];
-  if (token < 0 || token >= m.V || si.p < 0 || si.p >= P.max_seq) {
+  // inputs of the launch; every thread of every workgroup takes the same decision
+  const int32_t token0 = P.tokens[0];
+  const int32_t p0 = P.positions[0];
+  if (token0 < 0 || token0 >= m.V || p0 < 0 || p0 >= P.max_seq) {
     if (w == 0 && tid == 0) {
-      uint32_t bit = (token < 0 || token >= m.V) ? kStatusTokenRange : 0u;
-      if (si.p < 0 || si.p >= P.max_seq) bit |= kStatusPosOverflow;
+      uint32_t bit = (token0 < 0 || token0 >= m.V) ? kStatusTokenRange : 0u;
+      if (p0 < 0 || p0 >= P.max_seq) bit |= kStatusPosOverflow;
       __hip_atomic_fetch_or(P.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
-  si.ap = att_plan(m, si.p);
-  si.nunits = w < si.ap.units ? c_div(si.ap.units - w, m.nwg) : 0;
-  const int mfirst = m.nwg - 1 - w;  // merge units are dealt from the last workgroup down
-  const int nmerge_here = mfirst < si.ap.nmerge ? c_div(si.ap.nmerge - mfirst, m.nwg) : 0;
-  const int oseg = seg_o(si.nunits);
+  // a launch of several steps appends positions p0, p0 + 1, ... and reads them back in later steps
+  const int p_new = P.n_steps > 1 ? p0 : P.max_seq;
 
   const int rd0 = drow_lo(m, w), nrd = drow_lo(m, w + 1) - rd0;  // this WG's d rows (O, x ownership)
   const int f0 = ffn_lo32(m, w), nf = ffn_lo32(m, w + 1) - f0;     // this WG's FFN slice
@@ -872,9 +904,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   const int gD = nf / m.vpl;
   const int mc = max_chunks(m);
 
-  // Phase timestamps go to LDS and are copied out at the end of the step: a global store here
-  // would hold up the next memory wait of wave 0 (stores share the in-order vector memory
-  // counter with the loads).
+  // Phase timestamps go to LDS and are copied out at the end of the launch (the last step's): a
+  // global store here would hold up the next memory wait of wave 0 (stores share the in-order
+  // vector memory counter with the loads).
   uint64_t* const tr = P.trace ? P.trace + (int64_t)w * trace_stride(m.L) : nullptr;
   __shared__ uint64_t trl[kTraceMaxSlots];
   const int trn = (int)trace_stride(m.L);
@@ -883,11 +915,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   auto stamp = [&](int slot) {
     if (tr && tid == 0) trl[slot] = now_ticks();
   };
-  stamp(0);
 
-  // ---- setup: segment tables, ring, split tables, RoPE row, embedding row ----
+  // ---- once per launch: the wave split of every tile ----
   if (tid == 0) sm.abort_flag = 0;
-  build_segments(P, si, w, wave, sm);
   if (tid < kTiles) {
     for (int v = 0; v <= kWaves; ++v) {
       int lo, hi;
@@ -898,17 +928,50 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     tile_shape(m, w, tid, T, C);
     for (int v = 0; v < kWaves; ++v) sm.first[tid][v] = C > 0 ? sm.split[tid][v] / C : 0;
   }
+
+  Xchg<RING> xc{P, __builtin_amdgcn_make_buffer_rsrc(P.ll, (short)0, (int)(P.lo.total * 8), 0x00020000), sm};
+  const float inv_sqrt_hd = 1.0f / sqrtf((float)m.hd);
+  const SegEntry* tab = sm.segs[wave];
+  NormFold fold;
+  float r_attn = 1.f, r_ffn = 1.f, r_final = 1.f;  // scales of the folded norms
+  Ring<RING> rg;
+  rg.slots = &sm.ring[wave][0][0];
+  rg.slot_lds = lds_addr_of(&sm.ring[wave][0][0]);
+  int32_t token = token0;
+
+  for (int step = 0; step < P.n_steps; ++step) {
+  const uint32_t tb0 = P.tag0 + (uint32_t)step * tag_stride(m);  // this step's tag base
+  StepInfo si{};
+  si.p = p0 + step;
+  if (step > 0) {
+    if (si.p >= P.max_seq) {  // the cache is full: the launch ends here (same decision everywhere)
+      if (w == 0 && tid == 0) __hip_atomic_fetch_or(P.status, kStatusPosOverflow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      goto drain;
+    }
+    // the previous step's loads have landed and every wave is done with the LDS tables
+    wait_vm<0>();
+    wg_barrier();
+    token = sm.next_token;
+  }
+  stamp(0);
+  si.ap = att_plan(m, si.p);
+  si.nunits = w < si.ap.units ? c_div(si.ap.units - w, m.nwg) : 0;
+  {
+  const int mfirst = m.nwg - 1 - w;  // merge units are dealt from the last workgroup down
+  const int nmerge_here = mfirst < si.ap.nmerge ? c_div(si.ap.nmerge - mfirst, m.nwg) : 0;
+  const int oseg = seg_o(si.nunits);
+
+  // ---- setup of the step: segment tables, ring, RoPE row, embedding row, cancel word ----
+  if (tid == 0) sm.cancel = ld_flag(P.cancel);
+  build_segments(P, si, w, wave, sm, p_new);
   for (int i = tid; i < m.hd / 2; i += kThreads) {
     const float2 cs = P.rope[(int64_t)si.p * (m.hd / 2) + i];
     sm.rope_c[i] = cs.x;
     sm.rope_s[i] = cs.y;
   }
   for (int i = tid; i < m.d; i += kThreads) sm.act[i] = load_w<WB>(P.embed, (int64_t)token * m.d + i);
-  wg_barrier();  // segment tables visible
+  wg_barrier();  // segment tables and the cancel word visible
 
-  Ring<RING> rg;
-  rg.slots = &sm.ring[wave][0][0];
-  rg.slot_lds = lds_addr_of(&sm.ring[wave][0][0]);
   rg.cnt = 0;
   rg.is.tab = sm.segs[wave];
   rg.is.lm = &sm.lm_seg[wave];
@@ -921,12 +984,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   rg.is.last = P.blob;
   rg.is.load();
   for (int s = 0; s < RING; ++s) rg.is.issue(rg.slot_lds + s * kPacketBytes);
-
-  Xchg<RING> xc{P, __builtin_amdgcn_make_buffer_rsrc(P.ll, (short)0, (int)(P.lo.total * 8), 0x00020000), sm};
-  const float inv_sqrt_hd = 1.0f / sqrtf((float)m.hd);
-  const SegEntry* tab = sm.segs[wave];
-  NormFold fold;
-  float r_attn = 1.f, r_ffn = 1.f, r_final = 1.f;  // scales of the folded norms
+  if (sm.cancel) {  // cancelled before the step began: leave through the drain like a failed wait
+    if (tid == 0) {
+      __hip_atomic_fetch_or(P.status, kStatusCancelled, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(P.abortf, P.tag0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    goto drain;
+  }
   stamp(1);
 
   for (int layer = 0; layer < m.L; ++layer) {
@@ -945,7 +1009,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         }
       };
       if (layer > 0) {
-        if (!xc.gather(ll_tag(m, P.seq, layer - 1, kX), m.d / 2, [&](int k) -> int64_t { return P.lo.x + 2 * (int64_t)k; },
+        if (!xc.gather(ll_tag(tb0, layer - 1, kX), m.d / 2, [&](int k) -> int64_t { return P.lo.x + 2 * (int64_t)k; },
                        put_x, [&] { fold.finish(sm); }))
           goto drain;
       } else {
@@ -967,7 +1031,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     wg_barrier();
     stamp(trace_slot(layer, 2));
     if (tid < nq)
-      ll_store(P.ll, P.lo.qkv + rq0 + tid, row_total(sm, kTileQKV, m.cd, tid) * r_attn, ll_tag(m, P.seq, layer, kQKV));
+      ll_store(P.ll, P.lo.qkv + rq0 + tid, row_total(sm, kTileQKV, m.cd, tid) * r_attn, ll_tag(tb0, layer, kQKV));
     stamp(trace_slot(layer, 3));
     // ---- attention units: one chunk of positions of one kv head each ----
     for (int k = 0; k < si.nunits; ++k) {
@@ -978,7 +1042,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       const int64_t voff = P.lo.qkv + m.qdim + m.kvdim + (int64_t)u.g * m.hd;
       const int nqp = G * m.hd / 2, nkp = m.hd / 2;
       const bool ok = xc.gather(
-          ll_tag(m, P.seq, layer, kQKV), nqp + 2 * nkp,
+          ll_tag(tb0, layer, kQKV), nqp + 2 * nkp,
           [&](int k2) -> int64_t {
             return k2 < nqp ? qoff + 2 * k2 : (k2 < nqp + nkp ? koff + 2 * (k2 - nqp) : voff + 2 * (k2 - nqp - nkp));
           },
@@ -1015,27 +1079,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         if (tid < m.hd) {
           const int i = tid;
           float kk = sm.u.att.kp[i], vv = sm.u.att.vp[i];
-          const int64_t kh = (((int64_t)layer * 2 + 0) * m.hkv + u.g) * m.S + si.p;
-          const int64_t vh = (((int64_t)layer * 2 + 1) * m.hkv + u.g) * m.S + si.p;
           if constexpr (KB == 2) {
-            const uint32_t kb = bf16_rne_bits(kk), vb = bf16_rne_bits(vv);
-            kk = __uint_as_float(kb << 16);
-            vv = __uint_as_float(vb << 16);
-            if (u.last) {
-              ((uint16_t*)P.kv)[kh * m.hd + i] = (uint16_t)kb;
-              ((uint16_t*)P.kv)[vh * m.hd + i] = (uint16_t)vb;
-            }
-          } else {
-            if (u.last) {
-              ((float*)P.kv)[kh * m.hd + i] = kk;
-              ((float*)P.kv)[vh * m.hd + i] = vv;
-            }
+            kk = __uint_as_float(bf16_rne_bits(kk) << 16);
+            vv = __uint_as_float(bf16_rne_bits(vv) << 16);
           }
           sm.u.att.kp[i] = kk;
           sm.u.att.vp[i] = vv;
         }
         wg_barrier();
         if (k == 0) stamp(trace_slot(layer, 6));
+        if (u.last) {
+          // append K and V at position p as 32-bit words with device-scope stores, so a later step
+          // of the same launch reads them on another compute unit (coherent loads, see Issuer)
+          constexpr int EPW = 4 / KB;  // cache elements per word
+          const int nw = m.hd / EPW;
+          if (tid < 2 * nw) {
+            const int kvs = tid / nw, j = tid - kvs * nw;  // slot 0: K, 1: V
+            const float* src = kvs ? sm.u.att.vp : sm.u.att.kp;
+            uint32_t word;
+            if constexpr (KB == 2) word = (__float_as_uint(src[2 * j]) >> 16) | (__float_as_uint(src[2 * j + 1]) & 0xffff0000u);
+            else word = __float_as_uint(src[j]);
+            const int64_t row = (((int64_t)layer * 2 + kvs) * m.hkv + u.g) * m.S + si.p;
+            __hip_atomic_store((uint32_t*)(P.kv + row * m.hd * KB) + j, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
       }
       // score of the current position (last chunk only), one wave per query head
       if (u.last && wave < G) {
@@ -1075,7 +1142,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
           Lsum += e;
           acc = fmaf(e, sm.u.att.vp[i], acc);
         }
-        const uint32_t tag = ll_tag(m, P.seq, layer, kATTP);
+        const uint32_t tag = ll_tag(tb0, layer, kATTP);
         const int hq = u.g * G + h;
         const int64_t at = P.lo.attp + ((int64_t)hq * mc + u.c) * (m.hd + 2);
         ll_store(P.ll, at + 2 + i, acc, tag);
@@ -1103,7 +1170,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       const int64_t head_at = P.lo.attp + (int64_t)hq * mc * (m.hd + 2);
       float* st = sm.u.stage;  // [NC][2 + MS]
       const bool ok = xc.gather(
-          ll_tag(m, P.seq, layer, kATTP), NC * ppc,
+          ll_tag(tb0, layer, kATTP), NC * ppc,
           [&](int k2) -> int64_t {
             const int c = k2 / ppc, t = k2 - c * ppc;
             const int64_t cb = head_at + (int64_t)c * (m.hd + 2);
@@ -1130,7 +1197,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         }
         Ls = wave_sum(Ls);
         const float invL = 1.0f / Ls;
-        const uint32_t tag = ll_tag(m, P.seq, layer, kO);
+        const uint32_t tag = ll_tag(tb0, layer, kO);
         if (MS >= 8 && MS <= 64) {
           // lane = (chunk group cg, element i): cg sums chunks cg, cg + CG, ...; then a fixed
           // butterfly over the chunk groups (lanes i + MS, i + 2 MS, ...)
@@ -1155,7 +1222,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     }
     stamp(trace_slot(layer, 12));
     // ---- output projection rows + residual ----
-    if (!xc.gather_vec(ll_tag(m, P.seq, layer, kO), P.lo.o, m.qdim, sm.act)) goto drain;
+    if (!xc.gather_vec(ll_tag(tb0, layer, kO), P.lo.o, m.qdim, sm.act)) goto drain;
     stamp(trace_slot(layer, 13));
     consume_rows<RING, WB>(rg, tab[oseg], m.cq, sm.act, sm.rowpart[wave]);
     wg_barrier();
@@ -1163,13 +1230,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     if (tid < nrd) {
       const float xp = sm.xo[tid] + row_total(sm, kTileO, m.cq, tid);
       sm.xo[tid] = xp;
-      ll_store(P.ll, P.lo.xp + rd0 + tid, xp, ll_tag(m, P.seq, layer, kXP));
+      ll_store(P.ll, P.lo.xp + rd0 + tid, xp, ll_tag(tb0, layer, kXP));
     }
     stamp(trace_slot(layer, 15));
     // ---- gate/up rows of this workgroup's FFN slice ----
     load_piece_gains<WB>(g_ffn, m.d, fold.g);
     fold.ss = 0.f;
-    if (!xc.gather(ll_tag(m, P.seq, layer, kXP), m.d / 2, [&](int k) -> int64_t { return P.lo.xp + 2 * (int64_t)k; },
+    if (!xc.gather(ll_tag(tb0, layer, kXP), m.d / 2, [&](int k) -> int64_t { return P.lo.xp + 2 * (int64_t)k; },
                    [&](int k, float a, float b) { fold.put(sm.act, k, a, b); }, [&] { fold.finish(sm); }))
       goto drain;
     r_ffn = norm_scale(sm, m.d, P.eps);
@@ -1186,7 +1253,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     wg_barrier();
     stamp(trace_slot(layer, 19));
     // ---- down projection of the slice, for all d rows, published block by block ----
-    consume_down<RING, WB>(rg, tab[oseg + 2], gD, sm.a, P.ll, P.lo.dp + (int64_t)w * m.d, ll_tag(m, P.seq, layer, kDP));
+    consume_down<RING, WB>(rg, tab[oseg + 2], gD, sm.a, P.ll, P.lo.dp + (int64_t)w * m.d, ll_tag(tb0, layer, kDP));
     stamp(trace_slot(layer, 20));
     // ---- sum every slice's contribution to this workgroup's rows; residual add ----
     {
@@ -1194,7 +1261,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       const int hp = nrd / 2;  // pieces per producer
       const bool ok = nrd == 0 ||
                       xc.gather(
-                          ll_tag(m, P.seq, layer, kDP), m.nwg * hp,
+                          ll_tag(tb0, layer, kDP), m.nwg * hp,
                           [&](int k2) -> int64_t {
                             const int q = k2 / hp, j = k2 - q * hp;
                             return P.lo.dp + (int64_t)q * m.d + rd0 + 2 * j;
@@ -1218,13 +1285,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         else if (T == 32) s = xsum16(sum_rows16(s));
         else if (T == 16) s = sum_rows16(s);
         else s = sum_rows8(s);
-        if (j == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(m, P.seq, layer, kX));
+        if (j == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(tb0, layer, kX));
       } else {
         for (int r = wave; r < nrd; r += kWaves) {
           float s = 0.f;
           for (int q = lane; q < m.nwg; q += 64) s += st[r * m.nwg + q];
           s = wave_sum(s);
-          if (lane == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(m, P.seq, layer, kX));
+          if (lane == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(tb0, layer, kX));
         }
       }
       // no barrier: the staging area is next written after the next layer's x gather, which
@@ -1236,7 +1303,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   // ---- final norm, LM head rows, argmax ----
   load_piece_gains<WB>(P.norms + (int64_t)m.L * 2 * m.d * m.wbytes, m.d, fold.g);
   fold.ss = 0.f;
-  if (!xc.gather(ll_tag(m, P.seq, m.L - 1, kX), m.d / 2, [&](int k) -> int64_t { return P.lo.x + 2 * (int64_t)k; },
+  if (!xc.gather(ll_tag(tb0, m.L - 1, kX), m.d / 2, [&](int k) -> int64_t { return P.lo.x + 2 * (int64_t)k; },
                  [&](int k, float a, float b) { fold.put(sm.act, k, a, b); }, [&] { fold.finish(sm); }))
     goto drain;
   r_final = norm_scale(sm, m.d, P.eps);
@@ -1250,7 +1317,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     bool nan = false;
     for (int r = tid; r < nl; r += kThreads) {
       const float val = row_total(sm, kTileLM, m.cd, r) * r_final;
-      if (P.logits) P.logits[rl0 + r] = val;
+      if (P.logits) P.logits[(int64_t)step * m.V + rl0 + r] = val;
       if (val != val) { nan = true; continue; }
       if (better(val, rl0 + r, best, besti)) { best = val; besti = rl0 + r; }
     }
@@ -1264,19 +1331,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     if (tid == 0) {
       for (int v = 1; v < kWaves; ++v)
         if (better(sm.red[v], sm.redi[v], best, besti)) { best = sm.red[v]; besti = sm.redi[v]; }
-      const uint32_t tag = ll_tag(m, P.seq, m.L, kLM);
+      const uint32_t tag = ll_tag(tb0, m.L, kLM);
       ll_store_bits(P.ll, P.lo.lm + 2 * w, __float_as_uint(best), tag);
       ll_store_bits(P.ll, P.lo.lm + 2 * w + 1, (uint32_t)besti, tag);
     }
   }
   stamp(trace_slot(m.L, 2));
-  if (w == 0) {
-    const bool ok = xc.gather(ll_tag(m, P.seq, m.L, kLM), m.nwg, [&](int k) -> int64_t { return P.lo.lm + 2 * (int64_t)k; },
+  // Workgroup 0 writes the step's outputs. When another step follows, every workgroup takes the
+  // argmax itself (the same bits from the same words), so the next token needs no further hop.
+  if (w == 0 || step + 1 < P.n_steps) {
+    const bool ok = xc.gather(ll_tag(tb0, m.L, kLM), m.nwg, [&](int k) -> int64_t { return P.lo.lm + 2 * (int64_t)k; },
                               [&](int k, float a, float b) {
                                 sm.u.stage[2 * k] = a;
                                 sm.u.stage[2 * k + 1] = b;
                               });
-    if (!ok || ld_flag(P.abortf)) goto drain;
+    // (every workgroup's LM words are in, so none of them gave up: the decision is uniform)
+    if (!ok) goto drain;
     if (wave == 0) {
       float best = -INFINITY;
       int32_t besti = 0x7fffffff;
@@ -1287,12 +1357,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       }
       wave_argmax(best, besti);
       if (lane == 0) {
-        P.tokens[0] = besti == 0x7fffffff ? 0 : besti;
-        P.positions[0] = si.p + 1;
+        const int32_t next = besti == 0x7fffffff ? 0 : besti;
+        sm.next_token = next;  // read after the barrier that opens the next step
+        if (w == 0 && !P.progress) {
+          P.tokens[0] = next;
+          P.positions[0] = si.p + 1;
+          if (P.out_tokens) P.out_tokens[step] = next;
+        } else if (w == 0) {
+          // outputs written through to memory and complete before the count that announces them
+          __hip_atomic_store(P.tokens, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          __hip_atomic_store(P.positions, si.p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          if (P.out_tokens) __hip_atomic_store(P.out_tokens + step, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          wait_vm<0>();
+          __hip_atomic_store(P.progress, (uint32_t)(step + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
       }
     }
     stamp(trace_slot(m.L, 3));
   }
+  }  // the step's plan
+  }  // steps
 drain:
   wait_vm<0>();
   if (tr) {

@@ -158,9 +158,11 @@ KD_HD int64_t trace_stride(int L) { return 2 + (int64_t)kTraceLayerEvents * L + 
 constexpr int kTraceMaxLayers = 40;  // step tracing covers models of up to this many layers
 constexpr int kTraceMaxSlots = 2 + kTraceLayerEvents * kTraceMaxLayers + 4;
 
-// Tag of vector `kind` of layer `layer` (layer == L for the LM head) in step `seq`.
-KD_HD uint32_t ll_tag(const Dims& m, uint32_t seq, int layer, int kind) {
-  return seq * (uint32_t)(8 * (m.L + 1)) + (uint32_t)(8 * layer + kind);
-}
+// Tags one step uses: 8 per layer plus 8 for the LM head. A call of n steps takes the n * stride
+// tags from its base; the host never hands out a range that wraps past zero (tag 0 is what a
+// cleared word holds, so it never names a live vector).
+KD_HD uint32_t tag_stride(const Dims& m) { return (uint32_t)(8 * (m.L + 1)); }
+// Tag of vector `kind` of layer `layer` (layer == L for the LM head) in the step whose tags start at `base`.
+KD_HD uint32_t ll_tag(uint32_t base, int layer, int kind) { return base + (uint32_t)(8 * layer + kind); }
 
 }  // namespace kd

@@ -31,6 +31,10 @@ KD_STATUS_TOKEN_RANGE = 0x1
 KD_STATUS_POS_OVERFLOW = 0x2
 KD_STATUS_SYNC_TIMEOUT = 0x4
 KD_STATUS_NAN = 0x8
+KD_STATUS_CANCELLED = 0x10
+
+KD_CTRL_CANCEL = 1
+KD_CTRL_WAIT_LIMIT_US = 2
 
 KD_DTYPE_F32 = 0
 KD_DTYPE_BF16 = 1
@@ -39,6 +43,8 @@ EXPORTS = (
     "kd_init",
     "kd_kv_layout",
     "kd_step",
+    "kd_generate",
+    "kd_control",
     "kd_device_status",
     "kd_destroy",
     "kd_strerror",
@@ -100,6 +106,10 @@ def library() -> ctypes.CDLL:
         lib.kd_kv_layout.restype = ctypes.c_int
         lib.kd_step.argtypes = [ctypes.c_void_p] * 6
         lib.kd_step.restype = ctypes.c_int
+        lib.kd_generate.argtypes = [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 7
+        lib.kd_generate.restype = ctypes.c_int
+        lib.kd_control.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]
+        lib.kd_control.restype = ctypes.c_int
         lib.kd_device_status.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
         lib.kd_device_status.restype = ctypes.c_int
         lib.kd_destroy.argtypes = [ctypes.c_void_p]
@@ -176,6 +186,21 @@ def kd_step(handle: int, tokens, positions, kv, logits=None, stream=None) -> Non
     )
 
 
+def kd_generate(handle: int, n_steps: int, tokens, positions, kv, out_tokens=None, logits=None, progress=None,
+                stream=None) -> None:
+    """Enqueue n_steps greedy decode steps in one call (device buffers as torch tensors or raw pointers)."""
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(
+        library().kd_generate(handle, int(n_steps), _dev_ptr(tokens), _dev_ptr(positions), _dev_ptr(kv),
+                              _dev_ptr(out_tokens), _dev_ptr(logits), _dev_ptr(progress), s),
+        "kd_generate",
+    )
+
+
+def kd_control(handle: int, op: int, value: int) -> None:
+    _check(library().kd_control(handle, int(op), int(value)), "kd_control")
+
+
 def kd_device_status(handle: int, clear: bool = False) -> int:
     bits = ctypes.c_uint32()
     _check(library().kd_device_status(handle, ctypes.byref(bits), int(bool(clear))), "kd_device_status")
@@ -241,6 +266,13 @@ class Decoder:
     def step(self, write_logits: bool = True, stream=None) -> None:
         kd_step(self.handle, self.tokens, self.positions, self.kv, self.logits if write_logits else None,
                 stream if stream is not None else self.torch.cuda.current_stream(self.device))
+
+    def generate(self, n_steps: int, out_tokens=None, logits=None, progress=None, stream=None) -> None:
+        kd_generate(self.handle, n_steps, self.tokens, self.positions, self.kv, out_tokens, logits, progress,
+                    stream if stream is not None else self.torch.cuda.current_stream(self.device))
+
+    def control(self, op: int, value: int) -> None:
+        kd_control(self.handle, op, value)
 
     def status(self, clear: bool = False) -> int:
         return kd_device_status(self.handle, clear)

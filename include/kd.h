@@ -52,10 +52,18 @@ extern "C" {
 #define KD_ERR_LAUNCH (-6)      /* the kernel launch was rejected by the HIP runtime */
 
 /* ---- sticky device status bits (kd_device_status) ------------------------ */
-#define KD_STATUS_TOKEN_RANGE 0x1u     /* an input token was outside [0, vocab): that step wrote nothing */
-#define KD_STATUS_POS_OVERFLOW 0x2u    /* a position was outside [0, max_seq): that step wrote nothing */
-#define KD_STATUS_SYNC_TIMEOUT 0x4u    /* an inter-workgroup wait timed out; the step was abandoned */
-#define KD_STATUS_NAN 0x8u             /* a NaN reached the logits; the argmax skipped it */
+#define KD_STATUS_TOKEN_RANGE 0x1u  /* an input token was outside [0, vocab): that call wrote nothing */
+#define KD_STATUS_POS_OVERFLOW 0x2u /* a position was outside [0, max_seq): the call wrote nothing for it
+                                       (kd_generate: it stopped at the step that would overflow) */
+#define KD_STATUS_SYNC_TIMEOUT 0x4u /* batch 1: a wait for another workgroup ran past the wait limit; that
+                                       call was abandoned (later calls run normally) */
+#define KD_STATUS_NAN 0x8u          /* a NaN reached the logits; the argmax skipped it */
+#define KD_STATUS_CANCELLED 0x10u   /* the cancel word was set (kd_control): the call was abandoned */
+
+/* ---- kd_control operations ---------------------------------------------- */
+#define KD_CTRL_CANCEL 1        /* value != 0 sets the handle's cancel word, 0 clears it */
+#define KD_CTRL_WAIT_LIMIT_US 2 /* batch 1: longest wait for another workgroup, in microseconds
+                                   (0 .. 60e6; default 2e6) */
 
 /* ---- number formats ---------------------------------------------------------- */
 #define KD_DTYPE_F32 0  /* IEEE binary32 */
@@ -121,43 +129,113 @@ typedef struct kd_handle kd_handle;
 
 /*
  * Validate cfg, pack the weights into library-owned device memory on the
- * current HIP device, and allocate every buffer a step needs.
- * Host memory in w may be freed as soon as kd_init returns; it is only read.
- * Synchronous. On success *out receives the handle. On error it returns a
- * negative code, leaves *out NULL and keeps no device memory.
+ * current HIP device, and allocate every buffer a step needs. The schedule and
+ * every address are fixed here, before the first step, so no step plans or
+ * allocates anything ("Why is real-time AI inference 56x more expensive?",
+ * section "decide everything ahead of time").
+ *   cfg  host, read only: the model and run configuration (see kd_config).
+ *   w    host, read only: canonical row-major weights in cfg->weight_dtype. They
+ *        may be freed as soon as kd_init returns.
+ *   out  host: receives the handle, which the library owns until kd_destroy.
+ * Synchronous. Returns KD_OK, or KD_ERR_INVALID_ARG (NULL pointer, inconsistent
+ * cfg), KD_ERR_UNSUPPORTED (a shape or GPU this library does not handle),
+ * KD_ERR_NO_DEVICE, KD_ERR_OOM or KD_ERR_HIP; on error *out stays NULL and no
+ * device memory is kept.
  */
 int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out);
 
 /*
- * Layout of the caller-owned KV cache for cfg.  The cache is one device buffer
- * of kv_dtype values indexed [layer][slot][session][kv_head][position][dim]:
- *   slot 0 holds K after RoPE, slot 1 holds V.
- * strides[0..5] receive the element strides of those six indices (dim stride is 1);
- * the position extent is max_seq + 7 rounded up to a multiple of 16.  *bytes receives the
- * buffer size.  Host-only computation, no device needed.
+ * Layout of the caller-owned KV cache for cfg. A session's cache is allocated
+ * once for its whole length and stays in place for the session: it is read at
+ * every step and cannot be freed or moved out between steps ("17k tokens/sec"
+ * page, best practice 3 on pre-allocated contiguous KV memory; "Why is real-time
+ * AI inference 56x more expensive?", section "why it is so expensive").
+ * The cache is one device buffer of kv_dtype values indexed
+ * [layer][slot][session][kv_head][position][dim]: slot 0 holds K after RoPE,
+ * slot 1 holds V.
+ *   cfg      host, read only.
+ *   bytes    host: receives the buffer size in bytes.
+ *   strides  host array of 6: receives the element strides of the six indices (dim stride
+ *            is 1); the position extent is max_seq + 7 rounded up to a multiple of 16.
+ * Host-only computation, no device needed. Returns KD_OK or KD_ERR_INVALID_ARG.
  */
 int kd_kv_layout(const kd_config* cfg, size_t* bytes, size_t strides[6]);
 
 /*
  * Enqueue one decode step on `stream` (a hipStream_t; NULL = the null stream) and return.
+ * The whole step runs on the GPU with no host round trip between operations: per step the
+ * host only hands over the input and takes the output ("Why is real-time AI inference 56x
+ * more expensive?", section "keep the work resident on the GPU"; "Real-time LLM inference
+ * on standard data-centre GPUs (3,000 tokens/s single request)", section "technical
+ * principles": one resident kernel, no launch or kernel-boundary gaps).
  *   tokens    device int32[batch], in/out: read as this step's input ids, overwritten with the
- *             greedy next ids.
+ *             greedy next ids (lowest index on ties).
  *   positions device int32[batch], in/out: read as the position p of each input token (the
  *             step attends over cached positions 0..p and writes K,V at p), then incremented.
  *   kv        device buffer laid out as kd_kv_layout reports; read and written.
  *   logits    device float[batch, vocab] written with this step's logits, or NULL to skip.
- * No allocation, no synchronisation and no host<->device copy happen here.  Device-detected
- * input errors set sticky status bits (kd_device_status) and leave outputs unchanged.
+ * All four are caller-owned. No allocation, no synchronisation and no host<->device copy
+ * happen here. Returns KD_OK, KD_ERR_INVALID_ARG (NULL handle or buffer), KD_ERR_HIP or
+ * KD_ERR_LAUNCH. Device-detected errors set sticky status bits (kd_device_status):
+ * invalid input leaves every output unchanged; a timed-out or cancelled step stops where it
+ * was (tokens and positions unchanged, logits possibly in part). Each call is its own: the
+ * next one runs normally.
+ * Batch 1 launches one workgroup per compute unit and relies on all of them being resident
+ * together (each needs most of a CU's local memory, so on an otherwise idle GPU they are).
+ * If another kernel holds compute units, the waits between workgroups end at the wait limit
+ * (KD_CTRL_WAIT_LIMIT_US) with KD_STATUS_SYNC_TIMEOUT instead of hanging.
  */
 int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* logits, void* stream);
 
-/* Read (and optionally clear) the sticky KD_STATUS_* bits.  Synchronises with the device. */
+/*
+ * Run n_steps greedy decode steps as one persistent launch (batch 1) and return: each step is
+ * fed the token the step before chose, on the device, and the workgroups stay resident from
+ * one step to the next; the host only takes the output ("Why is real-time AI inference 56x
+ * more expensive?", section "keep the work resident on the GPU": the program stays on the
+ * GPU and its threads do not exit between ticks). For batch > 1 the n_steps ticks' kernel
+ * sequences are enqueued back to back on the stream, with the same device-side feedback.
+ *   tokens, positions, kv  as for kd_step; after the call they hold the last step's next
+ *             tokens and positions + n_steps.
+ *   out_tokens device int32[n_steps][batch], or NULL: the greedy token of every step.
+ *   logits    device float[n_steps][batch][vocab], or NULL: the logits of every step.
+ *   progress  device (or host-pinned, device-visible) uint32, or NULL: set to the number of
+ *             completed steps after each step, written through to memory after that step's
+ *             outputs, so the host can poll it while the call runs.
+ * Same errors and ownership as kd_step, plus KD_ERR_INVALID_ARG for n_steps < 1. A step
+ * whose position would reach max_seq is not run (KD_STATUS_POS_OVERFLOW); a timed-out or
+ * cancelled step ends the call (the outputs of earlier steps stay).
+ */
+int kd_generate(kd_handle* h, int32_t n_steps, int32_t* tokens, int32_t* positions, void* kv, int32_t* out_tokens,
+                float* logits, uint32_t* progress, void* stream);
+
+/*
+ * Read (and optionally clear) the sticky KD_STATUS_* bits. Synchronises with the device.
+ * A late or abandoned step must be visible to the caller, not hidden in an average
+ * ("Why is real-time AI inference 56x more expensive?", section "why it is so expensive":
+ * tokens/s and mean latency can look fine while one session stutters).
+ *   bits   host: receives the bits.   clear  nonzero: reset them to 0 afterwards.
+ * Returns KD_OK, KD_ERR_INVALID_ARG or KD_ERR_HIP. The caller's current device is kept.
+ */
 int kd_device_status(kd_handle* h, uint32_t* bits, int clear);
 
-/* Free everything the library owns. NULL is accepted. Caller buffers are never touched. */
+/*
+ * Host controls of a handle (no passage of the pages defines these; they are this library's
+ * failure handling).
+ *   KD_CTRL_CANCEL         value != 0 sets the cancel word: a call that starts while it is set,
+ *                          or that is waiting on another workgroup when it is set, stops with
+ *                          KD_STATUS_CANCELLED. value 0 clears it. Synchronous; may be called
+ *                          while a call runs on another stream (it uses a stream of its own).
+ *   KD_CTRL_WAIT_LIMIT_US  batch 1: longest wait for another workgroup before the call gives up
+ *                          with KD_STATUS_SYNC_TIMEOUT; applies to later calls.
+ * Returns KD_OK, KD_ERR_INVALID_ARG (unknown op, value out of range) or KD_ERR_HIP.
+ */
+int kd_control(kd_handle* h, int32_t op, int64_t value);
+
+/* Free everything the library owns. NULL is accepted. Caller buffers are never touched.
+ * Synchronises with the device. (No passage of the pages defines teardown.) */
 void kd_destroy(kd_handle* h);
 
-/* Static description of a status code. */
+/* Static description of a status code. (No passage of the pages defines it.) */
 const char* kd_strerror(int code);
 
 /*
