@@ -23,12 +23,38 @@
 namespace {
 
 constexpr int kRing = 13;
-constexpr uint64_t kDefaultSpinTicks = 200000000ull;  // 2 s of the 100 MHz realtime counter
+constexpr uint32_t kDefaultSpinUs = 2000000;  // 2 s
 constexpr int kFlagStatus = 0, kFlagAbort = 1, kFlagSkip = 2, kFlagCancel = 3;
 
 // Zero n 64-bit words (a kernel rather than a memset, so that a captured graph replays it reliably).
 __global__ void clear_words_kernel(uint64_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// ---- plain stream read, the measured ceiling the decode kernels are compared with ---------------
+// Workgroup b reads its own contiguous run of `per` 16-byte pieces, eight 4 KB rows of the run per
+// iteration (each row one coalesced 16-byte load per thread), with non-temporal loads; the pieces
+// past the last full run are swept grid-wide. The pieces are folded together and the fold is handed
+// to an empty asm statement, so the compiler must keep every load. (On MI355X this shape read
+// 7.1 TB/s over 4 GiB, against 6.2-7.0 TB/s for a grid-stride sweep.)
+constexpr int kStreamU = 8;
+constexpr int kStreamGrid = 8192;
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, int64_t per, int64_t n) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* q = (const u32x4*)p + (int64_t)blockIdx.x * per + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int64_t it = 0; it < per; it += kStreamU * 256) {
+    u32x4 v[kStreamU];
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) v[u] = __builtin_nontemporal_load(q + it + u * 256);
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) acc ^= v[u];
+  }
+  const u32x4* r = (const u32x4*)p;
+  for (int64_t i = (int64_t)gridDim.x * per + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    acc ^= __builtin_nontemporal_load(r + i);
+  asm volatile("" ::"v"(acc.x ^ acc.y ^ acc.z ^ acc.w));
 }
 
 struct Buffers {
@@ -52,11 +78,12 @@ void free_buffers(Buffers& b) {
 
 typedef void (*KernelFn)(kd::Params);
 
-KernelFn pick_kernel(int wbytes, int hd) {
-  if (wbytes == 2 && hd == 128) return kd::decode_step_kernel<kRing, 2, 2, 128>;
-  if (wbytes == 2 && hd == 64) return kd::decode_step_kernel<kRing, 2, 2, 64>;
-  if (wbytes == 4 && hd == 128) return kd::decode_step_kernel<kRing, 4, 4, 128>;
-  if (wbytes == 4 && hd == 64) return kd::decode_step_kernel<kRing, 4, 4, 64>;
+// The one-step kernel, or (multi) the kernel that may run several steps per launch.
+KernelFn pick_kernel(int wbytes, int hd, bool multi) {
+  if (wbytes == 2 && hd == 128) return multi ? kd::decode_step_kernel<kRing, 2, 2, 128, true> : kd::decode_step_kernel<kRing, 2, 2, 128, false>;
+  if (wbytes == 2 && hd == 64) return multi ? kd::decode_step_kernel<kRing, 2, 2, 64, true> : kd::decode_step_kernel<kRing, 2, 2, 64, false>;
+  if (wbytes == 4 && hd == 128) return multi ? kd::decode_step_kernel<kRing, 4, 4, 128, true> : kd::decode_step_kernel<kRing, 4, 4, 128, false>;
+  if (wbytes == 4 && hd == 64) return multi ? kd::decode_step_kernel<kRing, 4, 4, 64, true> : kd::decode_step_kernel<kRing, 4, 4, 64, false>;
   return nullptr;
 }
 
@@ -68,9 +95,10 @@ struct kd_handle {
   kd::Dims m{};
   kd::LLLayout lo{};
   Buffers buf;
-  KernelFn kernel = nullptr;
+  KernelFn kernel = nullptr;        // one step per launch
+  KernelFn kernel_multi = nullptr;  // several steps per launch (kd_generate)
   uint32_t next_tag = 0;  // tag base of the next launch (advances by steps * tag_stride)
-  uint64_t spin_ticks = kDefaultSpinTicks;
+  uint32_t spin_us = kDefaultSpinUs;
   int64_t lds_bytes = 0;
   uint64_t* trace = nullptr;
   hipStream_t ctl = nullptr;  // private non-blocking stream for cancel-word writes
@@ -229,11 +257,13 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
                                    cfg->vocab, cfg->max_seq, nwg, wb, kb);
   rc = check_supported(cfg, m);
   if (rc != KD_OK) return rc;
-  KernelFn kern = pick_kernel(wb, cfg->head_dim);
-  if (!kern) return KD_ERR_UNSUPPORTED;
-  int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, kd::kThreads, 0) != hipSuccess) return KD_ERR_HIP;
-  if (occ < 1) return KD_ERR_UNSUPPORTED;
+  KernelFn kern = pick_kernel(wb, cfg->head_dim, false), kern_multi = pick_kernel(wb, cfg->head_dim, true);
+  if (!kern || !kern_multi) return KD_ERR_UNSUPPORTED;
+  for (KernelFn k : {kern, kern_multi}) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)k, kd::kThreads, 0) != hipSuccess) return KD_ERR_HIP;
+    if (occ < 1) return KD_ERR_UNSUPPORTED;
+  }
   hipFuncAttributes fattr;
   if (hipFuncGetAttributes(&fattr, (const void*)kern) != hipSuccess) return KD_ERR_HIP;
 
@@ -244,6 +274,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
   h->m = m;
   h->lo = kd::ll_layout(m);
   h->kernel = kern;
+  h->kernel_multi = kern_multi;
   h->lds_bytes = (int64_t)fattr.sharedSizeBytes;
   h->next_tag = kd::tag_stride(m);
 
@@ -341,15 +372,11 @@ uint32_t take_tags(uint32_t* next, uint32_t stride, int n, bool* clear) {
   return t;
 }
 
-// Launch n steps of the batch-1 kernel with the exchange words at ll and the abort word at abortf.
-int launch_steps(kd_handle* h, uint64_t* ll, uint32_t* abortf, uint32_t* next_tag, int n, int32_t* tokens,
-                 int32_t* positions, void* kv, float* logits, int32_t* out_tokens, uint32_t* progress, hipStream_t stream) {
-  bool clear = false;
-  const uint32_t tag0 = take_tags(next_tag, kd::tag_stride(h->m), n, &clear);
-  if (clear) {
-    hipLaunchKernelGGL(clear_words_kernel, dim3(256), dim3(256), 0, stream, ll, (int64_t)h->lo.total);
-    if (hipGetLastError() != hipSuccess) return KD_ERR_LAUNCH;
-  }
+// Launch n steps of the batch-1 kernel with the exchange words at ll, the abort word at abortf and
+// tags from tag0 on.
+int launch_steps_at(kd_handle* h, uint64_t* ll, uint32_t* abortf, uint32_t tag0, int n, int32_t* tokens,
+                    int32_t* positions, void* kv, float* logits, int32_t* out_tokens, uint32_t* progress,
+                    hipStream_t stream) {
   kd::Params P{};
   P.blob = h->buf.blob;
   P.embed = h->buf.embed;
@@ -361,13 +388,12 @@ int launch_steps(kd_handle* h, uint64_t* ll, uint32_t* abortf, uint32_t* next_ta
   P.tokens = tokens;
   P.positions = positions;
   P.logits = logits;
-  P.status = h->buf.flags + kFlagStatus;
+  P.flags = h->buf.flags;
   P.abortf = abortf;
-  P.cancel = h->buf.flags + kFlagCancel;
   P.trace = h->trace;
   P.out_tokens = out_tokens;
   P.progress = progress;
-  P.spin_ticks = h->spin_ticks;
+  P.spin_us = h->spin_us;
   P.tag0 = tag0;
   P.n_steps = n;
   P.max_seq = h->cfg.max_seq;
@@ -377,8 +403,22 @@ int launch_steps(kd_handle* h, uint64_t* ll, uint32_t* abortf, uint32_t* next_ta
   // One workgroup per compute unit, and a workgroup needs most of a CU's LDS, so on an idle
   // device the whole grid is resident at once. If another kernel holds CUs, the waits between
   // workgroups time out and the launch ends with KD_STATUS_SYNC_TIMEOUT instead of hanging.
-  const hipError_t e = hipLaunchKernel((const void*)h->kernel, dim3(h->m.nwg), dim3(kd::kThreads), args, 0, stream);
+  const hipError_t e =
+      hipLaunchKernel((const void*)(n > 1 ? h->kernel_multi : h->kernel), dim3(h->m.nwg), dim3(kd::kThreads), args, 0, stream);
   return e == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+// The same with the handle's own exchange words and tag counter.
+int launch_steps(kd_handle* h, int n, int32_t* tokens, int32_t* positions, void* kv, float* logits, int32_t* out_tokens,
+                 uint32_t* progress, hipStream_t stream) {
+  bool clear = false;
+  const uint32_t tag0 = take_tags(&h->next_tag, kd::tag_stride(h->m), n, &clear);
+  if (clear) {
+    hipLaunchKernelGGL(clear_words_kernel, dim3(256), dim3(256), 0, stream, h->buf.ll, (int64_t)h->lo.total);
+    if (hipGetLastError() != hipSuccess) return KD_ERR_LAUNCH;
+  }
+  return launch_steps_at(h, h->buf.ll, h->buf.flags + kFlagAbort, tag0, n, tokens, positions, kv, logits, out_tokens,
+                         progress, stream);
 }
 
 // Makes h's device current for the lifetime of the guard, then restores the caller's.
@@ -405,8 +445,7 @@ int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* 
   if (!g.ok) return KD_ERR_HIP;
   if (h->batched)
     return kd::bt::batch_step(h->bs, tokens, positions, kv, logits, (hipStream_t)stream, h->buf.flags, nullptr, nullptr, 0);
-  return launch_steps(h, h->buf.ll, h->buf.flags + kFlagAbort, &h->next_tag, 1, tokens, positions, kv, logits, nullptr,
-                      nullptr, (hipStream_t)stream);
+  return launch_steps(h, 1, tokens, positions, kv, logits, nullptr, nullptr, (hipStream_t)stream);
 }
 
 int kd_generate(kd_handle* h, int32_t n_steps, int32_t* tokens, int32_t* positions, void* kv, int32_t* out_tokens,
@@ -425,8 +464,7 @@ int kd_generate(kd_handle* h, int32_t n_steps, int32_t* tokens, int32_t* positio
     }
     return KD_OK;
   }
-  return launch_steps(h, h->buf.ll, h->buf.flags + kFlagAbort, &h->next_tag, n_steps, tokens, positions, kv, logits,
-                      out_tokens, progress, (hipStream_t)stream);
+  return launch_steps(h, n_steps, tokens, positions, kv, logits, out_tokens, progress, (hipStream_t)stream);
 }
 
 int kd_control(kd_handle* h, int32_t op, int64_t value) {
@@ -443,7 +481,7 @@ int kd_control(kd_handle* h, int32_t op, int64_t value) {
     }
     case KD_CTRL_WAIT_LIMIT_US:
       if (value < 0 || value > 60000000) return KD_ERR_INVALID_ARG;
-      h->spin_ticks = (uint64_t)value * 100u;  // 100 MHz counter
+      h->spin_us = (uint32_t)value;
       return KD_OK;
     default:
       return KD_ERR_INVALID_ARG;
@@ -472,6 +510,15 @@ void kd_destroy(kd_handle* h) {
     if (h->batched) kd::bt::batch_free(h->bs);
   }
   delete h;
+}
+
+int kd_stream_read(const void* buf, size_t bytes, void* stream) {
+  if (!buf || bytes == 0 || bytes % 16 != 0 || ((uintptr_t)buf & 15u) != 0) return KD_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)(bytes / 16);
+  const int64_t row = (int64_t)kStreamU * 256;
+  const int64_t per = n / kStreamGrid / row * row;  // whole iterations per workgroup; the rest grid-wide
+  hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamGrid), dim3(256), 0, (hipStream_t)stream, (const uint4*)buf, per, n);
+  return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
 
 int kd_trace(kd_handle* h, uint64_t* dev_buf, int64_t words, int64_t* stride) {

@@ -89,11 +89,11 @@ inline bool fused_silu(const BatchState& st) { return st.g_gu.KS == 1; }
 
 typedef void (*AttFn)(const float*, const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, int, int, int, float*,
                       const uint32_t*);
+// G = 3 cannot occur: n_q_heads * 128 would be a multiple of 3, never 256 times a power of two.
 inline AttFn att_for(int G) {
   switch (G) {
     case 1: return attention_kernel<1>;
     case 2: return attention_kernel<2>;
-    case 3: return attention_kernel<3>;
     case 4: return attention_kernel<4>;
     default: return nullptr;
   }
@@ -104,7 +104,7 @@ inline int batch_check(const kd_config* c) {
   if (c->weight_dtype != KD_DTYPE_BF16 || c->kv_dtype != KD_DTYPE_BF16) return KD_ERR_UNSUPPORTED;
   if (c->head_dim != 128) return KD_ERR_UNSUPPORTED;
   const int G = c->n_q_heads / c->n_kv_heads;
-  if (G > kMaxG) return KD_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4) return KD_ERR_UNSUPPORTED;
   const int64_t qdim = (int64_t)c->n_q_heads * c->head_dim, nqkv = qdim + 2LL * c->n_kv_heads * c->head_dim;
   // every GEMM's K must split into ranges of 2, 4, 8, 16 or 32 chunks of 128
   for (int64_t K : {(int64_t)c->d_model, qdim, (int64_t)c->ffn_dim}) {

@@ -57,20 +57,20 @@ struct Params {
   int32_t* tokens;
   int32_t* positions;
   float* logits;
-  uint32_t* status;          // sticky status bits
+  uint32_t* flags;           // [0] sticky status bits, [3] cancel word (nonzero: abandon the call)
   uint32_t* abortf;          // tag base of the last call a workgroup gave up on
-  const uint32_t* cancel;    // nonzero: abandon the call (set by the host between or during calls)
   uint64_t* trace;           // per-workgroup phase timestamps (100 MHz clock), or null
-  int32_t* out_tokens;       // [n_steps] greedy token of every step, or null
-  uint32_t* progress;        // steps completed so far (system-scope store after each step), or null
-  uint64_t spin_ticks;       // longest wait for another workgroup, in 100 MHz ticks
+  int32_t* out_tokens;       // multi-step launches: [n_steps] greedy token of every step, or null
+  uint32_t* progress;        // multi-step launches: steps completed (system-scope store after each), or null
+  uint32_t spin_us;          // longest wait for another workgroup, in microseconds
   uint32_t tag0;             // tag base of step 0; step s uses tag0 + s * tag_stride
-  int32_t n_steps;           // decode steps this launch runs, each fed the previous step's token
+  int32_t n_steps;           // multi-step launches: decode steps, each fed the previous step's token
   int32_t max_seq;
   float eps;
   Dims m;
 };
 
+constexpr int kFlagStatus = 0, kFlagCancel = 3;  // words of Params::flags
 constexpr uint32_t kStatusTokenRange = 0x1u, kStatusPosOverflow = 0x2u, kStatusTimeout = 0x4u, kStatusNaN = 0x8u,
                    kStatusCancelled = 0x10u;
 constexpr int kMaxRowsD = 64;                  // most d rows one workgroup owns
@@ -300,6 +300,20 @@ struct SegEntry {
 };
 constexpr int32_t kNoCoherent = 0x7fffffff;
 
+// A segment entry read from LDS, marked wave-uniform (every lane reads the same entry), so that the
+// loop bounds and packet addresses derived from it stay in scalar registers.
+__device__ __forceinline__ SegEntry uniform(const SegEntry& e) {
+  SegEntry u;
+  const uint64_t b = (uint64_t)(uintptr_t)e.base;
+  const uint32_t lo32 = __builtin_amdgcn_readfirstlane((uint32_t)b), hi32 = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  u.base = (const uint8_t*)(uintptr_t)(((uint64_t)hi32 << 32) | lo32);
+  u.lo = __builtin_amdgcn_readfirstlane(e.lo);
+  u.hi = __builtin_amdgcn_readfirstlane(e.hi);
+  u.kind = __builtin_amdgcn_readfirstlane(e.kind);
+  u.coh = __builtin_amdgcn_readfirstlane(e.coh);
+  return u;
+}
+
 // Per-layer order of a wave's segments: QKV, (K, V) of each attention unit, O, gate/up, down.
 __device__ __forceinline__ int seg_o(int nunits) { return 1 + 2 * nunits; }
 
@@ -423,7 +437,9 @@ __device__ __forceinline__ void build_segments(const Params& P, const StepInfo& 
   put(sm.lm_seg[v], P.blob + (m.off_lm + (int64_t)p_lo(m.V, m.nwg, w) * m.d) * m.wbytes, lo, hi, kSegOnce);
 }
 
-// Walks this wave's packet sequence ahead of the consumer and issues the loads.
+// Walks this wave's packet sequence ahead of the consumer and issues the loads. COH: the launch
+// runs several steps, so packets from a segment's `coh` index on are loaded coherently.
+template <bool COH>
 struct Issuer {
   const SegEntry* tab;
   const SegEntry* lm;
@@ -443,7 +459,7 @@ struct Issuer {
   }
   __device__ __forceinline__ void load() {
     while (layer <= L) {
-      const SegEntry s = layer < L ? tab[e] : *lm;
+      const SegEntry s = uniform(layer < L ? tab[e] : *lm);
       if (s.hi > s.lo) {
         base = s.base + (s.kind == kSegWeight ? layer * wstride : (s.kind == kSegKV ? layer * kvstride : 0));
         idx = s.lo;
@@ -461,22 +477,22 @@ struct Issuer {
     bool c = false;
     if (layer <= L) {
       a = base + (int64_t)idx * kPacketBytes;
-      c = idx >= coh;
+      if constexpr (COH) c = idx >= coh;
       last = a;
       if (++idx == hi) { next_entry(); load(); }
     }
-    if (c) dma_packet_coherent(a + lane_id() * 16, slot_addr);
+    if (COH && c) dma_packet_coherent(a + lane_id() * 16, slot_addr);
     else dma_packet(a + lane_id() * 16, slot_addr);
   }
 };
 
 // Consumer side of the ring: take the next packet (waiting for its load), then give the slot back.
-template <int RING>
+template <int RING, bool COH>
 struct Ring {
   const uint4* slots;  // this wave's RING x 64 x 16 bytes
   uint32_t slot_lds;   // LDS address of slot 0
   uint32_t cnt;
-  Issuer is;
+  Issuer<COH> is;
   __device__ __forceinline__ uint4 take() const {
     // RING loads were issued after the oldest one's slot was last refilled, minus nothing: any
     // other memory operation issued since only makes this wait longer, never shorter.
@@ -529,10 +545,10 @@ __device__ __forceinline__ void unpack16(const uint4 w, float* out) {
 // Row-split matrix-vector product over packets [s.lo, s.hi): packets are row chunks of 64*vpl
 // values; act is the input vector. A row's lane sums are reduced across the wave when the row (or
 // this wave's share of it) ends; part[r - first row] receives the wave's sum.
-template <int RING, int WB>
+template <int RING, int WB, bool COH>
 // (The segment is taken by value: a copy in registers is not reloaded from LDS after every
 // LDS-DMA refill, whose asm clobbers memory.)
-__device__ __forceinline__ void consume_rows(Ring<RING>& rg, const SegEntry s, int C, const float* act, float* part) {
+__device__ __forceinline__ void consume_rows(Ring<RING, COH>& rg, const SegEntry s, int C, const float* act, float* part) {
   constexpr int VPL = 16 / WB;
   const int lane = lane_id();
   int r = s.lo / C;
@@ -556,8 +572,8 @@ __device__ __forceinline__ void consume_rows(Ring<RING>& rg, const SegEntry s, i
 // Down projection of this WG's FFN slice over the wave's whole 64-row blocks: packets hold 64 rows
 // x vpl columns; lane l owns row 64*b + l, and all lanes read the same slice values. Each finished
 // block is published at once as 64 contiguous exchange words.
-template <int RING, int WB>
-__device__ __forceinline__ void consume_down(Ring<RING>& rg, const SegEntry s, int g, const float* a, uint64_t* ll,
+template <int RING, int WB, bool COH>
+__device__ __forceinline__ void consume_down(Ring<RING, COH>& rg, const SegEntry s, int g, const float* a, uint64_t* ll,
                                              int64_t dp_at, uint32_t tag) {
   constexpr int VPL = 16 / WB;
   const int lane = lane_id();
@@ -596,8 +612,8 @@ __device__ __forceinline__ float halve16(float x, float y) {
 // Branch-free: all kMaxGroup head slots are computed (slots h >= G get q = 0 and are never read
 // back), and positions past the unit's end are masked by selects, so the LDS reads of a packet
 // are issued together rather than one per branch.
-template <int RING, int KB, int HD>
-__device__ __forceinline__ void consume_attention(Ring<RING>& rg, const SegEntry sk, const Unit& u, int G, Smem<RING>& sm,
+template <int RING, int KB, int HD, bool COH>
+__device__ __forceinline__ void consume_attention(Ring<RING, COH>& rg, const SegEntry sk, const Unit& u, int G, Smem<RING>& sm,
                                                   int v, float* accv) {
   constexpr int KVPL = 16 / KB;
   constexpr int LPP = HD / KVPL;
@@ -717,7 +733,7 @@ struct Xchg {
   // only the workgroups of this launch compare against. A later launch runs normally.
   __device__ __forceinline__ void fail(uint32_t bit) {
     if (lane_id() == 0) {
-      __hip_atomic_fetch_or(P.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(P.flags + kFlagStatus, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(P.abortf, P.tag0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     sm.abort_flag = 1;
@@ -756,8 +772,8 @@ struct Xchg {
         if (__all(ok)) break;
         if (!started) { t0 = now_ticks(); started = true; }
         if ((spin & 15) == 15) {
-          if (now_ticks() - t0 > P.spin_ticks) { fail(kStatusTimeout); dead = true; break; }
-          if (ld_flag(P.cancel)) { fail(kStatusCancelled); dead = true; break; }
+          if (now_ticks() - t0 > (uint64_t)P.spin_us * 100u) { fail(kStatusTimeout); dead = true; break; }
+          if (ld_flag(P.flags + kFlagCancel)) { fail(kStatusCancelled); dead = true; break; }
           if (ld_flag(P.abortf) == P.tag0 || sm.abort_flag) { sm.abort_flag = 1; dead = true; break; }
         }
       }
@@ -770,7 +786,8 @@ struct Xchg {
     }
     fin();
     wg_barrier();
-    return sm.abort_flag == 0;
+    // the same LDS word for every lane: say so, so that the branch on it stays uniform
+    return __builtin_amdgcn_readfirstlane(sm.abort_flag) == 0;
   }
 
   // Gather n consecutive exchange words (n even) starting at word `at` into dst[0..n).
@@ -872,7 +889,9 @@ __device__ __forceinline__ int trace_slot(int layer, int ev) { return 2 + kTrace
 // Every wave executes the same sequence of workgroup barriers. A failed wait sets the LDS abort
 // flag before the barrier that ends its gather; all waves test the flag right after that barrier
 // and leave together, after their LDS-DMA loads have landed.
-template <int RING, int WB, int KB, int HD>
+// MULTI: the launch may run several steps (kd_generate); without it the kernel runs exactly one,
+// with no step loop and no coherent-load choice in the streaming loops.
+template <int RING, int WB, int KB, int HD, bool MULTI>
 __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P_arg) {
   __shared__ Smem<RING> sm;
   // work on a private copy: references into the kernel-argument segment would force a stack copy
@@ -890,12 +909,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     if (w == 0 && tid == 0) {
       uint32_t bit = (token0 < 0 || token0 >= m.V) ? kStatusTokenRange : 0u;
       if (p0 < 0 || p0 >= P.max_seq) bit |= kStatusPosOverflow;
-      __hip_atomic_fetch_or(P.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(P.flags + kFlagStatus, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
   // a launch of several steps appends positions p0, p0 + 1, ... and reads them back in later steps
-  const int p_new = P.n_steps > 1 ? p0 : P.max_seq;
+  const int n_steps = MULTI ? P.n_steps : 1;
+  const int p_new = n_steps > 1 ? p0 : P.max_seq;
 
   const int rd0 = drow_lo(m, w), nrd = drow_lo(m, w + 1) - rd0;  // this WG's d rows (O, x ownership)
   const int f0 = ffn_lo32(m, w), nf = ffn_lo32(m, w + 1) - f0;     // this WG's FFN slice
@@ -934,24 +954,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   const SegEntry* tab = sm.segs[wave];
   NormFold fold;
   float r_attn = 1.f, r_ffn = 1.f, r_final = 1.f;  // scales of the folded norms
-  Ring<RING> rg;
+  Ring<RING, MULTI> rg;
   rg.slots = &sm.ring[wave][0][0];
   rg.slot_lds = lds_addr_of(&sm.ring[wave][0][0]);
   int32_t token = token0;
 
-  for (int step = 0; step < P.n_steps; ++step) {
+  for (int step = 0; step < n_steps; ++step) {
   const uint32_t tb0 = P.tag0 + (uint32_t)step * tag_stride(m);  // this step's tag base
   StepInfo si{};
   si.p = p0 + step;
   if (step > 0) {
     if (si.p >= P.max_seq) {  // the cache is full: the launch ends here (same decision everywhere)
-      if (w == 0 && tid == 0) __hip_atomic_fetch_or(P.status, kStatusPosOverflow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (w == 0 && tid == 0) __hip_atomic_fetch_or(P.flags + kFlagStatus, kStatusPosOverflow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       goto drain;
     }
     // the previous step's loads have landed and every wave is done with the LDS tables
     wait_vm<0>();
     wg_barrier();
-    token = sm.next_token;
+    token = __builtin_amdgcn_readfirstlane(sm.next_token);
   }
   stamp(0);
   si.ap = att_plan(m, si.p);
@@ -962,7 +982,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   const int oseg = seg_o(si.nunits);
 
   // ---- setup of the step: segment tables, ring, RoPE row, embedding row, cancel word ----
-  if (tid == 0) sm.cancel = ld_flag(P.cancel);
+  if (tid == 0) sm.cancel = ld_flag(P.flags + kFlagCancel);
   build_segments(P, si, w, wave, sm, p_new);
   for (int i = tid; i < m.hd / 2; i += kThreads) {
     const float2 cs = P.rope[(int64_t)si.p * (m.hd / 2) + i];
@@ -984,9 +1004,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   rg.is.last = P.blob;
   rg.is.load();
   for (int s = 0; s < RING; ++s) rg.is.issue(rg.slot_lds + s * kPacketBytes);
-  if (sm.cancel) {  // cancelled before the step began: leave through the drain like a failed wait
+  if (__builtin_amdgcn_readfirstlane(sm.cancel)) {  // cancelled before the step began: leave like a failed wait
     if (tid == 0) {
-      __hip_atomic_fetch_or(P.status, kStatusCancelled, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(P.flags + kFlagStatus, kStatusCancelled, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(P.abortf, P.tag0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     goto drain;
@@ -1027,7 +1047,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     stamp(trace_slot(layer, 0));
     stamp(trace_slot(layer, 1));
     // ---- QKV rows ----
-    consume_rows<RING, WB>(rg, tab[0], m.cd, sm.act, sm.rowpart[wave]);
+    consume_rows<RING, WB, MULTI>(rg, uniform(tab[0]), m.cd, sm.act, sm.rowpart[wave]);
     wg_barrier();
     stamp(trace_slot(layer, 2));
     if (tid < nq)
@@ -1111,7 +1131,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         t = wave_sum(t);
         if (lane == 0) sm.u.att.sp[wave] = t;
       }
-      consume_attention<RING, KB, HD>(rg, tab[1 + 2 * k], u, G, sm, wave, sm.act + (int64_t)wave * kMaxGroup * HD);
+      consume_attention<RING, KB, HD, MULTI>(rg, uniform(tab[1 + 2 * k]), u, G, sm, wave, sm.act + (int64_t)wave * kMaxGroup * HD);
       if (k == 0) stamp(trace_slot(layer, 7));
       wg_barrier();
       if (k == 0) stamp(trace_slot(layer, 8));
@@ -1224,7 +1244,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     // ---- output projection rows + residual ----
     if (!xc.gather_vec(ll_tag(tb0, layer, kO), P.lo.o, m.qdim, sm.act)) goto drain;
     stamp(trace_slot(layer, 13));
-    consume_rows<RING, WB>(rg, tab[oseg], m.cq, sm.act, sm.rowpart[wave]);
+    consume_rows<RING, WB, MULTI>(rg, uniform(tab[oseg]), m.cq, sm.act, sm.rowpart[wave]);
     wg_barrier();
     stamp(trace_slot(layer, 14));
     if (tid < nrd) {
@@ -1242,7 +1262,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     r_ffn = norm_scale(sm, m.d, P.eps);
     stamp(trace_slot(layer, 16));
     stamp(trace_slot(layer, 17));
-    consume_rows<RING, WB>(rg, tab[oseg + 1], m.cd, sm.act, sm.rowpart[wave]);
+    consume_rows<RING, WB, MULTI>(rg, uniform(tab[oseg + 1]), m.cd, sm.act, sm.rowpart[wave]);
     wg_barrier();
     stamp(trace_slot(layer, 18));
     if (tid < nf) {
@@ -1253,7 +1273,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     wg_barrier();
     stamp(trace_slot(layer, 19));
     // ---- down projection of the slice, for all d rows, published block by block ----
-    consume_down<RING, WB>(rg, tab[oseg + 2], gD, sm.a, P.ll, P.lo.dp + (int64_t)w * m.d, ll_tag(tb0, layer, kDP));
+    consume_down<RING, WB, MULTI>(rg, uniform(tab[oseg + 2]), gD, sm.a, P.ll, P.lo.dp + (int64_t)w * m.d, ll_tag(tb0, layer, kDP));
     stamp(trace_slot(layer, 20));
     // ---- sum every slice's contribution to this workgroup's rows; residual add ----
     {
@@ -1308,7 +1328,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     goto drain;
   r_final = norm_scale(sm, m.d, P.eps);
   stamp(trace_slot(m.L, 0));
-  consume_rows<RING, WB>(rg, sm.lm_seg[wave], m.cd, sm.act, sm.rowpart[wave]);
+  consume_rows<RING, WB, MULTI>(rg, uniform(sm.lm_seg[wave]), m.cd, sm.act, sm.rowpart[wave]);
   wg_barrier();
   stamp(trace_slot(m.L, 1));
   {
@@ -1322,7 +1342,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       if (better(val, rl0 + r, best, besti)) { best = val; besti = rl0 + r; }
     }
     wave_argmax(best, besti);
-    if (__any(nan) && lane == 0) __hip_atomic_fetch_or(P.status, kStatusNaN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__any(nan) && lane == 0) __hip_atomic_fetch_or(P.flags + kFlagStatus, kStatusNaN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (lane == 0) {
       sm.red[wave] = best;
       sm.redi[wave] = besti;
@@ -1339,7 +1359,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   stamp(trace_slot(m.L, 2));
   // Workgroup 0 writes the step's outputs. When another step follows, every workgroup takes the
   // argmax itself (the same bits from the same words), so the next token needs no further hop.
-  if (w == 0 || step + 1 < P.n_steps) {
+  if (w == 0 || step + 1 < n_steps) {
     const bool ok = xc.gather(ll_tag(tb0, m.L, kLM), m.nwg, [&](int k) -> int64_t { return P.lo.lm + 2 * (int64_t)k; },
                               [&](int k, float a, float b) {
                                 sm.u.stage[2 * k] = a;
@@ -1359,11 +1379,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
       if (lane == 0) {
         const int32_t next = besti == 0x7fffffff ? 0 : besti;
         sm.next_token = next;  // read after the barrier that opens the next step
-        if (w == 0 && !P.progress) {
+        if (w == 0 && (!MULTI || !P.progress)) {
           P.tokens[0] = next;
           P.positions[0] = si.p + 1;
-          if (P.out_tokens) P.out_tokens[step] = next;
-        } else if (w == 0) {
+          if (MULTI && P.out_tokens) P.out_tokens[step] = next;
+        } else if (MULTI && w == 0) {
           // outputs written through to memory and complete before the count that announces them
           __hip_atomic_store(P.tokens, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
           __hip_atomic_store(P.positions, si.p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);

@@ -50,6 +50,7 @@ EXPORTS = (
     "kd_strerror",
     "kd_get_info",
     "kd_trace",
+    "kd_stream_read",
 )
 
 
@@ -120,6 +121,8 @@ def library() -> ctypes.CDLL:
         lib.kd_get_info.restype = ctypes.c_int
         lib.kd_trace.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
         lib.kd_trace.restype = ctypes.c_int
+        lib.kd_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        lib.kd_stream_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -235,6 +238,12 @@ def kd_trace(handle: int, dev_buf=None, words: int = 0) -> int:
     stride = ctypes.c_int64()
     _check(library().kd_trace(handle, _dev_ptr(dev_buf), int(words), ctypes.byref(stride)), "kd_trace")
     return stride.value
+
+
+def kd_stream_read(buf, nbytes: int, stream=None) -> None:
+    """Enqueue one plain read of nbytes of the device buffer (measurement of the HBM read rate)."""
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(library().kd_stream_read(_dev_ptr(buf), int(nbytes), s), "kd_stream_read")
 
 
 class Decoder:

@@ -1,20 +1,24 @@
 """Decode-step benchmark: tokens/s on one MI355X and the fraction of the HBM roofline.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2b|8b|2b_long|tiny|11b_x56]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b|2b|2b_long|tiny|11b_x56]
 
 One "step" is one kd_step: a whole decode step of every session. At batch 1 it is one persistent
 kernel launch; for the 56 lockstep sessions it is one tick, a fixed kernel sequence on one stream.
-The default workload is the 2B-class decoder at batch 1. Its 512-token prompt is fed one token per
-step to fill the KV cache; this is untimed. Pre-filled workloads write the seeded cache contents
-instead. Then W warm-up steps and K timed steps follow, each feeding back the greedy tokens of
-the step before.
+The default workload is the Llama-3-8B-shaped decoder at batch 1, the largest batch-1 workload.
+Its prompt is fed one token per step to fill the KV cache; this is untimed. Pre-filled workloads
+write the seeded cache contents instead. Then W warm-up steps and K timed steps follow, each
+feeding back the greedy tokens of the step before. The same positions are then run once more as
+one kd_generate call (the resident loop), timed as a whole.
 
 Printed on stdout, as one JSON line:
   value          tokens/s over the timed steps (B tokens per step, all sessions), inputs resident in HBM
   roofline       algorithmic bytes per step (every weight, the KV cache over 0..p, the KV write,
                  the logits) divided by the kernel's mean duration. The duration comes from HIP
                  events on the launch stream; the peak is the HBM spec of 8 TB/s.
+  stream_ceiling the read rate of a plain streaming kernel on the same GPU in the same run, and
+                 the decode kernel's achieved rate as a fraction of it
   cpu_baseline   the CPU oracle, run for a bounded number of decode steps on the host cores
+  extra          the 2B batch-1 workload measured the same way in the same run (default run only)
 Everything else goes to stderr.
 """
 
@@ -105,41 +109,177 @@ def nearest_rank(values, q: float) -> float:
     return float(v[max(0, int(np.ceil(q * len(v))) - 1)])
 
 
-def fill_prefilled_cache(wl, dec, torch) -> None:
-    """Write the seeded pre-filled K/V values of every session, one layer at a time."""
-    from concurrent.futures import ThreadPoolExecutor
-
+def measure(wl, args, torch, kd, roofline, steps: int, warmup: int, trace: bool, cpu_steps: int):
+    """Build the decoder of workload wl, fill its cache, time `steps` kd_step calls after `warmup`
+    untimed ones, then the same positions as one kd_generate call. Returns (result dict, decoder,
+    weights, first position, first token); the caller closes the decoder."""
     import workloads
 
     m = wl.model
-    storage = np.uint16 if m.kv_dtype == "bf16" else np.float32
-    view_dtype = torch.int16 if m.kv_dtype == "bf16" else torch.float32
-    host = np.zeros((2, wl.batch, m.n_kv_heads, wl.prefill_len, m.head_dim), storage)
-    kv = dec.kv_view().view(view_dtype)
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    B = wl.batch
+    if warmup + steps > wl.decode_steps:
+        steps = wl.decode_steps - warmup
+        log(f"{wl.name}: steps capped at {steps}: the workload has {wl.decode_steps} decode steps")
+    assert steps > 0
     t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=workers) as pool:
-        for l in range(m.n_layers):
-            def work(job, l=l):
-                s, b, g = job
-                host[s, b, g] = workloads.kv_prefill_block(wl, l, s, b, g)
+    weights = workloads.make_weights(m, seed=wl.weight_seed)
+    log(f"{wl.name}: weights generated in {time.perf_counter() - t0:.1f} s")
+    dec = kd.Decoder(m, weights, max_seq=wl.max_seq, batch=B, device="cuda:0")
+    info = kd.kd_get_info(dec.handle)
+    log(f"{wl.name}: kd_init done: {info}")
+    stream = torch.cuda.current_stream()
 
-            list(pool.map(work, [(s, b, g) for s in range(2) for b in range(wl.batch) for g in range(m.n_kv_heads)]))
-            kv[l, :, :, :, : wl.prefill_len] = torch.from_numpy(host.view(np.int16 if m.kv_dtype == "bf16" else np.float32))
-            if (l + 1) % 8 == 0 or l + 1 == m.n_layers:
-                log(f"pre-filled cache: {l + 1}/{m.n_layers} layers ({time.perf_counter() - t0:.1f} s)")
+    # fill the KV cache: the prompt fed one token per step, or the seeded pre-filled values
+    if wl.prefill_len > 0:
+        view_dtype = torch.int16 if m.kv_dtype == "bf16" else torch.float32
+        workloads.fill_kv_prefill_device(wl, dec.kv_view().view(view_dtype), torch, log=log)
+        dec.tokens.copy_(torch.from_numpy(workloads.make_first_tokens(wl)))
+        dec.positions.fill_(wl.prefill_len)
+    else:
+        prompt = torch.as_tensor(workloads.make_prompt(wl, 0), device=dec.device)
+        dec.positions.zero_()
+        for p in range(wl.prompt_len):
+            dec.tokens.copy_(prompt[p : p + 1])
+            dec.step(write_logits=False)
+    torch.cuda.synchronize()
+    if dec.status():
+        raise RuntimeError(f"{wl.name}: device status {dec.status():#x} after prefill")
+
+    for _ in range(warmup):
+        dec.step()
+    torch.cuda.synchronize()
+    first_pos = int(dec.positions[0].item())
+    first_token = int(dec.tokens[0].item())
+    tokens0, positions0 = dec.tokens.clone(), dec.positions.clone()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    whole0, whole1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    whole0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        dec.step(stream=stream)
+        ev[i][1].record(stream)
+    whole1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    status = dec.status()
+    if status:
+        raise RuntimeError(f"{wl.name}: device status {status:#x} during the timed steps")
+    tokens_steps = dec.tokens.clone()
+
+    elapsed_ms = whole0.elapsed_time(whole1)
+    per_step_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    positions = range(first_pos, first_pos + steps)
+    alg_bytes = np.array([roofline.step_bytes(m, B, p).total for p in positions], np.float64)
+    achieved_gbps = float(alg_bytes.mean() / (per_step_us.mean() * 1e-6) / 1e9)
+    tok_s = steps * B / (elapsed_ms * 1e-3)
+    bound_tok_s = roofline.tokens_per_s_bound(PEAK_HBM_GBPS * 1e9, float(alg_bytes.mean()), B)
+    p99 = nearest_rank(per_step_us, 0.99)
+    log(f"{wl.name}: {steps} steps x {B} sessions in {elapsed_ms:.2f} ms (wall {t_wall * 1e3:.1f} ms): {tok_s:.1f} tok/s, "
+        f"step mean {per_step_us.mean():.1f} us (p50 {np.percentile(per_step_us, 50):.1f}, "
+        f"p99 {p99:.1f}), {achieved_gbps:.0f} GB/s algorithmic, roofline {bound_tok_s:.0f} tok/s")
+
+    # the same positions again, as one resident call (the cache is rewritten with the same values)
+    dec.tokens.copy_(tokens0)
+    dec.positions.copy_(positions0)
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record(stream)
+    dec.generate(steps, stream=stream)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    if dec.status():
+        raise RuntimeError(f"{wl.name}: device status {dec.status():#x} during kd_generate")
+    same = bool(torch.equal(dec.tokens, tokens_steps))
+    gen_ms = g0.elapsed_time(g1)
+    resident = {"tok_s": round(steps * B / (gen_ms * 1e-3), 2), "itl_us_mean": round(gen_ms * 1e3 / steps, 2),
+                "same_tokens_as_kd_step": same}
+    log(f"{wl.name}: kd_generate of the same {steps} steps: {resident}")
+
+    if trace and B == 1:
+        from bandwidth_bound_transformer_amd import trace as tr
+
+        stride = kd.kd_trace(dec.handle, None, 0)
+        buf = torch.zeros(stride * info["workgroups"], dtype=torch.int64, device=dec.device)
+        kd.kd_trace(dec.handle, buf, buf.numel())
+        dec.tokens.copy_(tokens0)
+        dec.positions.copy_(positions0)
+        for _ in range(3):
+            dec.step()
+        torch.cuda.synchronize()
+        kd.kd_trace(dec.handle, None, 0)
+        raw = buf.cpu().numpy()
+        log("phase breakdown of one traced step:\n" + tr.summary(raw, m.n_layers, info["workgroups"]))
+        log(tr.critical_path(raw, m.n_layers, info["workgroups"]))
+        if args.trace_out:
+            np.save(args.trace_out, raw)
+        if args.trace_json:
+            with open(args.trace_json, "w") as f:
+                json.dump(tr.to_chrome_trace(raw, m.n_layers, info["workgroups"]), f)
+
+    cpu = None
+    if cpu_steps > 0:
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline(wl, weights, dec, torch, cpu_steps, args.cpu_seconds, first_pos, first_token)
+        log(f"cpu oracle: {cpu['value']:.3f} tok/s on {cpu['cores']} threads")
+
+    res = {
+        "workload": wl.name,
+        "tok_s": tok_s,
+        "steps": steps,
+        "elapsed_ms": elapsed_ms,
+        "per_step_us": per_step_us,
+        "alg_bytes": float(alg_bytes.mean()),
+        "achieved_gbps": achieved_gbps,
+        "bound_tok_s": bound_tok_s,
+        "p99_us": p99,
+        "first_pos": first_pos,
+        "resident": resident,
+        "cpu": cpu,
+    }
+    del weights
+    return res, dec
+
+
+def stream_ceiling(torch, kd, gib: int = 4, reps: int = 10) -> float:
+    """Read rate (GB/s) of the library's plain streaming kernel over a gib GiB buffer."""
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        kd.kd_stream_read(buf, nbytes, stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        kd.kd_stream_read(buf, nbytes, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    gbps = reps * nbytes / (a.elapsed_time(b) * 1e-3) / 1e9
+    del buf
+    log(f"stream ceiling: {gbps:.0f} GB/s reading {gib} GiB")
+    return gbps
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="2b", choices=["tiny", "2b", "8b", "2b_long", "11b_x56"])
+    ap.add_argument("--workload", default="8b", choices=["tiny", "2b", "8b", "2b_long", "11b_x56"])
+    ap.add_argument("--extra", default=None,
+                    help="comma-separated workloads measured after the headline one and reported under 'extra' "
+                         "(default: 2b when the headline is the default 8b, else none; 'none' for none)")
+    ap.add_argument("--extra-steps", type=int, default=500, help="timed steps of each extra workload")
+    ap.add_argument("--tick-budget-ms", type=float, default=160.0,
+                    help="lockstep sessions: a tick longer than this misses its deadline (the pages' 160 ms tick)")
     ap.add_argument("--cpu-steps", type=int, default=30,
                     help="most oracle decode steps (of one session) timed for cpu_baseline; 0 skips it")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="cpu_baseline stops stepping the oracle once this much time has passed")
+    ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the plain stream-read measurement")
     ap.add_argument("--trace", action="store_true", help="after timing, trace one step and print its phase breakdown")
     ap.add_argument("--trace-out", default=None, help="with --trace: also save the raw timestamp buffer (.npy)")
     ap.add_argument("--trace-json", default=None,
@@ -163,15 +303,6 @@ def main() -> int:
     wl = workloads.get(args.workload)
     m = wl.model
     B = wl.batch
-    decode_steps = wl.decode_steps
-    if args.warmup + args.steps > decode_steps:
-        args.steps = decode_steps - args.warmup
-        log(f"steps capped at {args.steps}: the workload has {decode_steps} decode steps")
-    assert args.steps > 0
-
-    t0 = time.perf_counter()
-    weights = workloads.make_weights(m, seed=wl.weight_seed)
-    log(f"weights generated in {time.perf_counter() - t0:.1f} s")
     torch.cuda.set_device(0)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -182,130 +313,109 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"calibration copy: {n} bytes read, {n} bytes written")
         del src, dst
-    dec = kd.Decoder(m, weights, max_seq=wl.max_seq, batch=B, device="cuda:0")
-    info = kd.kd_get_info(dec.handle)
-    log(f"kd_init done: {info}")
-    stream = torch.cuda.current_stream()
 
-    # fill the KV cache: the prompt fed one token per step, or the seeded pre-filled values
-    if wl.prefill_len > 0:
-        fill_prefilled_cache(wl, dec, torch)
-        dec.tokens.copy_(torch.from_numpy(workloads.make_first_tokens(wl)))
-        dec.positions.fill_(wl.prefill_len)
-    else:
-        prompt = torch.as_tensor(workloads.make_prompt(wl, 0), device=dec.device)
-        dec.positions.zero_()
-        for p in range(wl.prompt_len):
-            dec.tokens.copy_(prompt[p : p + 1])
-            dec.step(write_logits=False)
-    torch.cuda.synchronize()
-    if dec.status():
-        log(f"device status {dec.status():#x} after prefill")
+    try:
+        r, dec = measure(wl, args, torch, kd, roofline, args.steps, args.warmup, args.trace, args.cpu_steps)
+    except RuntimeError as e:
+        log(str(e))
         return 1
+    dec.close()
+    del dec
+    torch.cuda.empty_cache()
 
-    for _ in range(args.warmup):
-        dec.step()
-    torch.cuda.synchronize()
-    first_pos = int(dec.positions[0].item())
-    first_token = int(dec.tokens[0].item())
+    extra_names = args.extra
+    if extra_names is None:
+        extra_names = "2b" if args.workload == "8b" else "none"
+    extra = {}
+    for name in [n for n in extra_names.split(",") if n and n != "none"]:
+        try:
+            e, d2 = measure(workloads.get(name), args, torch, kd, roofline, args.extra_steps, args.warmup, False, 0)
+        except RuntimeError as err:
+            log(str(err))
+            return 1
+        d2.close()
+        del d2
+        torch.cuda.empty_cache()
+        extra[name] = {
+            "value": round(e["tok_s"], 2),
+            "unit": "tok/s",
+            "steps": e["steps"],
+            "ms_per_step": round(e["elapsed_ms"] / e["steps"], 4),
+            "positions": [e["first_pos"], e["first_pos"] + e["steps"] - 1],
+            "roofline_frac": round(e["achieved_gbps"] / PEAK_HBM_GBPS, 4),
+            "achieved_gbps": round(e["achieved_gbps"], 1),
+            "frac_of_roofline_tok_s": round(e["tok_s"] / e["bound_tok_s"], 4),
+            "roofline_tok_s": round(e["bound_tok_s"], 1),
+            "itl_us": {"p50": round(float(np.percentile(e["per_step_us"], 50)), 2),
+                       "p99": round(nearest_rank(e["per_step_us"], 0.99), 2)},
+            "resident": e["resident"],
+            "traffic": measured_traffic(name, KERNEL_SOURCES if workloads.get(name).batch == 1 else BATCH_SOURCES),
+        }
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    whole0, whole1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    whole0.record(stream)
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        dec.step(stream=stream)
-        ev[i][1].record(stream)
-    whole1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    status = dec.status()
-    if status:
-        log(f"device status {status:#x} during the timed steps")
-        return 1
-
-    elapsed_ms = whole0.elapsed_time(whole1)
-    per_step_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-    positions = range(first_pos, first_pos + args.steps)
-    alg_bytes = np.array([roofline.step_bytes(m, B, p).total for p in positions], np.float64)
-    achieved_gbps = float(alg_bytes.mean() / (per_step_us.mean() * 1e-6) / 1e9)
-    tok_s = args.steps * B / (elapsed_ms * 1e-3)
-    bound_tok_s = roofline.tokens_per_s_bound(PEAK_HBM_GBPS * 1e9, float(alg_bytes.mean()), B)
-    p99 = nearest_rank(per_step_us, 0.99)
-    log(f"{args.steps} steps x {B} sessions in {elapsed_ms:.2f} ms (wall {t_wall * 1e3:.1f} ms): {tok_s:.1f} tok/s, "
-        f"step mean {per_step_us.mean():.1f} us (p50 {np.percentile(per_step_us, 50):.1f}, "
-        f"p99 {p99:.1f}), {achieved_gbps:.0f} GB/s algorithmic, roofline {bound_tok_s:.0f} tok/s")
-
-    if args.trace and B == 1:
-        from bandwidth_bound_transformer_amd import trace as tr
-
-        stride = kd.kd_trace(dec.handle, None, 0)
-        buf = torch.zeros(stride * info["workgroups"], dtype=torch.int64, device=dec.device)
-        kd.kd_trace(dec.handle, buf, buf.numel())
-        for _ in range(3):
-            dec.step()
-        torch.cuda.synchronize()
-        kd.kd_trace(dec.handle, None, 0)
-        raw = buf.cpu().numpy()
-        log("phase breakdown of one traced step:\n" + tr.summary(raw, m.n_layers, info["workgroups"]))
-        log(tr.critical_path(raw, m.n_layers, info["workgroups"]))
-        if args.trace_out:
-            np.save(args.trace_out, raw)
-        if args.trace_json:
-            with open(args.trace_json, "w") as f:
-                json.dump(tr.to_chrome_trace(raw, m.n_layers, info["workgroups"]), f)
-
-    cpu = None
-    if args.cpu_steps > 0:
-        log("timing the CPU oracle ...")
-        cpu = cpu_baseline(wl, weights, dec, torch, args.cpu_steps, args.cpu_seconds, first_pos, first_token)
-        log(f"cpu oracle: {cpu['value']:.3f} tok/s on {cpu['cores']} threads")
-
+    ceiling = None if args.no_stream_ceiling else stream_ceiling(torch, kd)
+    per_step_us = r["per_step_us"]
     traffic = measured_traffic(wl.name, KERNEL_SOURCES if B == 1 else BATCH_SOURCES)
     out = {
         "metric": METRIC if B == 1 else METRIC_SESSIONS,
-        "value": round(tok_s, 2),
+        "value": round(r["tok_s"], 2),
         "unit": "tok/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": r["steps"],
         "warmup": args.warmup,
-        "ms_per_step": round(elapsed_ms / args.steps, 4),
+        "ms_per_step": round(r["elapsed_ms"] / r["steps"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # arithmetic: fp32 FMAs on bf16 weights at batch 1; bf16 (hi/lo) matrix-core products otherwise
+        "dtype": "f32" if B == 1 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": wl.name,
             "description": wl.description,
             "layers": m.n_layers, "d_model": m.d_model, "q_heads": m.n_q_heads, "kv_heads": m.n_kv_heads,
             "head_dim": m.head_dim, "ffn": m.ffn_dim, "vocab": m.vocab, "weight_dtype": m.weight_dtype,
-            "kv_dtype": m.kv_dtype, "batch": B, "positions": [first_pos, first_pos + args.steps - 1],
+            "kv_dtype": m.kv_dtype, "batch": B, "positions": [r["first_pos"], r["first_pos"] + r["steps"] - 1],
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
             "bound": "hbm",
-            "achieved": round(achieved_gbps, 1),
+            "achieved": round(r["achieved_gbps"], 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
-            "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4),
+            "frac": round(r["achieved_gbps"] / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
             "kernel": "decode_step_kernel" if B == 1 else "one tick (the kd_step kernel sequence)",
-            "algorithmic_bytes_per_launch": round(float(alg_bytes.mean())),
+            "algorithmic_bytes_per_launch": round(r["alg_bytes"]),
             "kernel_mean_us": round(float(per_step_us.mean()), 2),
         },
-        "roofline_tok_s": round(bound_tok_s, 1),
-        "frac_of_roofline_tok_s": round(tok_s / bound_tok_s, 4),
-        "itl_us": {"p50": round(float(np.percentile(per_step_us, 50)), 2), "p99": round(p99, 2)},
-        "cpu_baseline": cpu,
+        "stream_ceiling": None if ceiling is None else {
+            "achieved_gbps": round(ceiling, 1),
+            "frac_of_stream_ceiling": round(r["achieved_gbps"] / ceiling, 4),
+            "kernel": "stream_read_kernel (kd_stream_read, 4 GiB, 16-byte non-temporal loads)",
+        },
+        "roofline_tok_s": round(r["bound_tok_s"], 1),
+        "frac_of_roofline_tok_s": round(r["tok_s"] / r["bound_tok_s"], 4),
+        "itl_us": {"p50": round(float(np.percentile(per_step_us, 50)), 2), "p99": round(r["p99_us"], 2)},
+        "resident": r["resident"],
+        "cpu_baseline": r["cpu"],
+        "extra": extra or None,
     }
+    if ceiling is not None:
+        for e in extra.values():
+            e["frac_of_stream_ceiling"] = round(e["achieved_gbps"] / ceiling, 4)
     if B > 1:
-        out["tick_latency_ms"] = {"p50": round(float(np.percentile(per_step_us, 50)) / 1e3, 4), "p99": round(p99 / 1e3, 4),
+        budget_us = args.tick_budget_ms * 1e3
+        med = float(np.percentile(per_step_us, 50))
+        out["tick_latency_ms"] = {"p50": round(med / 1e3, 4), "p99": round(r["p99_us"] / 1e3, 4),
                                   "max": round(float(per_step_us.max()) / 1e3, 4)}
+        out["deadline"] = {
+            "budget_ms": args.tick_budget_ms,
+            "ticks": int(len(per_step_us)),
+            "missed_ticks": int(np.sum(per_step_us > budget_us)),
+            "missed_session_ticks": int(np.sum(per_step_us > budget_us)) * B,
+            "ticks_over_1.1x_median": int(np.sum(per_step_us > 1.1 * med)),
+        }
     print(json.dumps(out), flush=True)
-    dec.close()
     return 0
 
 

@@ -81,7 +81,7 @@ extern "C" {
  *   batch        sessions stepped together in lockstep. batch == 1 runs the single persistent
  *                kernel. 2 <= batch <= 64 runs the lockstep-sessions path: the projections become
  *                small-M GEMMs on the matrix cores. That path needs bf16 weights and cache,
- *                head_dim 128, d_model one of 256, 512, 1024, 2048 or 4096, n_q_heads*head_dim
+ *                head_dim 128, G of 1, 2 or 4, d_model one of 256, 512, 1024, 2048 or 4096, n_q_heads*head_dim
  *                and ffn_dim each 256 times a power of two, and d_model, 2*ffn_dim,
  *                (n_q_heads+2*n_kv_heads)*head_dim and vocab multiples of 128.
  *   norm_eps     RMSNorm epsilon (inside the square root).
@@ -250,6 +250,15 @@ const char* kd_strerror(int code);
  * Returns KD_ERR_INVALID_ARG if the buffer is too small.
  */
 int kd_trace(kd_handle* h, uint64_t* dev_buf, int64_t words, int64_t* stride);
+
+/*
+ * Measurement aid (no passage of the pages defines it): enqueue one plain read of `bytes` bytes
+ * of device memory at buf (16-byte aligned, a multiple of 16 bytes) on `stream`, with 16-byte
+ * non-temporal loads over the whole GPU, and return. Timed by the caller, it gives the
+ * sustained read rate of this GPU's HBM that the decode kernels are compared with.
+ * Returns KD_OK, KD_ERR_INVALID_ARG or KD_ERR_LAUNCH.
+ */
+int kd_stream_read(const void* buf, size_t bytes, void* stream);
 
 /*
  * Facts about an initialised handle (for measurement and tests).

@@ -90,6 +90,7 @@ def test_null_arguments_rejected():
     assert lib.kd_init(ctypes.byref(cfg), None, None) == kd.KD_ERR_INVALID_ARG
     assert lib.kd_init(ctypes.byref(cfg), None, ctypes.byref(h)) == kd.KD_ERR_INVALID_ARG
     assert lib.kd_step(None, None, None, None, None, None) == kd.KD_ERR_INVALID_ARG
+    assert lib.kd_stream_read(None, 1 << 20, None) == kd.KD_ERR_INVALID_ARG
     assert lib.kd_generate(None, 4, None, None, None, None, None, None, None) == kd.KD_ERR_INVALID_ARG
     assert lib.kd_control(None, kd.KD_CTRL_CANCEL, 1) == kd.KD_ERR_INVALID_ARG
     bits = ctypes.c_uint32()

@@ -84,7 +84,9 @@ def _check_tick(gl, g_tok, want, tag):
 
 def test_clone_x56_every_session(torch, kdm):
     """56 sessions, 200 ticks from a 48-position pre-filled cache: logits, tokens, positions and the
-    K/V each tick appends, for every session. Tie-flips may touch at most 1% of the tokens."""
+    K/V each tick appends, for every session. At most 4 of the 11,200 tokens may be tie-flips
+    (2 seen): a flip needs the oracle's top-2 margin within twice the step's measured error, and
+    with hi/lo bf16 activations that error is about 1e-4 of the largest logit."""
     wl = _clone()
     m = wl.model
     w = workloads.make_weights(m, seed=wl.weight_seed)
@@ -110,7 +112,7 @@ def test_clone_x56_every_session(torch, kdm):
             flips += flip
         tok = g_tok.astype(np.int64)
     print(f"clone_x56: max rel logit err {worst:.3e} over {wl.gen_tokens} ticks x {wl.batch} sessions, tie-flips {flips}")
-    assert flips <= max(2, wl.gen_tokens * wl.batch // 100)
+    assert flips <= 4
     assert dec.status() == 0
     assert np.all(dec.positions.cpu().numpy() == wl.prefill_len + wl.gen_tokens)
     # the appended positions hold K (after RoPE) and V as the oracle stored them
@@ -165,23 +167,24 @@ def test_clone_x56_bad_input_writes_nothing(torch, kdm):
 
 
 def test_11b_x56_sampled_sessions(torch, kdm):
-    """The 11B-class decoder at its real shape and launch configuration (56 sessions, KV cache
-    pre-filled to 4096 positions): four ticks, logits and tokens of sessions 0, 27 and 55 against
-    the oracle (which carries only those sessions' caches)."""
+    """The 11B-class decoder at its real shape, launch configuration and full extent: 56 sessions,
+    every cache pre-filled to 4096 positions, 200 ticks. Sessions 0, 27 and 55 are checked
+    against the oracle at ticks 1 and 2 (oracle fed the recipe's pre-filled cache) and at tick 200
+    (oracle started from the GPU's cache after 199 ticks), with the K/V the last tick appends."""
     wl = workloads.get("11b_x56")
     m = wl.model
     w = workloads.make_weights(m, seed=wl.weight_seed)
     print("11b: weights ready", flush=True)
     dec = kdm.Decoder(m, w, max_seq=wl.max_seq, batch=wl.batch)
+    workloads.fill_kv_prefill_device(wl, dec.kv_view().view(torch.int16), torch)
     sessions = [0, 27, 55]
-    _fill_sessions(dec, wl, sessions, torch)
     o = _oracle_with_prefill(wl, w, sessions)
     print("11b: caches filled", flush=True)
     first = workloads.make_first_tokens(wl)
     dec.tokens.copy_(torch.from_numpy(first))
     dec.positions.fill_(wl.prefill_len)
     tok = first.astype(np.int64)
-    for t in range(4):
+    for t in range(2):
         p = wl.prefill_len + t
         dec.step()
         gl = dec.logits.cpu().numpy()
@@ -189,7 +192,34 @@ def test_11b_x56_sampled_sessions(torch, kdm):
         want_all = o.step_sessions(range(len(sessions)), [int(tok[b]) for b in sessions], [p] * len(sessions))
         for i, b in enumerate(sessions):
             err, _ = _check_tick(gl[b], g_tok[b], want_all[i], (t, b))
-            print(f"11b tick {t} session {b}: rel logit err {err:.3e}", flush=True)
+            print(f"11b tick {t + 1} session {b}: rel logit err {err:.3e}", flush=True)
         tok = g_tok.astype(np.int64)
-    assert dec.status() == 0
+    del o
+    for _ in range(wl.gen_tokens - 3):
+        dec.step(write_logits=False)
+    torch.cuda.synchronize()
+    last = wl.prefill_len + wl.gen_tokens - 1
+    assert dec.status() == 0 and bool(torch.all(dec.positions == last))
+    print(f"11b: GPU at tick {wl.gen_tokens} (position {last})", flush=True)
+    o = ref.Oracle(m, w, batch=len(sessions), max_seq=wl.max_seq)
+    kv = dec.kv_view()
+    for i, b in enumerate(sessions):
+        for l in range(m.n_layers):
+            c = kv[l, :, b, :, :last].float().cpu().numpy()
+            for g in range(m.n_kv_heads):
+                o.load_kv(i, l, g, c[0, g], c[1, g])
+    tok = dec.tokens.cpu().numpy().astype(np.int64)
+    dec.step()
+    gl = dec.logits.cpu().numpy()
+    g_tok = dec.tokens.cpu().numpy()
+    want_all = o.step_sessions(range(len(sessions)), [int(tok[b]) for b in sessions], [last] * len(sessions))
+    for i, b in enumerate(sessions):
+        err, _ = _check_tick(gl[b], g_tok[b], want_all[i], (wl.gen_tokens, b))
+        print(f"11b tick {wl.gen_tokens} session {b}: rel logit err {err:.3e}", flush=True)
+        for l in (0, m.n_layers - 1):
+            got = kv[l, :, b, :, last].float().cpu().numpy()
+            for s, ref_cache in ((0, o.k_cache), (1, o.v_cache)):
+                exp = ref_cache[i, l, :, last]
+                assert np.max(np.abs(got[s] - exp)) <= BF16_TOL * np.max(np.abs(exp))
+    assert dec.status() == 0 and bool(torch.all(dec.positions == last + 1))
     dec.close()

@@ -131,13 +131,15 @@ def test_input_errors_set_status_and_write_nothing(torch, kdm, tiny):
 
 
 def test_2b_prompt512_generation(torch, kdm):
-    """2B-class decoder at its real shape: the 512-token prompt, then 8 greedy tokens."""
+    """2B-class decoder at its real shape and full extent: the 512-token prompt, then all 512
+    greedy tokens; every step's logits and token against the oracle's full-sequence recomputation
+    on the GPU's token sequence (teacher-forced), tie-flips counted."""
     wl = workloads.get("2b")
     w = workloads.make_weights(wl.model, seed=wl.weight_seed)
     print("2b: weights ready", flush=True)
     dec = _decoder(kdm, wl, w)
     prompt = workloads.make_prompt(wl, 0)
-    n_gen = 8
+    n_gen = wl.gen_tokens
     toks, logits = gh.run_prompt(dec, prompt, n_gen, torch)
     assert dec.status() == 0
     print("2b: GPU run done; oracle ...", flush=True)
@@ -146,7 +148,8 @@ def test_2b_prompt512_generation(torch, kdm):
     worst, flips, defects = gh.compare_sequence(toks, logits, want, BF16_TOL)
     print(f"2b: max rel logit err {worst:.3e} over {len(seq)} steps, tie-flips {flips}")
     assert worst <= BF16_TOL
-    assert not defects
+    assert not defects and flips <= 2
+    assert int(dec.positions.item()) == wl.prompt_len + wl.gen_tokens - 1
     dec.close()
 
 
@@ -169,12 +172,41 @@ def test_8b_short_prompt(torch, kdm):
     dec.close()
 
 
+def _oracle_from_gpu_cache(m, w, dec, n, max_seq):
+    """An oracle whose cache holds the GPU's cache contents at positions 0..n-1."""
+    o = ref.Oracle(m, w, batch=1, max_seq=max_seq)
+    kv = dec.kv_view()
+    for l in range(m.n_layers):
+        c = kv[l, :, 0, :, :n].float().cpu().numpy()  # [K/V][kv head][position][dim]
+        for g in range(m.n_kv_heads):
+            o.load_kv(0, l, g, c[0, g], c[1, g])
+    return o
+
+
+def _check_steps_from_cache(dec, o, tok, first_pos, n, tag):
+    """Step GPU and oracle n times from the same cache and token; logits, token, appended K/V."""
+    for i in range(n):
+        dec.step()
+        gl = dec.logits[0].cpu().numpy()
+        want = o.step_one(0, tok, first_pos + i)
+        err = gh.inf_rel_err(gl, want)
+        print(f"{tag}: position {first_pos + i}: rel logit err {err:.3e}", flush=True)
+        assert err <= BF16_TOL
+        g_tok = int(dec.tokens.item())
+        if g_tok != int(ref.greedy_token(want[None])[0]):
+            assert gh.top2_margin(want) <= 2 * np.max(np.abs(gl - want))
+        tok = g_tok
+    assert dec.status() == 0
+    return tok
+
+
 def test_8b_full_prompt_sampled_steps(torch, kdm):
-    """Llama-3-8B shape at the benchmark's positions: the 1024-token prompt runs on the GPU, then
-    the steps at positions 1023 and 1024 are checked against the oracle, which starts from the
-    GPU's cache of positions 0..1022 (sampled outputs at full size; the prompt path itself is
-    checked from position 0 by the 2B and short 8B tests). The K/V appended at 1023 and 1024 must
-    match what the oracle stored."""
+    """Llama-3-8B shape at the benchmark's positions and full extent: the 1024-token prompt and all
+    255 decode steps run on the GPU. The steps at positions 1023 and 1024 (the first of the decode)
+    and at 1277 and 1278 (its last two) are checked against the oracle, which starts from the GPU's
+    cache before each pair (sampled outputs at full size; the prompt path itself is checked from
+    position 0 by the 2B and short 8B tests). The K/V appended at those positions must match what
+    the oracle stored."""
     wl = workloads.get("8b")
     m = wl.model
     w = workloads.make_weights(m, seed=wl.weight_seed)
@@ -190,36 +222,34 @@ def test_8b_full_prompt_sampled_steps(torch, kdm):
     torch.cuda.synchronize()
     assert dec.status() == 0 and int(dec.positions.item()) == P - 1
     print(f"8b full: GPU prompt 0..{P - 2} done", flush=True)
-    o = ref.Oracle(m, w, batch=1, max_seq=P + 2)
+    o = _oracle_from_gpu_cache(m, w, dec, P - 1, P + 2)
+    dec.tokens.fill_(int(prompt[P - 1]))
+    tok = _check_steps_from_cache(dec, o, int(prompt[P - 1]), P - 1, 2, "8b full")
     kv = dec.kv_view()
-    for l in range(m.n_layers):
-        c = kv[l, :, 0, :, : P - 1].float().cpu().numpy()  # [K/V][kv head][position][dim]
-        for g in range(m.n_kv_heads):
-            o.load_kv(0, l, g, c[0, g], c[1, g])
-    tok = int(prompt[P - 1])
-    dec.tokens.fill_(tok)
-    for i in range(2):
-        dec.step()
-        gl = dec.logits[0].cpu().numpy()
-        want = o.step_one(0, tok, P - 1 + i)
-        err = gh.inf_rel_err(gl, want)
-        print(f"8b full: position {P - 1 + i}: rel logit err {err:.3e}", flush=True)
-        assert err <= BF16_TOL
-        g_tok = int(dec.tokens.item())
-        if g_tok != int(ref.greedy_token(want[None])[0]):
-            assert gh.top2_margin(want) <= 2 * np.max(np.abs(gl - want))
-        tok = g_tok
-    assert dec.status() == 0
     for l in (0, m.n_layers - 1):
         got = kv[l, :, 0, :, P - 1 : P + 1].float().cpu().numpy()
         for s, ref_cache in ((0, o.k_cache), (1, o.v_cache)):
             exp = ref_cache[0, l, :, P - 1 : P + 1]
             assert np.max(np.abs(got[s] - exp)) <= 2e-2 * np.max(np.abs(exp))
+    del o
+    # the rest of the decode on the GPU, up to the last two positions
+    last = wl.max_seq - 2  # 1277: the decode's steps run at positions 1023 .. 1278
+    while int(dec.positions.item()) < last:
+        dec.step(write_logits=False)
+    torch.cuda.synchronize()
+    assert dec.status() == 0 and int(dec.positions.item()) == last
+    tok = int(dec.tokens.item())
+    print(f"8b full: GPU decode to position {last - 1} done", flush=True)
+    o = _oracle_from_gpu_cache(m, w, dec, last, wl.max_seq)
+    _check_steps_from_cache(dec, o, tok, last, 2, "8b full")
+    assert int(dec.positions.item()) == wl.max_seq
     dec.close()
 
 
 def test_2b_long_context_prefilled(torch, kdm):
-    """2B decoder with the KV cache pre-filled to 32768 positions: two steps from the seeded first token."""
+    """2B decoder with the KV cache pre-filled to 32768 positions, over the workload's full extent:
+    the first two of its 128 steps from the seeded first token, then (after the GPU has run the
+    rest) its last two, each pair against the oracle."""
     wl = workloads.get("2b_long")
     m = wl.model
     w = workloads.make_weights(m, seed=wl.weight_seed)
@@ -255,4 +285,16 @@ def test_2b_long_context_prefilled(torch, kdm):
     for l in (0, m.n_layers - 1):
         got = kv[l, 0, 0, :, wl.prefill_len : wl.prefill_len + 2].float().cpu().numpy()
         assert np.max(np.abs(got - o.k_cache[0, l, :, wl.prefill_len : wl.prefill_len + 2])) <= 2e-2 * np.max(np.abs(got))
+    del o
+    # the rest of the workload's 128 steps on the GPU; its last two against the oracle started
+    # from the GPU's cache (positions 0 .. 32893)
+    last = wl.max_seq - 2
+    while int(dec.positions.item()) < last:
+        dec.step(write_logits=False)
+    torch.cuda.synchronize()
+    assert dec.status() == 0 and int(dec.positions.item()) == last
+    print(f"2b_long: GPU at position {last}", flush=True)
+    o = _oracle_from_gpu_cache(m, w, dec, last, wl.max_seq)
+    _check_steps_from_cache(dec, o, int(dec.tokens.item()), last, 2, "2b_long last")
+    assert int(dec.positions.item()) == wl.max_seq
     dec.close()

@@ -24,6 +24,7 @@ from .gen import (
     make_first_tokens,
     kv_prefill_block,
     fill_kv_prefill,
+    fill_kv_prefill_device,
     bf16_bits_from_f32,
     f32_from_bf16_bits,
 )
@@ -40,6 +41,7 @@ __all__ = [
     "make_first_tokens",
     "kv_prefill_block",
     "fill_kv_prefill",
+    "fill_kv_prefill_device",
     "bf16_bits_from_f32",
     "f32_from_bf16_bits",
 ]

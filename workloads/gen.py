@@ -140,3 +140,32 @@ def fill_kv_prefill(wl: Workload, out: np.ndarray, sessions=None, workers: int |
 
     with ThreadPoolExecutor(max_workers=workers or _workers()) as pool:
         list(pool.map(work, jobs))
+
+
+def fill_kv_prefill_device(wl: Workload, kv_storage_view, torch, sessions=None, log=None) -> None:
+    """Write the pre-filled values of ``sessions`` (default: all) into a device cache.
+
+    ``kv_storage_view`` is the caller's cache viewed [L][2][B][Hkv][S][hd] with the storage's
+    bit patterns (torch.int16 for bf16, torch.float32 for f32). One layer at a time: the blocks
+    are generated on host threads, then copied in one transfer.
+    """
+    m = wl.model
+    sessions = list(range(wl.batch)) if sessions is None else list(sessions)
+    storage = np.uint16 if m.kv_dtype == "bf16" else np.float32
+    host = np.zeros((2, len(sessions), m.n_kv_heads, wl.prefill_len, m.head_dim), storage)
+    jobs = [(s, i, g) for s in range(2) for i in range(len(sessions)) for g in range(m.n_kv_heads)]
+    with ThreadPoolExecutor(max_workers=_workers()) as pool:
+        for l in range(m.n_layers):
+            def work(job, l=l):
+                s, i, g = job
+                host[s, i, g] = kv_prefill_block(wl, l, s, sessions[i], g)
+
+            list(pool.map(work, jobs))
+            src = torch.from_numpy(host.view(np.int16) if m.kv_dtype == "bf16" else host)
+            if sessions == list(range(wl.batch)):
+                kv_storage_view[l, :, :, :, : wl.prefill_len] = src
+            else:
+                for i, b in enumerate(sessions):
+                    kv_storage_view[l, :, b, :, : wl.prefill_len] = src[:, i]
+            if log and ((l + 1) % 8 == 0 or l + 1 == m.n_layers):
+                log(f"pre-filled cache: {l + 1}/{m.n_layers} layers")
