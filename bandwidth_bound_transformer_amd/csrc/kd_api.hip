@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -29,6 +30,34 @@ constexpr int kFlagStatus = 0, kFlagAbort = 1, kFlagSkip = 2, kFlagCancel = 3;
 // Zero n 64-bit words (a kernel rather than a memset, so that a captured graph replays it reliably).
 __global__ void clear_words_kernel(uint64_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// ---- static scratch of kd_step_noalloc ----------------------------------------------------------
+// 16 MiB per GPU, held until the process ends: word 0 is the abort word, the exchange words start
+// at word kScratchHead. Host code never uses the array's name as an address: kd_init resolves the
+// array's device address once per device and keeps it in g_scratch[device].
+constexpr int64_t kScratchWords = (int64_t)2 << 20;
+constexpr int64_t kScratchHead = 32;
+__device__ __align__(256) uint64_t scratch[kScratchWords];
+
+constexpr int kMaxDevices = 64;
+struct StaticScratch {
+  uint64_t* ptr = nullptr;  // device address of `scratch` on this device
+  uint32_t next_tag = 0;    // tag base of the next call on this device (shared by every handle)
+};
+std::mutex g_scratch_mu;
+StaticScratch g_scratch[kMaxDevices];
+
+// With dev current: resolve the array's address once for this device. Returns false on failure.
+bool resolve_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[dev].ptr) return true;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return false;
+  g_scratch[dev].ptr = (uint64_t*)ptr;
+  g_scratch[dev].next_tag = 0;
+  return true;
 }
 
 // ---- plain stream read, the measured ceiling the decode kernels are compared with ---------------
@@ -188,6 +217,7 @@ const char* kd_strerror(int code) {
     case KD_ERR_OOM: return "device memory allocation failed";
     case KD_ERR_HIP: return "HIP runtime call failed";
     case KD_ERR_LAUNCH: return "kernel launch rejected";
+    case KD_ERR_SCRATCH: return "the model needs more exchange memory than the static scratch of kd_step_noalloc holds (16 MiB)";
     default: return "unknown error code";
   }
 }
@@ -292,6 +322,8 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
     KD_TRY(hipMemset(h->buf.ll, 0, (size_t)h->lo.total * 8));
     KD_TRY(hipMemset(h->buf.flags, 0, 256));
     KD_TRY(hipStreamCreateWithFlags(&h->ctl, hipStreamNonBlocking));
+    // kd_step_noalloc's scratch on this device (if this fails, that entry point reports KD_ERR_HIP)
+    (void)resolve_scratch(dev);
     const size_t row = (size_t)d * wb;
     for (int l = 0; l < m.L; ++l) {
       const kd_layer_weights& lw = w->layers[l];
@@ -446,6 +478,32 @@ int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* 
   if (h->batched)
     return kd::bt::batch_step(h->bs, tokens, positions, kv, logits, (hipStream_t)stream, h->buf.flags, nullptr, nullptr, 0);
   return launch_steps(h, 1, tokens, positions, kv, logits, nullptr, nullptr, (hipStream_t)stream);
+}
+
+int kd_step_noalloc(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* logits, void* stream) {
+  if (!h || !tokens || !positions || !kv) return KD_ERR_INVALID_ARG;
+  if (h->batched) return KD_ERR_UNSUPPORTED;
+  if (h->device < 0 || h->device >= kMaxDevices) return KD_ERR_HIP;
+  if (h->lo.total > kScratchWords - kScratchHead) return KD_ERR_SCRATCH;
+  DeviceGuard g(h->device);
+  if (!g.ok) return KD_ERR_HIP;
+  uint64_t* base = nullptr;
+  uint32_t tag0 = 0;
+  bool clear = false;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    base = g_scratch[h->device].ptr;
+    if (!base) return KD_ERR_HIP;
+    uint32_t& next = g_scratch[h->device].next_tag;
+    if (next == 0) next = kd::tag_stride(h->m);
+    tag0 = take_tags(&next, kd::tag_stride(h->m), 1, &clear);
+  }
+  if (clear) {  // the device's tags start over: no word of the array may keep an old tag
+    hipLaunchKernelGGL(clear_words_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream, base, kScratchWords);
+    if (hipGetLastError() != hipSuccess) return KD_ERR_LAUNCH;
+  }
+  return launch_steps_at(h, base + kScratchHead, (uint32_t*)base, tag0, 1, tokens, positions, kv, logits, nullptr, nullptr,
+                         (hipStream_t)stream);
 }
 
 int kd_generate(kd_handle* h, int32_t n_steps, int32_t* tokens, int32_t* positions, void* kv, int32_t* out_tokens,

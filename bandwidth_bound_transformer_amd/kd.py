@@ -26,6 +26,7 @@ KD_ERR_NO_DEVICE = -3
 KD_ERR_OOM = -4
 KD_ERR_HIP = -5
 KD_ERR_LAUNCH = -6
+KD_ERR_SCRATCH = -7
 
 KD_STATUS_TOKEN_RANGE = 0x1
 KD_STATUS_POS_OVERFLOW = 0x2
@@ -43,6 +44,7 @@ EXPORTS = (
     "kd_init",
     "kd_kv_layout",
     "kd_step",
+    "kd_step_noalloc",
     "kd_generate",
     "kd_control",
     "kd_device_status",
@@ -107,6 +109,8 @@ def library() -> ctypes.CDLL:
         lib.kd_kv_layout.restype = ctypes.c_int
         lib.kd_step.argtypes = [ctypes.c_void_p] * 6
         lib.kd_step.restype = ctypes.c_int
+        lib.kd_step_noalloc.argtypes = [ctypes.c_void_p] * 6
+        lib.kd_step_noalloc.restype = ctypes.c_int
         lib.kd_generate.argtypes = [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 7
         lib.kd_generate.restype = ctypes.c_int
         lib.kd_control.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]
@@ -186,6 +190,15 @@ def kd_step(handle: int, tokens, positions, kv, logits=None, stream=None) -> Non
     _check(
         library().kd_step(handle, _dev_ptr(tokens), _dev_ptr(positions), _dev_ptr(kv), _dev_ptr(logits), s),
         "kd_step",
+    )
+
+
+def kd_step_noalloc(handle: int, tokens, positions, kv, logits=None, stream=None) -> None:
+    """kd_step with the library's static scratch instead of the handle's exchange memory."""
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(
+        library().kd_step_noalloc(handle, _dev_ptr(tokens), _dev_ptr(positions), _dev_ptr(kv), _dev_ptr(logits), s),
+        "kd_step_noalloc",
     )
 
 

@@ -50,6 +50,7 @@ extern "C" {
 #define KD_ERR_OOM (-4)         /* device memory allocation failed */
 #define KD_ERR_HIP (-5)         /* a HIP runtime call failed */
 #define KD_ERR_LAUNCH (-6)      /* the kernel launch was rejected by the HIP runtime */
+#define KD_ERR_SCRATCH (-7)     /* kd_step_noalloc: the handle needs more than its 16 MiB static scratch */
 
 /* ---- sticky device status bits (kd_device_status) ------------------------ */
 #define KD_STATUS_TOKEN_RANGE 0x1u  /* an input token was outside [0, vocab): that call wrote nothing */
@@ -186,6 +187,24 @@ int kd_kv_layout(const kd_config* cfg, size_t* bytes, size_t strides[6]);
  * (KD_CTRL_WAIT_LIMIT_US) with KD_STATUS_SYNC_TIMEOUT instead of hanging.
  */
 int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* logits, void* stream);
+
+/*
+ * kd_step for callers that cannot allocate device memory at the time of the call (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation). Same arguments,
+ * results, ownership and errors as kd_step at batch 1, bit for bit; it allocates nothing and
+ * calls no allocating routine. The step's exchange memory (the words workgroups pass between
+ * phases, and the abort word) is not the handle's but one static device array of 16 MiB per GPU,
+ * set up by kd_init and held until the process ends. The caller still passes inputs and outputs.
+ *   Returns KD_ERR_UNSUPPORTED for batch > 1, and KD_ERR_SCRATCH (before launching anything) when
+ *   the model's exchange memory exceeds 16 MiB. On a 256-CU MI355X every shape kd_init accepts
+ *   fits (at most 12.3 MiB, at d_model 4096 with 4 q heads per kv head; the 2B and Llama-3-8B
+ *   shapes need 8.1 and 12.2 MiB); the check guards GPUs with more compute units.
+ * Every call on one GPU shares that GPU's array, so calls that overlap on one GPU race, also
+ * from different handles: issue them in order (one stream, or synchronised). Nothing in the array
+ * needs clearing between calls: every call tags its words with tags no earlier call on that GPU
+ * used (the array is cleared, by a kernel on the stream, only when the tags start over).
+ */
+int kd_step_noalloc(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* logits, void* stream);
 
 /*
  * Run n_steps greedy decode steps as one persistent launch (batch 1) and return: each step is

@@ -50,7 +50,7 @@ def test_struct_layout_matches_binding():
 
 
 def test_strerror_covers_every_code():
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         assert kd.kd_strerror(code) and "unknown" not in kd.kd_strerror(code)
     assert "unknown" in kd.kd_strerror(-99)
 
@@ -90,6 +90,7 @@ def test_null_arguments_rejected():
     assert lib.kd_init(ctypes.byref(cfg), None, None) == kd.KD_ERR_INVALID_ARG
     assert lib.kd_init(ctypes.byref(cfg), None, ctypes.byref(h)) == kd.KD_ERR_INVALID_ARG
     assert lib.kd_step(None, None, None, None, None, None) == kd.KD_ERR_INVALID_ARG
+    assert lib.kd_step_noalloc(None, None, None, None, None, None) == kd.KD_ERR_INVALID_ARG
     assert lib.kd_stream_read(None, 1 << 20, None) == kd.KD_ERR_INVALID_ARG
     assert lib.kd_generate(None, 4, None, None, None, None, None, None, None) == kd.KD_ERR_INVALID_ARG
     assert lib.kd_control(None, kd.KD_CTRL_CANCEL, 1) == kd.KD_ERR_INVALID_ARG
