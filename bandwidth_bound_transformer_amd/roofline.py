@@ -11,7 +11,8 @@ The count below is what the method itself must move per step, not what an
 implementation happens to move:
 
 * every layer weight, the final norm and the LM head, once per step (once per
-  tick for all B sessions together);
+  tick for all B sessions together); for fp8 models, one byte per matrix
+  element plus a float32 scale per matrix row, and bf16 norm gains;
 * one embedding row per session;
 * per session, the KV cache over positions 0..p (K and V, every layer and kv head);
 * per session, the K and V written at position p;
@@ -47,8 +48,8 @@ def step_bytes(shape, batch: int, position: int, write_logits: bool = True) -> S
     """Bytes of one step in which every session attends over positions 0..position."""
     kv_per_pos = shape.n_layers * 2 * shape.n_kv_heads * shape.head_dim * shape.kv_bytes
     return StepBytes(
-        weights=streamed_params(shape) * shape.weight_bytes,
-        embedding=batch * shape.d_model * shape.weight_bytes,
+        weights=shape.streamed_weight_bytes(),
+        embedding=batch * shape.d_model * shape.embed_bytes,
         kv_read=batch * (position + 1) * kv_per_pos,
         kv_write=batch * kv_per_pos,
         logits=batch * shape.vocab * 4 if write_logits else 0,

@@ -38,6 +38,13 @@ decides:
   value is rounded to float32, then to bf16 for a bf16 cache.
 * The next token is the argmax of the logits rounded to float32, lowest
   index on ties. The kernel takes that decision in float32.
+
+FP8 weights. Lowering the precision of the parameters cuts the bytes every
+token reads ("17k tokens/sec" page, best practice 2 and FAQ 3, which names
+FP8). An fp8 model stores each projection matrix and the LM head as OCP FP8
+E4M3 codes with one float32 scale per output row; its embedding and norm gains
+are bf16. The oracle is fed those codes and scales and computes with the
+weights they stand for, code value times row scale, exactly in float64.
 """
 
 from __future__ import annotations
@@ -82,9 +89,31 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     return f32.astype(np.float64)
 
 
-def weight_f64(w: np.ndarray, dtype: str) -> np.ndarray:
-    """float64 values of a stored weight tensor (bf16 bit patterns or float32)."""
-    if dtype == "bf16":
+def fp8_e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Exact value of OCP FP8 E4M3 bit patterns: sign, 4 exponent bits (bias 7), 3 fraction bits.
+
+    Exponent field 0 holds the subnormals f/8 * 2**-6; every other field e holds
+    (1 + f/8) * 2**(e - 7). There are no infinities; S.1111.111 is NaN.
+    """
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    f = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, f / 8.0 * 2.0**-6, (1.0 + f / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    out = sign * mag
+    return np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, out)
+
+
+def weight_f64(w, dtype: str) -> np.ndarray:
+    """float64 values of a stored weight tensor.
+
+    bf16 bit patterns or float32 arrays; for fp8 models, an object with ``codes`` (E4M3 bit
+    patterns, [rows, cols]) and ``scale`` (float32 [rows]) for each projection matrix, whose
+    value is the code's value times its row's scale, and bf16 patterns for the rest.
+    """
+    if dtype == "fp8" and hasattr(w, "codes"):
+        return fp8_e4m3_to_f64(w.codes) * np.asarray(w.scale, np.float32).astype(np.float64)[:, None]
+    if dtype in ("bf16", "fp8"):
         return bf16_to_f64(w)
     if dtype == "f32":
         return np.asarray(w, np.float32).astype(np.float64)

@@ -47,9 +47,20 @@ def bf16_value(bits: int) -> float:
     return _from_bits32(int(bits) << 16)
 
 
+def _fp8_rows(t):
+    """An E4M3 matrix (codes and per-row scales) -> nested list of Python floats. The codes are
+    decoded by torch's float8_e4m3fn type, not by a formula of this file or of the oracle."""
+    import torch
+
+    vals = torch.from_numpy(t.codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).tolist()
+    return [[v * float(s) for v in row] for row, s in zip(vals, t.scale.tolist())]
+
+
 def _tolist(t, dtype):
     """Stored tensor -> nested list of Python floats."""
-    if dtype == "bf16":
+    if hasattr(t, "codes"):
+        return _fp8_rows(t)
+    if dtype in ("bf16", "fp8"):
         conv = bf16_value
     else:
         conv = float

@@ -15,7 +15,9 @@ What each pin rests on:
   unit vector; RMS of an RMSNorm output; silu at special points; zero
   attention and FFN outputs leave the embedding untouched;
 * library routines: torch's float32 -> bfloat16 conversion, numpy's argmax
-  and scipy's logistic function.
+  and scipy's logistic function; torch's float8_e4m3fn type for the value of
+  every FP8 E4M3 code, and the brute force fed the weights torch decodes for
+  an fp8 model.
 """
 
 from __future__ import annotations
@@ -29,6 +31,8 @@ from . import brute_force
 
 MICRO_GQA = ModelShape(2, 16, 4, 2, 8, 24, 40, rope_base=10000.0, weight_dtype="bf16", kv_dtype="bf16")
 MICRO_MHA_F32 = ModelShape(1, 12, 3, 3, 4, 20, 33, rope_base=500.0, weight_dtype="f32", kv_dtype="f32")
+MICRO_FP8 = ModelShape(2, 16, 4, 2, 8, 24, 40, rope_base=10000.0, weight_dtype="fp8", kv_dtype="bf16")
+FP8_MATRICES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
 
 def micro_weights(shape: ModelShape, seed: int = 7) -> dict:
@@ -49,6 +53,28 @@ def micro_weights(shape: ModelShape, seed: int = 7) -> dict:
         for name in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
             vals = rng.standard_normal(lw[name].shape).astype(np.float32) * np.float32(0.4)
             lw[name] = workloads.bf16_bits_from_f32(vals) if shape.weight_dtype == "bf16" else vals
+    return w
+
+
+def micro_fp8_weights(seed: int = 41) -> dict:
+    """An fp8 micro model whose codes cover every finite E4M3 value (both signs, the subnormals,
+    448) and whose row scales differ from row to row, so a code misread or a scale applied to the
+    wrong row or column shows."""
+    w = micro_weights(MICRO_GQA, seed=seed)
+    w["dtype"] = "fp8"
+    rng = np.random.default_rng(seed + 2000)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+
+    def fp8(shape):
+        codes = rng.choice(finite, size=shape).astype(np.uint8)
+        codes.reshape(-1)[: finite.size] = finite[: min(finite.size, codes.size)]
+        scale = (rng.uniform(0.25, 2.0, shape[0]) * (0.4 / 448.0)).astype(np.float32)
+        return workloads.Fp8Matrix(codes, scale)
+
+    for lw in w["layers"]:
+        for name in FP8_MATRICES:
+            lw[name] = fp8(lw[name].shape)
+    w["lm_head"] = fp8(w["lm_head"].shape)
     return w
 
 
@@ -314,6 +340,26 @@ def pin_sessions_independent(mod):
         assert not np.any(multi.k_cache[s, :, :, n:])
 
 
+def pin_fp8(mod):
+    """FP8 E4M3 weights: every code's value equals torch's float8_e4m3fn value, and an fp8 micro
+    model steps exactly as the brute force fed the weights torch decodes (codes times row scales)."""
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    ours = mod.fp8_e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    w = micro_fp8_weights()
+    o = mod.Oracle(MICRO_FP8, w, batch=1, max_seq=8)
+    feeds = [(3, 0), (17, 1), (39, 2), (0, 3), (22, 4)]
+    want = brute_force.decode(MICRO_FP8, w, feeds)
+    for (tok, pos), r in zip(feeds, want):
+        got = o.step_one(0, tok, pos)
+        assert _rel(got, r) < 1e-9, (pos, _rel(got, r))
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_brute_force_prefilled,
@@ -328,4 +374,5 @@ ALL_PINS = [
     pin_bf16,
     pin_identity_layers,
     pin_sessions_independent,
+    pin_fp8,
 ]

@@ -71,6 +71,14 @@ MUTANTS = {
         "vc = self.v_cache[session, l, :, : position + 1]",
         "vc = self.v_cache[i, l, :, : position + 1]",
     ),
+    # fp8 weights: exponent bias, subnormals, the sign, and which axis the scales run along
+    "fp8_bias_8": ("np.exp2((e - 7).astype(np.float64))", "np.exp2((e - 8).astype(np.float64))"),
+    "fp8_subnormals_as_normals": ("np.where(e == 0, f / 8.0 * 2.0**-6,", "np.where(e < 0, f / 8.0 * 2.0**-6,"),
+    "fp8_sign_ignored": ("sign = np.where(c & 0x80, -1.0, 1.0)", "sign = np.where(c & 0x00, -1.0, 1.0)"),
+    "fp8_scale_per_column": (
+        "np.asarray(w.scale, np.float32).astype(np.float64)[:, None]",
+        "np.resize(np.asarray(w.scale, np.float32).astype(np.float64), w.codes.shape[1])[None, :]",
+    ),
 }
 
 # cheapest pins first: a mutant stops at its first failing pin
@@ -87,6 +95,7 @@ PIN_ORDER = [
     oracle_pins.pin_incremental_equals_full,
     oracle_pins.pin_silu,
     oracle_pins.pin_sessions_independent,
+    oracle_pins.pin_fp8,
     lambda mod: oracle_pins.pin_bf16(mod, n_random=1 << 14),
 ]
 

@@ -27,6 +27,9 @@ from .gen import (
     fill_kv_prefill_device,
     bf16_bits_from_f32,
     f32_from_bf16_bits,
+    Fp8Matrix,
+    quantize_rows_e4m3,
+    E4M3_MAX,
 )
 
 __all__ = [
@@ -44,4 +47,7 @@ __all__ = [
     "fill_kv_prefill_device",
     "bf16_bits_from_f32",
     "f32_from_bf16_bits",
+    "Fp8Matrix",
+    "quantize_rows_e4m3",
+    "E4M3_MAX",
 ]

@@ -12,6 +12,11 @@ Recipe (stated once, used by every consumer):
 * Prompt ids for session b: uniform integers in [0, vocab) from
   SeedSequence([prompt_seed, b]).  First tokens of pre-filled workloads use
   SeedSequence([first_token_seed, b]) the same way.
+* fp8 workloads draw exactly the bf16 workload's weights, then quantise each
+  projection matrix and the LM head row by row: a row's scale is its largest
+  magnitude divided by 448 (the largest finite E4M3 value), and its codes are
+  the OCP FP8 E4M3 values nearest to weight / scale (torch's float8_e4m3fn
+  conversion).  The embedding and the norm gains stay bf16.
 * Pre-filled KV values: for layer l, slot s (0 = K after RoPE, 1 = V), session
   b and kv head g, an array [prefill_len, head_dim] of N(0,1) float32 draws
   from SeedSequence([kv_seed, l, s, b, g]), rounded to bf16 for bf16 caches.
@@ -21,6 +26,7 @@ from __future__ import annotations
 
 import os
 from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -40,6 +46,43 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
 def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
     """Exact float32 values of bf16 bit patterns."""
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+E4M3_MAX = 448.0  # largest finite OCP FP8 E4M3 value
+
+
+@dataclass(frozen=True)
+class Fp8Matrix:
+    """A matrix stored as OCP FP8 E4M3 codes with one float32 scale per row.
+
+    The value of element (r, c) is (E4M3 value of codes[r, c]) * scale[r]."""
+
+    codes: np.ndarray  # uint8 [rows, cols]
+    scale: np.ndarray  # float32 [rows]
+
+    @property
+    def shape(self) -> tuple:
+        return self.codes.shape
+
+    @property
+    def size(self) -> int:
+        return self.codes.size
+
+    @property
+    def nbytes(self) -> int:
+        return self.codes.nbytes + self.scale.nbytes
+
+
+def quantize_rows_e4m3(w: np.ndarray) -> Fp8Matrix:
+    """Per-row absmax quantisation of a float32 matrix to E4M3 codes and float32 scales."""
+    import torch
+
+    w = np.ascontiguousarray(w, np.float32)
+    amax = np.max(np.abs(w), axis=1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = np.clip(w / scale[:, None], -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    codes = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return Fp8Matrix(codes, scale)
 
 
 def _workers() -> int:
@@ -74,22 +117,27 @@ def make_weights(shape: ModelShape, seed: int = 0, workers: int | None = None) -
 
     Returns a dict: ``embed`` [V, d], ``layers`` (list of dicts with the nine
     per-layer tensors), ``final_norm`` [d], ``lm_head`` [V, d] and ``dtype``.
-    bf16 tensors are uint16 bit patterns; f32 tensors are float32.
+    bf16 tensors are uint16 bit patterns; f32 tensors are float32. For fp8
+    models the seven matrices of each layer and the LM head are ``Fp8Matrix``
+    objects, and the embedding and gains are bf16.
     """
-    as_bf16 = shape.weight_dtype == "bf16"
+    fp8 = shape.weight_dtype == "fp8"
+    as_bf16 = shape.weight_dtype in ("bf16", "fp8")
     store = np.uint16 if as_bf16 else np.float32
     one = bf16_bits_from_f32(np.ones(1, np.float32))[0] if as_bf16 else np.float32(1.0)
     w = {"dtype": shape.weight_dtype, "layers": []}
     with ThreadPoolExecutor(max_workers=workers or _workers()) as pool:
-        def matrix(name: str, index: int) -> np.ndarray:
+        def matrix(name: str, index: int, quantise: bool = True):
             arr = np.empty(shape.tensor_shape(name), dtype=store)
             _fill_matrix(arr, seed, index, as_bf16, pool)
+            if fp8 and quantise:
+                return quantize_rows_e4m3(f32_from_bf16_bits(arr))
             return arr
 
         def gain(name: str) -> np.ndarray:
             return np.full(shape.tensor_shape(name), one, dtype=store)
 
-        w["embed"] = matrix("embed", 0)
+        w["embed"] = matrix("embed", 0, quantise=False)
         for l in range(shape.n_layers):
             base = 1 + TENSORS_PER_LAYER * l
             layer = {}

@@ -17,6 +17,11 @@ The five presets are the decode workloads this library is measured on:
 * ``2b_long`` -- the 2B decoder with a KV cache pre-filled to 32768 positions
                  with N(0,1) bf16 values; 128 greedy tokens (the KV read grows
                  with context: "17k tokens/sec" page, FAQ on long context).
+* ``2b_fp8``, ``8b_fp8`` -- the 2B and 8B decoders with their projection matrices
+                 and LM head quantised to FP8 E4M3, one float32 scale per output
+                 row; embedding, norm gains and KV cache stay bf16 ("17k
+                 tokens/sec" page, best practice 2 and FAQ 3: lower-precision
+                 parameters cut the bytes each token reads).
 * ``11b_x56`` -- 40 layers, d_model 4096, 32 q / 8 kv heads, SwiGLU 16384,
                  vocab 128256, bf16; 56 sessions stepped in lockstep, each with
                  its own KV cache pre-filled to 4096 positions; 200 ticks
@@ -61,7 +66,7 @@ class ModelShape:
     vocab: int
     rope_base: float = 10000.0
     norm_eps: float = 1e-5
-    weight_dtype: str = "bf16"  # "bf16" or "f32"
+    weight_dtype: str = "bf16"  # "bf16", "f32" or "fp8" (E4M3 projection matrices, bf16 embedding and gains)
     kv_dtype: str = "bf16"  # "bf16" or "f32"
 
     @property
@@ -78,7 +83,18 @@ class ModelShape:
 
     @property
     def weight_bytes(self) -> int:
-        return 2 if self.weight_dtype == "bf16" else 4
+        """Bytes of one element of a projection matrix (or of any weight, for bf16 and f32)."""
+        return {"bf16": 2, "f32": 4, "fp8": 1}[self.weight_dtype]
+
+    @property
+    def embed_bytes(self) -> int:
+        """Bytes of one element of the embedding and the norm gains (bf16 for fp8 models)."""
+        return 4 if self.weight_dtype == "f32" else 2
+
+    @property
+    def matrix_rows_per_layer(self) -> int:
+        """Output rows of a layer's seven matrices (one fp8 scale each)."""
+        return self.q_dim + 2 * self.kv_dim + self.d_model + 2 * self.ffn_dim + self.d_model
 
     @property
     def kv_bytes(self) -> int:
@@ -107,6 +123,19 @@ class ModelShape:
 
     def total_params(self) -> int:
         return 2 * self.vocab * self.d_model + self.n_layers * self.layer_params() + self.d_model
+
+    def streamed_weight_bytes(self) -> int:
+        """Bytes of everything a step reads once: every layer, the final norm and the LM head.
+
+        fp8 models store each projection matrix as one byte per element plus one float32 scale
+        per output row, and their norm gains in bf16."""
+        d, V, L = self.d_model, self.vocab, self.n_layers
+        if self.weight_dtype != "fp8":
+            return (L * self.layer_params() + d + V * d) * self.weight_bytes
+        matrices = L * (self.layer_params() - 2 * d) + V * d
+        scales = 4 * (L * self.matrix_rows_per_layer + V)
+        gains = 2 * (2 * L * d + d)
+        return matrices + scales + gains
 
 
 @dataclass(frozen=True)
@@ -151,6 +180,8 @@ _TINY = ModelShape(2, 256, 4, 4, 64, 1024, 1024, rope_base=10000.0, weight_dtype
 _2B = ModelShape(26, 2048, 16, 4, 128, 8192, 32000, rope_base=10000.0)
 _8B = ModelShape(32, 4096, 32, 8, 128, 14336, 128256, rope_base=500000.0)
 _11B = ModelShape(40, 4096, 32, 8, 128, 16384, 128256, rope_base=500000.0)
+_2B_FP8 = replace(_2B, weight_dtype="fp8")
+_8B_FP8 = replace(_8B, weight_dtype="fp8")
 
 PRESETS = {
     "tiny": Workload("tiny", _TINY, batch=1, prompt_len=32, gen_tokens=64,
@@ -163,6 +194,10 @@ PRESETS = {
                         description="2B decoder, KV pre-filled to 32768 positions"),
     "11b_x56": Workload("11b_x56", _11B, batch=56, prefill_len=4096, gen_tokens=200,
                         description="11B decoder, 56 lockstep sessions, KV at 4096"),
+    "2b_fp8": Workload("2b_fp8", _2B_FP8, batch=1, prompt_len=512, gen_tokens=512,
+                       description="2B decoder, batch 1, E4M3 weights with per-row scales"),
+    "8b_fp8": Workload("8b_fp8", _8B_FP8, batch=1, prompt_len=1024, gen_tokens=256,
+                       description="Llama-3-8B-shaped decoder, batch 1, E4M3 weights with per-row scales"),
 }
 
 
