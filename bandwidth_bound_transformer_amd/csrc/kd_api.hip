@@ -91,6 +91,7 @@ struct Buffers {
   uint8_t* embed = nullptr;
   uint8_t* norms = nullptr;
   float2* rope = nullptr;     // [S][hd/2] (cos, sin)
+  float* scales = nullptr;    // fp8 weights: row scales (Dims::sc_*)
   uint64_t* ll = nullptr;
   uint32_t* flags = nullptr;  // [0] sticky status bits, [1] abort word, [2] tick skip flag (B > 1), [3] cancel word
 };
@@ -100,6 +101,7 @@ void free_buffers(Buffers& b) {
   if (b.embed) (void)hipFree(b.embed);
   if (b.norms) (void)hipFree(b.norms);
   if (b.rope) (void)hipFree(b.rope);
+  if (b.scales) (void)hipFree(b.scales);
   if (b.ll) (void)hipFree(b.ll);
   if (b.flags) (void)hipFree(b.flags);
   b = Buffers{};
@@ -109,6 +111,7 @@ typedef void (*KernelFn)(kd::Params);
 
 // The one-step kernel, or (multi) the kernel that may run several steps per launch.
 KernelFn pick_kernel(int wbytes, int hd, bool multi) {
+  if (wbytes == 1 && hd == 128) return multi ? kd::decode_step_kernel<kRing, 1, 2, 128, true> : kd::decode_step_kernel<kRing, 1, 2, 128, false>;
   if (wbytes == 2 && hd == 128) return multi ? kd::decode_step_kernel<kRing, 2, 2, 128, true> : kd::decode_step_kernel<kRing, 2, 2, 128, false>;
   if (wbytes == 2 && hd == 64) return multi ? kd::decode_step_kernel<kRing, 2, 2, 64, true> : kd::decode_step_kernel<kRing, 2, 2, 64, false>;
   if (wbytes == 4 && hd == 128) return multi ? kd::decode_step_kernel<kRing, 4, 4, 128, true> : kd::decode_step_kernel<kRing, 4, 4, 128, false>;
@@ -138,7 +141,8 @@ struct kd_handle {
 namespace {
 
 bool dtype_ok(int32_t t) { return t == KD_DTYPE_F32 || t == KD_DTYPE_BF16; }
-int dtype_bytes(int32_t t) { return t == KD_DTYPE_BF16 ? 2 : 4; }
+bool weight_dtype_ok(int32_t t) { return dtype_ok(t) || t == KD_DTYPE_FP8_E4M3; }
+int dtype_bytes(int32_t t) { return t == KD_DTYPE_FP8_E4M3 ? 1 : (t == KD_DTYPE_BF16 ? 2 : 4); }
 
 // Structural checks that need no device.
 int check_config(const kd_config* c) {
@@ -147,7 +151,7 @@ int check_config(const kd_config* c) {
       c->ffn_dim <= 0 || c->vocab <= 0 || c->max_seq <= 0 || c->batch <= 0)
     return KD_ERR_INVALID_ARG;
   if (c->n_q_heads % c->n_kv_heads != 0 || c->head_dim % 2 != 0) return KD_ERR_INVALID_ARG;
-  if (!dtype_ok(c->weight_dtype) || !dtype_ok(c->kv_dtype)) return KD_ERR_INVALID_ARG;
+  if (!weight_dtype_ok(c->weight_dtype) || !dtype_ok(c->kv_dtype)) return KD_ERR_INVALID_ARG;
   if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f)) return KD_ERR_INVALID_ARG;
   if (c->max_seq > (1 << 24) || c->vocab > (1 << 30)) return KD_ERR_INVALID_ARG;
   return KD_OK;
@@ -157,15 +161,18 @@ int check_config(const kd_config* c) {
 int check_supported(const kd_config* c, const kd::Dims& m) {
   if (c->batch != 1) return KD_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return KD_ERR_UNSUPPORTED;
-  if (c->weight_dtype != c->kv_dtype) return KD_ERR_UNSUPPORTED;
+  // fp8 matrices come with bf16 embedding, gains and cache, and head_dim 128
+  if (c->weight_dtype == KD_DTYPE_FP8_E4M3 ? (c->kv_dtype != KD_DTYPE_BF16 || c->head_dim != 128)
+                                            : c->weight_dtype != c->kv_dtype)
+    return KD_ERR_UNSUPPORTED;
   if (m.G > kd::kMaxGroup || (int64_t)m.G * m.hd > kd::kThreads) return KD_ERR_UNSUPPORTED;
-  if (m.d > kd::kMaxDim || m.qdim > kd::kMaxDim || m.d % 64 != 0) return KD_ERR_UNSUPPORTED;
+  if (m.d > kd::kMaxDim || m.qdim > kd::kMaxDim || m.d % kd::down_block_rows(m) != 0) return KD_ERR_UNSUPPORTED;
   if ((int64_t)m.d * m.wbytes % kd::kPacketBytes || (int64_t)m.qdim * m.wbytes % kd::kPacketBytes) return KD_ERR_UNSUPPORTED;
-  if (m.F % m.vpl != 0 || m.F / m.vpl < m.nwg) return KD_ERR_UNSUPPORTED;  // every workgroup owns an FFN slice
+  if (m.F % kd::ffn_unit(m) != 0 || m.F / kd::ffn_unit(m) < m.nwg) return KD_ERR_UNSUPPORTED;  // every workgroup owns an FFN slice
   // per-workgroup shares must fit the LDS arrays and the thread count
   const int64_t nrd_max = 2 * kd::ceil_div(m.d / 2, m.nwg);
   const int64_t nq_max = kd::ceil_div(m.nqkv, m.nwg);
-  const int64_t nf_max = m.vpl * kd::ceil_div(m.F / m.vpl, m.nwg);
+  const int64_t nf_max = kd::ffn_unit(m) * kd::ceil_div(m.F / kd::ffn_unit(m), m.nwg);
   if (nrd_max > kd::kMaxRowsD || nq_max > kd::kThreads || nf_max > kd::kMaxSlice) return KD_ERR_UNSUPPORTED;
   if ((int64_t)m.nwg * nrd_max > kd::kStageWords || 2 * (int64_t)m.nwg > kd::kStageWords) return KD_ERR_UNSUPPORTED;
   // rows one wave's packet range can span, for every row-split tile of every workgroup
@@ -244,9 +251,13 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
   int rc = check_config(cfg);
   if (rc != KD_OK) return rc;
   if (!w || !w->embed || !w->layers || !w->final_norm || !w->lm_head) return KD_ERR_INVALID_ARG;
+  const bool fp8 = cfg->weight_dtype == KD_DTYPE_FP8_E4M3;
+  if (fp8 && !w->s_lm_head) return KD_ERR_INVALID_ARG;
   for (int l = 0; l < cfg->n_layers; ++l) {
     const kd_layer_weights& lw = w->layers[l];
     if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.w_gate || !lw.w_up || !lw.w_down)
+      return KD_ERR_INVALID_ARG;
+    if (fp8 && (!lw.s_wq || !lw.s_wk || !lw.s_wv || !lw.s_wo || !lw.s_gate || !lw.s_up || !lw.s_down))
       return KD_ERR_INVALID_ARG;
   }
   int ndev = 0;
@@ -258,6 +269,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return KD_ERR_UNSUPPORTED;
 
   const int wb = dtype_bytes(cfg->weight_dtype), kb = dtype_bytes(cfg->kv_dtype);
+  const int eb = fp8 ? 2 : wb;  // embedding and norm gains
   const int nwg = prop.multiProcessorCount;
   if (cfg->batch > 1) {
     rc = kd::bt::batch_check(cfg);
@@ -313,8 +325,9 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
     const int64_t d = m.d;
     const size_t blob_bytes = (size_t)m.blob_elems * wb;
     if (hipMalloc(&h->buf.blob, blob_bytes) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
-    if (hipMalloc(&h->buf.embed, (size_t)m.V * d * wb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
-    if (hipMalloc(&h->buf.norms, (size_t)(2 * m.L + 1) * d * wb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
+    if (hipMalloc(&h->buf.embed, (size_t)m.V * d * eb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
+    if (hipMalloc(&h->buf.norms, (size_t)(2 * m.L + 1) * d * eb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
+    if (fp8 && hipMalloc(&h->buf.scales, (size_t)kd::scale_layout(m).total * sizeof(float)) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     if (hipMalloc(&h->buf.ll, (size_t)h->lo.total * 8) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     if (hipMalloc(&h->buf.rope, (size_t)m.S * (m.hd / 2) * sizeof(float2)) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     if (hipMalloc(&h->buf.flags, 256) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
@@ -324,7 +337,9 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
     KD_TRY(hipStreamCreateWithFlags(&h->ctl, hipStreamNonBlocking));
     // kd_step_noalloc's scratch on this device (if this fails, that entry point reports KD_ERR_HIP)
     (void)resolve_scratch(dev);
-    const size_t row = (size_t)d * wb;
+    const size_t row = (size_t)d * wb, erow = (size_t)d * eb;
+    const kd::ScaleLayout sl = kd::scale_layout(m);
+    std::vector<float> sc(fp8 ? (size_t)sl.total : 0);
     for (int l = 0; l < m.L; ++l) {
       const kd_layer_weights& lw = w->layers[l];
       uint8_t* lay = h->buf.blob + (size_t)l * m.layer_elems * wb;
@@ -334,7 +349,10 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
       KD_TRY(hipMemcpy(lay + m.off_o * wb, lw.wo, (size_t)d * m.qdim * wb, hipMemcpyHostToDevice));
       KD_TRY(hipMemcpy(tmp, lw.w_gate, (size_t)m.F * row, hipMemcpyHostToDevice));
       KD_TRY(hipMemcpy(tmp + (size_t)m.F * row, lw.w_up, (size_t)m.F * row, hipMemcpyHostToDevice));
-      if (wb == 2)
+      if (wb == 1)
+        hipLaunchKernelGGL(kd::pack_gate_up_kernel<uint8_t>, dim3(4096), dim3(256), 0, 0, (uint8_t*)(lay + m.off_gu * wb),
+                           (const uint8_t*)tmp, (const uint8_t*)(tmp + (size_t)m.F * row), m);
+      else if (wb == 2)
         hipLaunchKernelGGL(kd::pack_gate_up_kernel<uint16_t>, dim3(4096), dim3(256), 0, 0, (uint16_t*)(lay + m.off_gu * wb),
                            (const uint16_t*)tmp, (const uint16_t*)(tmp + (size_t)m.F * row), m);
       else
@@ -343,7 +361,10 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
       KD_TRY(hipGetLastError());
       KD_TRY(hipDeviceSynchronize());
       KD_TRY(hipMemcpy(tmp, lw.w_down, (size_t)d * m.F * wb, hipMemcpyHostToDevice));
-      if (wb == 2)
+      if (wb == 1)
+        hipLaunchKernelGGL(kd::pack_down_kernel<uint8_t>, dim3(4096), dim3(256), 0, 0, (uint8_t*)(lay + m.off_d * wb),
+                           (const uint8_t*)tmp, m);
+      else if (wb == 2)
         hipLaunchKernelGGL(kd::pack_down_kernel<uint16_t>, dim3(4096), dim3(256), 0, 0, (uint16_t*)(lay + m.off_d * wb),
                            (const uint16_t*)tmp, m);
       else
@@ -351,12 +372,30 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
                            (const float*)tmp, m);
       KD_TRY(hipGetLastError());
       KD_TRY(hipDeviceSynchronize());
-      KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * l) * row, lw.attn_norm, row, hipMemcpyHostToDevice));
-      KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * l + 1) * row, lw.ffn_norm, row, hipMemcpyHostToDevice));
+      KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * l) * erow, lw.attn_norm, erow, hipMemcpyHostToDevice));
+      KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * l + 1) * erow, lw.ffn_norm, erow, hipMemcpyHostToDevice));
+      if (fp8) {
+        // row scales in the rows' packed order: QKV (q, k, v), O, each workgroup's [gate; up] slice, down
+        float* L0 = sc.data() + (size_t)l * sl.layer;
+        std::memcpy(L0, lw.s_wq, sizeof(float) * m.qdim);
+        std::memcpy(L0 + m.qdim, lw.s_wk, sizeof(float) * m.kvdim);
+        std::memcpy(L0 + m.qdim + m.kvdim, lw.s_wv, sizeof(float) * m.kvdim);
+        std::memcpy(L0 + sl.o, lw.s_wo, sizeof(float) * d);
+        for (int64_t wg = 0; wg < m.nwg; ++wg) {
+          const int64_t f0 = kd::ffn_lo(m, wg), nf = kd::ffn_lo(m, wg + 1) - f0;
+          std::memcpy(L0 + sl.gu + 2 * f0, lw.s_gate + f0, sizeof(float) * nf);
+          std::memcpy(L0 + sl.gu + 2 * f0 + nf, lw.s_up + f0, sizeof(float) * nf);
+        }
+        std::memcpy(L0 + sl.d, lw.s_down, sizeof(float) * d);
+      }
     }
-    KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * m.L) * row, w->final_norm, row, hipMemcpyHostToDevice));
+    KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * m.L) * erow, w->final_norm, erow, hipMemcpyHostToDevice));
     KD_TRY(hipMemcpy(h->buf.blob + (size_t)m.off_lm * wb, w->lm_head, (size_t)m.V * row, hipMemcpyHostToDevice));
-    KD_TRY(hipMemcpy(h->buf.embed, w->embed, (size_t)m.V * row, hipMemcpyHostToDevice));
+    KD_TRY(hipMemcpy(h->buf.embed, w->embed, (size_t)m.V * erow, hipMemcpyHostToDevice));
+    if (fp8) {
+      std::memcpy(sc.data() + sl.lm, w->s_lm_head, sizeof(float) * m.V);
+      KD_TRY(hipMemcpy(h->buf.scales, sc.data(), sc.size() * sizeof(float), hipMemcpyHostToDevice));
+    }
     {
       // RoPE: pair (i, i + hd/2) turns by position * base^(-2i/hd); angles, cos and sin in float64
       const int half = m.hd / 2;
@@ -413,6 +452,7 @@ int launch_steps_at(kd_handle* h, uint64_t* ll, uint32_t* abortf, uint32_t tag0,
   P.blob = h->buf.blob;
   P.embed = h->buf.embed;
   P.norms = h->buf.norms;
+  P.scales = h->buf.scales;
   P.rope = h->buf.rope;
   P.ll = ll;
   P.lo = h->lo;
@@ -608,7 +648,8 @@ int kd_get_info(kd_handle* h, int64_t info[8]) {
   }
   info[0] = h->m.nwg;
   info[1] = kd::kThreads;
-  info[2] = h->m.blob_elems * h->m.wbytes + (int64_t)h->m.V * h->m.d * h->m.wbytes + (int64_t)(2 * h->m.L + 1) * h->m.d * h->m.wbytes;
+  info[2] = h->m.blob_elems * h->m.wbytes + (int64_t)h->m.V * h->m.d * kd::embed_bytes(h->m) +
+            (int64_t)(2 * h->m.L + 1) * h->m.d * kd::embed_bytes(h->m) + (h->buf.scales ? kd::scale_layout(h->m).total * 4 : 0);
   info[3] = h->lds_bytes;
   info[4] = kRing;
   return KD_OK;

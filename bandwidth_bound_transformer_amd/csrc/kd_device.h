@@ -48,8 +48,9 @@ namespace kd {
 
 struct Params {
   const uint8_t* blob;   // packed layer weights and LM head, weight dtype
-  const uint8_t* embed;  // [V][d], weight dtype
-  const uint8_t* norms;  // [L][2][d] attention/FFN gains, then final gain [d], weight dtype
+  const uint8_t* embed;  // [V][d], bf16 (fp8 and bf16 models) or f32
+  const uint8_t* norms;  // [L][2][d] attention/FFN gains, then final gain [d], embedding dtype
+  const float* scales;   // fp8 weights: row scales laid out as scale_layout() says (else null)
   const float2* rope;    // [S][hd/2] (cos, sin) of position * theta_i
   uint64_t* ll;          // exchange words
   LLLayout lo;
@@ -282,7 +283,12 @@ __device__ __forceinline__ float load_w(const uint8_t* base, int64_t i) {
 // ----------------------------------------------------------------------------------------------
 __device__ __forceinline__ int p_lo(int n, int parts, int i) { return (int)(((uint32_t)n * (uint32_t)i) / (uint32_t)parts); }
 __device__ __forceinline__ int c_div(int a, int b) { return (a + b - 1) / b; }
-__device__ __forceinline__ int ffn_lo32(const Dims& m, int w) { return m.vpl * p_lo(m.F / m.vpl, m.nwg, w); }
+// FFN columns per slice unit and rows per down block, fixed by the matrix element size (the values
+// ffn_unit() and down_block_rows() give, as compile-time constants of each kernel)
+template <int WB> constexpr int kFu = WB == 1 ? 8 : 16 / WB;
+template <int WB> constexpr int kDbr = WB == 1 ? 128 : 64;
+template <int WB>
+__device__ __forceinline__ int ffn_lo32(const Dims& m, int w) { return kFu<WB> * p_lo(m.F / kFu<WB>, m.nwg, w); }
 // d rows are owned in pairs, so every workgroup's run of exchange words starts 16-byte aligned
 __device__ __forceinline__ int drow_lo(const Dims& m, int w) { return 2 * p_lo(m.d / 2, m.nwg, w); }
 
@@ -374,22 +380,24 @@ __device__ __forceinline__ Unit unit_of(const StepInfo& si, int w, int k, int nw
   return u;
 }
 
-// Packets of each tile of workgroup w, and how many packets a row (or 64-row block) spans.
+// Packets of each tile of workgroup w, and how many packets a row (or down block) spans.
+template <int WB>
 __device__ __forceinline__ void tile_shape(const Dims& m, int w, int tile, int& T, int& C) {
   if (tile == kTileQKV) { C = m.cd; T = (p_lo(m.nqkv, m.nwg, w + 1) - p_lo(m.nqkv, m.nwg, w)) * C; }
   else if (tile == kTileO) { C = m.cq; T = (drow_lo(m, w + 1) - drow_lo(m, w)) * C; }
-  else if (tile == kTileGU) { C = m.cd; T = 2 * (ffn_lo32(m, w + 1) - ffn_lo32(m, w)) * C; }
-  else if (tile == kTileD) { C = (ffn_lo32(m, w + 1) - ffn_lo32(m, w)) / m.vpl; T = (m.d / 64) * C; }
+  else if (tile == kTileGU) { C = m.cd; T = 2 * (ffn_lo32<WB>(m, w + 1) - ffn_lo32<WB>(m, w)) * C; }
+  else if (tile == kTileD) { C = (ffn_lo32<WB>(m, w + 1) - ffn_lo32<WB>(m, w)) / kFu<WB>; T = (m.d / kDbr<WB>) * C; }
   else { C = m.cd; T = (p_lo(m.V, m.nwg, w + 1) - p_lo(m.V, m.nwg, w)) * C; }
 }
 
-// Packet range [lo, hi) of wave v in a tile. The down tile is cut at whole 64-row blocks, so each
-// block's sum is finished by one wave.
+// Packet range [lo, hi) of wave v in a tile. The down tile is cut at whole blocks of dbr rows, so
+// each block's sum is finished by one wave.
+template <int WB>
 __device__ __forceinline__ void wave_range(const Dims& m, int w, int tile, int v, int& lo, int& hi) {
   int T, C;
-  tile_shape(m, w, tile, T, C);
+  tile_shape<WB>(m, w, tile, T, C);
   if (tile == kTileD) {
-    const int nb = m.d / 64;
+    const int nb = m.d / kDbr<WB>;
     lo = (int)wave_lo(nb, v) * C;
     hi = (int)wave_lo(nb, v + 1) * C;
   } else {
@@ -401,7 +409,7 @@ __device__ __forceinline__ void wave_range(const Dims& m, int w, int tile, int v
 // Fill wave v's segment table (done by the wave itself).
 // K/V positions from p_new on were appended earlier in this launch (by a multi-step launch), so
 // their packets are loaded coherently; p_new = max_seq when no such position exists.
-template <int RING>
+template <int RING, int WB>
 __device__ __forceinline__ void build_segments(const Params& P, const StepInfo& si, int w, int v, Smem<RING>& sm,
                                                int p_new) {
   const Dims& m = P.m;
@@ -415,7 +423,7 @@ __device__ __forceinline__ void build_segments(const Params& P, const StepInfo& 
   };
   SegEntry* t = sm.segs[v];
   int lo, hi;
-  wave_range(m, w, kTileQKV, v, lo, hi);
+  wave_range<WB>(m, w, kTileQKV, v, lo, hi);
   put(t[0], P.blob + (m.off_qkv + (int64_t)p_lo(m.nqkv, m.nwg, w) * m.d) * m.wbytes, lo, hi, kSegWeight);
   for (int k = 0; k < si.nunits; ++k) {
     const Unit u = unit_of(si, w, k, m.nwg);
@@ -427,13 +435,13 @@ __device__ __forceinline__ void build_segments(const Params& P, const StepInfo& 
     put(t[2 + 2 * k], P.kv + vbase * m.hd * m.kvbytes, p_lo(n, kWaves, v), p_lo(n, kWaves, v + 1), kSegKV, coh);
   }
   const int o = seg_o(si.nunits);
-  wave_range(m, w, kTileO, v, lo, hi);
+  wave_range<WB>(m, w, kTileO, v, lo, hi);
   put(t[o], P.blob + (m.off_o + (int64_t)drow_lo(m, w) * m.qdim) * m.wbytes, lo, hi, kSegWeight);
-  wave_range(m, w, kTileGU, v, lo, hi);
-  put(t[o + 1], P.blob + (m.off_gu + (int64_t)2 * ffn_lo32(m, w) * m.d) * m.wbytes, lo, hi, kSegWeight);
-  wave_range(m, w, kTileD, v, lo, hi);
-  put(t[o + 2], P.blob + (m.off_d + (int64_t)m.d * ffn_lo32(m, w)) * m.wbytes, lo, hi, kSegWeight);
-  wave_range(m, w, kTileLM, v, lo, hi);
+  wave_range<WB>(m, w, kTileGU, v, lo, hi);
+  put(t[o + 1], P.blob + (m.off_gu + (int64_t)2 * ffn_lo32<WB>(m, w) * m.d) * m.wbytes, lo, hi, kSegWeight);
+  wave_range<WB>(m, w, kTileD, v, lo, hi);
+  put(t[o + 2], P.blob + (m.off_d + (int64_t)m.d * ffn_lo32<WB>(m, w)) * m.wbytes, lo, hi, kSegWeight);
+  wave_range<WB>(m, w, kTileLM, v, lo, hi);
   put(sm.lm_seg[v], P.blob + (m.off_lm + (int64_t)p_lo(m.V, m.nwg, w) * m.d) * m.wbytes, lo, hi, kSegOnce);
 }
 
@@ -508,10 +516,29 @@ struct Ring {
 // ----------------------------------------------------------------------------------------------
 // packet arithmetic
 // ----------------------------------------------------------------------------------------------
-// One 16-byte lane load of weights times the matching activation values (8 bf16 or 4 f32).
+// Eight fp8 E4M3 weights (two 32-bit words) times a[0..8). gfx950's packed conversion reads the
+// OCP E4M3 format: byte k of a word becomes element k of the pair it selects.
+__device__ __forceinline__ float dot8_fp8(uint32_t lo, uint32_t hi, const float* a) {
+  const float4 a0 = *(const float4*)a, a1 = *(const float4*)(a + 4);
+  const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false), p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  const auto p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false), p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+  float s = p0[0] * a0.x;
+  s = fmaf(p0[1], a0.y, s);
+  s = fmaf(p1[0], a0.z, s);
+  s = fmaf(p1[1], a0.w, s);
+  s = fmaf(p2[0], a1.x, s);
+  s = fmaf(p2[1], a1.y, s);
+  s = fmaf(p3[0], a1.z, s);
+  s = fmaf(p3[1], a1.w, s);
+  return s;
+}
+
+// One 16-byte lane load of weights times the matching activation values (16 fp8, 8 bf16 or 4 f32).
 template <int WB>
 __device__ __forceinline__ float dot16(const uint4 w, const float* a) {
-  if constexpr (WB == 2) {
+  if constexpr (WB == 1) {
+    return dot8_fp8(w.x, w.y, a) + dot8_fp8(w.z, w.w, a + 8);
+  } else if constexpr (WB == 2) {
     const float4 a0 = *(const float4*)a, a1 = *(const float4*)(a + 4);
     float s = bf16_lo(w.x) * a0.x;
     s = fmaf(bf16_hi(w.x), a0.y, s);
@@ -575,8 +602,29 @@ __device__ __forceinline__ void consume_rows(Ring<RING, COH>& rg, const SegEntry
 template <int RING, int WB, bool COH>
 __device__ __forceinline__ void consume_down(Ring<RING, COH>& rg, const SegEntry s, int g, const float* a, uint64_t* ll,
                                              int64_t dp_at, uint32_t tag) {
-  constexpr int VPL = 16 / WB;
   const int lane = lane_id();
+  if constexpr (WB == 1) {
+    // fp8: 128-row blocks; lane l sums row 128 b + l from the first 8 bytes of its pieces and row
+    // 128 b + 64 + l from the last 8, over 8 slice columns per packet
+    int b = s.lo / g;
+    int j = 0;
+    float acc0 = 0.f, acc1 = 0.f;
+    for (int i = s.lo; i < s.hi; ++i) {
+      const uint4 wv = rg.take();
+      acc0 += dot8_fp8(wv.x, wv.y, a + j * 8);
+      acc1 += dot8_fp8(wv.z, wv.w, a + j * 8);
+      rg.give();
+      if (++j == g) {
+        ll_store(ll, dp_at + (int64_t)b * 128 + lane, acc0, tag);
+        ll_store(ll, dp_at + (int64_t)b * 128 + 64 + lane, acc1, tag);
+        acc0 = acc1 = 0.f;
+        j = 0;
+        ++b;
+      }
+    }
+    return;
+  }
+  constexpr int VPL = 16 / WB;
   int b = s.lo / g;
   int j = 0;
   float acc = 0.f;
@@ -897,6 +945,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   // work on a private copy: references into the kernel-argument segment would force a stack copy
   const Params P = P_arg;
   const Dims m = P.m;
+  constexpr int EB = WB == 1 ? 2 : WB;  // embedding and norm gains: bf16 when the matrices are fp8
+  constexpr bool FP8 = WB == 1;         // matrices hold E4M3 codes; each row's total is times its scale
+  const ScaleLayout scl_at = FP8 ? scale_layout(m) : ScaleLayout{};
   const int w = (int)blockIdx.x;
   const int tid = (int)threadIdx.x;
   const int wave = wave_id();
@@ -918,10 +969,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   const int p_new = n_steps > 1 ? p0 : P.max_seq;
 
   const int rd0 = drow_lo(m, w), nrd = drow_lo(m, w + 1) - rd0;  // this WG's d rows (O, x ownership)
-  const int f0 = ffn_lo32(m, w), nf = ffn_lo32(m, w + 1) - f0;     // this WG's FFN slice
+  const int f0 = ffn_lo32<WB>(m, w), nf = ffn_lo32<WB>(m, w + 1) - f0;  // this WG's FFN slice
   const int rq0 = p_lo(m.nqkv, m.nwg, w), nq = p_lo(m.nqkv, m.nwg, w + 1) - rq0;
   const int rl0 = p_lo(m.V, m.nwg, w), nl = p_lo(m.V, m.nwg, w + 1) - rl0;
-  const int gD = nf / m.vpl;
+  const int gD = nf / kFu<WB>;  // down packets per block of dbr rows
   const int mc = max_chunks(m);
 
   // Phase timestamps go to LDS and are copied out at the end of the launch (the last step's): a
@@ -941,11 +992,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   if (tid < kTiles) {
     for (int v = 0; v <= kWaves; ++v) {
       int lo, hi;
-      wave_range(m, w, tid, v < kWaves ? v : kWaves - 1, lo, hi);
+      wave_range<WB>(m, w, tid, v < kWaves ? v : kWaves - 1, lo, hi);
       sm.split[tid][v] = v < kWaves ? lo : hi;
     }
     int T, C;
-    tile_shape(m, w, tid, T, C);
+    tile_shape<WB>(m, w, tid, T, C);
     for (int v = 0; v < kWaves; ++v) sm.first[tid][v] = C > 0 ? sm.split[tid][v] / C : 0;
   }
 
@@ -983,13 +1034,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
 
   // ---- setup of the step: segment tables, ring, RoPE row, embedding row, cancel word ----
   if (tid == 0) sm.cancel = ld_flag(P.flags + kFlagCancel);
-  build_segments(P, si, w, wave, sm, p_new);
+  build_segments<RING, WB>(P, si, w, wave, sm, p_new);
   for (int i = tid; i < m.hd / 2; i += kThreads) {
     const float2 cs = P.rope[(int64_t)si.p * (m.hd / 2) + i];
     sm.rope_c[i] = cs.x;
     sm.rope_s[i] = cs.y;
   }
-  for (int i = tid; i < m.d; i += kThreads) sm.act[i] = load_w<WB>(P.embed, (int64_t)token * m.d + i);
+  for (int i = tid; i < m.d; i += kThreads) sm.act[i] = load_w<EB>(P.embed, (int64_t)token * m.d + i);
   wg_barrier();  // segment tables and the cancel word visible
 
   rg.cnt = 0;
@@ -1014,10 +1065,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   stamp(1);
 
   for (int layer = 0; layer < m.L; ++layer) {
-    const uint8_t* g_attn = P.norms + ((int64_t)layer * 2 + 0) * m.d * m.wbytes;
-    const uint8_t* g_ffn = P.norms + ((int64_t)layer * 2 + 1) * m.d * m.wbytes;
+    const uint8_t* g_attn = P.norms + ((int64_t)layer * 2 + 0) * m.d * EB;
+    const uint8_t* g_ffn = P.norms + ((int64_t)layer * 2 + 1) * m.d * EB;
+    // fp8 row scales of this layer: each thread that publishes a row loads its scale ahead of the
+    // gather before it, so the load's latency hides behind that wait
+    const float* const scl = FP8 ? P.scales + (int64_t)layer * scl_at.layer : nullptr;
+    float s_q = 1.f;
+    if constexpr (FP8)
+      if (tid < nq) s_q = scl[rq0 + tid];
     // ---- x (this WG's rows kept raw for the residual), RMSNorm folded into the gather ----
-    load_piece_gains<WB>(g_attn, m.d, fold.g);
+    load_piece_gains<EB>(g_attn, m.d, fold.g);
     fold.ss = 0.f;
     {
       auto put_x = [&](int k, float a, float b) {
@@ -1051,7 +1108,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     wg_barrier();
     stamp(trace_slot(layer, 2));
     if (tid < nq)
-      ll_store(P.ll, P.lo.qkv + rq0 + tid, row_total(sm, kTileQKV, m.cd, tid) * r_attn, ll_tag(tb0, layer, kQKV));
+      ll_store(P.ll, P.lo.qkv + rq0 + tid, row_total(sm, kTileQKV, m.cd, tid) * r_attn * s_q, ll_tag(tb0, layer, kQKV));
     stamp(trace_slot(layer, 3));
     // ---- attention units: one chunk of positions of one kv head each ----
     for (int k = 0; k < si.nunits; ++k) {
@@ -1242,19 +1299,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     }
     stamp(trace_slot(layer, 12));
     // ---- output projection rows + residual ----
+    float s_o = 1.f;
+    if constexpr (FP8)
+      if (tid < nrd) s_o = scl[scl_at.o + rd0 + tid];
     if (!xc.gather_vec(ll_tag(tb0, layer, kO), P.lo.o, m.qdim, sm.act)) goto drain;
     stamp(trace_slot(layer, 13));
     consume_rows<RING, WB, MULTI>(rg, uniform(tab[oseg]), m.cq, sm.act, sm.rowpart[wave]);
     wg_barrier();
     stamp(trace_slot(layer, 14));
     if (tid < nrd) {
-      const float xp = sm.xo[tid] + row_total(sm, kTileO, m.cq, tid);
+      const float xp = sm.xo[tid] + row_total(sm, kTileO, m.cq, tid) * s_o;
       sm.xo[tid] = xp;
       ll_store(P.ll, P.lo.xp + rd0 + tid, xp, ll_tag(tb0, layer, kXP));
     }
     stamp(trace_slot(layer, 15));
     // ---- gate/up rows of this workgroup's FFN slice ----
-    load_piece_gains<WB>(g_ffn, m.d, fold.g);
+    float s_g = 1.f, s_u = 1.f;
+    if constexpr (FP8)
+      if (tid < nf) {
+        s_g = scl[scl_at.gu + 2 * f0 + tid];
+        s_u = scl[scl_at.gu + 2 * f0 + nf + tid];
+      }
+    load_piece_gains<EB>(g_ffn, m.d, fold.g);
     fold.ss = 0.f;
     if (!xc.gather(ll_tag(tb0, layer, kXP), m.d / 2, [&](int k) -> int64_t { return P.lo.xp + 2 * (int64_t)k; },
                    [&](int k, float a, float b) { fold.put(sm.act, k, a, b); }, [&] { fold.finish(sm); }))
@@ -1266,8 +1332,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     wg_barrier();
     stamp(trace_slot(layer, 18));
     if (tid < nf) {
-      const float gt = row_total(sm, kTileGU, m.cd, tid) * r_ffn;
-      const float up = row_total(sm, kTileGU, m.cd, nf + tid) * r_ffn;
+      const float gt = row_total(sm, kTileGU, m.cd, tid) * r_ffn * s_g;
+      const float up = row_total(sm, kTileGU, m.cd, nf + tid) * r_ffn * s_u;
       sm.a[tid] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;  // hardware reciprocal (1 ulp)
     }
     wg_barrier();
@@ -1279,6 +1345,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     {
       float* st = sm.u.stage;  // [nrd][nwg]: each row's partials contiguous (conflict-free reads)
       const int hp = nrd / 2;  // pieces per producer
+      // T = kThreads / nrd threads per row when nrd is a power of two from 8 to 64, else one wave
+      // per row (see below); fp8: the scale of the row this thread finishes, loaded ahead
+      float s_d = 1.f;
+      if constexpr (FP8) {
+        const bool pt = nrd >= 8 && nrd <= 64 && (nrd & (nrd - 1)) == 0;
+        const int rr = pt ? tid / (kThreads / max(nrd, 1)) : wave;
+        if (rr < nrd) s_d = scl[scl_at.d + rd0 + rr];
+      }
       const bool ok = nrd == 0 ||
                       xc.gather(
                           ll_tag(tb0, layer, kDP), m.nwg * hp,
@@ -1305,12 +1379,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
         else if (T == 32) s = xsum16(sum_rows16(s));
         else if (T == 16) s = sum_rows16(s);
         else s = sum_rows8(s);
-        if (j == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(tb0, layer, kX));
+        if (j == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s * s_d, ll_tag(tb0, layer, kX));
       } else {
         for (int r = wave; r < nrd; r += kWaves) {
           float s = 0.f;
           for (int q = lane; q < m.nwg; q += 64) s += st[r * m.nwg + q];
           s = wave_sum(s);
+          if constexpr (FP8) s *= r == wave ? s_d : scl[scl_at.d + rd0 + r];
           if (lane == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(tb0, layer, kX));
         }
       }
@@ -1321,7 +1396,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   }
 
   // ---- final norm, LM head rows, argmax ----
-  load_piece_gains<WB>(P.norms + (int64_t)m.L * 2 * m.d * m.wbytes, m.d, fold.g);
+  float s_l = 1.f;  // fp8: scale of this thread's first LM-head row
+  if constexpr (FP8)
+    if (tid < nl) s_l = P.scales[scl_at.lm + rl0 + tid];
+  load_piece_gains<EB>(P.norms + (int64_t)m.L * 2 * m.d * EB, m.d, fold.g);
   fold.ss = 0.f;
   if (!xc.gather(ll_tag(tb0, m.L - 1, kX), m.d / 2, [&](int k) -> int64_t { return P.lo.x + 2 * (int64_t)k; },
                  [&](int k, float a, float b) { fold.put(sm.act, k, a, b); }, [&] { fold.finish(sm); }))
@@ -1336,7 +1414,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     int32_t besti = 0x7fffffff;
     bool nan = false;
     for (int r = tid; r < nl; r += kThreads) {
-      const float val = row_total(sm, kTileLM, m.cd, r) * r_final;
+      float val = row_total(sm, kTileLM, m.cd, r) * r_final;
+      if constexpr (FP8) val *= r == tid ? s_l : P.scales[scl_at.lm + rl0 + r];
       if (P.logits) P.logits[(int64_t)step * m.V + rl0 + r] = val;
       if (val != val) { nan = true; continue; }
       if (better(val, rl0 + r, best, besti)) { best = val; besti = rl0 + r; }

@@ -53,7 +53,7 @@ KD_HD int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Dims {
   int32_t L, d, hq, hkv, hd, F, V, S, nwg;  // S: KV positions allocated per (layer, slot, session, head)
-  int32_t wbytes, kvbytes;                 // 2 (bf16) or 4 (f32)
+  int32_t wbytes, kvbytes;                 // matrix elements: 1 (fp8), 2 (bf16) or 4 (f32); cache: 2 or 4
   int32_t G, qdim, kvdim, nqkv;            // nqkv = qdim + 2*kvdim rows of the fused QKV matrix
   int32_t vpl;                             // weight values per 16-byte lane load
   int32_t kv_vpl;                          // KV values per 16-byte lane load
@@ -62,6 +62,22 @@ struct Dims {
   int64_t off_qkv, off_o, off_gu, off_d, layer_elems, off_lm;  // element offsets in the packed blob
   int64_t blob_elems;
 };
+
+// fp8 row scales (floats): per layer the QKV rows, the O rows, the gate/up rows in packed order and
+// the down rows; then the LM head's rows.
+struct ScaleLayout {
+  int64_t o, gu, d, layer, lm, total;
+};
+KD_HD ScaleLayout scale_layout(const Dims& m) {
+  ScaleLayout s{};
+  s.o = m.nqkv;
+  s.gu = s.o + m.d;
+  s.d = s.gu + (int64_t)2 * m.F;
+  s.layer = s.d + m.d;
+  s.lm = (int64_t)m.L * s.layer;
+  s.total = s.lm + m.V;
+  return s;
+}
 
 KD_HD Dims make_dims(int L, int d, int hq, int hkv, int hd, int F, int V, int max_seq, int nwg, int wbytes, int kvbytes) {
   Dims m{};
@@ -83,8 +99,15 @@ KD_HD Dims make_dims(int L, int d, int hq, int hkv, int hd, int F, int V, int ma
   return m;
 }
 
-// FFN columns owned by workgroup w: [ffn_lo(w), ffn_lo(w+1)), aligned to whole 16-byte lane loads.
-KD_HD int64_t ffn_lo(const Dims& m, int64_t w) { return (int64_t)m.vpl * part_lo(m.F / m.vpl, m.nwg, w); }
+// Element bytes of the embedding and the norm gains: bf16 when the matrices are fp8.
+KD_HD int32_t embed_bytes(const Dims& m) { return m.wbytes == 1 ? 2 : m.wbytes; }
+// FFN columns per slice unit (a workgroup owns whole units). fp8 keeps 8-column units: a down
+// packet then holds two 64-row halves of 8 columns each, so a down block is 128 rows.
+KD_HD int32_t ffn_unit(const Dims& m) { return m.wbytes == 1 ? 8 : m.vpl; }
+KD_HD int32_t down_block_rows(const Dims& m) { return m.wbytes == 1 ? 128 : 64; }
+
+// FFN columns owned by workgroup w: [ffn_lo(w), ffn_lo(w+1)), whole units of ffn_unit columns.
+KD_HD int64_t ffn_lo(const Dims& m, int64_t w) { return (int64_t)ffn_unit(m) * part_lo(m.F / ffn_unit(m), m.nwg, w); }
 
 // Element offset of workgroup w's down-projection packets inside a layer's down block.
 KD_HD int64_t down_wg_off(const Dims& m, int64_t w) { return (int64_t)m.d * ffn_lo(m, w); }

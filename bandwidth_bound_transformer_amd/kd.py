@@ -39,6 +39,7 @@ KD_CTRL_WAIT_LIMIT_US = 2
 
 KD_DTYPE_F32 = 0
 KD_DTYPE_BF16 = 1
+KD_DTYPE_FP8_E4M3 = 2
 
 EXPORTS = (
     "kd_init",
@@ -80,8 +81,13 @@ class kd_config(ctypes.Structure):
     ]
 
 
+_LAYER_TENSORS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+_LAYER_SCALES = (("wq", "s_wq"), ("wk", "s_wk"), ("wv", "s_wv"), ("wo", "s_wo"), ("w_gate", "s_gate"), ("w_up", "s_up"),
+                 ("w_down", "s_down"))
+
+
 class kd_layer_weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")]
+    _fields_ = [(n, ctypes.c_void_p) for n in _LAYER_TENSORS] + [(s, ctypes.c_void_p) for _, s in _LAYER_SCALES]
 
 
 class kd_weights(ctypes.Structure):
@@ -90,6 +96,7 @@ class kd_weights(ctypes.Structure):
         ("layers", ctypes.POINTER(kd_layer_weights)),
         ("final_norm", ctypes.c_void_p),
         ("lm_head", ctypes.c_void_p),
+        ("s_lm_head", ctypes.c_void_p),
     ]
 
 
@@ -142,7 +149,7 @@ def _check(code: int, what: str) -> None:
 
 def make_config(shape, batch: int = 1, max_seq: int = 1) -> kd_config:
     """kd_config of a ``workloads.ModelShape``."""
-    dt = {"f32": KD_DTYPE_F32, "bf16": KD_DTYPE_BF16}
+    dt = {"f32": KD_DTYPE_F32, "bf16": KD_DTYPE_BF16, "fp8": KD_DTYPE_FP8_E4M3}
     return kd_config(
         shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim,
         shape.vocab, max_seq, batch, shape.norm_eps, shape.rope_base, dt[shape.weight_dtype], dt[shape.kv_dtype],
@@ -163,14 +170,25 @@ def kd_kv_layout(cfg: kd_config):
     return nbytes.value, tuple(strides)
 
 
+def _tensor_ptrs(t):
+    """(data pointer, row-scale pointer or None): an fp8 matrix carries codes and scales."""
+    if hasattr(t, "codes"):
+        return _host_ptr(t.codes), _host_ptr(t.scale)
+    return _host_ptr(t), None
+
+
 def kd_init(cfg: kd_config, weights: dict) -> int:
     """Pack ``weights`` (dict from ``workloads.make_weights``) onto the current device; returns a handle."""
-    names = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+    scale_of = dict(_LAYER_SCALES)
     layers = (kd_layer_weights * cfg.n_layers)()
     for i, lw in enumerate(weights["layers"]):
-        for n in names:
-            setattr(layers[i], n, _host_ptr(lw[n]))
-    w = kd_weights(_host_ptr(weights["embed"]), layers, _host_ptr(weights["final_norm"]), _host_ptr(weights["lm_head"]))
+        for n in _LAYER_TENSORS:
+            data, scale = _tensor_ptrs(lw[n])
+            setattr(layers[i], n, data)
+            if scale is not None:
+                setattr(layers[i], scale_of[n], scale)
+    lm, lm_scale = _tensor_ptrs(weights["lm_head"])
+    w = kd_weights(_host_ptr(weights["embed"]), layers, _host_ptr(weights["final_norm"]), lm, lm_scale)
     h = ctypes.c_void_p()
     _check(library().kd_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)), "kd_init")
     return h.value

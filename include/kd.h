@@ -69,6 +69,12 @@ extern "C" {
 /* ---- number formats ---------------------------------------------------------- */
 #define KD_DTYPE_F32 0  /* IEEE binary32 */
 #define KD_DTYPE_BF16 1 /* bfloat16: the top 16 bits of a binary32 */
+/* OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 fraction bits; no infinities; S.1111.111 is
+   NaN), weight_dtype only: the projection matrices and the LM head are E4M3 codes with one float32
+   scale per output row, and the embedding, the norm gains and the cache are bf16. Cutting the
+   bytes of the parameters cuts what every token reads ("17k tokens/sec" page, best practice 2 on
+   model quantisation, and its FAQ question 3, which names FP8). */
+#define KD_DTYPE_FP8_E4M3 2
 
 /*
  * Model and run configuration, fixed at kd_init.
@@ -87,7 +93,9 @@ extern "C" {
  *                (n_q_heads+2*n_kv_heads)*head_dim and vocab multiples of 128.
  *   norm_eps     RMSNorm epsilon (inside the square root).
  *   rope_base    RoPE base: pair (i, i + head_dim/2) turns by position * rope_base^(-2i/head_dim).
- *   weight_dtype KD_DTYPE_BF16 or KD_DTYPE_F32; kv_dtype likewise (must match weight_dtype).
+ *   weight_dtype KD_DTYPE_BF16 or KD_DTYPE_F32, with kv_dtype the same; or KD_DTYPE_FP8_E4M3
+ *                with kv_dtype KD_DTYPE_BF16 (batch 1, head_dim 128, d_model and q_dim multiples
+ *                of 1024, ffn_dim a multiple of 8 with ffn_dim/8 >= the GPU's compute units).
  */
 typedef struct kd_config {
   int32_t n_layers;
@@ -105,7 +113,10 @@ typedef struct kd_config {
   int32_t kv_dtype;
 } kd_config;
 
-/* Host pointers to one layer's tensors, row-major, in weight_dtype (bf16 = uint16 patterns). */
+/* Host pointers to one layer's tensors, row-major, in weight_dtype (bf16 = uint16 patterns). With
+ * KD_DTYPE_FP8_E4M3 the seven matrices are uint8 E4M3 codes, the gains bf16, and the s_* arrays
+ * hold the float32 scale of each output row of the matching matrix: the weight at (r, c) is the
+ * code's value times row r's scale. For other weight types the s_* pointers are ignored. */
 typedef struct kd_layer_weights {
   const void* attn_norm; /* [d_model] */
   const void* wq;        /* [n_q_heads*head_dim, d_model] */
@@ -116,6 +127,13 @@ typedef struct kd_layer_weights {
   const void* w_gate;    /* [ffn_dim, d_model] */
   const void* w_up;      /* [ffn_dim, d_model] */
   const void* w_down;    /* [d_model, ffn_dim] */
+  const float* s_wq;     /* [n_q_heads*head_dim]  fp8 only: row scales */
+  const float* s_wk;     /* [n_kv_heads*head_dim] */
+  const float* s_wv;     /* [n_kv_heads*head_dim] */
+  const float* s_wo;     /* [d_model] */
+  const float* s_gate;   /* [ffn_dim] */
+  const float* s_up;     /* [ffn_dim] */
+  const float* s_down;   /* [d_model] */
 } kd_layer_weights;
 
 /* Host pointers to all weights.  layers points to n_layers entries. */
@@ -124,6 +142,7 @@ typedef struct kd_weights {
   const kd_layer_weights* layers; /* [n_layers] */
   const void* final_norm;         /* [d_model] */
   const void* lm_head;            /* [vocab, d_model] (separate from embed) */
+  const float* s_lm_head;         /* [vocab] fp8 only: row scales of lm_head */
 } kd_weights;
 
 typedef struct kd_handle kd_handle;

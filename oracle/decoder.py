@@ -104,6 +104,11 @@ def fp8_e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
     return np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, out)
 
 
+# the value of every code, from the definition above (large matrices index it rather than
+# evaluating the definition element by element)
+_E4M3_VALUES = fp8_e4m3_to_f64(np.arange(256, dtype=np.uint8))
+
+
 def weight_f64(w, dtype: str) -> np.ndarray:
     """float64 values of a stored weight tensor.
 
@@ -112,7 +117,7 @@ def weight_f64(w, dtype: str) -> np.ndarray:
     value is the code's value times its row's scale, and bf16 patterns for the rest.
     """
     if dtype == "fp8" and hasattr(w, "codes"):
-        return fp8_e4m3_to_f64(w.codes) * np.asarray(w.scale, np.float32).astype(np.float64)[:, None]
+        return _E4M3_VALUES[np.asarray(w.codes, np.uint8)] * np.asarray(w.scale, np.float32).astype(np.float64)[:, None]
     if dtype in ("bf16", "fp8"):
         return bf16_to_f64(w)
     if dtype == "f32":

@@ -44,9 +44,30 @@ def test_header_compiles_as_c():
 
 
 def test_struct_layout_matches_binding():
-    assert ctypes.sizeof(kd.kd_config) == 13 * 4
-    assert ctypes.sizeof(kd.kd_layer_weights) == 9 * 8
-    assert ctypes.sizeof(kd.kd_weights) == 4 * 8
+    """Every field of the ctypes structs sits where a C compiler puts it, given kd.h."""
+    structs = {"kd_config": kd.kd_config, "kd_layer_weights": kd.kd_layer_weights, "kd_weights": kd.kd_weights}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "kd.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'  printf("{name} size %zu\\n", sizeof({name}));')
+        for field, _ in cls._fields_:
+            lines.append(f'  printf("{name} {field} %zu\\n", offsetof({name}, {field}));')
+    lines += ["  return 0;", "}"]
+    exe = os.path.join(os.environ.get("TMPDIR", "/tmp"), f"kd_layout_{os.getpid()}")
+    res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-x", "c", "-", "-o", exe],
+                         input="\n".join(lines) + "\n", capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    try:
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    finally:
+        os.unlink(exe)
+    want = {}
+    for line in filter(None, out):
+        sname, field, val = line.split()
+        want[(sname, field)] = int(val)
+    for name, cls in structs.items():
+        assert ctypes.sizeof(cls) == want[(name, "size")], name
+        for field, _ in cls._fields_:
+            assert getattr(cls, field).offset == want[(name, field)], (name, field)
 
 
 def test_strerror_covers_every_code():
