@@ -136,6 +136,8 @@ struct kd_handle {
   hipStream_t ctl = nullptr;  // private non-blocking stream for cancel-word writes
   bool batched = false;  // B > 1: the lockstep-sessions path (kd_batch.h)
   kd::bt::BatchState bs;
+  bool prefill = false;  // batch 1 with kd_prefill: the lockstep kernels, rows = prompt positions
+  kd::bt::BatchState ps;
 };
 
 namespace {
@@ -154,12 +156,19 @@ int check_config(const kd_config* c) {
   if (!weight_dtype_ok(c->weight_dtype) || !dtype_ok(c->kv_dtype)) return KD_ERR_INVALID_ARG;
   if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f)) return KD_ERR_INVALID_ARG;
   if (c->max_seq > (1 << 24) || c->vocab > (1 << 30)) return KD_ERR_INVALID_ARG;
+  if (c->prefill_chunk < 0 || c->prefill_chunk > 64 || c->prefill_chunk == 1) return KD_ERR_INVALID_ARG;
   return KD_OK;
 }
 
 // Limits of this implementation for a valid configuration, given the grid size.
 int check_supported(const kd_config* c, const kd::Dims& m) {
   if (c->batch != 1) return KD_ERR_UNSUPPORTED;
+  if (c->prefill_chunk > 0) {  // the lockstep kernels must take the shape
+    kd_config pc = *c;
+    pc.batch = c->prefill_chunk;
+    const int rc = kd::bt::batch_check(&pc);
+    if (rc != KD_OK) return rc;
+  }
   if (c->head_dim != 64 && c->head_dim != 128) return KD_ERR_UNSUPPORTED;
   // fp8 matrices come with bf16 embedding, gains and cache, and head_dim 128
   if (c->weight_dtype == KD_DTYPE_FP8_E4M3 ? (c->kv_dtype != KD_DTYPE_BF16 || c->head_dim != 128)
@@ -272,6 +281,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
   const int eb = fp8 ? 2 : wb;  // embedding and norm gains
   const int nwg = prop.multiProcessorCount;
   if (cfg->batch > 1) {
+    if (cfg->prefill_chunk != 0) return KD_ERR_INVALID_ARG;  // lockstep handles take no prefill
     rc = kd::bt::batch_check(cfg);
     if (rc != KD_OK) return rc;
     kd_handle* hb = new (std::nothrow) kd_handle();
@@ -413,6 +423,14 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
     (void)hipFree(tmp);
     tmp = nullptr;
   }
+  if (cfg->prefill_chunk > 0) {
+    // the prefill engine: the lockstep kernels with prefill_chunk rows (weights in their tile layout)
+    kd_config pc = *cfg;
+    pc.batch = cfg->prefill_chunk;
+    rc = kd::bt::batch_init(&pc, w, nwg, h->ps);
+    if (rc != KD_OK) goto fail;
+    h->prefill = true;
+  }
   *out = h;
   return KD_OK;
 
@@ -420,6 +438,7 @@ fail:
   if (tmp) (void)hipFree(tmp);
   if (h->ctl) (void)hipStreamDestroy(h->ctl);
   free_buffers(h->buf);
+  if (h->prefill) kd::bt::batch_free(h->ps);
   delete h;
   return rc;
 }
@@ -546,6 +565,15 @@ int kd_step_noalloc(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv,
                          (hipStream_t)stream);
 }
 
+int kd_prefill(kd_handle* h, const int32_t* prompt, int32_t n, int32_t* tokens, int32_t* positions, void* kv,
+               float* logits, void* stream) {
+  if (!h || !prompt || !tokens || !positions || !kv || n < 1) return KD_ERR_INVALID_ARG;
+  if (!h->prefill) return KD_ERR_UNSUPPORTED;
+  DeviceGuard g(h->device);
+  if (!g.ok) return KD_ERR_HIP;
+  return kd::bt::batch_prefill(h->ps, prompt, n, tokens, positions, kv, logits, (hipStream_t)stream, h->buf.flags);
+}
+
 int kd_generate(kd_handle* h, int32_t n_steps, int32_t* tokens, int32_t* positions, void* kv, int32_t* out_tokens,
                 float* logits, uint32_t* progress, void* stream) {
   if (!h || !tokens || !positions || !kv || n_steps < 1) return KD_ERR_INVALID_ARG;
@@ -606,6 +634,7 @@ void kd_destroy(kd_handle* h) {
     if (h->ctl) (void)hipStreamDestroy(h->ctl);
     free_buffers(h->buf);
     if (h->batched) kd::bt::batch_free(h->bs);
+    if (h->prefill) kd::bt::batch_free(h->ps);
   }
   delete h;
 }
@@ -652,6 +681,7 @@ int kd_get_info(kd_handle* h, int64_t info[8]) {
             (int64_t)(2 * h->m.L + 1) * h->m.d * kd::embed_bytes(h->m) + (h->buf.scales ? kd::scale_layout(h->m).total * 4 : 0);
   info[3] = h->lds_bytes;
   info[4] = kRing;
+  info[5] = h->prefill ? h->ps.B : 0;
   return KD_OK;
 }
 

@@ -661,5 +661,33 @@ __global__ void progress_kernel(uint32_t* progress, uint32_t value, const uint32
   __hip_atomic_store(progress, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// ---------------------------------------------------------------------------------------------
+// prefill: a chunk of prompt positions of one session as the rows of a tick
+// ---------------------------------------------------------------------------------------------
+// Rows b < nb of a prefill chunk: prompt token first + b at position *pos0 + first + b.
+// Grid: one workgroup of 64 threads (nb <= 64).
+__global__ void prefill_rows_kernel(const int32_t* __restrict__ prompt, int first, int nb, const int32_t* __restrict__ pos0,
+                                    int32_t* __restrict__ tokens, int32_t* __restrict__ positions) {
+  const int b = (int)threadIdx.x;
+  if (b >= nb) return;
+  tokens[b] = prompt[first + b];
+  positions[b] = *pos0 + first + b;
+}
+
+// After the last chunk: the last row's greedy token and next position (the argmax already wrote
+// them into the row arrays) and its logits go to the caller. Grid: any, 256 threads.
+__global__ void prefill_finish_kernel(const int32_t* __restrict__ row_tokens, const int32_t* __restrict__ row_positions,
+                                      int last, const float* __restrict__ row_logits, int V, int32_t* tokens,
+                                      int32_t* positions, float* logits, const uint32_t* skip) {
+  if (*skip) return;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t == 0) {
+    tokens[0] = row_tokens[last];
+    positions[0] = row_positions[last];
+  }
+  if (logits)
+    for (int64_t v = t; v < V; v += (int64_t)gridDim.x * blockDim.x) logits[v] = row_logits[(int64_t)last * V + v];
+}
+
 }  // namespace bt
 }  // namespace kd

@@ -43,15 +43,20 @@ struct BatchState {
   float* Qs = nullptr;              // [B][hq * hd] rotated, scaled queries
   float* part = nullptr;            // attention chunk partials [B][hq][NCmax][hd + 2]
   float* logits = nullptr;          // [B][V] when the caller passes none
+  int32_t* rows_tok = nullptr;      // prefill: the chunk's tokens, then its greedy tokens [B]
+  int32_t* rows_pos = nullptr;      // prefill: the chunk's positions [B]
   size_t w_qkv = 0, w_o = 0, w_gu = 0, w_d = 0, w_lm = 0;  // element offsets inside a layer / the blob
 };
 
 // Split-K factor of a GEMM: the power of two whose estimated time is least, over K ranges of
-// 2, 4, 8, 16 or 32 chunks of 128 K (the unrolled kernel variants). The estimate: the weight
+// 2, 4, 7, 8, 14, 16, 28 or 32 chunks of 128 K (the unrolled kernel variants; 7, 14 and 28 take
+// K = 14336, the Llama-3-8B FFN width). The estimate: the weight
 // stream at about 6.5 TB/s, or, when there are too few workgroups for that, rounds of one
 // workgroup per CU each paying a fixed start-up latency and streaming at a single CU's rate;
 // plus writing and reading back the fp32 partial sums. Returns -1 if no split is valid.
-inline bool chunks_ok(int nch) { return nch == 2 || nch == 4 || nch == 8 || nch == 16 || nch == 32; }
+inline bool chunks_ok(int nch) {
+  return nch == 2 || nch == 4 || nch == 7 || nch == 8 || nch == 14 || nch == 16 || nch == 28 || nch == 32;
+}
 inline int pick_ks(int N, int K, int B, int nwg) {
   const double bw = 6.5e12, bw_cu = 50e9, start = 3e-6;
   const int nch_all = K / kKC;
@@ -78,8 +83,11 @@ inline GemmFn gemm_for(int nch) {
   switch (nch) {
     case 2: return gemm_kernel<2, SILU>;
     case 4: return gemm_kernel<4, SILU>;
+    case 7: return gemm_kernel<7, SILU>;
     case 8: return gemm_kernel<8, SILU>;
+    case 14: return gemm_kernel<14, SILU>;
     case 16: return gemm_kernel<16, SILU>;
+    case 28: return gemm_kernel<28, SILU>;
     case 32: return gemm_kernel<32, SILU>;
     default: return nullptr;
   }
@@ -106,7 +114,7 @@ inline int batch_check(const kd_config* c) {
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return KD_ERR_UNSUPPORTED;
   const int64_t qdim = (int64_t)c->n_q_heads * c->head_dim, nqkv = qdim + 2LL * c->n_kv_heads * c->head_dim;
-  // every GEMM's K must split into ranges of 2, 4, 8, 16 or 32 chunks of 128
+  // every GEMM's K must split into ranges of 2, 4, 7, 8, 14, 16, 28 or 32 chunks of 128
   for (int64_t K : {(int64_t)c->d_model, qdim, (int64_t)c->ffn_dim}) {
     if (K % kKC) return KD_ERR_UNSUPPORTED;
     int64_t nch = K / kKC;
@@ -119,7 +127,8 @@ inline int batch_check(const kd_config* c) {
 }
 
 inline void batch_free(BatchState& st) {
-  void* ptrs[] = {st.w, st.embed, st.norms, st.rope, st.X, st.Ahi, st.Alo, st.A2hi, st.A2lo, st.P, st.Qs, st.part, st.logits};
+  void* ptrs[] = {st.w,  st.embed, st.norms, st.rope, st.X,      st.Ahi,      st.Alo,      st.A2hi,
+                  st.A2lo, st.P,   st.Qs,    st.part, st.logits, st.rows_tok, st.rows_pos};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   st = BatchState{};
@@ -184,6 +193,8 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, BatchSta
   KD_BT_ALLOC(st.Qs, (size_t)st.B * st.qdim * 4);
   KD_BT_ALLOC(st.part, (size_t)st.B * st.hq * st.NCmax * (st.hd + 2) * 4);
   KD_BT_ALLOC(st.logits, (size_t)st.B * st.V * 4);
+  KD_BT_ALLOC(st.rows_tok, (size_t)st.B * 4);
+  KD_BT_ALLOC(st.rows_pos, (size_t)st.B * 4);
   KD_BT_TRY(hipMemset(st.Ahi, 0, (size_t)kM * st.lda * 2));  // padding rows stay zero for good
   KD_BT_TRY(hipMemset(st.Alo, 0, (size_t)kM * st.lda * 2));
   KD_BT_TRY(hipMemset(st.A2hi, 0, (size_t)kM * st.lda * 2));
@@ -260,41 +271,53 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, BatchSta
 // Kernels one tick enqueues: check, embed+norm, 10 per layer, LM head, argmax.
 inline int batch_kernels_per_tick(const BatchState& st) { return 2 + (fused_silu(st) ? 9 : 10) * st.L + 2; }
 
-// Enqueue one tick. flags: [0] sticky status bits, [2] this tick's skip flag, [3] the cancel word.
-// out (optional) receives the tick's B tokens; progress (optional) is set to progress_value after it.
-inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions, void* kvp, float* logits,
-                      hipStream_t s, uint32_t* flags, int32_t* out, uint32_t* progress, uint32_t progress_value) {
+// Where a tick's rows keep their K and V: element strides of the cache's layer, K/V slot, row
+// (session) and kv head. Lockstep sessions each have their own slab; the rows of a prefill chunk
+// all share one session's, with row stride 0.
+struct KvStrides {
+  int64_t layer, slot, row, head;
+};
+inline KvStrides session_strides(const BatchState& st) {
+  const int64_t head = (int64_t)st.S * st.hd, row = st.hkv * head, slot = st.B * row;
+  return {2 * slot, slot, row, head};
+}
+
+// Enqueue one tick of nb <= B rows. flags: [0] sticky status bits, [2] this tick's skip flag, [3]
+// the cancel word. lm: run the LM head and the argmax (which writes tokens and advances
+// positions). out (optional) receives the tick's tokens; progress (optional) is set to
+// progress_value after it.
+inline int batch_tick(const BatchState& st, int nb, int32_t* tokens, int32_t* positions, void* kvp, KvStrides kvs,
+                      float* logits, bool lm, hipStream_t s, uint32_t* flags, int32_t* out, uint32_t* progress,
+                      uint32_t progress_value) {
   uint32_t* status = flags;
   const uint32_t* skip = flags + 2;
   uint16_t* kv = (uint16_t*)kvp;
-  const int64_t kv_head = (int64_t)st.S * st.hd, kv_sess = st.hkv * kv_head, kv_slot = st.B * kv_sess,
-                kv_layer = 2 * kv_slot;
   float* lg = logits ? logits : st.logits;
   auto gemm = [&](const uint16_t* W, const Gemm& g, float* out) {
     hipLaunchKernelGGL(gemm_for<false>(g.K / (g.KS * kKC)), dim3((g.N / kNB) * g.KS), dim3(kGemmThreads), 0, s, W, g.N,
-                       g.K, (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, out, g.KS, st.B, skip,
+                       g.K, (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, out, g.KS, nb, skip,
                        (uint16_t*)nullptr, (uint16_t*)nullptr);
   };
   auto norm = [&](int mode, const Gemm* g, int gain_index) {
-    hipLaunchKernelGGL(residual_norm_kernel, dim3(st.B), dim3(1024), 0, s, mode, (const uint16_t*)st.embed,
+    hipLaunchKernelGGL(residual_norm_kernel, dim3(nb), dim3(1024), 0, s, mode, (const uint16_t*)st.embed,
                        (const int32_t*)tokens, (const float*)st.P, g ? g->KS : 0, st.X,
                        (const uint16_t*)(st.norms + (size_t)gain_index * st.d), st.d, st.eps, st.Ahi, st.Alo, st.lda,
-                       st.B, skip);
+                       nb, skip);
   };
-  hipLaunchKernelGGL(check_kernel, dim3(1), dim3(1), 0, s, (const int32_t*)tokens, (const int32_t*)positions, st.B, st.V,
+  hipLaunchKernelGGL(check_kernel, dim3(1), dim3(1), 0, s, (const int32_t*)tokens, (const int32_t*)positions, nb, st.V,
                      st.max_seq, status, flags + 2, (const uint32_t*)(flags + 3));
   norm(0, nullptr, 0);
   for (int l = 0; l < st.L; ++l) {
     const uint16_t* lay = st.w + (size_t)l * st.layer_elems;
-    uint16_t* kvl = kv + (int64_t)l * kv_layer;
+    uint16_t* kvl = kv + (int64_t)l * kvs.layer;
     gemm(lay + st.w_qkv, st.g_qkv, st.P);
-    hipLaunchKernelGGL(qkv_epilogue_kernel, dim3(st.hq + 2 * st.hkv, st.B), dim3(st.hd), 0, s, (const float*)st.P,
+    hipLaunchKernelGGL(qkv_epilogue_kernel, dim3(st.hq + 2 * st.hkv, nb), dim3(st.hd), 0, s, (const float*)st.P,
                        st.g_qkv.KS, st.nqkv, st.hq, st.hkv, st.hd, (const float2*)st.rope, (const int32_t*)positions,
-                       st.Qs, kvl, kv_slot, kv_sess, kv_head, st.B, skip);
-    hipLaunchKernelGGL(att_for(st.hq / st.hkv), dim3(st.NCmax, st.hkv, st.B), dim3(kAttThreads), 0, s, (const float*)st.Qs,
-                       (const uint16_t*)kvl, kv_slot, kv_sess, kv_head, (const int32_t*)positions, st.hq, st.hkv,
+                       st.Qs, kvl, kvs.slot, kvs.row, kvs.head, nb, skip);
+    hipLaunchKernelGGL(att_for(st.hq / st.hkv), dim3(st.NCmax, st.hkv, nb), dim3(kAttThreads), 0, s, (const float*)st.Qs,
+                       (const uint16_t*)kvl, kvs.slot, kvs.row, kvs.head, (const int32_t*)positions, st.hq, st.hkv,
                        st.NCmax, st.part, skip);
-    hipLaunchKernelGGL(merge_kernel, dim3(st.hq, st.B), dim3(st.hd), 0, s, (const float*)st.part,
+    hipLaunchKernelGGL(merge_kernel, dim3(st.hq, nb), dim3(st.hd), 0, s, (const float*)st.part,
                        (const int32_t*)positions, st.hq, st.hd, st.CH, st.NCmax, st.Ahi, st.Alo, st.lda, skip);
     gemm(lay + st.w_o, st.g_o, st.P);
     norm(1, &st.g_o, 2 * l + 1);
@@ -303,23 +326,56 @@ inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions,
       // projection reads (the first is still being read while gate/up runs)
       const Gemm& g = st.g_gu;
       hipLaunchKernelGGL(gemm_for<true>(g.K / kKC), dim3(g.N / kNB), dim3(kGemmThreads), 0, s, lay + st.w_gu, g.N, g.K,
-                         (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, st.P, 1, st.B, skip, st.A2hi, st.A2lo);
+                         (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, st.P, 1, nb, skip, st.A2hi, st.A2lo);
       const Gemm& gd = st.g_d;
       hipLaunchKernelGGL(gemm_for<false>(gd.K / (gd.KS * kKC)), dim3((gd.N / kNB) * gd.KS), dim3(kGemmThreads), 0, s,
                          lay + st.w_d, gd.N, gd.K, (const uint16_t*)st.A2hi, (const uint16_t*)st.A2lo, st.lda, st.P, gd.KS,
-                         st.B, skip, (uint16_t*)nullptr, (uint16_t*)nullptr);
+                         nb, skip, (uint16_t*)nullptr, (uint16_t*)nullptr);
     } else {
       gemm(lay + st.w_gu, st.g_gu, st.P);
-      hipLaunchKernelGGL(silu_kernel, dim3(st.F / 256, st.B), dim3(256), 0, s, (const float*)st.P, st.g_gu.KS, st.F, st.Ahi,
-                         st.Alo, st.lda, st.B, skip);
+      hipLaunchKernelGGL(silu_kernel, dim3(st.F / 256, nb), dim3(256), 0, s, (const float*)st.P, st.g_gu.KS, st.F, st.Ahi,
+                         st.Alo, st.lda, nb, skip);
       gemm(lay + st.w_d, st.g_d, st.P);
     }
     norm(1, &st.g_d, l + 1 < st.L ? 2 * (l + 1) : 2 * st.L);
   }
-  gemm(st.w + st.w_lm, st.g_lm, lg);
-  hipLaunchKernelGGL(argmax_kernel, dim3(st.B), dim3(1024), 0, s, (const float*)lg, st.V, tokens, positions, status, skip,
-                     out);
+  if (lm) {
+    gemm(st.w + st.w_lm, st.g_lm, lg);
+    hipLaunchKernelGGL(argmax_kernel, dim3(nb), dim3(1024), 0, s, (const float*)lg, st.V, tokens, positions, status, skip,
+                       out);
+  }
   if (progress) hipLaunchKernelGGL(progress_kernel, dim3(1), dim3(1), 0, s, progress, progress_value, skip);
+  return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+// One tick of all B lockstep sessions.
+inline int batch_step(const BatchState& st, int32_t* tokens, int32_t* positions, void* kvp, float* logits,
+                      hipStream_t s, uint32_t* flags, int32_t* out, uint32_t* progress, uint32_t progress_value) {
+  return batch_tick(st, st.B, tokens, positions, kvp, session_strides(st), logits, true, s, flags, out, progress,
+                    progress_value);
+}
+
+// Prefill of one session (batch-1 cache layout): the n prompt tokens at positions *positions ..
+// *positions + n - 1, in chunks of up to B positions, each chunk one tick whose rows are its
+// positions. Every row appends its K and V to the session's cache and attends over positions 0 ..
+// its own, so the chunks must run in order. Only the last chunk runs the LM head; its last row's
+// greedy token, next position and logits go to tokens[0], positions[0] and logits.
+inline int batch_prefill(const BatchState& st, const int32_t* prompt, int n, int32_t* tokens, int32_t* positions,
+                         void* kvp, float* logits, hipStream_t s, uint32_t* flags) {
+  const int64_t head = (int64_t)st.S * st.hd, slot = st.hkv * head;
+  const KvStrides one{2 * slot, slot, 0, head};
+  for (int first = 0; first < n; first += st.B) {
+    const int nb = std::min(st.B, n - first);
+    const bool last = first + nb == n;
+    hipLaunchKernelGGL(prefill_rows_kernel, dim3(1), dim3(64), 0, s, prompt, first, nb, (const int32_t*)positions,
+                       st.rows_tok, st.rows_pos);
+    const int rc = batch_tick(st, nb, st.rows_tok, st.rows_pos, kvp, one, nullptr, last, s, flags, nullptr, nullptr, 0);
+    if (rc != KD_OK) return rc;
+    if (last)
+      hipLaunchKernelGGL(prefill_finish_kernel, dim3(64), dim3(256), 0, s, (const int32_t*)st.rows_tok,
+                         (const int32_t*)st.rows_pos, nb - 1, (const float*)st.logits, st.V, tokens, positions, logits,
+                         (const uint32_t*)(flags + 2));
+  }
   return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
 

@@ -46,6 +46,7 @@ EXPORTS = (
     "kd_kv_layout",
     "kd_step",
     "kd_step_noalloc",
+    "kd_prefill",
     "kd_generate",
     "kd_control",
     "kd_device_status",
@@ -78,6 +79,7 @@ class kd_config(ctypes.Structure):
         ("rope_base", ctypes.c_float),
         ("weight_dtype", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
+        ("prefill_chunk", ctypes.c_int32),
     ]
 
 
@@ -118,6 +120,8 @@ def library() -> ctypes.CDLL:
         lib.kd_step.restype = ctypes.c_int
         lib.kd_step_noalloc.argtypes = [ctypes.c_void_p] * 6
         lib.kd_step_noalloc.restype = ctypes.c_int
+        lib.kd_prefill.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 5
+        lib.kd_prefill.restype = ctypes.c_int
         lib.kd_generate.argtypes = [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 7
         lib.kd_generate.restype = ctypes.c_int
         lib.kd_control.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]
@@ -147,12 +151,13 @@ def _check(code: int, what: str) -> None:
         raise KDError(code, what)
 
 
-def make_config(shape, batch: int = 1, max_seq: int = 1) -> kd_config:
+def make_config(shape, batch: int = 1, max_seq: int = 1, prefill_chunk: int = 0) -> kd_config:
     """kd_config of a ``workloads.ModelShape``."""
     dt = {"f32": KD_DTYPE_F32, "bf16": KD_DTYPE_BF16, "fp8": KD_DTYPE_FP8_E4M3}
     return kd_config(
         shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim,
         shape.vocab, max_seq, batch, shape.norm_eps, shape.rope_base, dt[shape.weight_dtype], dt[shape.kv_dtype],
+        prefill_chunk,
     )
 
 
@@ -220,6 +225,16 @@ def kd_step_noalloc(handle: int, tokens, positions, kv, logits=None, stream=None
     )
 
 
+def kd_prefill(handle: int, prompt, n: int, tokens, positions, kv, logits=None, stream=None) -> None:
+    """Enqueue the prompt (device int32[n]) on the matrix cores; tokens[0] receives the next token."""
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(
+        library().kd_prefill(handle, _dev_ptr(prompt), int(n), _dev_ptr(tokens), _dev_ptr(positions), _dev_ptr(kv),
+                             _dev_ptr(logits), s),
+        "kd_prefill",
+    )
+
+
 def kd_generate(handle: int, n_steps: int, tokens, positions, kv, out_tokens=None, logits=None, progress=None,
                 stream=None) -> None:
     """Enqueue n_steps greedy decode steps in one call (device buffers as torch tensors or raw pointers)."""
@@ -280,13 +295,13 @@ def kd_stream_read(buf, nbytes: int, stream=None) -> None:
 class Decoder:
     """A handle plus the device buffers one session needs (torch for memory and streams only)."""
 
-    def __init__(self, shape, weights: dict, max_seq: int, batch: int = 1, device: str = "cuda:0"):
+    def __init__(self, shape, weights: dict, max_seq: int, batch: int = 1, device: str = "cuda:0", prefill_chunk: int = 0):
         import torch
 
         self.torch = torch
         self.device = torch.device(device)
         self.shape = shape
-        self.cfg = make_config(shape, batch, max_seq)
+        self.cfg = make_config(shape, batch, max_seq, prefill_chunk)
         with torch.cuda.device(self.device):
             self.handle = kd_init(self.cfg, weights)
         nbytes, self.kv_strides = kd_kv_layout(self.cfg)
@@ -306,6 +321,12 @@ class Decoder:
     def step(self, write_logits: bool = True, stream=None) -> None:
         kd_step(self.handle, self.tokens, self.positions, self.kv, self.logits if write_logits else None,
                 stream if stream is not None else self.torch.cuda.current_stream(self.device))
+
+    def prefill(self, prompt, write_logits: bool = True, stream=None) -> None:
+        """Run ``prompt`` (a device int32 tensor) from positions[0] on; tokens[0] gets the next token."""
+        kd_prefill(self.handle, prompt, prompt.numel(), self.tokens, self.positions, self.kv,
+                   self.logits if write_logits else None,
+                   stream if stream is not None else self.torch.cuda.current_stream(self.device))
 
     def generate(self, n_steps: int, out_tokens=None, logits=None, progress=None, stream=None) -> None:
         kd_generate(self.handle, n_steps, self.tokens, self.positions, self.kv, out_tokens, logits, progress,

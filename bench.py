@@ -18,7 +18,10 @@ Printed on stdout, as one JSON line:
   stream_ceiling the read rate of a plain streaming kernel on the same GPU in the same run, and
                  the decode kernel's achieved rate as a fraction of it
   cpu_baseline   the CPU oracle, run for a bounded number of decode steps on the host cores
-  extra          the 2B batch-1 workload measured the same way in the same run (default run only)
+  extra          the 2B batch-1 workload, and the 8B and 2B with FP8 weights, measured the same way
+                 in the same run (default run only)
+  ttft           bf16 prompts: time to the first token with kd_prefill (the prompt on the matrix
+                 cores), beside the time the same prompt takes one step per token
 Everything else goes to stderr.
 """
 
@@ -124,12 +127,16 @@ def measure(wl, args, torch, kd, roofline, steps: int, warmup: int, trace: bool,
     t0 = time.perf_counter()
     weights = workloads.make_weights(m, seed=wl.weight_seed)
     log(f"{wl.name}: weights generated in {time.perf_counter() - t0:.1f} s")
-    dec = kd.Decoder(m, weights, max_seq=wl.max_seq, batch=B, device="cuda:0")
+    # bf16 batch-1 prompts also run through kd_prefill (the matrix cores, 64 positions a pass)
+    chunk = 64 if (B == 1 and m.weight_dtype == "bf16" and wl.prompt_len > 0) else 0
+    dec = kd.Decoder(m, weights, max_seq=wl.max_seq, batch=B, device="cuda:0", prefill_chunk=chunk)
     info = kd.kd_get_info(dec.handle)
     log(f"{wl.name}: kd_init done: {info}")
     stream = torch.cuda.current_stream()
 
-    # fill the KV cache: the prompt fed one token per step, or the seeded pre-filled values
+    # fill the KV cache: the prompt fed one token per step (timed), then, where set up, through
+    # kd_prefill (timed: the time to the first token), or the seeded pre-filled values
+    ttft = None
     if wl.prefill_len > 0:
         view_dtype = torch.int16 if m.kv_dtype == "bf16" else torch.float32
         workloads.fill_kv_prefill_device(wl, dec.kv_view().view(view_dtype), torch, log=log)
@@ -137,10 +144,38 @@ def measure(wl, args, torch, kd, roofline, steps: int, warmup: int, trace: bool,
         dec.positions.fill_(wl.prefill_len)
     else:
         prompt = torch.as_tensor(workloads.make_prompt(wl, 0), device=dec.device)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         dec.positions.zero_()
+        torch.cuda.synchronize()
+        a.record(stream)
         for p in range(wl.prompt_len):
             dec.tokens.copy_(prompt[p : p + 1])
-            dec.step(write_logits=False)
+            dec.step(write_logits=False, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        stepwise_ms = a.elapsed_time(b)
+        first_stepwise = int(dec.tokens[0].item())
+        log(f"{wl.name}: prompt of {wl.prompt_len} tokens one step each: {stepwise_ms:.2f} ms")
+        if chunk:
+            runs = []
+            for _ in range(2):  # the second run is reported; the first warms the kernels
+                dec.positions.zero_()
+                torch.cuda.synchronize()
+                a.record(stream)
+                dec.prefill(prompt, stream=stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                runs.append(a.elapsed_time(b))
+            ttft = {
+                "ms": round(runs[-1], 3),
+                "prompt_tokens": wl.prompt_len,
+                "prefill_tok_s": round(wl.prompt_len / (runs[-1] * 1e-3), 1),
+                "chunk_positions": chunk,
+                "stepwise_prompt_ms": round(stepwise_ms, 2),
+                "same_first_token_as_stepwise": int(dec.tokens[0].item()) == first_stepwise,
+                "what": "kd_prefill of the whole prompt (prompt tokens in HBM) to the first greedy token",
+            }
+            log(f"{wl.name}: time to first token via kd_prefill: {runs} ms")
     torch.cuda.synchronize()
     if dec.status():
         raise RuntimeError(f"{wl.name}: device status {dec.status():#x} after prefill")
@@ -238,6 +273,7 @@ def measure(wl, args, torch, kd, roofline, steps: int, warmup: int, trace: bool,
         "first_pos": first_pos,
         "resident": resident,
         "cpu": cpu,
+        "ttft": ttft,
     }
     del weights
     return res, dec
@@ -268,7 +304,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="8b", choices=["tiny", "2b", "8b", "2b_long", "11b_x56"])
+    ap.add_argument("--workload", default="8b", choices=["tiny", "2b", "8b", "2b_long", "11b_x56", "2b_fp8", "8b_fp8"])
     ap.add_argument("--extra", default=None,
                     help="comma-separated workloads measured after the headline one and reported under 'extra' "
                          "(default: 2b when the headline is the default 8b, else none; 'none' for none)")
@@ -325,7 +361,7 @@ def main() -> int:
 
     extra_names = args.extra
     if extra_names is None:
-        extra_names = "2b" if args.workload == "8b" else "none"
+        extra_names = "2b,8b_fp8,2b_fp8" if args.workload == "8b" else "none"
     extra = {}
     for name in [n for n in extra_names.split(",") if n and n != "none"]:
         try:
@@ -349,6 +385,8 @@ def main() -> int:
             "itl_us": {"p50": round(float(np.percentile(e["per_step_us"], 50)), 2),
                        "p99": round(nearest_rank(e["per_step_us"], 0.99), 2)},
             "resident": e["resident"],
+            "ttft": e["ttft"],
+            "weight_dtype": workloads.get(name).model.weight_dtype,
             "traffic": measured_traffic(name, KERNEL_SOURCES if workloads.get(name).batch == 1 else BATCH_SOURCES),
         }
 
@@ -397,6 +435,7 @@ def main() -> int:
         "frac_of_roofline_tok_s": round(r["tok_s"] / r["bound_tok_s"], 4),
         "itl_us": {"p50": round(float(np.percentile(per_step_us, 50)), 2), "p99": round(r["p99_us"], 2)},
         "resident": r["resident"],
+        "ttft": r["ttft"],
         "cpu_baseline": r["cpu"],
         "extra": extra or None,
     }

@@ -89,10 +89,15 @@ extern "C" {
  *                kernel. 2 <= batch <= 64 runs the lockstep-sessions path: the projections become
  *                small-M GEMMs on the matrix cores. That path needs bf16 weights and cache,
  *                head_dim 128, G of 1, 2 or 4, d_model one of 256, 512, 1024, 2048 or 4096, n_q_heads*head_dim
- *                and ffn_dim each 256 times a power of two, and d_model, 2*ffn_dim,
+ *                and ffn_dim each split into 2, 4, 7, 8, 14, 16, 28 or 32 runs of 128 after halving
+ *                (e.g. 256 times a power of two, or 14336), and d_model, 2*ffn_dim,
  *                (n_q_heads+2*n_kv_heads)*head_dim and vocab multiples of 128.
  *   norm_eps     RMSNorm epsilon (inside the square root).
  *   rope_base    RoPE base: pair (i, i + head_dim/2) turns by position * rope_base^(-2i/head_dim).
+ *   prefill_chunk batch 1 only: 0, or 2..64 to set up kd_prefill, which runs a prompt in chunks of
+ *                this many positions as small-M GEMMs on the matrix cores (the shape must meet the
+ *                lockstep path's conditions above; the library then holds a second copy of the
+ *                weights, in the matrix cores' tile layout).
  *   weight_dtype KD_DTYPE_BF16 or KD_DTYPE_F32, with kv_dtype the same; or KD_DTYPE_FP8_E4M3
  *                with kv_dtype KD_DTYPE_BF16 (batch 1, head_dim 128, d_model and q_dim multiples
  *                of 1024, ffn_dim a multiple of 8 with ffn_dim/8 >= the GPU's compute units).
@@ -111,6 +116,7 @@ typedef struct kd_config {
   float rope_base;
   int32_t weight_dtype;
   int32_t kv_dtype;
+  int32_t prefill_chunk;
 } kd_config;
 
 /* Host pointers to one layer's tensors, row-major, in weight_dtype (bf16 = uint16 patterns). With
@@ -226,6 +232,28 @@ int kd_step(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* 
 int kd_step_noalloc(kd_handle* h, int32_t* tokens, int32_t* positions, void* kv, float* logits, void* stream);
 
 /*
+ * Run a prompt through the decoder on the matrix cores (batch 1, a handle made with
+ * prefill_chunk > 0) and return: the step before decoding, and what sets the time to the first
+ * token ("Kog 3000 tok/s real-time inference", section "deployable parameters and monitoring
+ * checklist", which tracks time to first token beside the time between tokens). The n prompt
+ * tokens go in at positions p .. p+n-1, where p = positions[0] on the device (0 for a fresh
+ * session, or the end of an earlier context), in chunks of prefill_chunk positions. Each chunk
+ * is one pass of the lockstep kernels with its positions as the rows of the small-M GEMMs; each
+ * row appends its K and V and attends over positions 0 .. its own, as one-token steps would.
+ *   prompt    device int32[n], read only.
+ *   tokens    device int32[1]: receives the greedy token after the last prompt position.
+ *   positions device int32[1], in/out: read as p, then set to p + n.
+ *   kv        the caller's cache (kd_kv_layout), read and written.
+ *   logits    device float[vocab] receiving the logits of the last prompt position, or NULL.
+ * Enqueued on `stream`; no allocation, no synchronisation. Returns KD_OK, KD_ERR_INVALID_ARG
+ * (NULL pointer, n < 1), KD_ERR_UNSUPPORTED (no prefill set up at kd_init) or KD_ERR_LAUNCH.
+ * A chunk whose tokens or positions are out of range sets the status bits and writes nothing
+ * (its positions stay unfilled); the outputs are written only when the last chunk ran.
+ */
+int kd_prefill(kd_handle* h, const int32_t* prompt, int32_t n, int32_t* tokens, int32_t* positions, void* kv,
+               float* logits, void* stream);
+
+/*
  * Run n_steps greedy decode steps as one persistent launch (batch 1) and return: each step is
  * fed the token the step before chose, on the device, and the workgroups stay resident from
  * one step to the next; the host only takes the output ("Why is real-time AI inference 56x
@@ -303,6 +331,7 @@ int kd_stream_read(const void* buf, size_t bytes, void* stream);
  *   info[0] workgroups in the persistent grid      info[1] threads per workgroup
  *   info[2] packed weight bytes on the device      info[3] LDS bytes per workgroup
  *   info[4] ring depth (1 KB packets per compute wave)
+ *   info[5] prefill chunk (positions per kd_prefill pass; 0: kd_prefill not set up)
  * For batch > 1: info[0] = 0 (no persistent grid), info[1] threads per GEMM workgroup,
  *   info[2] weight bytes on the device, info[5] kernels one kd_step enqueues,
  *   info[6] split-K factors of the QKV / O / gate-up / down GEMMs (one byte each, low first),
