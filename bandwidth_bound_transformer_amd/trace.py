@@ -1,7 +1,7 @@
 """Decode the per-workgroup phase timestamps written by a traced kd_step.
 
 Layout (see kd_trace in include/kd.h): per workgroup, slot 0 = step start, slot 1 = setup
-done, then 16 phase boundaries per layer, then 4 final ones. The timestamps come from the
+done, then 24 phase boundaries per layer (23 used), then 4 final ones. The timestamps come from the
 GPU's 100 MHz constant clock (10 ns ticks). A boundary a workgroup did not reach (e.g. no
 attention unit assigned) holds 0 and is skipped.
 """
