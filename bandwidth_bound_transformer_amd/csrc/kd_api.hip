@@ -295,7 +295,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
     }
     if (hipMemset(hb->buf.flags, 0, 256) != hipSuccess) rc = KD_ERR_HIP;
     if (rc == KD_OK && hipStreamCreateWithFlags(&hb->ctl, hipStreamNonBlocking) != hipSuccess) rc = KD_ERR_HIP;
-    if (rc == KD_OK) rc = kd::bt::batch_init(cfg, w, nwg, hb->bs);
+    if (rc == KD_OK) rc = kd::bt::batch_init(cfg, w, nwg, true, hb->bs);
     if (rc != KD_OK) {
       if (hb->ctl) (void)hipStreamDestroy(hb->ctl);
       free_buffers(hb->buf);
@@ -427,7 +427,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
     // the prefill engine: the lockstep kernels with prefill_chunk rows (weights in their tile layout)
     kd_config pc = *cfg;
     pc.batch = cfg->prefill_chunk;
-    rc = kd::bt::batch_init(&pc, w, nwg, h->ps);
+    rc = kd::bt::batch_init(&pc, w, nwg, false, h->ps);
     if (rc != KD_OK) goto fail;
     h->prefill = true;
   }

@@ -33,7 +33,7 @@ constexpr int kNB = 32 * kGemmWaves;  // GEMM output columns per workgroup: 32 p
 constexpr int kKC = 128;           // K per LDS chunk of the activation block
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kAttThreads = 256;   // 4 waves; 16 lanes per KV position (hd = 128, bf16)
-constexpr int kChunk = 512;        // KV positions per attention workgroup
+constexpr int kChunk = 512;        // KV positions per attention workgroup (twice that for large session batches)
 constexpr int kMaxG = 4;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -357,14 +357,14 @@ __global__ __launch_bounds__(128) void qkv_epilogue_kernel(const float* __restri
 // ---------------------------------------------------------------------------------------------
 // attention over one chunk of positions of one (session, kv head), for its G query heads
 // ---------------------------------------------------------------------------------------------
-// Grid: (NCmax, hkv, B) workgroups of 4 waves. Chunk c covers positions [c kChunk, min((c+1) kChunk, p+1)),
+// Grid: (NCmax, hkv, B) workgroups of 4 waves. Chunk c covers positions [c CHUNK, min((c+1) CHUNK, p+1)),
 // where p is the session's current position (already appended). 16 lanes hold one position (8 dims
 // each, hd = 128); a wave reads 4 positions per 1 KB load, and waves take packets round-robin.
 // Each lane group keeps a running (max, sum, acc) per head; groups and waves are then merged.
 // Output: part[((b hq + h) NCmax + c) (hd + 2) + {0: max, 1: sum, 2 + i: acc_i}].
 // G = q heads per kv head. Weights are exp2 of base-2 scores on the hardware exp2 (a result below
 // 2^-126 may flush to zero; such a weight is far below the sum's rounding).
-template <int G>
+template <int G, int CHUNK>
 __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __restrict__ Qs,
                                                                  const uint16_t* __restrict__ kv, int64_t kv_slot,
                                                                  int64_t kv_sess, int64_t kv_head,
@@ -376,9 +376,9 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __r
   __shared__ float sm[4][G][HD + 2];
   const int c = (int)blockIdx.x, g = (int)blockIdx.y, b = (int)blockIdx.z;
   const int P1 = positions[b] + 1;
-  const int j0 = c * kChunk;
+  const int j0 = c * CHUNK;
   if (j0 >= P1) return;
-  const int j1 = min(j0 + kChunk, P1);
+  const int j1 = min(j0 + CHUNK, P1);
   const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = lane >> 4, dim0 = (lane & 15) * 8;
   // scores in base-2 units: q carries 1/sqrt(hd) and log2(e), so exp(s - m) = exp2(s2 - m2)
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __r
   // past the current one are masked out; their loads re-read the chunk's first position. K and V
   // are read once per tick: non-temporal loads.
   constexpr int U = 4;
-  constexpr int kIt = kChunk / (16 * U);
+  constexpr int kIt = CHUNK / (16 * U);
   auto load = [&](int it, u32x4 (&kw)[U], u32x4 (&vw)[U]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {

@@ -98,14 +98,16 @@ inline bool fused_silu(const BatchState& st) { return st.g_gu.KS == 1; }
 typedef void (*AttFn)(const float*, const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, int, int, int, float*,
                       const uint32_t*);
 // G = 3 cannot occur: n_q_heads * 128 would be a multiple of 3, never 256 times a power of two.
-inline AttFn att_for(int G) {
+template <int CHUNK>
+inline AttFn att_for_g(int G) {
   switch (G) {
-    case 1: return attention_kernel<1>;
-    case 2: return attention_kernel<2>;
-    case 4: return attention_kernel<4>;
+    case 1: return attention_kernel<1, CHUNK>;
+    case 2: return attention_kernel<2, CHUNK>;
+    case 4: return attention_kernel<4, CHUNK>;
     default: return nullptr;
   }
 }
+inline AttFn att_for(int G, int chunk) { return chunk == 2 * kChunk ? att_for_g<2 * kChunk>(G) : att_for_g<kChunk>(G); }
 
 inline int batch_check(const kd_config* c) {
   if (c->batch < 2 || c->batch > kM) return KD_ERR_UNSUPPORTED;
@@ -149,7 +151,9 @@ inline void batch_free(BatchState& st) {
     }                                                                  \
   } while (0)
 
-inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, BatchState& st) {
+// sessions: a lockstep-sessions handle (each row a session); false for the prefill engine, whose
+// rows are positions of one session.
+inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, bool sessions, BatchState& st) {
   st = BatchState{};
   st.B = c->batch; st.L = c->n_layers; st.d = c->d_model; st.hq = c->n_q_heads; st.hkv = c->n_kv_heads;
   st.hd = c->head_dim; st.F = c->ffn_dim; st.V = c->vocab; st.max_seq = c->max_seq; st.eps = c->norm_eps;
@@ -164,8 +168,9 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, BatchSta
   for (const Gemm* g : {&st.g_qkv, &st.g_o, &st.g_gu, &st.g_d})
     if (g->KS < 1) return KD_ERR_UNSUPPORTED;
   st.g_lm = {st.V, st.d, 1};  // written straight into the logits: no split
-  // attention: chunks of 512 positions (enough units to fill the device for any session count here)
-  st.CH = kChunk;
+  // attention: chunks of 512 positions, or 1024 for session batches whose sessions and kv heads
+  // alone give a workgroup per compute unit (the merge then has half the chunks to combine)
+  st.CH = sessions && (int64_t)st.B * st.hkv >= nwg ? 2 * kChunk : kChunk;
   st.NCmax = (st.max_seq + st.CH - 1) / st.CH;
 
   const size_t d = st.d;
@@ -314,7 +319,7 @@ inline int batch_tick(const BatchState& st, int nb, int32_t* tokens, int32_t* po
     hipLaunchKernelGGL(qkv_epilogue_kernel, dim3(st.hq + 2 * st.hkv, nb), dim3(st.hd), 0, s, (const float*)st.P,
                        st.g_qkv.KS, st.nqkv, st.hq, st.hkv, st.hd, (const float2*)st.rope, (const int32_t*)positions,
                        st.Qs, kvl, kvs.slot, kvs.row, kvs.head, nb, skip);
-    hipLaunchKernelGGL(att_for(st.hq / st.hkv), dim3(st.NCmax, st.hkv, nb), dim3(kAttThreads), 0, s, (const float*)st.Qs,
+    hipLaunchKernelGGL(att_for(st.hq / st.hkv, st.CH), dim3(st.NCmax, st.hkv, nb), dim3(kAttThreads), 0, s, (const float*)st.Qs,
                        (const uint16_t*)kvl, kvs.slot, kvs.row, kvs.head, (const int32_t*)positions, st.hq, st.hkv,
                        st.NCmax, st.part, skip);
     hipLaunchKernelGGL(merge_kernel, dim3(st.hq, nb), dim3(st.hd), 0, s, (const float*)st.part,
