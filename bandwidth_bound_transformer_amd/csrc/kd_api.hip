@@ -156,7 +156,7 @@ int check_config(const kd_config* c) {
   if (!weight_dtype_ok(c->weight_dtype) || !dtype_ok(c->kv_dtype)) return KD_ERR_INVALID_ARG;
   if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f)) return KD_ERR_INVALID_ARG;
   if (c->max_seq > (1 << 24) || c->vocab > (1 << 30)) return KD_ERR_INVALID_ARG;
-  if (c->prefill_chunk < 0 || c->prefill_chunk > 64 || c->prefill_chunk == 1) return KD_ERR_INVALID_ARG;
+  if (c->prefill_chunk < 0 || c->prefill_chunk > kd::bt::kMPrefill || c->prefill_chunk == 1) return KD_ERR_INVALID_ARG;
   return KD_OK;
 }
 
@@ -166,7 +166,7 @@ int check_supported(const kd_config* c, const kd::Dims& m) {
   if (c->prefill_chunk > 0) {  // the lockstep kernels must take the shape
     kd_config pc = *c;
     pc.batch = c->prefill_chunk;
-    const int rc = kd::bt::batch_check(&pc);
+    const int rc = kd::bt::batch_check(&pc, kd::bt::kMPrefill);
     if (rc != KD_OK) return rc;
   }
   if (c->head_dim != 64 && c->head_dim != 128) return KD_ERR_UNSUPPORTED;

@@ -26,6 +26,7 @@ namespace kd {
 namespace bt {
 
 constexpr int kM = 64;             // sessions padded to four 16-row MFMA tiles
+constexpr int kMPrefill = 128;     // prefill positions per pass: eight 16-row tiles
 // Four waves per GEMM workgroup, so two workgroups share a CU (registers and LDS allow two):
 // one's start-up and barrier waits overlap the other's streaming.
 constexpr int kGemmWaves = 4;
@@ -140,7 +141,8 @@ constexpr int kPF = 2;  // chunks in flight per wave
 // SILU (gate/up without a K split only): instead of partial sums, the workgroup writes
 // SiLU(gate) * up of its 64 FFN columns as the hi/lo activation block Ohi/Olo of the down
 // projection. Its 128 rows are two groups of [32 gate rows; the 32 up rows of the same columns].
-template <int NCH, bool SILU>
+// MT: 16-row tiles of the activation block (4: up to 64 rows, the session ticks; 8: up to 128, prefill).
+template <int NCH, bool SILU, int MT>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __restrict__ W, int N, int K,
                                                                 const uint16_t* __restrict__ Ahi,
                                                                 const uint16_t* __restrict__ Alo, int lda,
@@ -148,7 +150,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
                                                                 uint16_t* __restrict__ Ohi, uint16_t* __restrict__ Olo) {
   if (*skip) return;
   // [buffer][hi, lo][row][16-byte piece of the 128-K chunk, padded by one against bank conflicts]
-  __shared__ u32x4 As[2][2][kM][kKC / 8 + 1];
+  constexpr int kRows = 16 * MT;
+  constexpr int kHiLoShift = MT == 8 ? 11 : 10;  // piece index -> hi/lo half: log2(kRows * 16)
+  static_assert(MT == 4 || MT == 8, "64 or 128 rows");
+  __shared__ u32x4 As[2][2][kRows][kKC / 8 + 1];
   const int unit = (int)blockIdx.x;
   const int nb = unit / KS, s = unit - nb * KS;
   const int k0 = s * (NCH * kKC);
@@ -159,8 +164,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
 #pragma unroll
   for (int j = 0; j < 2; ++j) wt[j] = (const u32x4*)W + ((size_t)(rb0 + j) * (K / 32) + k0 / 32) * 64 + lane;
 
-  // activation chunk: 2 x 64 rows x 16 pieces of 16 bytes = 2048 pieces, 4 per thread
-  constexpr int kAPer = 2 * kM * (kKC / 8) / kGemmThreads;
+  // activation chunk: 2 x kRows rows x 16 pieces of 16 bytes, 4 (or 8) per thread
+  constexpr int kAPer = 2 * kRows * (kKC / 8) / kGemmThreads;
   // ext_vector_type registers (HIP's uint4 is a struct with a union, which the compiler keeps in
   // scratch memory when it sits in an array)
   struct Slot {
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
 #pragma unroll
     for (int j = 0; j < kAPer; ++j) {
       const int idx = tid + kGemmThreads * j;
-      const int hl = idx >> 10, r = (idx >> 4) & 63, cc = idx & 15;
+      const int hl = idx >> kHiLoShift, r = (idx >> 4) & (kRows - 1), cc = idx & 15;
       sl.a[j] = *(const u32x4*)((hl ? Alo : Ahi) + (size_t)r * lda + k0 + c * kKC + cc * 8);
     }
     // weights are read once per tick: non-temporal loads
@@ -181,25 +186,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
       for (int t = 0; t < 4; ++t) sl.w[j][t] = __builtin_nontemporal_load(wt[j] + (size_t)(c * 4 + t) * 64);
   };
 
-  f32x4 acc[2][4];
+  f32x4 acc[2][MT];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // one chunk: activation slot -> LDS buffer, barrier, 64 MFMAs, then refill the slot kPF ahead
   auto step = [&](int c, Slot& sl) __attribute__((always_inline)) {
     const int buf = c & 1;
 #pragma unroll
     for (int j = 0; j < kAPer; ++j) {
       const int idx = tid + kGemmThreads * j;
-      const int hl = idx >> 10, r = (idx >> 4) & 63, cc = idx & 15;
+      const int hl = idx >> kHiLoShift, r = (idx >> 4) & (kRows - 1), cc = idx & 15;
       As[buf][hl][r][cc] = sl.a[j];
     }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         // lane l supplies K = 32 t + 8 (l / 16) .. + 8 of row 16 mt + l % 16: piece 4 t + l / 16
         const int r = mt * 16 + (lane & 15);
         const bf16x8 ah = __builtin_bit_cast(bf16x8, As[buf][0][r][t * 4 + q]);
@@ -223,14 +228,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
     // the workgroup's 128 rows x B sessions through LDS (As is free once every wave is past its
     // last chunk), then SiLU(gate) * up for 64 columns
     constexpr int LDC = kNB + 1;
-    static_assert(sizeof(As) >= sizeof(float) * kM * LDC, "the SiLU staging must fit in the activation tile");
+    static_assert(sizeof(As) >= sizeof(float) * kRows * LDC, "the SiLU staging must fit in the activation tile");
     static_assert(kNB % 64 == 0, "a workgroup's rows must be whole [32 gate; 32 up] groups");
     float* Cs = reinterpret_cast<float*>(&As[0][0][0][0]);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) Cs[(mt * 16 + q * 4 + i) * LDC + 32 * wave + 16 * j + (lane & 15)] = acc[j][mt][i];
     __syncthreads();
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
   for (int j = 0; j < 2; ++j) {
     const int n = (rb0 + j) * 16 + (lane & 15);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = mt * 16 + q * 4 + i;
@@ -665,7 +670,7 @@ __global__ void progress_kernel(uint32_t* progress, uint32_t value, const uint32
 // prefill: a chunk of prompt positions of one session as the rows of a tick
 // ---------------------------------------------------------------------------------------------
 // Rows b < nb of a prefill chunk: prompt token first + b at position *pos0 + first + b.
-// Grid: one workgroup of 64 threads (nb <= 64).
+// Grid: one workgroup of kMPrefill threads (nb <= kMPrefill).
 __global__ void prefill_rows_kernel(const int32_t* __restrict__ prompt, int first, int nb, const int32_t* __restrict__ pos0,
                                     int32_t* __restrict__ tokens, int32_t* __restrict__ positions) {
   const int b = (int)threadIdx.x;

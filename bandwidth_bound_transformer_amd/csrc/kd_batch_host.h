@@ -27,6 +27,7 @@ struct BatchState {
   int B = 0, L = 0, d = 0, hq = 0, hkv = 0, hd = 0, F = 0, V = 0, S = 0, max_seq = 0;
   int nqkv = 0, qdim = 0, lda = 0;  // lda: row stride of the hi/lo activation blocks
   int CH = 0, NCmax = 0;            // attention chunk length and most chunks per (session, kv head)
+  int MT = 4;                       // 16-row tiles of the activation blocks: 4 (B <= 64) or 8 (B <= 128, prefill)
   float eps = 0.f;
   Gemm g_qkv, g_o, g_gu, g_d, g_lm;
   size_t layer_elems = 0;           // per-layer weight elements: qkv, o, gate/up (interleaved), down
@@ -78,20 +79,23 @@ inline int pick_ks(int N, int K, int B, int nwg) {
 }
 typedef void (*GemmFn)(const uint16_t*, int, int, const uint16_t*, const uint16_t*, int, float*, int, int, const uint32_t*,
                        uint16_t*, uint16_t*);
-template <bool SILU>
-inline GemmFn gemm_for(int nch) {
+template <bool SILU, int MT>
+inline GemmFn gemm_for_mt(int nch) {
   switch (nch) {
-    case 2: return gemm_kernel<2, SILU>;
-    case 4: return gemm_kernel<4, SILU>;
-    case 7: return gemm_kernel<7, SILU>;
-    case 8: return gemm_kernel<8, SILU>;
-    case 14: return gemm_kernel<14, SILU>;
-    case 16: return gemm_kernel<16, SILU>;
-    case 28: return gemm_kernel<28, SILU>;
-    case 32: return gemm_kernel<32, SILU>;
+    case 2: return gemm_kernel<2, SILU, MT>;
+    case 4: return gemm_kernel<4, SILU, MT>;
+    case 7: return gemm_kernel<7, SILU, MT>;
+    case 8: return gemm_kernel<8, SILU, MT>;
+    case 14: return gemm_kernel<14, SILU, MT>;
+    case 16: return gemm_kernel<16, SILU, MT>;
+    case 28: return gemm_kernel<28, SILU, MT>;
+    case 32: return gemm_kernel<32, SILU, MT>;
     default: return nullptr;
   }
 }
+// mt: 16-row tiles of the activation block (4 for up to 64 rows, 8 for up to 128)
+template <bool SILU>
+inline GemmFn gemm_for(int nch, int mt) { return mt == 8 ? gemm_for_mt<SILU, 8>(nch) : gemm_for_mt<SILU, 4>(nch); }
 // gate/up without a K split writes SiLU(gate) * up itself (no silu_kernel launch)
 inline bool fused_silu(const BatchState& st) { return st.g_gu.KS == 1; }
 
@@ -109,8 +113,9 @@ inline AttFn att_for_g(int G) {
 }
 inline AttFn att_for(int G, int chunk) { return chunk == 2 * kChunk ? att_for_g<2 * kChunk>(G) : att_for_g<kChunk>(G); }
 
-inline int batch_check(const kd_config* c) {
-  if (c->batch < 2 || c->batch > kM) return KD_ERR_UNSUPPORTED;
+// max_rows: kM for session handles, kMPrefill for the prefill engine
+inline int batch_check(const kd_config* c, int max_rows = kM) {
+  if (c->batch < 2 || c->batch > max_rows) return KD_ERR_UNSUPPORTED;
   if (c->weight_dtype != KD_DTYPE_BF16 || c->kv_dtype != KD_DTYPE_BF16) return KD_ERR_UNSUPPORTED;
   if (c->head_dim != 128) return KD_ERR_UNSUPPORTED;
   const int G = c->n_q_heads / c->n_kv_heads;
@@ -155,7 +160,7 @@ inline void batch_free(BatchState& st) {
 // rows are positions of one session.
 inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, bool sessions, BatchState& st) {
   st = BatchState{};
-  st.B = c->batch; st.L = c->n_layers; st.d = c->d_model; st.hq = c->n_q_heads; st.hkv = c->n_kv_heads;
+  st.B = c->batch; st.MT = c->batch > kM ? 8 : 4; st.L = c->n_layers; st.d = c->d_model; st.hq = c->n_q_heads; st.hkv = c->n_kv_heads;
   st.hd = c->head_dim; st.F = c->ffn_dim; st.V = c->vocab; st.max_seq = c->max_seq; st.eps = c->norm_eps;
   st.S = (int)((((int64_t)c->max_seq + 7 + 15) / 16) * 16);
   st.qdim = st.hq * st.hd;
@@ -190,20 +195,21 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, bool ses
   KD_BT_ALLOC(st.norms, (size_t)(2 * st.L + 1) * d * 2);
   KD_BT_ALLOC(st.rope, (size_t)st.S * (st.hd / 2) * sizeof(float2));
   KD_BT_ALLOC(st.X, (size_t)st.B * d * 4);
-  KD_BT_ALLOC(st.Ahi, (size_t)kM * st.lda * 2);
-  KD_BT_ALLOC(st.Alo, (size_t)kM * st.lda * 2);
-  KD_BT_ALLOC(st.A2hi, (size_t)kM * st.lda * 2);
-  KD_BT_ALLOC(st.A2lo, (size_t)kM * st.lda * 2);
+  const size_t rows = (size_t)16 * st.MT;
+  KD_BT_ALLOC(st.Ahi, rows * st.lda * 2);
+  KD_BT_ALLOC(st.Alo, rows * st.lda * 2);
+  KD_BT_ALLOC(st.A2hi, rows * st.lda * 2);
+  KD_BT_ALLOC(st.A2lo, rows * st.lda * 2);
   KD_BT_ALLOC(st.P, p_elems * 4);
   KD_BT_ALLOC(st.Qs, (size_t)st.B * st.qdim * 4);
   KD_BT_ALLOC(st.part, (size_t)st.B * st.hq * st.NCmax * (st.hd + 2) * 4);
   KD_BT_ALLOC(st.logits, (size_t)st.B * st.V * 4);
   KD_BT_ALLOC(st.rows_tok, (size_t)st.B * 4);
   KD_BT_ALLOC(st.rows_pos, (size_t)st.B * 4);
-  KD_BT_TRY(hipMemset(st.Ahi, 0, (size_t)kM * st.lda * 2));  // padding rows stay zero for good
-  KD_BT_TRY(hipMemset(st.Alo, 0, (size_t)kM * st.lda * 2));
-  KD_BT_TRY(hipMemset(st.A2hi, 0, (size_t)kM * st.lda * 2));
-  KD_BT_TRY(hipMemset(st.A2lo, 0, (size_t)kM * st.lda * 2));
+  KD_BT_TRY(hipMemset(st.Ahi, 0, rows * st.lda * 2));  // padding rows stay zero for good
+  KD_BT_TRY(hipMemset(st.Alo, 0, rows * st.lda * 2));
+  KD_BT_TRY(hipMemset(st.A2hi, 0, rows * st.lda * 2));
+  KD_BT_TRY(hipMemset(st.A2lo, 0, rows * st.lda * 2));
 
   // Every matrix goes row-major into a staging buffer, then tile_pack_kernel writes it into the
   // blob in the tile layout the GEMM streams.
@@ -299,7 +305,7 @@ inline int batch_tick(const BatchState& st, int nb, int32_t* tokens, int32_t* po
   uint16_t* kv = (uint16_t*)kvp;
   float* lg = logits ? logits : st.logits;
   auto gemm = [&](const uint16_t* W, const Gemm& g, float* out) {
-    hipLaunchKernelGGL(gemm_for<false>(g.K / (g.KS * kKC)), dim3((g.N / kNB) * g.KS), dim3(kGemmThreads), 0, s, W, g.N,
+    hipLaunchKernelGGL(gemm_for<false>(g.K / (g.KS * kKC), st.MT), dim3((g.N / kNB) * g.KS), dim3(kGemmThreads), 0, s, W, g.N,
                        g.K, (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, out, g.KS, nb, skip,
                        (uint16_t*)nullptr, (uint16_t*)nullptr);
   };
@@ -330,10 +336,10 @@ inline int batch_tick(const BatchState& st, int nb, int32_t* tokens, int32_t* po
       // gate/up writes SiLU(gate) * up into the second activation block, which the down
       // projection reads (the first is still being read while gate/up runs)
       const Gemm& g = st.g_gu;
-      hipLaunchKernelGGL(gemm_for<true>(g.K / kKC), dim3(g.N / kNB), dim3(kGemmThreads), 0, s, lay + st.w_gu, g.N, g.K,
+      hipLaunchKernelGGL(gemm_for<true>(g.K / kKC, st.MT), dim3(g.N / kNB), dim3(kGemmThreads), 0, s, lay + st.w_gu, g.N, g.K,
                          (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, st.P, 1, nb, skip, st.A2hi, st.A2lo);
       const Gemm& gd = st.g_d;
-      hipLaunchKernelGGL(gemm_for<false>(gd.K / (gd.KS * kKC)), dim3((gd.N / kNB) * gd.KS), dim3(kGemmThreads), 0, s,
+      hipLaunchKernelGGL(gemm_for<false>(gd.K / (gd.KS * kKC), st.MT), dim3((gd.N / kNB) * gd.KS), dim3(kGemmThreads), 0, s,
                          lay + st.w_d, gd.N, gd.K, (const uint16_t*)st.A2hi, (const uint16_t*)st.A2lo, st.lda, st.P, gd.KS,
                          nb, skip, (uint16_t*)nullptr, (uint16_t*)nullptr);
     } else {
@@ -372,7 +378,7 @@ inline int batch_prefill(const BatchState& st, const int32_t* prompt, int n, int
   for (int first = 0; first < n; first += st.B) {
     const int nb = std::min(st.B, n - first);
     const bool last = first + nb == n;
-    hipLaunchKernelGGL(prefill_rows_kernel, dim3(1), dim3(64), 0, s, prompt, first, nb, (const int32_t*)positions,
+    hipLaunchKernelGGL(prefill_rows_kernel, dim3(1), dim3(kMPrefill), 0, s, prompt, first, nb, (const int32_t*)positions,
                        st.rows_tok, st.rows_pos);
     const int rc = batch_tick(st, nb, st.rows_tok, st.rows_pos, kvp, one, nullptr, last, s, flags, nullptr, nullptr, 0);
     if (rc != KD_OK) return rc;

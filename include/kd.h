@@ -94,7 +94,7 @@ extern "C" {
  *                (n_q_heads+2*n_kv_heads)*head_dim and vocab multiples of 128.
  *   norm_eps     RMSNorm epsilon (inside the square root).
  *   rope_base    RoPE base: pair (i, i + head_dim/2) turns by position * rope_base^(-2i/head_dim).
- *   prefill_chunk batch 1 only: 0, or 2..64 to set up kd_prefill, which runs a prompt in chunks of
+ *   prefill_chunk batch 1 only: 0, or 2..128 to set up kd_prefill, which runs a prompt in chunks of
  *                this many positions as small-M GEMMs on the matrix cores (the shape must meet the
  *                lockstep path's conditions above; the library then holds a second copy of the
  *                weights, in the matrix cores' tile layout).

@@ -73,7 +73,7 @@ def _cache_close(a, b, n, tag):
     assert ratio <= 2.0**-6
 
 
-@pytest.mark.parametrize("chunk", [64, 16])
+@pytest.mark.parametrize("chunk", [128, 64, 16])
 def test_prefill_small_ragged_and_continued(torch, kdm, chunk):
     """100 prompt tokens (a last chunk that ends mid-chunk), then 30 more from position 100, then a
     decode step: cache, tokens and logits against one-token steps and the oracle."""
@@ -147,14 +147,15 @@ def test_2b_prefill_then_decode(torch, kdm):
 
 
 def test_8b_prefill_1024(torch, kdm):
-    """The Llama-3-8B shape's 1024-token prompt through kd_prefill (16 chunks): its cache against the one
-    one-token steps fill, and the last position's logits against the oracle run from that cache."""
+    """The Llama-3-8B shape's 1024-token prompt through kd_prefill (8 chunks of 128, the eight-tile
+    GEMMs): its cache against the one one-token steps fill, and the last position's logits against the
+    oracle run from that cache."""
     wl = workloads.get("8b")
     m = wl.model
     w = workloads.make_weights(m, seed=wl.weight_seed)
     prompt = workloads.make_prompt(wl, 0)
     P = len(prompt)
-    pre = kdm.Decoder(m, w, max_seq=wl.max_seq, prefill_chunk=64)
+    pre = kdm.Decoder(m, w, max_seq=wl.max_seq, prefill_chunk=128)
     pre.positions.zero_()
     pre.prefill(torch.as_tensor(prompt, device=pre.device))
     torch.cuda.synchronize()
@@ -192,6 +193,10 @@ def test_prefill_refusals(torch, kdm):
         kdm.kd_prefill(pre.handle, p_d, 0, pre.tokens, pre.positions, pre.kv)
     assert e.value.code == kdm.KD_ERR_INVALID_ARG
     pre.close()
+    for bad in (1, 129, -1):  # a pass holds 2..128 positions
+        with pytest.raises(kdm.KDError) as e:
+            kdm.kd_init(kdm.make_config(SMALL, 1, 64, prefill_chunk=bad), w)
+        assert e.value.code == kdm.KD_ERR_INVALID_ARG
     fp8 = ModelShape(2, 1024, 8, 2, 128, 2048, 4096, weight_dtype="fp8", kv_dtype="bf16")
     with pytest.raises(kdm.KDError) as e:
         kdm.kd_init(kdm.make_config(fp8, 1, 64, prefill_chunk=64), workloads.make_weights(fp8, seed=1))
