@@ -558,6 +558,173 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const float* __r
 }
 
 // ---------------------------------------------------------------------------------------------
+// prefill attention: every row of a pass attends over the same session's cache
+// ---------------------------------------------------------------------------------------------
+// The rows of a prefill pass are consecutive positions of one session, so one chunk of its cache
+// serves all of them, and the scores and weighted sums are dense products: queries x positions
+// and weights x values. Workgroup (c, g, rg) loads K and V of positions [c kChunkPrefill, + that)
+// of kv head g into LDS once, and each of its four waves takes 16 queries (16 / G rows x the G
+// q heads of g) through the matrix cores, 32 positions at a time:
+//   S^T = K Q^T   (A: 16 positions x 32 dims of K from LDS; B: q as bf16 hi/lo, both products),
+//   online softmax per query (base-2 units, running max, the sum kept per lane),
+//   O += P V      (A: the weights as bf16 hi/lo; B: V from LDS).
+// The weights need no shuffle: lane l holds S^T for query l % 16 at positions 4 (l / 16) + i and
+// 16 + 4 (l / 16) + i, which are exactly the eight values of the A operand of P V if the 32
+// positions are taken in that order; V's B operand is read from LDS in the same order.
+// Output: chunk partials in the layout attention_kernel writes (merge_kernel combines them).
+// Grid: (NCmax, hkv, ceil(nb / (64 / G))) workgroups of 256 threads; rows must be consecutive
+// positions (prefill_rows_kernel sets them so).
+constexpr int kChunkPrefill = 256;
+constexpr int kKvPitch = 136;  // bf16 per LDS row: 128 dims + 16 bytes against bank conflicts
+template <int G>
+__global__ __launch_bounds__(256) void prefill_attention_kernel(const float* __restrict__ Qs, const uint16_t* __restrict__ kv,
+                                                                int64_t kv_slot, int64_t kv_head,
+                                                                const int32_t* __restrict__ positions, int nb, int hq,
+                                                                int NCmax, float* __restrict__ part, const uint32_t* skip) {
+  if (*skip) return;
+  constexpr int HD = 128, RW = 16 / G;  // rows per wave
+  __shared__ uint16_t Ks[kChunkPrefill][kKvPitch], Vs[kChunkPrefill][kKvPitch];
+  const int c = (int)blockIdx.x, g = (int)blockIdx.y, rg = (int)blockIdx.z;
+  const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j0 = c * kChunkPrefill;
+  const int row0 = rg * 4 * RW, nrow = min(4 * RW, nb - row0);
+  const int pwg = positions[row0 + nrow - 1];  // the workgroup's last row attends furthest
+  if (j0 > pwg) return;
+  const int jend = min(j0 + kChunkPrefill, pwg + 1);
+  // K and V of positions [j0, jend) into LDS, zeros after (so that masked weights multiply zeros)
+  {
+    const uint16_t* kb = kv + kv_head * g;
+    const uint16_t* vb = kb + kv_slot;
+    constexpr int kPer = kChunkPrefill * (HD / 8) / 256;  // 16-byte pieces per thread
+    u32x4 kk[kPer], vv[kPer];
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      const int e = tid + 256 * t, pr = e >> 4, pc = e & 15;
+      kk[t] = vv[t] = u32x4{0u, 0u, 0u, 0u};
+      if (j0 + pr < jend) {
+        kk[t] = __builtin_nontemporal_load((const u32x4*)(kb + (int64_t)(j0 + pr) * HD + pc * 8));
+        vv[t] = __builtin_nontemporal_load((const u32x4*)(vb + (int64_t)(j0 + pr) * HD + pc * 8));
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      const int e = tid + 256 * t, pr = e >> 4, pc = e & 15;
+      *(u32x4*)&Ks[pr][pc * 8] = kk[t];
+      *(u32x4*)&Vs[pr][pc * 8] = vv[t];
+    }
+  }
+  __syncthreads();
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int q = lane & 15, grp = lane >> 4;
+  // this lane's query on the S side: row row0 + wave RW + q / G, head g G + q % G
+  const int qrow = row0 + wave * RW + q / G;
+  const int qlim = qrow < nb ? positions[qrow] : -1;  // it attends 0..qlim
+  bf16x8 qhi[4], qlo[4];
+  {
+    const float* qp = Qs + ((size_t)(qrow < nb ? qrow : row0) * hq + g * G + q % G) * HD + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint16_t h8[8], l8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split_hilo(qp[32 * ks + e] * kLog2e, h8[e], l8[e]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qhi[ks][e] = __builtin_bit_cast(__bf16, h8[e]);
+        qlo[ks][e] = __builtin_bit_cast(__bf16, l8[e]);
+      }
+    }
+  }
+  float m_run = -INFINITY, l_part = 0.f;
+  f32x4 o[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nblk = (jend - j0 + 31) / 32;
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int pb = 32 * blk;
+    f32x4 sc[2];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      sc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)&Ks[pb + 16 * pt + q][32 * ks + 8 * grp]);
+        sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qhi[ks], sc[pt], 0, 0, 0);
+        sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[ks], sc[pt], 0, 0, 0);
+      }
+    }
+    // lane: query q at positions pb + 16 pt + 4 grp + i; masked past the query's own position
+    float sv[8], mb = m_run;
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = j0 + pb + 16 * pt + 4 * grp + i <= qlim ? sc[pt][i] : -INFINITY;
+        sv[4 * pt + i] = v;
+        mb = fmaxf(mb, v);
+      }
+    {
+      float a, b2;
+      swap16(mb, a, b2);
+      mb = fmaxf(a, b2);
+      swap32(mb, a, b2);
+      mb = fmaxf(a, b2);  // the query's max over all four lane groups
+    }
+    const float mref = mb == -INFINITY ? 0.f : mb;  // nothing valid yet: every weight is exp2(-inf) = 0
+    const float r = __builtin_amdgcn_exp2f(m_run - mref);
+    m_run = mb;
+    l_part *= r;
+    bf16x8 phi, plo;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float w = __builtin_amdgcn_exp2f(sv[k] - mref);
+      l_part += w;
+      uint16_t h, l;
+      split_hilo(w, h, l);
+      phi[k] = __builtin_bit_cast(__bf16, h);
+      plo[k] = __builtin_bit_cast(__bf16, l);
+    }
+    // the O rows this lane holds are queries 4 grp + i: their rescale factors
+    float rq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rq[i] = __shfl(r, 4 * grp + i);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[nt][i] *= rq[i];
+      // V's B operand in the same position order: pb + 4 grp + j (j < 4), pb + 12 + 4 grp + j (j >= 4)
+      bf16x8 vf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vf[j] = __builtin_bit_cast(__bf16, Vs[pb + (j < 4 ? 0 : 12) + 4 * grp + j][16 * nt + q]);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vf, o[nt], 0, 0, 0);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vf, o[nt], 0, 0, 0);
+    }
+  }
+  // the query's sum over its four lane groups
+  {
+    float a, b2;
+    swap16(l_part, a, b2);
+    l_part = a + b2;
+    swap32(l_part, a, b2);
+    l_part = a + b2;
+  }
+  // partials: lane group 0 writes the max and sum of its query; every lane its O values
+  if (grp == 0 && qrow < nb) {
+    float* out = part + (((size_t)qrow * hq + g * G + q % G) * NCmax + c) * (HD + 2);
+    out[0] = m_run * 0.6931471805599453f;  // natural-log units for the merge
+    out[1] = l_part;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qq = 4 * grp + i, orow = row0 + wave * RW + qq / G;
+    if (orow < nb) {
+      float* out = part + (((size_t)orow * hq + g * G + qq % G) * NCmax + c) * (HD + 2) + 2;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) out[16 * nt + q] = o[nt][i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // merge the chunks of one (session, q head) and hand o to the O GEMM as hi/lo
 // ---------------------------------------------------------------------------------------------
 // Grid: (hq, B) workgroups of hd threads.

@@ -112,6 +112,16 @@ inline AttFn att_for_g(int G) {
   }
 }
 inline AttFn att_for(int G, int chunk) { return chunk == 2 * kChunk ? att_for_g<2 * kChunk>(G) : att_for_g<kChunk>(G); }
+typedef void (*PrefillAttFn)(const float*, const uint16_t*, int64_t, int64_t, const int32_t*, int, int, int, float*,
+                             const uint32_t*);
+inline PrefillAttFn prefill_att_for(int G) {
+  switch (G) {
+    case 1: return prefill_attention_kernel<1>;
+    case 2: return prefill_attention_kernel<2>;
+    case 4: return prefill_attention_kernel<4>;
+    default: return nullptr;
+  }
+}
 
 // max_rows: kM for session handles, kMPrefill for the prefill engine
 inline int batch_check(const kd_config* c, int max_rows = kM) {
@@ -174,8 +184,9 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, bool ses
     if (g->KS < 1) return KD_ERR_UNSUPPORTED;
   st.g_lm = {st.V, st.d, 1};  // written straight into the logits: no split
   // attention: chunks of 512 positions, or 1024 for session batches whose sessions and kv heads
-  // alone give a workgroup per compute unit (the merge then has half the chunks to combine)
-  st.CH = sessions && (int64_t)st.B * st.hkv >= nwg ? 2 * kChunk : kChunk;
+  // alone give a workgroup per compute unit (the merge then has half the chunks to combine); the
+  // prefill engine's chunks of 256 positions serve every row of a pass at once
+  st.CH = !sessions ? kChunkPrefill : (int64_t)st.B * st.hkv >= nwg ? 2 * kChunk : kChunk;
   st.NCmax = (st.max_seq + st.CH - 1) / st.CH;
 
   const size_t d = st.d;
@@ -325,9 +336,17 @@ inline int batch_tick(const BatchState& st, int nb, int32_t* tokens, int32_t* po
     hipLaunchKernelGGL(qkv_epilogue_kernel, dim3(st.hq + 2 * st.hkv, nb), dim3(st.hd), 0, s, (const float*)st.P,
                        st.g_qkv.KS, st.nqkv, st.hq, st.hkv, st.hd, (const float2*)st.rope, (const int32_t*)positions,
                        st.Qs, kvl, kvs.slot, kvs.row, kvs.head, nb, skip);
-    hipLaunchKernelGGL(att_for(st.hq / st.hkv, st.CH), dim3(st.NCmax, st.hkv, nb), dim3(kAttThreads), 0, s, (const float*)st.Qs,
-                       (const uint16_t*)kvl, kvs.slot, kvs.row, kvs.head, (const int32_t*)positions, st.hq, st.hkv,
-                       st.NCmax, st.part, skip);
+    if (kvs.row == 0) {
+      // prefill: the rows are consecutive positions of one session; a chunk of its cache serves all
+      const int G = st.hq / st.hkv, rows_per_wg = 64 / G;
+      hipLaunchKernelGGL(prefill_att_for(G), dim3(st.NCmax, st.hkv, (nb + rows_per_wg - 1) / rows_per_wg), dim3(256), 0,
+                         s, (const float*)st.Qs, (const uint16_t*)kvl, kvs.slot, kvs.head, (const int32_t*)positions, nb,
+                         st.hq, st.NCmax, st.part, skip);
+    } else {
+      hipLaunchKernelGGL(att_for(st.hq / st.hkv, st.CH), dim3(st.NCmax, st.hkv, nb), dim3(kAttThreads), 0, s, (const float*)st.Qs,
+                         (const uint16_t*)kvl, kvs.slot, kvs.row, kvs.head, (const int32_t*)positions, st.hq, st.hkv,
+                         st.NCmax, st.part, skip);
+    }
     hipLaunchKernelGGL(merge_kernel, dim3(st.hq, nb), dim3(st.hd), 0, s, (const float*)st.part,
                        (const int32_t*)positions, st.hq, st.hd, st.CH, st.NCmax, st.Ahi, st.Alo, st.lda, skip);
     gemm(lay + st.w_o, st.g_o, st.P);
