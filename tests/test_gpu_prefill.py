@@ -30,6 +30,8 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-2
 # small enough for the oracle, and a shape both the batch-1 kernel and the lockstep kernels take
 SMALL = ModelShape(2, 512, 4, 2, 128, 2048, 2048, rope_base=10000.0)
+# plain multi-head attention (one q head per kv head): the prefill attention's G = 1 instantiation
+SMALL_MHA = ModelShape(2, 512, 4, 4, 128, 2048, 2048, rope_base=10000.0)
 
 
 @pytest.fixture(scope="module")
@@ -73,15 +75,17 @@ def _cache_close(a, b, n, tag):
     assert ratio <= 2.0**-6
 
 
-@pytest.mark.parametrize("chunk", [128, 64, 16])
-def test_prefill_small_ragged_and_continued(torch, kdm, chunk):
+@pytest.mark.parametrize("chunk,mha", [(128, False), (64, False), (16, False), (128, True)])
+def test_prefill_small_ragged_and_continued(torch, kdm, chunk, mha):
     """100 prompt tokens (a last chunk that ends mid-chunk), then 30 more from position 100, then a
-    decode step: cache, tokens and logits against one-token steps and the oracle."""
-    w = workloads.make_weights(SMALL, seed=4)
+    decode step: cache, tokens and logits against one-token steps and the oracle (two q heads per kv
+    head, or one)."""
+    SHAPE = SMALL_MHA if mha else SMALL
+    w = workloads.make_weights(SHAPE, seed=4)
     rng = np.random.default_rng(12)
-    prompt = rng.integers(0, SMALL.vocab, 130).astype(np.int32)
-    pre = kdm.Decoder(SMALL, w, max_seq=160, prefill_chunk=chunk)
-    step = kdm.Decoder(SMALL, w, max_seq=160)
+    prompt = rng.integers(0, SHAPE.vocab, 130).astype(np.int32)
+    pre = kdm.Decoder(SHAPE, w, max_seq=160, prefill_chunk=chunk)
+    step = kdm.Decoder(SHAPE, w, max_seq=160)
     assert kdm.kd_get_info(pre.handle)["kernels_per_step"] == chunk  # info[5]: the prefill chunk
     p_d = torch.as_tensor(prompt, device=pre.device)
     pre.positions.zero_()
@@ -89,7 +93,7 @@ def test_prefill_small_ragged_and_continued(torch, kdm, chunk):
     torch.cuda.synchronize()
     assert pre.status() == 0
     assert int(pre.positions.item()) == 100
-    want = ref.forward_full(SMALL, w, prompt[:100])[-1]
+    want = ref.forward_full(SHAPE, w, prompt[:100])[-1]
     err = gh.inf_rel_err(pre.logits[0].cpu().numpy(), want)
     print(f"prefill chunk {chunk}: last-position rel logit err {err:.3e}")
     assert err <= TOL
@@ -100,14 +104,14 @@ def test_prefill_small_ragged_and_continued(torch, kdm, chunk):
     pre.prefill(p_d[100:130])
     torch.cuda.synchronize()
     assert pre.status() == 0 and int(pre.positions.item()) == 130
-    want = ref.forward_full(SMALL, w, prompt[:130])
+    want = ref.forward_full(SHAPE, w, prompt[:130])
     err = gh.inf_rel_err(pre.logits[0].cpu().numpy(), want[-1])
     assert err <= TOL
     nxt = int(pre.tokens.item())
     # a decode step from the prefilled cache
     pre.step()
     got = pre.logits[0].cpu().numpy()
-    want2 = ref.forward_full(SMALL, w, list(prompt[:130]) + [nxt])[-1]
+    want2 = ref.forward_full(SHAPE, w, list(prompt[:130]) + [nxt])[-1]
     err2 = gh.inf_rel_err(got, want2)
     print(f"prefill chunk {chunk}: continued prefill err {err:.3e}, next decode step err {err2:.3e}")
     assert err2 <= TOL
