@@ -120,6 +120,39 @@ def test_prefill_small_ragged_and_continued(torch, kdm, chunk, mha):
     step.close()
 
 
+def test_prefill_chunk_boundary_and_single_position(torch, kdm):
+    """256 prompt tokens in two full passes of 128 (ending on a 256-position attention chunk), then one
+    more token alone at position 256 (a pass of one row that opens the next chunk): logits against
+    the oracle, and the one-row pass against a one-token step from the same cache."""
+    w = workloads.make_weights(SMALL, seed=6)
+    rng = np.random.default_rng(13)
+    prompt = rng.integers(0, SMALL.vocab, 257).astype(np.int32)
+    pre = kdm.Decoder(SMALL, w, max_seq=300, prefill_chunk=128)
+    p_d = torch.as_tensor(prompt, device=pre.device)
+    pre.positions.zero_()
+    pre.prefill(p_d[:256])
+    torch.cuda.synchronize()
+    assert pre.status() == 0 and int(pre.positions.item()) == 256
+    want = ref.forward_full(SMALL, w, prompt[:257])
+    err = gh.inf_rel_err(pre.logits[0].cpu().numpy(), want[255])
+    assert err <= TOL, err
+    step = kdm.Decoder(SMALL, w, max_seq=300)
+    step.kv_view().copy_(pre.kv_view())
+    step.positions.fill_(256)
+    step.tokens.fill_(int(prompt[256]))
+    step.step()
+    pre.prefill(p_d[256:257])
+    torch.cuda.synchronize()
+    assert pre.status() == 0 and int(pre.positions.item()) == 257
+    got = pre.logits[0].cpu().numpy()
+    err1 = gh.inf_rel_err(got, want[256])
+    err2 = gh.inf_rel_err(got, step.logits[0].cpu().numpy())
+    print(f"prefill at a chunk boundary: rel logit err {err:.3e}; one-row pass {err1:.3e} (oracle), {err2:.3e} (one-token step)")
+    assert err1 <= TOL and err2 <= TOL
+    pre.close()
+    step.close()
+
+
 def test_2b_prefill_then_decode(torch, kdm):
     """The 2B decoder's 512-token prompt through kd_prefill (8 chunks of 64), against the cache one-token
     steps fill, then 8 greedy decode steps from it, every logit against the oracle."""
