@@ -17,6 +17,11 @@
 //   --> LM-head GEMM (logits) --> argmax (next token, position + 1)
 // A GEMM writes split-K partial sums; the kernel after it adds them in a fixed order, so results
 // are bitwise reproducible.
+//
+// The same sequence runs a prefill pass (kd_prefill): up to 128 consecutive prompt positions of one
+// session as the rows, all sharing its cache. Then the GEMMs take eight 16-row tiles, and the
+// attention is prefill_attention_kernel, which loads each chunk of the cache once for every row of
+// the pass and computes scores and weighted sums on the matrix cores.
 #pragma once
 #include <hip/hip_runtime.h>
 
