@@ -280,9 +280,12 @@ def measure(wl, args, torch, kd, roofline, steps: int, warmup: int, trace: bool,
 
 
 def stream_ceiling(torch, kd, gib: int = 4, reps: int = 10) -> float:
-    """Read rate (GB/s) of the library's plain streaming kernel over a gib GiB buffer."""
+    """Read rate (GB/s) of the library's plain streaming kernel over a gib GiB buffer of random bytes,
+    like the weights and caches it is compared with."""
     nbytes = gib << 30
-    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(1)
+    buf = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda:0", generator=g)
     stream = torch.cuda.current_stream()
     for _ in range(2):
         kd.kd_stream_read(buf, nbytes, stream)
@@ -431,7 +434,7 @@ def main() -> int:
         "stream_ceiling": None if ceiling is None else {
             "achieved_gbps": round(ceiling, 1),
             "frac_of_stream_ceiling": round(r["achieved_gbps"] / ceiling, 4),
-            "kernel": "stream_read_kernel (kd_stream_read, 4 GiB, 16-byte non-temporal loads)",
+            "kernel": "stream_read_kernel (kd_stream_read, 4 GiB of random bytes, 16-byte non-temporal loads)",
         },
         "roofline_tok_s": round(r["bound_tok_s"], 1),
         "frac_of_roofline_tok_s": round(r["tok_s"] / r["bound_tok_s"], 4),
