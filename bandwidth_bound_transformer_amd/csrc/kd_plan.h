@@ -26,7 +26,7 @@ constexpr int kChunkMin = 32;      // fewest cached positions per attention unit
 constexpr int kMaxUnits = 4;       // attention units one workgroup may hold in one step
 constexpr int kMergeWords = 4096;  // largest gather of one merge unit
 constexpr int kRowPart = 96;       // row partial sums kept per wave
-constexpr int kScorePos = 64;      // attention scores kept per wave (positions)
+constexpr int kScorePos = 96;      // attention scores kept per wave (positions)
 constexpr int kStageWords = 4096;  // staging area for gathers that are not the activation
 
 // Tag kinds of the vectors exchanged between workgroups (an exchange word carries value|tag).
