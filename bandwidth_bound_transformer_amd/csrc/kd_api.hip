@@ -668,7 +668,7 @@ int kd_get_info(kd_handle* h, int64_t info[8]) {
   if (h->batched) {
     const kd::bt::BatchState& b = h->bs;
     info[0] = 0;
-    info[1] = kd::bt::kGemmThreads;
+    info[1] = kd::bt::gemm_threads(h->bs.MT);
     info[2] = (int64_t)(b.w_lm + (size_t)b.V * b.d) * 2 + (int64_t)b.V * b.d * 2 + (int64_t)(2 * b.L + 1) * b.d * 2;
     info[5] = kd::bt::batch_kernels_per_tick(b);
     info[6] = b.g_qkv.KS | (b.g_o.KS << 8) | (b.g_gu.KS << 16) | (b.g_d.KS << 24);

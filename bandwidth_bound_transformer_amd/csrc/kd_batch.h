@@ -32,12 +32,15 @@ namespace bt {
 
 constexpr int kM = 64;             // sessions padded to four 16-row MFMA tiles
 constexpr int kMPrefill = 128;     // prefill positions per pass: eight 16-row tiles
-// Four waves per GEMM workgroup, so two workgroups share a CU (registers and LDS allow two):
-// one's start-up and barrier waits overlap the other's streaming.
-constexpr int kGemmWaves = 4;
-constexpr int kNB = 32 * kGemmWaves;  // GEMM output columns per workgroup: 32 per wave
+// A GEMM workgroup covers 128 output columns. With 64 activation rows (session ticks) it is 8
+// waves of one 16-column weight block each, and two workgroups share a CU, so one's start-up and
+// barrier waits overlap the other's streaming (measured: the 11B tick 1% shorter than with 4 waves
+// of two blocks). With 128 rows (prefill) it is 4 waves of two blocks, so that every activation
+// fragment a wave reads from LDS feeds two products (8 waves made the 8B prefill 15% slower).
+constexpr int kNB = 128;           // GEMM output columns per workgroup
+__host__ __device__ constexpr int gemm_waves(int mt) { return mt == 4 ? 8 : 4; }
+__host__ __device__ constexpr int gemm_threads(int mt) { return 64 * gemm_waves(mt); }
 constexpr int kKC = 128;           // K per LDS chunk of the activation block
-constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kAttThreads = 256;   // 4 waves; 16 lanes per KV position (hd = 128, bf16)
 constexpr int kChunk = 512;        // KV positions per attention workgroup (twice that for large session batches)
 constexpr int kMaxG = 4;
@@ -129,11 +132,11 @@ __global__ void tile_pack_kernel(const uint16_t* __restrict__ src, uint16_t* __r
 // ---------------------------------------------------------------------------------------------
 // small-M GEMM on MFMA: P[s][m][n] = sum over K-range s of (Ahi[m][k] + Alo[m][k]) * W[n][k]
 // ---------------------------------------------------------------------------------------------
-// Grid: (N / kNB) * KS workgroups of kGemmWaves waves; unit u covers columns [kNB (u / KS), + kNB) and K range
-// u % KS, in chunks of 128 K. Wave w owns two 16-row tiles of W (32 output columns), so every
-// activation fragment it reads from LDS feeds two products. Per chunk a lane loads four 1 KB
-// tiles of each of its row blocks (W in the tile layout above), straight into registers in the
-// B-operand layout.
+// Grid: (N / kNB) * KS workgroups of gemm_waves(MT) waves; unit u covers columns [kNB (u / KS), + kNB)
+// and K range u % KS, in chunks of 128 K. Wave w owns JW = 1 or 2 16-row tiles of W (16 JW output
+// columns), so every activation fragment it reads from LDS feeds JW products. Per chunk a lane loads
+// four 1 KB tiles of each of its row blocks (W in the tile layout above), straight into registers
+// in the B-operand layout.
 //
 // The weights (HBM) and the activation block (64 rows x 128 K, hi and lo; it stays in L2) are
 // loaded into registers kPF chunks ahead, in the same order, so a wait for one never holds up
@@ -148,7 +151,7 @@ constexpr int kPF = 2;  // chunks in flight per wave
 // projection. Its 128 rows are two groups of [32 gate rows; the 32 up rows of the same columns].
 // MT: 16-row tiles of the activation block (4: up to 64 rows, the session ticks; 8: up to 128, prefill).
 template <int NCH, bool SILU, int MT>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __restrict__ W, int N, int K,
+__global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* __restrict__ W, int N, int K,
                                                                 const uint16_t* __restrict__ Ahi,
                                                                 const uint16_t* __restrict__ Alo, int lda,
                                                                 float* __restrict__ P, int KS, int B, const uint32_t* skip,
@@ -167,36 +170,37 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
   const int k0 = s * (NCH * kKC);
   const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q = lane >> 4;
-  const int rb0 = nb * (kNB / 16) + 2 * wave;  // this wave's two 16-row blocks
-  const u32x4* wt[2];
+  constexpr int kThr = gemm_threads(MT), JW = kNB / 16 / gemm_waves(MT);
+  const int rb0 = nb * (kNB / 16) + JW * wave;  // this wave's JW 16-row blocks
+  const u32x4* wt[JW];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) wt[j] = (const u32x4*)W + ((size_t)(rb0 + j) * (K / 32) + k0 / 32) * 64 + lane;
+  for (int j = 0; j < JW; ++j) wt[j] = (const u32x4*)W + ((size_t)(rb0 + j) * (K / 32) + k0 / 32) * 64 + lane;
 
   // activation chunk: 2 x kRows rows x 16 pieces of 16 bytes, 4 (or 8) per thread
-  constexpr int kAPer = 2 * kRows * (kKC / 8) / kGemmThreads;
+  constexpr int kAPer = 2 * kRows * (kKC / 8) / kThr;
   // ext_vector_type registers (HIP's uint4 is a struct with a union, which the compiler keeps in
   // scratch memory when it sits in an array)
   struct Slot {
     u32x4 a[kAPer];
-    u32x4 w[2][4];
+    u32x4 w[JW][4];
   };
   auto load_chunk = [&](int c, Slot& sl) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kAPer; ++j) {
-      const int idx = tid + kGemmThreads * j;
+      const int idx = tid + kThr * j;
       const int hl = idx >> kHiLoShift, r = (idx >> 4) & (kRows - 1), cc = idx & 15;
       sl.a[j] = *(const u32x4*)((hl ? Alo : Ahi) + (size_t)r * lda + k0 + c * kKC + cc * 8);
     }
     // weights are read once per tick: non-temporal loads
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < JW; ++j)
 #pragma unroll
       for (int t = 0; t < 4; ++t) sl.w[j][t] = __builtin_nontemporal_load(wt[j] + (size_t)(c * 4 + t) * 64);
   };
 
-  f32x4 acc[2][MT];
+  f32x4 acc[JW][MT];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < JW; ++j)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // one chunk: activation slot -> LDS buffer, barrier, 64 MFMAs, then refill the slot kPF ahead
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
     const int buf = c & 1;
 #pragma unroll
     for (int j = 0; j < kAPer; ++j) {
-      const int idx = tid + kGemmThreads * j;
+      const int idx = tid + kThr * j;
       const int hl = idx >> kHiLoShift, r = (idx >> 4) & (kRows - 1), cc = idx & 15;
       As[buf][hl][r][cc] = sl.a[j];
     }
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
         const bf16x8 ah = __builtin_bit_cast(bf16x8, As[buf][0][r][t * 4 + q]);
         const bf16x8 al = __builtin_bit_cast(bf16x8, As[buf][1][r][t * 4 + q]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < JW; ++j) {
           const bf16x8 bw = __builtin_bit_cast(bf16x8, sl.w[j][t]);
           acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[j][mt], 0, 0, 0);
           acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[j][mt], 0, 0, 0);
@@ -241,13 +245,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
     float* Cs = reinterpret_cast<float*>(&As[0][0][0][0]);
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < JW; ++j)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Cs[(mt * 16 + q * 4 + i) * LDC + 32 * wave + 16 * j + (lane & 15)] = acc[j][mt][i];
+        for (int i = 0; i < 4; ++i) Cs[(mt * 16 + q * 4 + i) * LDC + 16 * JW * wave + 16 * j + (lane & 15)] = acc[j][mt][i];
     __syncthreads();
-    for (int e = tid; e < B * (kNB / 2); e += kGemmThreads) {
+    for (int e = tid; e < B * (kNB / 2); e += kThr) {
       const int m = e / (kNB / 2), c = e - m * (kNB / 2), grp = c / 32, ci = c - 32 * grp;
       const float gt = Cs[m * LDC + 64 * grp + ci], up = Cs[m * LDC + 64 * grp + 32 + ci];
       uint16_t hi, lo;
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint16_t* __re
   }
   // lane l holds rows 16 mt + 4 (l / 16) + i of column 16 (rb0 + j) + l % 16
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < JW; ++j) {
     const int n = (rb0 + j) * 16 + (lane & 15);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)

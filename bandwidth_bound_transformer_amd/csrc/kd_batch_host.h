@@ -316,7 +316,7 @@ inline int batch_tick(const BatchState& st, int nb, int32_t* tokens, int32_t* po
   uint16_t* kv = (uint16_t*)kvp;
   float* lg = logits ? logits : st.logits;
   auto gemm = [&](const uint16_t* W, const Gemm& g, float* out) {
-    hipLaunchKernelGGL(gemm_for<false>(g.K / (g.KS * kKC), st.MT), dim3((g.N / kNB) * g.KS), dim3(kGemmThreads), 0, s, W, g.N,
+    hipLaunchKernelGGL(gemm_for<false>(g.K / (g.KS * kKC), st.MT), dim3((g.N / kNB) * g.KS), dim3(gemm_threads(st.MT)), 0, s, W, g.N,
                        g.K, (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, out, g.KS, nb, skip,
                        (uint16_t*)nullptr, (uint16_t*)nullptr);
   };
@@ -355,10 +355,10 @@ inline int batch_tick(const BatchState& st, int nb, int32_t* tokens, int32_t* po
       // gate/up writes SiLU(gate) * up into the second activation block, which the down
       // projection reads (the first is still being read while gate/up runs)
       const Gemm& g = st.g_gu;
-      hipLaunchKernelGGL(gemm_for<true>(g.K / kKC, st.MT), dim3(g.N / kNB), dim3(kGemmThreads), 0, s, lay + st.w_gu, g.N, g.K,
+      hipLaunchKernelGGL(gemm_for<true>(g.K / kKC, st.MT), dim3(g.N / kNB), dim3(gemm_threads(st.MT)), 0, s, lay + st.w_gu, g.N, g.K,
                          (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, st.P, 1, nb, skip, st.A2hi, st.A2lo);
       const Gemm& gd = st.g_d;
-      hipLaunchKernelGGL(gemm_for<false>(gd.K / (gd.KS * kKC), st.MT), dim3((gd.N / kNB) * gd.KS), dim3(kGemmThreads), 0, s,
+      hipLaunchKernelGGL(gemm_for<false>(gd.K / (gd.KS * kKC), st.MT), dim3((gd.N / kNB) * gd.KS), dim3(gemm_threads(st.MT)), 0, s,
                          lay + st.w_d, gd.N, gd.K, (const uint16_t*)st.A2hi, (const uint16_t*)st.A2lo, st.lda, st.P, gd.KS,
                          nb, skip, (uint16_t*)nullptr, (uint16_t*)nullptr);
     } else {
