@@ -91,7 +91,7 @@ struct Buffers {
   uint8_t* embed = nullptr;
   uint8_t* norms = nullptr;
   float2* rope = nullptr;     // [S][hd/2] (cos, sin)
-  float* scales = nullptr;    // fp8 weights: row scales (Dims::sc_*)
+  float* scales = nullptr;    // fp8 or int8 weights: row scales (Dims::sc_*)
   uint64_t* ll = nullptr;
   uint32_t* flags = nullptr;  // [0] sticky status bits, [1] abort word, [2] tick skip flag (B > 1), [3] cancel word
 };
@@ -109,8 +109,11 @@ void free_buffers(Buffers& b) {
 
 typedef void (*KernelFn)(kd::Params);
 
-// The one-step kernel, or (multi) the kernel that may run several steps per launch.
-KernelFn pick_kernel(int wbytes, int hd, bool multi) {
+// The one-step kernel, or (multi) the kernel that may run several steps per launch. int8: the
+// one-byte matrix codes are int8 rather than E4M3.
+KernelFn pick_kernel(int wbytes, int hd, bool multi, bool int8) {
+  if (wbytes == 1 && hd == 128 && int8)
+    return multi ? kd::decode_step_kernel<kRing, 1, 2, 128, true, true> : kd::decode_step_kernel<kRing, 1, 2, 128, false, true>;
   if (wbytes == 1 && hd == 128) return multi ? kd::decode_step_kernel<kRing, 1, 2, 128, true> : kd::decode_step_kernel<kRing, 1, 2, 128, false>;
   if (wbytes == 2 && hd == 128) return multi ? kd::decode_step_kernel<kRing, 2, 2, 128, true> : kd::decode_step_kernel<kRing, 2, 2, 128, false>;
   if (wbytes == 2 && hd == 64) return multi ? kd::decode_step_kernel<kRing, 2, 2, 64, true> : kd::decode_step_kernel<kRing, 2, 2, 64, false>;
@@ -143,8 +146,10 @@ struct kd_handle {
 namespace {
 
 bool dtype_ok(int32_t t) { return t == KD_DTYPE_F32 || t == KD_DTYPE_BF16; }
-bool weight_dtype_ok(int32_t t) { return dtype_ok(t) || t == KD_DTYPE_FP8_E4M3; }
-int dtype_bytes(int32_t t) { return t == KD_DTYPE_FP8_E4M3 ? 1 : (t == KD_DTYPE_BF16 ? 2 : 4); }
+// one-byte matrix codes with a float32 scale per row
+bool quantised(int32_t t) { return t == KD_DTYPE_FP8_E4M3 || t == KD_DTYPE_INT8; }
+bool weight_dtype_ok(int32_t t) { return dtype_ok(t) || quantised(t); }
+int dtype_bytes(int32_t t) { return quantised(t) ? 1 : (t == KD_DTYPE_BF16 ? 2 : 4); }
 
 // Structural checks that need no device.
 int check_config(const kd_config* c) {
@@ -170,8 +175,8 @@ int check_supported(const kd_config* c, const kd::Dims& m) {
     if (rc != KD_OK) return rc;
   }
   if (c->head_dim != 64 && c->head_dim != 128) return KD_ERR_UNSUPPORTED;
-  // fp8 matrices come with bf16 embedding, gains and cache, and head_dim 128
-  if (c->weight_dtype == KD_DTYPE_FP8_E4M3 ? (c->kv_dtype != KD_DTYPE_BF16 || c->head_dim != 128)
+  // fp8 and int8 matrices come with bf16 embedding, gains and cache, and head_dim 128
+  if (quantised(c->weight_dtype) ? (c->kv_dtype != KD_DTYPE_BF16 || c->head_dim != 128)
                                             : c->weight_dtype != c->kv_dtype)
     return KD_ERR_UNSUPPORTED;
   if (m.G > kd::kMaxGroup || (int64_t)m.G * m.hd > kd::kThreads) return KD_ERR_UNSUPPORTED;
@@ -260,13 +265,13 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
   int rc = check_config(cfg);
   if (rc != KD_OK) return rc;
   if (!w || !w->embed || !w->layers || !w->final_norm || !w->lm_head) return KD_ERR_INVALID_ARG;
-  const bool fp8 = cfg->weight_dtype == KD_DTYPE_FP8_E4M3;
-  if (fp8 && !w->s_lm_head) return KD_ERR_INVALID_ARG;
+  const bool q8 = quantised(cfg->weight_dtype);  // one-byte codes with row scales (fp8 or int8)
+  if (q8 && !w->s_lm_head) return KD_ERR_INVALID_ARG;
   for (int l = 0; l < cfg->n_layers; ++l) {
     const kd_layer_weights& lw = w->layers[l];
     if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.w_gate || !lw.w_up || !lw.w_down)
       return KD_ERR_INVALID_ARG;
-    if (fp8 && (!lw.s_wq || !lw.s_wk || !lw.s_wv || !lw.s_wo || !lw.s_gate || !lw.s_up || !lw.s_down))
+    if (q8 && (!lw.s_wq || !lw.s_wk || !lw.s_wv || !lw.s_wo || !lw.s_gate || !lw.s_up || !lw.s_down))
       return KD_ERR_INVALID_ARG;
   }
   int ndev = 0;
@@ -278,7 +283,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return KD_ERR_UNSUPPORTED;
 
   const int wb = dtype_bytes(cfg->weight_dtype), kb = dtype_bytes(cfg->kv_dtype);
-  const int eb = fp8 ? 2 : wb;  // embedding and norm gains
+  const int eb = q8 ? 2 : wb;  // embedding and norm gains
   const int nwg = prop.multiProcessorCount;
   if (cfg->batch > 1) {
     if (cfg->prefill_chunk != 0) return KD_ERR_INVALID_ARG;  // lockstep handles take no prefill
@@ -309,7 +314,8 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
                                    cfg->vocab, cfg->max_seq, nwg, wb, kb);
   rc = check_supported(cfg, m);
   if (rc != KD_OK) return rc;
-  KernelFn kern = pick_kernel(wb, cfg->head_dim, false), kern_multi = pick_kernel(wb, cfg->head_dim, true);
+  const bool int8 = cfg->weight_dtype == KD_DTYPE_INT8;
+  KernelFn kern = pick_kernel(wb, cfg->head_dim, false, int8), kern_multi = pick_kernel(wb, cfg->head_dim, true, int8);
   if (!kern || !kern_multi) return KD_ERR_UNSUPPORTED;
   for (KernelFn k : {kern, kern_multi}) {
     int occ = 0;
@@ -337,7 +343,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
     if (hipMalloc(&h->buf.blob, blob_bytes) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     if (hipMalloc(&h->buf.embed, (size_t)m.V * d * eb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     if (hipMalloc(&h->buf.norms, (size_t)(2 * m.L + 1) * d * eb) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
-    if (fp8 && hipMalloc(&h->buf.scales, (size_t)kd::scale_layout(m).total * sizeof(float)) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
+    if (q8 && hipMalloc(&h->buf.scales, (size_t)kd::scale_layout(m).total * sizeof(float)) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     if (hipMalloc(&h->buf.ll, (size_t)h->lo.total * 8) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     if (hipMalloc(&h->buf.rope, (size_t)m.S * (m.hd / 2) * sizeof(float2)) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
     if (hipMalloc(&h->buf.flags, 256) != hipSuccess) { rc = KD_ERR_OOM; goto fail; }
@@ -349,7 +355,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
     (void)resolve_scratch(dev);
     const size_t row = (size_t)d * wb, erow = (size_t)d * eb;
     const kd::ScaleLayout sl = kd::scale_layout(m);
-    std::vector<float> sc(fp8 ? (size_t)sl.total : 0);
+    std::vector<float> sc(q8 ? (size_t)sl.total : 0);
     for (int l = 0; l < m.L; ++l) {
       const kd_layer_weights& lw = w->layers[l];
       uint8_t* lay = h->buf.blob + (size_t)l * m.layer_elems * wb;
@@ -384,7 +390,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
       KD_TRY(hipDeviceSynchronize());
       KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * l) * erow, lw.attn_norm, erow, hipMemcpyHostToDevice));
       KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * l + 1) * erow, lw.ffn_norm, erow, hipMemcpyHostToDevice));
-      if (fp8) {
+      if (q8) {
         // row scales in the rows' packed order: QKV (q, k, v), O, each workgroup's [gate; up] slice, down
         float* L0 = sc.data() + (size_t)l * sl.layer;
         std::memcpy(L0, lw.s_wq, sizeof(float) * m.qdim);
@@ -402,7 +408,7 @@ int kd_init(const kd_config* cfg, const kd_weights* w, kd_handle** out) {
     KD_TRY(hipMemcpy(h->buf.norms + (size_t)(2 * m.L) * erow, w->final_norm, erow, hipMemcpyHostToDevice));
     KD_TRY(hipMemcpy(h->buf.blob + (size_t)m.off_lm * wb, w->lm_head, (size_t)m.V * row, hipMemcpyHostToDevice));
     KD_TRY(hipMemcpy(h->buf.embed, w->embed, (size_t)m.V * erow, hipMemcpyHostToDevice));
-    if (fp8) {
+    if (q8) {
       std::memcpy(sc.data() + sl.lm, w->s_lm_head, sizeof(float) * m.V);
       KD_TRY(hipMemcpy(h->buf.scales, sc.data(), sc.size() * sizeof(float), hipMemcpyHostToDevice));
     }

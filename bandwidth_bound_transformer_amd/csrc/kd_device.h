@@ -48,9 +48,9 @@ namespace kd {
 
 struct Params {
   const uint8_t* blob;   // packed layer weights and LM head, weight dtype
-  const uint8_t* embed;  // [V][d], bf16 (fp8 and bf16 models) or f32
+  const uint8_t* embed;  // [V][d], bf16 (fp8, int8 and bf16 models) or f32
   const uint8_t* norms;  // [L][2][d] attention/FFN gains, then final gain [d], embedding dtype
-  const float* scales;   // fp8 weights: row scales laid out as scale_layout() says (else null)
+  const float* scales;   // fp8 or int8 weights: row scales laid out as scale_layout() says (else null)
   const float2* rope;    // [S][hd/2] (cos, sin) of position * theta_i
   uint64_t* ll;          // exchange words
   LLLayout lo;
@@ -533,11 +533,34 @@ __device__ __forceinline__ float dot8_fp8(uint32_t lo, uint32_t hi, const float*
   return s;
 }
 
-// One 16-byte lane load of weights times the matching activation values (16 fp8, 8 bf16 or 4 f32).
-template <int WB>
+// Eight int8 weights (two 32-bit words, byte k is element k) times a[0..8). Each signed byte
+// converts to float exactly (one sign-extending byte-select conversion per element).
+__device__ __forceinline__ float dot8_i8(uint32_t lo, uint32_t hi, const float* a) {
+  const float4 a0 = *(const float4*)a, a1 = *(const float4*)(a + 4);
+  float s = (float)(int8_t)lo * a0.x;
+  s = fmaf((float)(int8_t)(lo >> 8), a0.y, s);
+  s = fmaf((float)(int8_t)(lo >> 16), a0.z, s);
+  s = fmaf((float)((int32_t)lo >> 24), a0.w, s);
+  s = fmaf((float)(int8_t)hi, a1.x, s);
+  s = fmaf((float)(int8_t)(hi >> 8), a1.y, s);
+  s = fmaf((float)(int8_t)(hi >> 16), a1.z, s);
+  s = fmaf((float)((int32_t)hi >> 24), a1.w, s);
+  return s;
+}
+
+// Eight 1-byte codes times a[0..8): E4M3 or (I8) int8.
+template <bool I8>
+__device__ __forceinline__ float dot8_q8(uint32_t lo, uint32_t hi, const float* a) {
+  if constexpr (I8) return dot8_i8(lo, hi, a);
+  else return dot8_fp8(lo, hi, a);
+}
+
+// One 16-byte lane load of weights times the matching activation values (16 one-byte codes, 8 bf16
+// or 4 f32). I8: the one-byte codes are int8, else E4M3.
+template <int WB, bool I8 = false>
 __device__ __forceinline__ float dot16(const uint4 w, const float* a) {
   if constexpr (WB == 1) {
-    return dot8_fp8(w.x, w.y, a) + dot8_fp8(w.z, w.w, a + 8);
+    return dot8_q8<I8>(w.x, w.y, a) + dot8_q8<I8>(w.z, w.w, a + 8);
   } else if constexpr (WB == 2) {
     const float4 a0 = *(const float4*)a, a1 = *(const float4*)(a + 4);
     float s = bf16_lo(w.x) * a0.x;
@@ -572,7 +595,7 @@ __device__ __forceinline__ void unpack16(const uint4 w, float* out) {
 // Row-split matrix-vector product over packets [s.lo, s.hi): packets are row chunks of 64*vpl
 // values; act is the input vector. A row's lane sums are reduced across the wave when the row (or
 // this wave's share of it) ends; part[r - first row] receives the wave's sum.
-template <int RING, int WB, bool COH>
+template <int RING, int WB, bool COH, bool I8>
 // (The segment is taken by value: a copy in registers is not reloaded from LDS after every
 // LDS-DMA refill, whose asm clobbers memory.)
 __device__ __forceinline__ void consume_rows(Ring<RING, COH>& rg, const SegEntry s, int C, const float* act, float* part) {
@@ -584,7 +607,7 @@ __device__ __forceinline__ void consume_rows(Ring<RING, COH>& rg, const SegEntry
   float acc = 0.f;
   for (int i = s.lo; i < s.hi; ++i) {
     const uint4 wv = rg.take();
-    acc += dot16<WB>(wv, act + c * (64 * VPL) + lane * VPL);
+    acc += dot16<WB, I8>(wv, act + c * (64 * VPL) + lane * VPL);
     rg.give();
     if (++c == C || i + 1 == s.hi) {
       const float t = wave_sum(acc);
@@ -599,20 +622,20 @@ __device__ __forceinline__ void consume_rows(Ring<RING, COH>& rg, const SegEntry
 // Down projection of this WG's FFN slice over the wave's whole 64-row blocks: packets hold 64 rows
 // x vpl columns; lane l owns row 64*b + l, and all lanes read the same slice values. Each finished
 // block is published at once as 64 contiguous exchange words.
-template <int RING, int WB, bool COH>
+template <int RING, int WB, bool COH, bool I8>
 __device__ __forceinline__ void consume_down(Ring<RING, COH>& rg, const SegEntry s, int g, const float* a, uint64_t* ll,
                                              int64_t dp_at, uint32_t tag) {
   const int lane = lane_id();
   if constexpr (WB == 1) {
-    // fp8: 128-row blocks; lane l sums row 128 b + l from the first 8 bytes of its pieces and row
+    // one-byte codes: 128-row blocks; lane l sums row 128 b + l from the first 8 bytes of its pieces and row
     // 128 b + 64 + l from the last 8, over 8 slice columns per packet
     int b = s.lo / g;
     int j = 0;
     float acc0 = 0.f, acc1 = 0.f;
     for (int i = s.lo; i < s.hi; ++i) {
       const uint4 wv = rg.take();
-      acc0 += dot8_fp8(wv.x, wv.y, a + j * 8);
-      acc1 += dot8_fp8(wv.z, wv.w, a + j * 8);
+      acc0 += dot8_q8<I8>(wv.x, wv.y, a + j * 8);
+      acc1 += dot8_q8<I8>(wv.z, wv.w, a + j * 8);
       rg.give();
       if (++j == g) {
         ll_store(ll, dp_at + (int64_t)b * 128 + lane, acc0, tag);
@@ -630,7 +653,7 @@ __device__ __forceinline__ void consume_down(Ring<RING, COH>& rg, const SegEntry
   float acc = 0.f;
   for (int i = s.lo; i < s.hi; ++i) {
     const uint4 wv = rg.take();
-    acc += dot16<WB>(wv, a + j * VPL);
+    acc += dot16<WB, I8>(wv, a + j * VPL);
     rg.give();
     if (++j == g) {
       ll_store(ll, dp_at + (int64_t)b * 64 + lane, acc, tag);
@@ -939,15 +962,17 @@ __device__ __forceinline__ int trace_slot(int layer, int ev) { return 2 + kTrace
 // and leave together, after their LDS-DMA loads have landed.
 // MULTI: the launch may run several steps (kd_generate); without it the kernel runs exactly one,
 // with no step loop and no coherent-load choice in the streaming loops.
-template <int RING, int WB, int KB, int HD, bool MULTI>
+// I8 (with WB = 1): the one-byte matrix codes are int8 instead of E4M3.
+template <int RING, int WB, int KB, int HD, bool MULTI, bool I8 = false>
 __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P_arg) {
   __shared__ Smem<RING> sm;
   // work on a private copy: references into the kernel-argument segment would force a stack copy
   const Params P = P_arg;
   const Dims m = P.m;
-  constexpr int EB = WB == 1 ? 2 : WB;  // embedding and norm gains: bf16 when the matrices are fp8
-  constexpr bool FP8 = WB == 1;         // matrices hold E4M3 codes; each row's total is times its scale
-  const ScaleLayout scl_at = FP8 ? scale_layout(m) : ScaleLayout{};
+  constexpr int EB = WB == 1 ? 2 : WB;  // embedding and norm gains: bf16 when the matrices are 1-byte codes
+  constexpr bool Q8 = WB == 1;          // matrices hold E4M3 or int8 codes; each row's total is times its scale
+  static_assert(Q8 || !I8, "int8 codes are one byte");
+  const ScaleLayout scl_at = Q8 ? scale_layout(m) : ScaleLayout{};
   const int w = (int)blockIdx.x;
   const int tid = (int)threadIdx.x;
   const int wave = wave_id();
@@ -1067,11 +1092,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   for (int layer = 0; layer < m.L; ++layer) {
     const uint8_t* g_attn = P.norms + ((int64_t)layer * 2 + 0) * m.d * EB;
     const uint8_t* g_ffn = P.norms + ((int64_t)layer * 2 + 1) * m.d * EB;
-    // fp8 row scales of this layer: each thread that publishes a row loads its scale ahead of the
+    // row scales of this layer (fp8 or int8 codes): each thread that publishes a row loads its scale ahead of the
     // gather before it, so the load's latency hides behind that wait
-    const float* const scl = FP8 ? P.scales + (int64_t)layer * scl_at.layer : nullptr;
+    const float* const scl = Q8 ? P.scales + (int64_t)layer * scl_at.layer : nullptr;
     float s_q = 1.f;
-    if constexpr (FP8)
+    if constexpr (Q8)
       if (tid < nq) s_q = scl[rq0 + tid];
     // ---- x (this WG's rows kept raw for the residual), RMSNorm folded into the gather ----
     load_piece_gains<EB>(g_attn, m.d, fold.g);
@@ -1104,7 +1129,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     stamp(trace_slot(layer, 0));
     stamp(trace_slot(layer, 1));
     // ---- QKV rows ----
-    consume_rows<RING, WB, MULTI>(rg, uniform(tab[0]), m.cd, sm.act, sm.rowpart[wave]);
+    consume_rows<RING, WB, MULTI, I8>(rg, uniform(tab[0]), m.cd, sm.act, sm.rowpart[wave]);
     wg_barrier();
     stamp(trace_slot(layer, 2));
     if (tid < nq)
@@ -1300,11 +1325,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     stamp(trace_slot(layer, 12));
     // ---- output projection rows + residual ----
     float s_o = 1.f;
-    if constexpr (FP8)
+    if constexpr (Q8)
       if (tid < nrd) s_o = scl[scl_at.o + rd0 + tid];
     if (!xc.gather_vec(ll_tag(tb0, layer, kO), P.lo.o, m.qdim, sm.act)) goto drain;
     stamp(trace_slot(layer, 13));
-    consume_rows<RING, WB, MULTI>(rg, uniform(tab[oseg]), m.cq, sm.act, sm.rowpart[wave]);
+    consume_rows<RING, WB, MULTI, I8>(rg, uniform(tab[oseg]), m.cq, sm.act, sm.rowpart[wave]);
     wg_barrier();
     stamp(trace_slot(layer, 14));
     if (tid < nrd) {
@@ -1315,7 +1340,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     stamp(trace_slot(layer, 15));
     // ---- gate/up rows of this workgroup's FFN slice ----
     float s_g = 1.f, s_u = 1.f;
-    if constexpr (FP8)
+    if constexpr (Q8)
       if (tid < nf) {
         s_g = scl[scl_at.gu + 2 * f0 + tid];
         s_u = scl[scl_at.gu + 2 * f0 + nf + tid];
@@ -1328,7 +1353,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     r_ffn = norm_scale(sm, m.d, P.eps);
     stamp(trace_slot(layer, 16));
     stamp(trace_slot(layer, 17));
-    consume_rows<RING, WB, MULTI>(rg, uniform(tab[oseg + 1]), m.cd, sm.act, sm.rowpart[wave]);
+    consume_rows<RING, WB, MULTI, I8>(rg, uniform(tab[oseg + 1]), m.cd, sm.act, sm.rowpart[wave]);
     wg_barrier();
     stamp(trace_slot(layer, 18));
     if (tid < nf) {
@@ -1339,16 +1364,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     wg_barrier();
     stamp(trace_slot(layer, 19));
     // ---- down projection of the slice, for all d rows, published block by block ----
-    consume_down<RING, WB, MULTI>(rg, uniform(tab[oseg + 2]), gD, sm.a, P.ll, P.lo.dp + (int64_t)w * m.d, ll_tag(tb0, layer, kDP));
+    consume_down<RING, WB, MULTI, I8>(rg, uniform(tab[oseg + 2]), gD, sm.a, P.ll, P.lo.dp + (int64_t)w * m.d, ll_tag(tb0, layer, kDP));
     stamp(trace_slot(layer, 20));
     // ---- sum every slice's contribution to this workgroup's rows; residual add ----
     {
       float* st = sm.u.stage;  // [nrd][nwg]: each row's partials contiguous (conflict-free reads)
       const int hp = nrd / 2;  // pieces per producer
       // T = kThreads / nrd threads per row when nrd is a power of two from 8 to 64, else one wave
-      // per row (see below); fp8: the scale of the row this thread finishes, loaded ahead
+      // per row (see below); fp8 or int8: the scale of the row this thread finishes, loaded ahead
       float s_d = 1.f;
-      if constexpr (FP8) {
+      if constexpr (Q8) {
         const bool pt = nrd >= 8 && nrd <= 64 && (nrd & (nrd - 1)) == 0;
         const int rr = pt ? tid / (kThreads / max(nrd, 1)) : wave;
         if (rr < nrd) s_d = scl[scl_at.d + rd0 + rr];
@@ -1385,7 +1410,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
           float s = 0.f;
           for (int q = lane; q < m.nwg; q += 64) s += st[r * m.nwg + q];
           s = wave_sum(s);
-          if constexpr (FP8) s *= r == wave ? s_d : scl[scl_at.d + rd0 + r];
+          if constexpr (Q8) s *= r == wave ? s_d : scl[scl_at.d + rd0 + r];
           if (lane == 0) ll_store(P.ll, P.lo.x + rd0 + r, sm.xo[r] + s, ll_tag(tb0, layer, kX));
         }
       }
@@ -1396,8 +1421,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
   }
 
   // ---- final norm, LM head rows, argmax ----
-  float s_l = 1.f;  // fp8: scale of this thread's first LM-head row
-  if constexpr (FP8)
+  float s_l = 1.f;  // fp8 or int8: scale of this thread's first LM-head row
+  if constexpr (Q8)
     if (tid < nl) s_l = P.scales[scl_at.lm + rl0 + tid];
   load_piece_gains<EB>(P.norms + (int64_t)m.L * 2 * m.d * EB, m.d, fold.g);
   fold.ss = 0.f;
@@ -1406,7 +1431,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     goto drain;
   r_final = norm_scale(sm, m.d, P.eps);
   stamp(trace_slot(m.L, 0));
-  consume_rows<RING, WB, MULTI>(rg, uniform(sm.lm_seg[wave]), m.cd, sm.act, sm.rowpart[wave]);
+  consume_rows<RING, WB, MULTI, I8>(rg, uniform(sm.lm_seg[wave]), m.cd, sm.act, sm.rowpart[wave]);
   wg_barrier();
   stamp(trace_slot(m.L, 1));
   {
@@ -1415,7 +1440,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_kernel(const Params P
     bool nan = false;
     for (int r = tid; r < nl; r += kThreads) {
       float val = row_total(sm, kTileLM, m.cd, r) * r_final;
-      if constexpr (FP8) val *= r == tid ? s_l : P.scales[scl_at.lm + rl0 + r];
+      if constexpr (Q8) val *= r == tid ? s_l : P.scales[scl_at.lm + rl0 + r];
       if (P.logits) P.logits[(int64_t)step * m.V + rl0 + r] = val;
       if (val != val) { nan = true; continue; }
       if (better(val, rl0 + r, best, besti)) { best = val; besti = rl0 + r; }

@@ -40,6 +40,7 @@ KD_CTRL_WAIT_LIMIT_US = 2
 KD_DTYPE_F32 = 0
 KD_DTYPE_BF16 = 1
 KD_DTYPE_FP8_E4M3 = 2
+KD_DTYPE_INT8 = 3
 
 EXPORTS = (
     "kd_init",
@@ -153,7 +154,7 @@ def _check(code: int, what: str) -> None:
 
 def make_config(shape, batch: int = 1, max_seq: int = 1, prefill_chunk: int = 0) -> kd_config:
     """kd_config of a ``workloads.ModelShape``."""
-    dt = {"f32": KD_DTYPE_F32, "bf16": KD_DTYPE_BF16, "fp8": KD_DTYPE_FP8_E4M3}
+    dt = {"f32": KD_DTYPE_F32, "bf16": KD_DTYPE_BF16, "fp8": KD_DTYPE_FP8_E4M3, "int8": KD_DTYPE_INT8}
     return kd_config(
         shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim,
         shape.vocab, max_seq, batch, shape.norm_eps, shape.rope_base, dt[shape.weight_dtype], dt[shape.kv_dtype],
@@ -176,7 +177,7 @@ def kd_kv_layout(cfg: kd_config):
 
 
 def _tensor_ptrs(t):
-    """(data pointer, row-scale pointer or None): an fp8 matrix carries codes and scales."""
+    """(data pointer, row-scale pointer or None): an fp8 or int8 matrix carries codes and scales."""
     if hasattr(t, "codes"):
         return _host_ptr(t.codes), _host_ptr(t.scale)
     return _host_ptr(t), None

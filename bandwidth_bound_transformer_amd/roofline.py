@@ -11,7 +11,7 @@ The count below is what the method itself must move per step, not what an
 implementation happens to move:
 
 * every layer weight, the final norm and the LM head, once per step (once per
-  tick for all B sessions together); for fp8 models, one byte per matrix
+  tick for all B sessions together); for fp8 and int8 models, one byte per matrix
   element plus a float32 scale per matrix row, and bf16 norm gains;
 * one embedding row per session;
 * per session, the KV cache over positions 0..p (K and V, every layer and kv head);

@@ -1,6 +1,6 @@
 """Decode-step benchmark: tokens/s on one MI355X and the fraction of the HBM roofline.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b|2b|2b_long|tiny|11b_x56]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b|2b|2b_long|tiny|11b_x56|8b_fp8|2b_fp8|8b_int8|2b_int8]
 
 One "step" is one kd_step: a whole decode step of every session. At batch 1 it is one persistent
 kernel launch; for the 56 lockstep sessions it is one tick, a fixed kernel sequence on one stream.
@@ -18,8 +18,8 @@ Printed on stdout, as one JSON line:
   stream_ceiling the read rate of a plain streaming kernel on the same GPU in the same run, and
                  the decode kernel's achieved rate as a fraction of it
   cpu_baseline   the CPU oracle, run for a bounded number of decode steps on the host cores
-  extra          the 2B batch-1 workload, and the 8B and 2B with FP8 weights, measured the same way
-                 in the same run (default run only)
+  extra          the 2B batch-1 workload, and the 8B and 2B with FP8 and with int8 weights, measured the
+                 same way in the same run (default run only)
   ttft           bf16 prompts: time to the first token with kd_prefill (the prompt on the matrix
                  cores), beside the time the same prompt takes one step per token
 Everything else goes to stderr.
@@ -307,7 +307,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="8b", choices=["tiny", "2b", "8b", "2b_long", "11b_x56", "2b_fp8", "8b_fp8"])
+    ap.add_argument("--workload", default="8b", choices=["tiny", "2b", "8b", "2b_long", "11b_x56", "2b_fp8", "8b_fp8", "2b_int8", "8b_int8"])
     ap.add_argument("--prefill-chunk", type=int, default=128,
                     help="prompt positions per kd_prefill pass for bf16 batch-1 workloads (2..128)")
     ap.add_argument("--extra", default=None,
@@ -366,7 +366,7 @@ def main() -> int:
 
     extra_names = args.extra
     if extra_names is None:
-        extra_names = "2b,8b_fp8,2b_fp8" if args.workload == "8b" else "none"
+        extra_names = "2b,8b_fp8,2b_fp8,8b_int8,2b_int8" if args.workload == "8b" else "none"
     extra = {}
     for name in [n for n in extra_names.split(",") if n and n != "none"]:
         try:

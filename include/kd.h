@@ -75,6 +75,11 @@ extern "C" {
    bytes of the parameters cuts what every token reads ("17k tokens/sec" page, best practice 2 on
    model quantisation, and its FAQ question 3, which names FP8). */
 #define KD_DTYPE_FP8_E4M3 2
+/* int8 (two's complement, -128..127), weight_dtype only, laid out like KD_DTYPE_FP8_E4M3: the
+   projection matrices and the LM head are int8 codes with one float32 scale per output row (the
+   weight is code times scale), and the embedding, the norm gains and the cache are bf16 ("17k
+   tokens/sec" page, best practice 2, which names INT8 as the lower precision for the parameters). */
+#define KD_DTYPE_INT8 3
 
 /*
  * Model and run configuration, fixed at kd_init.
@@ -98,8 +103,8 @@ extern "C" {
  *                this many positions as small-M GEMMs on the matrix cores (the shape must meet the
  *                lockstep path's conditions above; the library then holds a second copy of the
  *                weights, in the matrix cores' tile layout).
- *   weight_dtype KD_DTYPE_BF16 or KD_DTYPE_F32, with kv_dtype the same; or KD_DTYPE_FP8_E4M3
- *                with kv_dtype KD_DTYPE_BF16 (batch 1, head_dim 128, d_model and q_dim multiples
+ *   weight_dtype KD_DTYPE_BF16 or KD_DTYPE_F32, with kv_dtype the same; or KD_DTYPE_FP8_E4M3 or
+ *                KD_DTYPE_INT8 with kv_dtype KD_DTYPE_BF16 (batch 1, head_dim 128, d_model and q_dim multiples
  *                of 1024, ffn_dim a multiple of 8 with ffn_dim/8 >= the GPU's compute units).
  */
 typedef struct kd_config {
@@ -120,9 +125,10 @@ typedef struct kd_config {
 } kd_config;
 
 /* Host pointers to one layer's tensors, row-major, in weight_dtype (bf16 = uint16 patterns). With
- * KD_DTYPE_FP8_E4M3 the seven matrices are uint8 E4M3 codes, the gains bf16, and the s_* arrays
- * hold the float32 scale of each output row of the matching matrix: the weight at (r, c) is the
- * code's value times row r's scale. For other weight types the s_* pointers are ignored. */
+ * KD_DTYPE_FP8_E4M3 (or KD_DTYPE_INT8) the seven matrices are one-byte E4M3 (or int8) codes, the
+ * gains bf16, and the s_* arrays hold the float32 scale of each output row of the matching matrix:
+ * the weight at (r, c) is the code's value times row r's scale. For other weight types the s_*
+ * pointers are ignored. */
 typedef struct kd_layer_weights {
   const void* attn_norm; /* [d_model] */
   const void* wq;        /* [n_q_heads*head_dim, d_model] */
@@ -133,7 +139,7 @@ typedef struct kd_layer_weights {
   const void* w_gate;    /* [ffn_dim, d_model] */
   const void* w_up;      /* [ffn_dim, d_model] */
   const void* w_down;    /* [d_model, ffn_dim] */
-  const float* s_wq;     /* [n_q_heads*head_dim]  fp8 only: row scales */
+  const float* s_wq;     /* [n_q_heads*head_dim]  fp8 and int8 only: row scales */
   const float* s_wk;     /* [n_kv_heads*head_dim] */
   const float* s_wv;     /* [n_kv_heads*head_dim] */
   const float* s_wo;     /* [d_model] */
@@ -148,7 +154,7 @@ typedef struct kd_weights {
   const kd_layer_weights* layers; /* [n_layers] */
   const void* final_norm;         /* [d_model] */
   const void* lm_head;            /* [vocab, d_model] (separate from embed) */
-  const float* s_lm_head;         /* [vocab] fp8 only: row scales of lm_head */
+  const float* s_lm_head;         /* [vocab] fp8 and int8 only: row scales of lm_head */
 } kd_weights;
 
 typedef struct kd_handle kd_handle;

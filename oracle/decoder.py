@@ -45,6 +45,11 @@ FP8). An fp8 model stores each projection matrix and the LM head as OCP FP8
 E4M3 codes with one float32 scale per output row; its embedding and norm gains
 are bf16. The oracle is fed those codes and scales and computes with the
 weights they stand for, code value times row scale, exactly in float64.
+
+INT8 weights (the same page, best practice 2, names INT8): the projection
+matrices and the LM head are int8 codes (two's complement) with one float32
+scale per output row; the weight is the code times its row's scale, exactly in
+float64. Everything else is as for fp8 models.
 """
 
 from __future__ import annotations
@@ -112,13 +117,15 @@ _E4M3_VALUES = fp8_e4m3_to_f64(np.arange(256, dtype=np.uint8))
 def weight_f64(w, dtype: str) -> np.ndarray:
     """float64 values of a stored weight tensor.
 
-    bf16 bit patterns or float32 arrays; for fp8 models, an object with ``codes`` (E4M3 bit
-    patterns, [rows, cols]) and ``scale`` (float32 [rows]) for each projection matrix, whose
-    value is the code's value times its row's scale, and bf16 patterns for the rest.
+    bf16 bit patterns or float32 arrays; for fp8 (int8) models, an object with ``codes`` (E4M3
+    bit patterns, or int8 values, [rows, cols]) and ``scale`` (float32 [rows]) for each projection
+    matrix, whose value is the code's value times its row's scale, and bf16 patterns for the rest.
     """
     if dtype == "fp8" and hasattr(w, "codes"):
         return _E4M3_VALUES[np.asarray(w.codes, np.uint8)] * np.asarray(w.scale, np.float32).astype(np.float64)[:, None]
-    if dtype in ("bf16", "fp8"):
+    if dtype == "int8" and hasattr(w, "codes"):
+        return np.asarray(w.codes, np.int8).astype(np.float64) * np.asarray(w.scale, np.float32).astype(np.float64)[:, None]
+    if dtype in ("bf16", "fp8", "int8"):
         return bf16_to_f64(w)
     if dtype == "f32":
         return np.asarray(w, np.float32).astype(np.float64)

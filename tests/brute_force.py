@@ -56,11 +56,17 @@ def _fp8_rows(t):
     return [[v * float(s) for v in row] for row, s in zip(vals, t.scale.tolist())]
 
 
+def _int8_rows(t):
+    """An int8 matrix (codes and per-row scales) -> nested list of Python floats: each code is read
+    as a Python int from the signed bytes, then times its row's scale."""
+    return [[int(v) * float(s) for v in row] for row, s in zip(t.codes.tolist(), t.scale.tolist())]
+
+
 def _tolist(t, dtype):
     """Stored tensor -> nested list of Python floats."""
     if hasattr(t, "codes"):
-        return _fp8_rows(t)
-    if dtype in ("bf16", "fp8"):
+        return _int8_rows(t) if t.codes.dtype.kind == "i" else _fp8_rows(t)
+    if dtype in ("bf16", "fp8", "int8"):
         conv = bf16_value
     else:
         conv = float

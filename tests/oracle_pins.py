@@ -17,7 +17,8 @@ What each pin rests on:
 * library routines: torch's float32 -> bfloat16 conversion, numpy's argmax
   and scipy's logistic function; torch's float8_e4m3fn type for the value of
   every FP8 E4M3 code, and the brute force fed the weights torch decodes for
-  an fp8 model.
+  an fp8 model; for an int8 model, the brute force fed each code as a Python
+  integer (every value -128..127 occurs) times its row's scale.
 """
 
 from __future__ import annotations
@@ -32,6 +33,7 @@ from . import brute_force
 MICRO_GQA = ModelShape(2, 16, 4, 2, 8, 24, 40, rope_base=10000.0, weight_dtype="bf16", kv_dtype="bf16")
 MICRO_MHA_F32 = ModelShape(1, 12, 3, 3, 4, 20, 33, rope_base=500.0, weight_dtype="f32", kv_dtype="f32")
 MICRO_FP8 = ModelShape(2, 16, 4, 2, 8, 24, 40, rope_base=10000.0, weight_dtype="fp8", kv_dtype="bf16")
+MICRO_INT8 = ModelShape(2, 16, 4, 2, 8, 24, 40, rope_base=10000.0, weight_dtype="int8", kv_dtype="bf16")
 FP8_MATRICES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
 
@@ -75,6 +77,28 @@ def micro_fp8_weights(seed: int = 41) -> dict:
         for name in FP8_MATRICES:
             lw[name] = fp8(lw[name].shape)
     w["lm_head"] = fp8(w["lm_head"].shape)
+    return w
+
+
+def micro_int8_weights(seed: int = 43) -> dict:
+    """An int8 micro model whose codes cover every value -128..127 and whose row scales differ
+    from row to row, so a code read without its sign, or a scale applied to the wrong row or
+    column, shows."""
+    w = micro_weights(MICRO_GQA, seed=seed)
+    w["dtype"] = "int8"
+    rng = np.random.default_rng(seed + 2000)
+    every = np.arange(-128, 128, dtype=np.int16).astype(np.int8)
+
+    def int8(shape):
+        codes = rng.integers(-128, 128, size=shape).astype(np.int8)
+        codes.reshape(-1)[: every.size] = every[: min(every.size, codes.size)]
+        scale = (rng.uniform(0.25, 2.0, shape[0]) * (0.4 / 127.0)).astype(np.float32)
+        return workloads.Int8Matrix(codes, scale)
+
+    for lw in w["layers"]:
+        for name in FP8_MATRICES:
+            lw[name] = int8(lw[name].shape)
+    w["lm_head"] = int8(w["lm_head"].shape)
     return w
 
 
@@ -360,6 +384,18 @@ def pin_fp8(mod):
         assert _rel(got, r) < 1e-9, (pos, _rel(got, r))
 
 
+def pin_int8(mod):
+    """int8 weights: an int8 micro model steps exactly as the brute force fed each code as a
+    Python integer times its row's scale."""
+    w = micro_int8_weights()
+    o = mod.Oracle(MICRO_INT8, w, batch=1, max_seq=8)
+    feeds = [(3, 0), (17, 1), (39, 2), (0, 3), (22, 4)]
+    want = brute_force.decode(MICRO_INT8, w, feeds)
+    for (tok, pos), r in zip(feeds, want):
+        got = o.step_one(0, tok, pos)
+        assert _rel(got, r) < 1e-9, (pos, _rel(got, r))
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_brute_force_prefilled,
@@ -375,4 +411,5 @@ ALL_PINS = [
     pin_identity_layers,
     pin_sessions_independent,
     pin_fp8,
+    pin_int8,
 ]

@@ -76,7 +76,18 @@ MUTANTS = {
     "fp8_subnormals_as_normals": ("np.where(e == 0, f / 8.0 * 2.0**-6,", "np.where(e < 0, f / 8.0 * 2.0**-6,"),
     "fp8_sign_ignored": ("sign = np.where(c & 0x80, -1.0, 1.0)", "sign = np.where(c & 0x00, -1.0, 1.0)"),
     "fp8_scale_per_column": (
-        "np.asarray(w.scale, np.float32).astype(np.float64)[:, None]",
+        "_E4M3_VALUES[np.asarray(w.codes, np.uint8)] * np.asarray(w.scale, np.float32).astype(np.float64)[:, None]",
+        "_E4M3_VALUES[np.asarray(w.codes, np.uint8)] * "
+        "np.resize(np.asarray(w.scale, np.float32).astype(np.float64), w.codes.shape[1])[None, :]",
+    ),
+    # int8 weights: the codes' sign, and which axis the scales run along
+    "int8_read_unsigned": (
+        "np.asarray(w.codes, np.int8).astype(np.float64)",
+        "np.asarray(w.codes, np.int8).view(np.uint8).astype(np.float64)",
+    ),
+    "int8_scale_per_column": (
+        "np.asarray(w.codes, np.int8).astype(np.float64) * np.asarray(w.scale, np.float32).astype(np.float64)[:, None]",
+        "np.asarray(w.codes, np.int8).astype(np.float64) * "
         "np.resize(np.asarray(w.scale, np.float32).astype(np.float64), w.codes.shape[1])[None, :]",
     ),
 }
@@ -96,6 +107,7 @@ PIN_ORDER = [
     oracle_pins.pin_silu,
     oracle_pins.pin_sessions_independent,
     oracle_pins.pin_fp8,
+    oracle_pins.pin_int8,
     lambda mod: oracle_pins.pin_bf16(mod, n_random=1 << 14),
 ]
 

@@ -30,6 +30,9 @@ from .gen import (
     Fp8Matrix,
     quantize_rows_e4m3,
     E4M3_MAX,
+    Int8Matrix,
+    quantize_rows_int8,
+    INT8_MAX,
 )
 
 __all__ = [
@@ -50,4 +53,7 @@ __all__ = [
     "Fp8Matrix",
     "quantize_rows_e4m3",
     "E4M3_MAX",
+    "Int8Matrix",
+    "quantize_rows_int8",
+    "INT8_MAX",
 ]

@@ -17,6 +17,9 @@ Recipe (stated once, used by every consumer):
   magnitude divided by 448 (the largest finite E4M3 value), and its codes are
   the OCP FP8 E4M3 values nearest to weight / scale (torch's float8_e4m3fn
   conversion).  The embedding and the norm gains stay bf16.
+* int8 workloads quantise the same bf16 weights row by row to int8: a row's
+  scale is its largest magnitude divided by 127, and its codes are weight /
+  scale (in float32) rounded to nearest, ties to even, within -127..127.
 * Pre-filled KV values: for layer l, slot s (0 = K after RoPE, 1 = V), session
   b and kv head g, an array [prefill_len, head_dim] of N(0,1) float32 draws
   from SeedSequence([kv_seed, l, s, b, g]), rounded to bf16 for bf16 caches.
@@ -85,6 +88,44 @@ def quantize_rows_e4m3(w: np.ndarray) -> Fp8Matrix:
     return Fp8Matrix(codes, scale)
 
 
+INT8_MAX = 127  # largest int8 code a row scale maps to (codes stay symmetric: -127..127)
+
+
+@dataclass(frozen=True)
+class Int8Matrix:
+    """A matrix stored as int8 codes with one float32 scale per row.
+
+    The value of element (r, c) is codes[r, c] * scale[r]."""
+
+    codes: np.ndarray  # int8 [rows, cols]
+    scale: np.ndarray  # float32 [rows]
+
+    @property
+    def shape(self) -> tuple:
+        return self.codes.shape
+
+    @property
+    def size(self) -> int:
+        return self.codes.size
+
+    @property
+    def nbytes(self) -> int:
+        return self.codes.nbytes + self.scale.nbytes
+
+
+def quantize_rows_int8(w: np.ndarray) -> Int8Matrix:
+    """Per-row absmax quantisation of a float32 matrix to int8 codes and float32 scales: scale =
+    max |row| / 127 (1 for an all-zero row), code = w / scale (float32) rounded to nearest, ties to
+    even, clipped to -127..127."""
+    import torch  # the same float32 arithmetic as numpy's, on all host threads
+
+    t = torch.from_numpy(np.ascontiguousarray(w, np.float32))
+    amax = t.abs().amax(dim=1)
+    scale = torch.where(amax > 0, amax / float(INT8_MAX), torch.ones_like(amax))
+    codes = torch.round(t / scale[:, None]).clamp_(-INT8_MAX, INT8_MAX).to(torch.int8)  # ties to even
+    return Int8Matrix(codes.numpy().copy(), scale.numpy().copy())
+
+
 def _workers() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -118,11 +159,13 @@ def make_weights(shape: ModelShape, seed: int = 0, workers: int | None = None) -
     Returns a dict: ``embed`` [V, d], ``layers`` (list of dicts with the nine
     per-layer tensors), ``final_norm`` [d], ``lm_head`` [V, d] and ``dtype``.
     bf16 tensors are uint16 bit patterns; f32 tensors are float32. For fp8
-    models the seven matrices of each layer and the LM head are ``Fp8Matrix``
-    objects, and the embedding and gains are bf16.
+    (int8) models the seven matrices of each layer and the LM head are
+    ``Fp8Matrix`` (``Int8Matrix``) objects, quantised from the bf16 model's
+    weights, and the embedding and gains are bf16.
     """
     fp8 = shape.weight_dtype == "fp8"
-    as_bf16 = shape.weight_dtype in ("bf16", "fp8")
+    int8 = shape.weight_dtype == "int8"
+    as_bf16 = shape.weight_dtype in ("bf16", "fp8", "int8")
     store = np.uint16 if as_bf16 else np.float32
     one = bf16_bits_from_f32(np.ones(1, np.float32))[0] if as_bf16 else np.float32(1.0)
     w = {"dtype": shape.weight_dtype, "layers": []}
@@ -132,6 +175,8 @@ def make_weights(shape: ModelShape, seed: int = 0, workers: int | None = None) -
             _fill_matrix(arr, seed, index, as_bf16, pool)
             if fp8 and quantise:
                 return quantize_rows_e4m3(f32_from_bf16_bits(arr))
+            if int8 and quantise:
+                return quantize_rows_int8(f32_from_bf16_bits(arr))
             return arr
 
         def gain(name: str) -> np.ndarray:

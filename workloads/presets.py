@@ -1,6 +1,6 @@
 """Model shapes and workload presets.
 
-The five presets are the decode workloads this library is measured on:
+The presets are the decode workloads this library is measured on:
 
 * ``tiny``    -- 2 layers, d_model 256, 4 heads x 64 (MHA), SwiGLU 1024,
                  vocab 1024, fp32 weights; 32-token prompt, 64 greedy tokens.
@@ -22,6 +22,10 @@ The five presets are the decode workloads this library is measured on:
                  row; embedding, norm gains and KV cache stay bf16 ("17k
                  tokens/sec" page, best practice 2 and FAQ 3: lower-precision
                  parameters cut the bytes each token reads).
+* ``2b_int8``, ``8b_int8`` -- the same with int8 codes: one float32 scale per
+                 output row (its largest magnitude over 127), codes rounded to
+                 nearest, ties to even (best practice 2 of the same page names
+                 INT8).
 * ``11b_x56`` -- 40 layers, d_model 4096, 32 q / 8 kv heads, SwiGLU 16384,
                  vocab 128256, bf16; 56 sessions stepped in lockstep, each with
                  its own KV cache pre-filled to 4096 positions; 200 ticks
@@ -66,7 +70,7 @@ class ModelShape:
     vocab: int
     rope_base: float = 10000.0
     norm_eps: float = 1e-5
-    weight_dtype: str = "bf16"  # "bf16", "f32" or "fp8" (E4M3 projection matrices, bf16 embedding and gains)
+    weight_dtype: str = "bf16"  # "bf16", "f32", "fp8" or "int8" (E4M3 or int8 projection matrices, bf16 embedding and gains)
     kv_dtype: str = "bf16"  # "bf16" or "f32"
 
     @property
@@ -84,16 +88,21 @@ class ModelShape:
     @property
     def weight_bytes(self) -> int:
         """Bytes of one element of a projection matrix (or of any weight, for bf16 and f32)."""
-        return {"bf16": 2, "f32": 4, "fp8": 1}[self.weight_dtype]
+        return {"bf16": 2, "f32": 4, "fp8": 1, "int8": 1}[self.weight_dtype]
+
+    @property
+    def quantised(self) -> bool:
+        """Projection matrices and LM head as one-byte codes with a float32 scale per row."""
+        return self.weight_dtype in ("fp8", "int8")
 
     @property
     def embed_bytes(self) -> int:
-        """Bytes of one element of the embedding and the norm gains (bf16 for fp8 models)."""
+        """Bytes of one element of the embedding and the norm gains (bf16 for fp8 and int8 models)."""
         return 4 if self.weight_dtype == "f32" else 2
 
     @property
     def matrix_rows_per_layer(self) -> int:
-        """Output rows of a layer's seven matrices (one fp8 scale each)."""
+        """Output rows of a layer's seven matrices (one scale each in fp8 and int8 models)."""
         return self.q_dim + 2 * self.kv_dim + self.d_model + 2 * self.ffn_dim + self.d_model
 
     @property
@@ -127,10 +136,10 @@ class ModelShape:
     def streamed_weight_bytes(self) -> int:
         """Bytes of everything a step reads once: every layer, the final norm and the LM head.
 
-        fp8 models store each projection matrix as one byte per element plus one float32 scale
-        per output row, and their norm gains in bf16."""
+        fp8 and int8 models store each projection matrix as one byte per element plus one float32
+        scale per output row, and their norm gains in bf16."""
         d, V, L = self.d_model, self.vocab, self.n_layers
-        if self.weight_dtype != "fp8":
+        if not self.quantised:
             return (L * self.layer_params() + d + V * d) * self.weight_bytes
         matrices = L * (self.layer_params() - 2 * d) + V * d
         scales = 4 * (L * self.matrix_rows_per_layer + V)
@@ -182,6 +191,8 @@ _8B = ModelShape(32, 4096, 32, 8, 128, 14336, 128256, rope_base=500000.0)
 _11B = ModelShape(40, 4096, 32, 8, 128, 16384, 128256, rope_base=500000.0)
 _2B_FP8 = replace(_2B, weight_dtype="fp8")
 _8B_FP8 = replace(_8B, weight_dtype="fp8")
+_2B_INT8 = replace(_2B, weight_dtype="int8")
+_8B_INT8 = replace(_8B, weight_dtype="int8")
 
 PRESETS = {
     "tiny": Workload("tiny", _TINY, batch=1, prompt_len=32, gen_tokens=64,
@@ -198,6 +209,10 @@ PRESETS = {
                        description="2B decoder, batch 1, E4M3 weights with per-row scales"),
     "8b_fp8": Workload("8b_fp8", _8B_FP8, batch=1, prompt_len=1024, gen_tokens=256,
                        description="Llama-3-8B-shaped decoder, batch 1, E4M3 weights with per-row scales"),
+    "2b_int8": Workload("2b_int8", _2B_INT8, batch=1, prompt_len=512, gen_tokens=512,
+                        description="2B decoder, batch 1, int8 weights with per-row scales"),
+    "8b_int8": Workload("8b_int8", _8B_INT8, batch=1, prompt_len=1024, gen_tokens=256,
+                        description="Llama-3-8B-shaped decoder, batch 1, int8 weights with per-row scales"),
 }
 
 
