@@ -32,13 +32,16 @@ namespace bt {
 
 constexpr int kM = 64;             // sessions padded to four 16-row MFMA tiles
 constexpr int kMPrefill = 128;     // prefill positions per pass: eight 16-row tiles
-// A GEMM workgroup covers 128 output columns. With 64 activation rows (session ticks) it is 8
-// waves of one 16-column weight block each, and two workgroups share a CU, so one's start-up and
-// barrier waits overlap the other's streaming (measured: the 11B tick 1% shorter than with 4 waves
-// of two blocks). With 128 rows (prefill) it is 4 waves of two blocks, so that every activation
-// fragment a wave reads from LDS feeds two products (8 waves made the 8B prefill 15% slower).
+// A GEMM workgroup covers 128 output columns with 8 waves. With 64 activation rows (session
+// ticks) each wave owns one 16-column weight block, and two workgroups share a CU, so one's
+// start-up and barrier waits overlap the other's streaming (measured: the 11B tick 1% shorter than
+// with 4 waves of two blocks). With 128 rows (prefill) each wave owns two blocks, so that every
+// activation fragment it reads from LDS feeds two products (one block per wave made the 8B prefill
+// 15% slower), and the waves split each 128-K chunk in two halves: waves w and w + 4 take the same
+// blocks over K 0-63 and 64-127 of every chunk, and their sums are added once at the end. The
+// prefill tile's 139 KB of LDS leaves one workgroup per CU, so this gives every SIMD two waves.
 constexpr int kNB = 128;           // GEMM output columns per workgroup
-__host__ __device__ constexpr int gemm_waves(int mt) { return mt == 4 ? 8 : 4; }
+__host__ __device__ constexpr int gemm_waves(int) { return 8; }
 __host__ __device__ constexpr int gemm_threads(int mt) { return 64 * gemm_waves(mt); }
 constexpr int kKC = 128;           // K per LDS chunk of the activation block
 constexpr int kAttThreads = 256;   // 4 waves; 16 lanes per KV position (hd = 128, bf16)
@@ -134,9 +137,10 @@ __global__ void tile_pack_kernel(const uint16_t* __restrict__ src, uint16_t* __r
 // ---------------------------------------------------------------------------------------------
 // Grid: (N / kNB) * KS workgroups of gemm_waves(MT) waves; unit u covers columns [kNB (u / KS), + kNB)
 // and K range u % KS, in chunks of 128 K. Wave w owns JW = 1 or 2 16-row tiles of W (16 JW output
-// columns), so every activation fragment it reads from LDS feeds JW products. Per chunk a lane loads
-// four 1 KB tiles of each of its row blocks (W in the tile layout above), straight into registers
-// in the B-operand layout.
+// columns), so every activation fragment it reads from LDS feeds JW products, and KH = 1 or 2
+// parts of each chunk's four 32-K steps (KH = 2: waves w and w + 4 share blocks, one K half each).
+// Per chunk a lane loads the 1 KB tiles of its K part of each of its row blocks (W in the tile
+// layout above), straight into registers in the B-operand layout.
 //
 // The weights (HBM) and the activation block (64 rows x 128 K, hi and lo; it stays in L2) are
 // loaded into registers kPF chunks ahead, in the same order, so a wait for one never holds up
@@ -170,8 +174,10 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
   const int k0 = s * (NCH * kKC);
   const int tid = (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q = lane >> 4;
-  constexpr int kThr = gemm_threads(MT), JW = kNB / 16 / gemm_waves(MT);
-  const int rb0 = nb * (kNB / 16) + JW * wave;  // this wave's JW 16-row blocks
+  constexpr int kThr = gemm_threads(MT), KH = MT == 8 ? 2 : 1, JW = kNB / 16 / (gemm_waves(MT) / KH);
+  constexpr int NT = 4 / KH;  // 32-K steps of a chunk per wave
+  const int kh = KH == 1 ? 0 : wave / (gemm_waves(MT) / KH);  // this wave's K part of every chunk
+  const int rb0 = nb * (kNB / 16) + JW * (KH == 1 ? wave : wave % (gemm_waves(MT) / KH));  // its JW 16-row blocks
   const u32x4* wt[JW];
 #pragma unroll
   for (int j = 0; j < JW; ++j) wt[j] = (const u32x4*)W + ((size_t)(rb0 + j) * (K / 32) + k0 / 32) * 64 + lane;
@@ -182,7 +188,7 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
   // scratch memory when it sits in an array)
   struct Slot {
     u32x4 a[kAPer];
-    u32x4 w[JW][4];
+    u32x4 w[JW][NT];
   };
   auto load_chunk = [&](int c, Slot& sl) __attribute__((always_inline)) {
 #pragma unroll
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
 #pragma unroll
     for (int j = 0; j < JW; ++j)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) sl.w[j][t] = __builtin_nontemporal_load(wt[j] + (size_t)(c * 4 + t) * 64);
+      for (int t = 0; t < NT; ++t) sl.w[j][t] = __builtin_nontemporal_load(wt[j] + (size_t)(c * 4 + kh * NT + t) * 64);
   };
 
   f32x4 acc[JW][MT];
@@ -214,13 +220,14 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
     }
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NT; ++t) {
+      const int tk = kh * NT + t;  // 32-K step of the chunk
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        // lane l supplies K = 32 t + 8 (l / 16) .. + 8 of row 16 mt + l % 16: piece 4 t + l / 16
+        // lane l supplies K = 32 tk + 8 (l / 16) .. + 8 of row 16 mt + l % 16: piece 4 tk + l / 16
         const int r = mt * 16 + (lane & 15);
-        const bf16x8 ah = __builtin_bit_cast(bf16x8, As[buf][0][r][t * 4 + q]);
-        const bf16x8 al = __builtin_bit_cast(bf16x8, As[buf][1][r][t * 4 + q]);
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, As[buf][0][r][tk * 4 + q]);
+        const bf16x8 al = __builtin_bit_cast(bf16x8, As[buf][1][r][tk * 4 + q]);
 #pragma unroll
         for (int j = 0; j < JW; ++j) {
           const bf16x8 bw = __builtin_bit_cast(bf16x8, sl.w[j][t]);
@@ -236,6 +243,32 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
   for (int c = 0; c < kPF && c < NCH; ++c) load_chunk(c, ring[c]);
 #pragma unroll
   for (int c = 0; c < NCH; ++c) step(c, ring[c % kPF]);
+  const int cw = 16 * (rb0 - nb * (kNB / 16));  // this wave's first column within the workgroup
+  if constexpr (KH == 2) {
+    // the second K half's sums through LDS (As is free once every wave is past its last chunk),
+    // added to the first half's; the waves of the second half then write nothing
+    constexpr int LDR = kNB + 1;
+    static_assert(sizeof(As) >= sizeof(float) * kRows * LDR, "the K-half staging must fit in the activation tile");
+    float* Rs = reinterpret_cast<float*>(&As[0][0][0][0]);
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+      for (int j = 0; j < JW; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Rs[(mt * 16 + q * 4 + i) * LDR + cw + 16 * j + (lane & 15)] = acc[j][mt][i];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int j = 0; j < JW; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[j][mt][i] += Rs[(mt * 16 + q * 4 + i) * LDR + cw + 16 * j + (lane & 15)];
+    }
+  }
   if constexpr (SILU) {
     // the workgroup's 128 rows x B sessions through LDS (As is free once every wave is past its
     // last chunk), then SiLU(gate) * up for 64 columns
@@ -244,12 +277,14 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
     static_assert(kNB % 64 == 0, "a workgroup's rows must be whole [32 gate; 32 up] groups");
     float* Cs = reinterpret_cast<float*>(&As[0][0][0][0]);
     __syncthreads();
+    if (kh == 0) {
 #pragma unroll
-    for (int j = 0; j < JW; ++j)
+      for (int j = 0; j < JW; ++j)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Cs[(mt * 16 + q * 4 + i) * LDC + 16 * JW * wave + 16 * j + (lane & 15)] = acc[j][mt][i];
+          for (int i = 0; i < 4; ++i) Cs[(mt * 16 + q * 4 + i) * LDC + cw + 16 * j + (lane & 15)] = acc[j][mt][i];
+    }
     __syncthreads();
     for (int e = tid; e < B * (kNB / 2); e += kThr) {
       const int m = e / (kNB / 2), c = e - m * (kNB / 2), grp = c / 32, ci = c - 32 * grp;
@@ -262,6 +297,7 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
     return;
   }
   // lane l holds rows 16 mt + 4 (l / 16) + i of column 16 (rb0 + j) + l % 16
+  if (kh != 0) return;
 #pragma unroll
   for (int j = 0; j < JW; ++j) {
     const int n = (rb0 + j) * 16 + (lane & 15);
