@@ -70,6 +70,19 @@ def test_struct_layout_matches_binding():
             assert getattr(cls, field).offset == want[(name, field)], (name, field)
 
 
+def test_header_constants_match_binding():
+    """Every numeric KD_* constant of kd.h that the binding defines has the header's value, and the
+    binding defines every number format and status code."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    consts = {n: int(v.rstrip("uU"), 0) for n, v in re.findall(r"#define\s+(KD_[A-Z0-9_]+)\s+\(?(-?(?:0x[0-9a-fA-F]+|\d+)[uU]?)\)?", text)}
+    assert {"KD_DTYPE_F32", "KD_DTYPE_BF16", "KD_DTYPE_FP8_E4M3", "KD_DTYPE_INT8"} <= set(consts)
+    for name, value in consts.items():
+        if name.startswith(("KD_DTYPE_", "KD_STATUS_", "KD_ERR_")) or name == "KD_OK":
+            assert hasattr(kd, name), name
+        if hasattr(kd, name):
+            assert getattr(kd, name) == value, (name, getattr(kd, name), value)
+
+
 def test_strerror_covers_every_code():
     for code in range(-7, 1):
         assert kd.kd_strerror(code) and "unknown" not in kd.kd_strerror(code)

@@ -121,6 +121,16 @@ def test_generate_equals_steps_2b(torch, kdm):
     _generate_vs_steps(torch, kdm, wl, w, 128, 64, "2b")
 
 
+@pytest.mark.parametrize("name", ["2b_fp8", "2b_int8"])
+def test_generate_equals_steps_one_byte_weights(torch, kdm, name):
+    """The resident loop of the one-byte kernels (E4M3 and int8 codes with row scales): 48 steps
+    after a 128-token prompt, bitwise equal to 48 kd_step calls."""
+    wl = workloads.get(name)
+    w = workloads.make_weights(wl.model, seed=wl.weight_seed)
+    print(f"{name} generate: weights ready", flush=True)
+    _generate_vs_steps(torch, kdm, wl, w, 128, 48, name)
+
+
 def test_generate_stops_at_cache_end(torch, kdm, tiny):
     """Asking for more steps than the cache holds runs the steps that fit, then stops with
     KD_STATUS_POS_OVERFLOW."""
