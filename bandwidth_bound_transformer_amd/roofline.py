@@ -76,6 +76,21 @@ def step_flops(shape, batch: int, position: int) -> int:
     return batch * (per_token + attn)
 
 
+MI355X_BF16_DENSE_FLOPS = 2.5e15  # matrix cores, dense bf16
+
+
+def prefill_flops(shape, prompt_len: int) -> int:
+    """Multiply-add work (2 flops each) of running a prompt of ``prompt_len`` positions from an
+    empty cache to its first token: every projection for every position, attention of position p
+    over 0..p (scores and weighted sums), and the LM head for the last position only."""
+    d, L = shape.d_model, shape.n_layers
+    matrix_params = shape.layer_params() - 2 * d  # the seven matrices of a layer
+    proj = 2 * prompt_len * L * matrix_params
+    attended = prompt_len * (prompt_len + 1) // 2  # sum over p of (p + 1)
+    attn = 2 * 2 * L * shape.n_q_heads * shape.head_dim * attended
+    return proj + attn + 2 * shape.vocab * d
+
+
 def tokens_per_s_bound(bandwidth_bytes_per_s: float, bytes_per_step: float, batch: int = 1) -> float:
     """Roofline tokens/s: ``batch`` tokens per step, each step limited by streaming its bytes."""
     return batch * bandwidth_bytes_per_s / bytes_per_step

@@ -173,6 +173,13 @@ def measure(wl, args, torch, kd, roofline, steps: int, warmup: int, trace: bool,
                 "chunk_positions": chunk,
                 "stepwise_prompt_ms": round(stepwise_ms, 2),
                 "same_first_token_as_stepwise": int(dec.tokens[0].item()) == first_stepwise,
+                # the whole prefill against the matrix cores' dense bf16 peak (algorithmic flops:
+                # every projection per position, causal attention, the last position's LM head)
+                "roofline": {"bound": "mfma", "unit": "TFLOP/s",
+                             "achieved": round(roofline.prefill_flops(m, wl.prompt_len) / (runs[-1] * 1e-3) / 1e12, 1),
+                             "peak": roofline.MI355X_BF16_DENSE_FLOPS / 1e12,
+                             "frac": round(roofline.prefill_flops(m, wl.prompt_len) / (runs[-1] * 1e-3)
+                                           / roofline.MI355X_BF16_DENSE_FLOPS, 4)},
                 "what": "kd_prefill of the whole prompt (prompt tokens in HBM) to the first greedy token",
             }
             log(f"{wl.name}: time to first token via kd_prefill: {runs} ms")

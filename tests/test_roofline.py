@@ -43,3 +43,21 @@ def test_decode_positions():
     assert roofline.decode_positions(workloads.get("2b")) == range(512, 1023)
     assert roofline.decode_positions(workloads.get("2b_long")) == range(32768, 32896)
     assert roofline.decode_positions(workloads.get("11b_x56")) == range(4096, 4296)
+
+
+def test_prefill_flops_counts_each_product_once():
+    """prefill_flops against a count made position by position for a small shape: the seven
+    matrices of every layer times each position, q.k and p.v over 0..p for each q head, and the LM
+    head once."""
+    from bandwidth_bound_transformer_amd import roofline
+    from workloads import ModelShape
+
+    m = ModelShape(3, 64, 4, 2, 16, 96, 50)
+    P = 7
+    count = 0
+    for p in range(P):
+        for _ in range(m.n_layers):
+            count += 2 * (m.q_dim * m.d_model + 2 * m.kv_dim * m.d_model + m.d_model * m.q_dim + 3 * m.ffn_dim * m.d_model)
+            count += m.n_q_heads * (p + 1) * m.head_dim * 2 * 2  # scores and weighted sums
+    count += 2 * m.vocab * m.d_model
+    assert roofline.prefill_flops(m, P) == count
