@@ -171,7 +171,7 @@ int check_supported(const kd_config* c, const kd::Dims& m) {
   if (c->prefill_chunk > 0) {  // the lockstep kernels must take the shape
     kd_config pc = *c;
     pc.batch = c->prefill_chunk;
-    const int rc = kd::bt::batch_check(&pc, kd::bt::kMPrefill);
+    const int rc = kd::bt::batch_check(&pc, kd::bt::kMPrefill, true);
     if (rc != KD_OK) return rc;
   }
   if (c->head_dim != 64 && c->head_dim != 128) return KD_ERR_UNSUPPORTED;

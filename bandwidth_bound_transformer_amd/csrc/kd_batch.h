@@ -114,6 +114,24 @@ __global__ void check_kernel(const int32_t* tokens, const int32_t* positions, in
 }
 
 // ---------------------------------------------------------------------------------------------
+// one-byte weights (E4M3 or int8 codes with a float32 scale per row) decoded to bf16
+// ---------------------------------------------------------------------------------------------
+// The prefill engine of an fp8 or int8 model computes with the weights the codes stand for, code
+// times its row's scale, rounded to bf16 once here (the pass is bound by the matrix cores, not by
+// the weight bytes). Row r of codes[rows][cols] goes to row (r / bin) * bout + boff + r % bin of
+// dst (bin = bout = rows, boff = 0 keeps the order; the gate/up interleave uses bin 32, bout 64).
+// Grid: one thread per code.
+__global__ void dequant_rows_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale, int rows,
+                                    int cols, int int8, int bin, int bout, int boff, uint16_t* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)rows * cols) return;
+  const int64_t r = i / cols, c = i - r * cols;
+  const uint32_t code = codes[i];
+  const float v = int8 ? (float)(int8_t)code : __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+  dst[((r / bin) * bout + boff + r % bin) * (int64_t)cols + c] = f_to_bf16(v * scale[r]);
+}
+
+// ---------------------------------------------------------------------------------------------
 // weight tiles: the layout the GEMM streams
 // ---------------------------------------------------------------------------------------------
 // A weight matrix W[N][K] is stored as tiles of 16 rows x 32 K (1 KB), tile (r, t) at index

@@ -123,10 +123,12 @@ inline PrefillAttFn prefill_att_for(int G) {
   }
 }
 
-// max_rows: kM for session handles, kMPrefill for the prefill engine
-inline int batch_check(const kd_config* c, int max_rows = kM) {
+// max_rows: kM for session handles, kMPrefill for the prefill engine. The prefill engine also takes
+// fp8 and int8 models: it keeps its own copy of the weights, decoded to bf16.
+inline int batch_check(const kd_config* c, int max_rows = kM, bool prefill = false) {
   if (c->batch < 2 || c->batch > max_rows) return KD_ERR_UNSUPPORTED;
-  if (c->weight_dtype != KD_DTYPE_BF16 || c->kv_dtype != KD_DTYPE_BF16) return KD_ERR_UNSUPPORTED;
+  const bool q8 = c->weight_dtype == KD_DTYPE_FP8_E4M3 || c->weight_dtype == KD_DTYPE_INT8;
+  if ((c->weight_dtype != KD_DTYPE_BF16 && !(prefill && q8)) || c->kv_dtype != KD_DTYPE_BF16) return KD_ERR_UNSUPPORTED;
   if (c->head_dim != 128) return KD_ERR_UNSUPPORTED;
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return KD_ERR_UNSUPPORTED;
@@ -223,12 +225,22 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, bool ses
   KD_BT_TRY(hipMemset(st.A2lo, 0, rows * st.lda * 2));
 
   // Every matrix goes row-major into a staging buffer, then tile_pack_kernel writes it into the
-  // blob in the tile layout the GEMM streams.
+  // blob in the tile layout the GEMM streams. fp8 and int8 matrices (the prefill engine of such a
+  // model) first land as codes and row scales, and dequant_rows_kernel writes code x scale into
+  // the staging buffer as bf16.
+  const bool q8 = c->weight_dtype != KD_DTYPE_BF16;
+  const int int8 = c->weight_dtype == KD_DTYPE_INT8;
   const size_t row = d * 2;
   uint16_t* stage = nullptr;
+  uint8_t* qcodes = nullptr;
+  float* qscale = nullptr;
   {
     size_t most = std::max({(size_t)st.nqkv * d, d * st.qdim, 2 * (size_t)st.F * d, (size_t)st.V * d});
-    if (hipMalloc(&stage, most * 2) != hipSuccess) {
+    size_t most_rows = std::max({(size_t)st.nqkv, d, (size_t)st.F, (size_t)st.V});
+    if (hipMalloc(&stage, most * 2) != hipSuccess ||
+        (q8 && (hipMalloc(&qcodes, most) != hipSuccess || hipMalloc(&qscale, most_rows * 4) != hipSuccess))) {
+      if (stage) (void)hipFree(stage);
+      if (qcodes) (void)hipFree(qcodes);
       batch_free(st);
       return KD_ERR_OOM;
     }
@@ -237,10 +249,24 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, bool ses
   do {                          \
     if ((expr) != hipSuccess) { \
       (void)hipFree(stage);     \
+      if (qcodes) (void)hipFree(qcodes); \
+      if (qscale) (void)hipFree(qscale); \
       batch_free(st);           \
       return KD_ERR_HIP;        \
     }                           \
   } while (0)
+  // codes[rows][cols] and their row scales (host) -> bf16 rows of dst, row r at
+  // (r / bin) * bout + boff + r % bin (the gate/up interleave; bin = rows keeps the order)
+  auto put_q8 = [&](uint16_t* dst, const void* codes, const float* scales, int rows, int cols, int bin, int bout,
+                    int boff) {
+    hipError_t e = hipMemcpy(qcodes, codes, (size_t)rows * cols, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(qscale, scales, (size_t)rows * 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)rows * cols;
+    hipLaunchKernelGGL(dequant_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, 0, (const uint8_t*)qcodes,
+                       (const float*)qscale, rows, cols, int8, bin, bout, boff, dst);
+    return hipGetLastError();
+  };
   auto pack = [&](uint16_t* dst, int N, int K) {
     const int64_t pieces = (int64_t)N * K / 8;
     hipLaunchKernelGGL(tile_pack_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, 0, (const uint16_t*)stage,
@@ -250,27 +276,49 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, bool ses
   for (int l = 0; l < st.L; ++l) {
     const kd_layer_weights& lw = w->layers[l];
     uint16_t* lay = st.w + (size_t)l * st.layer_elems;
-    KD_BT_STAGE_TRY(hipMemcpy(stage, lw.wq, (size_t)st.qdim * row, hipMemcpyHostToDevice));
-    KD_BT_STAGE_TRY(hipMemcpy(stage + (size_t)st.qdim * d, lw.wk, (size_t)st.hkv * st.hd * row, hipMemcpyHostToDevice));
-    KD_BT_STAGE_TRY(hipMemcpy(stage + (size_t)(st.qdim + st.hkv * st.hd) * d, lw.wv, (size_t)st.hkv * st.hd * row,
-                              hipMemcpyHostToDevice));
+    const int kvdim = st.hkv * st.hd;
+    if (q8) {
+      KD_BT_STAGE_TRY(put_q8(stage, lw.wq, lw.s_wq, st.qdim, st.d, st.qdim, st.qdim, 0));
+      KD_BT_STAGE_TRY(put_q8(stage + (size_t)st.qdim * d, lw.wk, lw.s_wk, kvdim, st.d, kvdim, kvdim, 0));
+      KD_BT_STAGE_TRY(put_q8(stage + (size_t)(st.qdim + kvdim) * d, lw.wv, lw.s_wv, kvdim, st.d, kvdim, kvdim, 0));
+    } else {
+      KD_BT_STAGE_TRY(hipMemcpy(stage, lw.wq, (size_t)st.qdim * row, hipMemcpyHostToDevice));
+      KD_BT_STAGE_TRY(hipMemcpy(stage + (size_t)st.qdim * d, lw.wk, (size_t)kvdim * row, hipMemcpyHostToDevice));
+      KD_BT_STAGE_TRY(hipMemcpy(stage + (size_t)(st.qdim + kvdim) * d, lw.wv, (size_t)kvdim * row, hipMemcpyHostToDevice));
+    }
     KD_BT_STAGE_TRY(pack(lay + st.w_qkv, st.nqkv, st.d));
-    KD_BT_STAGE_TRY(hipMemcpy(stage, lw.wo, d * st.qdim * 2, hipMemcpyHostToDevice));
+    if (q8)
+      KD_BT_STAGE_TRY(put_q8(stage, lw.wo, lw.s_wo, st.d, st.qdim, st.d, st.d, 0));
+    else
+      KD_BT_STAGE_TRY(hipMemcpy(stage, lw.wo, d * st.qdim * 2, hipMemcpyHostToDevice));
     KD_BT_STAGE_TRY(pack(lay + st.w_o, st.d, st.qdim));
     // gate/up interleaved in blocks of 32 rows: rows [64j, 64j+32) = gate rows [32j, 32j+32),
     // rows [64j+32, 64j+64) = the matching up rows, so every GEMM tile holds whole pairs
-    KD_BT_STAGE_TRY(hipMemcpy2D(stage, 64 * row, lw.w_gate, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
-    KD_BT_STAGE_TRY(hipMemcpy2D(stage + 32 * d, 64 * row, lw.w_up, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
+    if (q8) {
+      KD_BT_STAGE_TRY(put_q8(stage, lw.w_gate, lw.s_gate, st.F, st.d, 32, 64, 0));
+      KD_BT_STAGE_TRY(put_q8(stage, lw.w_up, lw.s_up, st.F, st.d, 32, 64, 32));
+    } else {
+      KD_BT_STAGE_TRY(hipMemcpy2D(stage, 64 * row, lw.w_gate, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
+      KD_BT_STAGE_TRY(hipMemcpy2D(stage + 32 * d, 64 * row, lw.w_up, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
+    }
     KD_BT_STAGE_TRY(pack(lay + st.w_gu, 2 * st.F, st.d));
-    KD_BT_STAGE_TRY(hipMemcpy(stage, lw.w_down, d * st.F * 2, hipMemcpyHostToDevice));
+    if (q8)
+      KD_BT_STAGE_TRY(put_q8(stage, lw.w_down, lw.s_down, st.d, st.F, st.d, st.d, 0));
+    else
+      KD_BT_STAGE_TRY(hipMemcpy(stage, lw.w_down, d * st.F * 2, hipMemcpyHostToDevice));
     KD_BT_STAGE_TRY(pack(lay + st.w_d, st.d, st.F));
     KD_BT_STAGE_TRY(hipMemcpy(st.norms + (size_t)(2 * l) * d, lw.attn_norm, row, hipMemcpyHostToDevice));
     KD_BT_STAGE_TRY(hipMemcpy(st.norms + (size_t)(2 * l + 1) * d, lw.ffn_norm, row, hipMemcpyHostToDevice));
   }
-  KD_BT_STAGE_TRY(hipMemcpy(stage, w->lm_head, (size_t)st.V * row, hipMemcpyHostToDevice));
+  if (q8)
+    KD_BT_STAGE_TRY(put_q8(stage, w->lm_head, w->s_lm_head, st.V, st.d, st.V, st.V, 0));
+  else
+    KD_BT_STAGE_TRY(hipMemcpy(stage, w->lm_head, (size_t)st.V * row, hipMemcpyHostToDevice));
   KD_BT_STAGE_TRY(pack(st.w + st.w_lm, st.V, st.d));
 #undef KD_BT_STAGE_TRY
   (void)hipFree(stage);
+  if (qcodes) (void)hipFree(qcodes);
+  if (qscale) (void)hipFree(qscale);
   KD_BT_TRY(hipMemcpy(st.norms + (size_t)(2 * st.L) * d, w->final_norm, row, hipMemcpyHostToDevice));
   KD_BT_TRY(hipMemcpy(st.embed, w->embed, (size_t)st.V * row, hipMemcpyHostToDevice));
   {

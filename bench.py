@@ -20,7 +20,7 @@ Printed on stdout, as one JSON line:
   cpu_baseline   the CPU oracle, run for a bounded number of decode steps on the host cores
   extra          the 2B batch-1 workload, and the 8B and 2B with FP8 and with int8 weights, measured the
                  same way in the same run (default run only)
-  ttft           bf16 prompts: time to the first token with kd_prefill (the prompt on the matrix
+  ttft           batch-1 prompts (bf16, fp8, int8): time to the first token with kd_prefill (the prompt on the matrix
                  cores), beside the time the same prompt takes one step per token
 Everything else goes to stderr.
 """
@@ -127,8 +127,8 @@ def measure(wl, args, torch, kd, roofline, steps: int, warmup: int, trace: bool,
     t0 = time.perf_counter()
     weights = workloads.make_weights(m, seed=wl.weight_seed)
     log(f"{wl.name}: weights generated in {time.perf_counter() - t0:.1f} s")
-    # bf16 batch-1 prompts also run through kd_prefill (the matrix cores, 128 positions a pass)
-    chunk = getattr(args, "prefill_chunk", 128) if (B == 1 and m.weight_dtype == "bf16" and wl.prompt_len > 0) else 0
+    # batch-1 prompts also run through kd_prefill (the matrix cores, 128 positions a pass)
+    chunk = getattr(args, "prefill_chunk", 128) if (B == 1 and m.weight_dtype in ("bf16", "fp8", "int8") and wl.prompt_len > 0) else 0
     dec = kd.Decoder(m, weights, max_seq=wl.max_seq, batch=B, device="cuda:0", prefill_chunk=chunk)
     info = kd.kd_get_info(dec.handle)
     log(f"{wl.name}: kd_init done: {info}")
@@ -316,7 +316,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="8b", choices=["tiny", "2b", "8b", "2b_long", "11b_x56", "2b_fp8", "8b_fp8", "2b_int8", "8b_int8"])
     ap.add_argument("--prefill-chunk", type=int, default=128,
-                    help="prompt positions per kd_prefill pass for bf16 batch-1 workloads (2..128)")
+                    help="prompt positions per kd_prefill pass for batch-1 workloads (2..128)")
     ap.add_argument("--extra", default=None,
                     help="comma-separated workloads measured after the headline one and reported under 'extra' "
                          "(default: 2b when the headline is the default 8b, else none; 'none' for none)")

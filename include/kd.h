@@ -101,8 +101,10 @@ extern "C" {
  *   rope_base    RoPE base: pair (i, i + head_dim/2) turns by position * rope_base^(-2i/head_dim).
  *   prefill_chunk batch 1 only: 0, or 2..128 to set up kd_prefill, which runs a prompt in chunks of
  *                this many positions as small-M GEMMs on the matrix cores (the shape must meet the
- *                lockstep path's conditions above; the library then holds a second copy of the
- *                weights, in the matrix cores' tile layout).
+ *                lockstep path's conditions above, except that fp8 and int8 weights are taken; the
+ *                library then holds a second copy of the weights, in bf16 in the matrix cores'
+ *                tile layout: for fp8 and int8 models each code times its row's scale, rounded to
+ *                bf16 once, so the prefill's results may differ from one-token steps by that rounding).
  *   weight_dtype KD_DTYPE_BF16 or KD_DTYPE_F32, with kv_dtype the same; or KD_DTYPE_FP8_E4M3 or
  *                KD_DTYPE_INT8 with kv_dtype KD_DTYPE_BF16 (batch 1, head_dim 128, d_model and q_dim multiples
  *                of 1024, ffn_dim a multiple of 8 with ffn_dim/8 >= the GPU's compute units).

@@ -120,6 +120,38 @@ def test_prefill_small_ragged_and_continued(torch, kdm, chunk, mha):
     step.close()
 
 
+@pytest.mark.parametrize("dtype", ["fp8", "int8"])
+def test_prefill_one_byte_weights(torch, kdm, dtype):
+    """An fp8 or int8 model: the prefill engine computes with its weights decoded to bf16 (code times
+    row scale, rounded once), the decode steps with the codes themselves. 100 prompt tokens in
+    passes of 64: the last position's logits against the oracle fed the same codes and scales, the
+    cache against one-token steps of the one-byte kernel, then a decode step from that cache."""
+    shape = ModelShape(2, 1024, 8, 2, 128, 2048, 4096, rope_base=10000.0, weight_dtype=dtype, kv_dtype="bf16")
+    w = workloads.make_weights(shape, seed=6)
+    prompt = np.random.default_rng(13).integers(0, shape.vocab, 100).astype(np.int32)
+    pre = kdm.Decoder(shape, w, max_seq=128, prefill_chunk=64)
+    step = kdm.Decoder(shape, w, max_seq=128)
+    p_d = torch.as_tensor(prompt, device=pre.device)
+    pre.positions.zero_()
+    pre.prefill(p_d)
+    torch.cuda.synchronize()
+    assert pre.status() == 0 and int(pre.positions.item()) == 100
+    want = ref.forward_full(shape, w, prompt)[-1]
+    err = gh.inf_rel_err(pre.logits[0].cpu().numpy(), want)
+    assert err <= TOL
+    assert int(pre.tokens.item()) == int(ref.greedy_token(want[None])[0]) or gh.top2_margin(want) <= 2 * err * np.max(np.abs(want))
+    _stepwise(step, prompt, torch)
+    _cache_close(pre.kv_view(), step.kv_view(), 100, f"{dtype} prefill, positions 0..99")
+    nxt = int(pre.tokens.item())
+    pre.step()
+    want2 = ref.forward_full(shape, w, list(prompt) + [nxt])[-1]
+    err2 = gh.inf_rel_err(pre.logits[0].cpu().numpy(), want2)
+    print(f"{dtype} prefill: last-position rel logit err {err:.3e}, next decode step {err2:.3e}")
+    assert err2 <= TOL and pre.status() == 0 and int(pre.positions.item()) == 101
+    pre.close()
+    step.close()
+
+
 def test_prefill_chunk_boundary_and_single_position(torch, kdm):
     """256 prompt tokens in two full passes of 128 (ending on a 256-position attention chunk), then one
     more token alone at position 256 (a pass of one row that opens the next chunk): logits against
@@ -234,7 +266,3 @@ def test_prefill_refusals(torch, kdm):
         with pytest.raises(kdm.KDError) as e:
             kdm.kd_init(kdm.make_config(SMALL, 1, 64, prefill_chunk=bad), w)
         assert e.value.code == kdm.KD_ERR_INVALID_ARG
-    fp8 = ModelShape(2, 1024, 8, 2, 128, 2048, 4096, weight_dtype="fp8", kv_dtype="bf16")
-    with pytest.raises(kdm.KDError) as e:
-        kdm.kd_init(kdm.make_config(fp8, 1, 64, prefill_chunk=64), workloads.make_weights(fp8, seed=1))
-    assert e.value.code == kdm.KD_ERR_UNSUPPORTED
