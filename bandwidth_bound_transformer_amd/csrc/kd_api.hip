@@ -171,7 +171,7 @@ int check_supported(const kd_config* c, const kd::Dims& m) {
   if (c->prefill_chunk > 0) {  // the lockstep kernels must take the shape
     kd_config pc = *c;
     pc.batch = c->prefill_chunk;
-    const int rc = kd::bt::batch_check(&pc, kd::bt::kMPrefill, true);
+    const int rc = kd::bt::batch_check(&pc, kd::bt::kMPrefill);
     if (rc != KD_OK) return rc;
   }
   if (c->head_dim != 64 && c->head_dim != 128) return KD_ERR_UNSUPPORTED;
@@ -675,7 +675,10 @@ int kd_get_info(kd_handle* h, int64_t info[8]) {
     const kd::bt::BatchState& b = h->bs;
     info[0] = 0;
     info[1] = kd::bt::gemm_threads(h->bs.MT);
-    info[2] = (int64_t)(b.w_lm + (size_t)b.V * b.d) * 2 + (int64_t)b.V * b.d * 2 + (int64_t)(2 * b.L + 1) * b.d * 2;
+    // packed weights (bf16 tiles, or one-byte tiles and their row scales), embedding, norm gains
+    info[2] = (b.q ? (int64_t)(b.w_lm + (size_t)b.V * b.d) + ((int64_t)b.L * (int64_t)b.srows + b.V) * 4
+                   : (int64_t)(b.w_lm + (size_t)b.V * b.d) * 2) +
+              (int64_t)b.V * b.d * 2 + (int64_t)(2 * b.L + 1) * b.d * 2;
     info[5] = kd::bt::batch_kernels_per_tick(b);
     info[6] = b.g_qkv.KS | (b.g_o.KS << 8) | (b.g_gu.KS << 16) | (b.g_d.KS << 24);
     info[7] = b.CH;

@@ -151,6 +151,53 @@ __global__ void tile_pack_kernel(const uint16_t* __restrict__ src, uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------------------------
+// one-byte weight tiles for the session GEMM
+// ---------------------------------------------------------------------------------------------
+// With fp8 or int8 weights a lane's 16 bytes hold two 32-K tiles: the first 8 codes are its part
+// of tile 2 p (W[16 r + l % 16][64 p + 8 (l / 16) .. + 8]), the last 8 its part of tile 2 p + 1
+// (the same 8 columns 32 further on), so a 64-lane load reads two tiles, 1 KB contiguous. Tile pair
+// (r, p) sits at index r * (K / 64) + p. Grid: one thread per 16-byte piece (N * K / 16).
+__global__ void tile_pack_q8_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int N, int K) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)N * K / 16) return;
+  const int lane = (int)(i & 63);
+  const int64_t pair = i >> 6, per_row_block = K / 64;
+  const int64_t rb = pair / per_row_block, p = pair - rb * per_row_block;
+  const int64_t row = rb * 16 + (lane & 15), k = p * 64 + (lane >> 4) * 8;
+  const uint2 a = *(const uint2*)(src + row * K + k), b = *(const uint2*)(src + row * K + k + 32);
+  ((u32x4*)dst)[i] = u32x4{a.x, a.y, b.x, b.y};
+}
+
+// Two bf16 values from bytes 2 H and 2 H + 1 of a word of one-byte codes (Q = 1: E4M3, 2: int8).
+// Both formats' values are bf16 values, so taking the top half of the float is exact.
+template <int Q, bool H>
+__device__ __forceinline__ uint32_t code_pair_bf16(uint32_t w) {
+  float f0, f1;
+  if constexpr (Q == 1) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, H);
+    f0 = f[0];
+    f1 = f[1];
+  } else {
+    f0 = (float)(int8_t)(w >> (H ? 16 : 0));
+    f1 = (float)(int8_t)(w >> (H ? 24 : 8));
+  }
+  return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+}
+// The B operand of one 32-K tile: bf16 weights as loaded (Q = 0), or tile `half` of a two-tile
+// load of one-byte codes, decoded.
+template <int Q>
+__device__ __forceinline__ bf16x8 weight_frag(u32x4 v, int half) {
+  if constexpr (Q == 0) {
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    const uint32_t w0 = half ? v.z : v.x, w1 = half ? v.w : v.y;
+    const u32x4 r = {code_pair_bf16<Q, false>(w0), code_pair_bf16<Q, true>(w0), code_pair_bf16<Q, false>(w1),
+                     code_pair_bf16<Q, true>(w1)};
+    return __builtin_bit_cast(bf16x8, r);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // small-M GEMM on MFMA: P[s][m][n] = sum over K-range s of (Ahi[m][k] + Alo[m][k]) * W[n][k]
 // ---------------------------------------------------------------------------------------------
 // Grid: (N / kNB) * KS workgroups of gemm_waves(MT) waves; unit u covers columns [kNB (u / KS), + kNB)
@@ -172,12 +219,15 @@ constexpr int kPF = 2;  // chunks in flight per wave
 // SiLU(gate) * up of its 64 FFN columns as the hi/lo activation block Ohi/Olo of the down
 // projection. Its 128 rows are two groups of [32 gate rows; the 32 up rows of the same columns].
 // MT: 16-row tiles of the activation block (4: up to 64 rows, the session ticks; 8: up to 128, prefill).
-template <int NCH, bool SILU, int MT>
+// Q: 0 bf16 weight tiles; 1 (E4M3) or 2 (int8) one-byte tiles (64 rows only), decoded to bf16 in
+// registers, each output column then times scale[n], its row's scale.
+template <int NCH, bool SILU, int MT, int Q>
 __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* __restrict__ W, int N, int K,
                                                                 const uint16_t* __restrict__ Ahi,
                                                                 const uint16_t* __restrict__ Alo, int lda,
                                                                 float* __restrict__ P, int KS, int B, const uint32_t* skip,
-                                                                uint16_t* __restrict__ Ohi, uint16_t* __restrict__ Olo) {
+                                                                uint16_t* __restrict__ Ohi, uint16_t* __restrict__ Olo,
+                                                                const float* __restrict__ scale) {
   if (*skip) return;
   // [buffer][hi, lo][row][16-byte piece of the 128-K chunk, padded against bank conflicts]. The pad
   // was measured: two pieces for 64 rows (the 11B tick 1.1% shorter than with one; 72 KB, still two
@@ -196,9 +246,13 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
   constexpr int NT = 4 / KH;  // 32-K steps of a chunk per wave
   const int kh = KH == 1 ? 0 : wave / (gemm_waves(MT) / KH);  // this wave's K part of every chunk
   const int rb0 = nb * (kNB / 16) + JW * (KH == 1 ? wave : wave % (gemm_waves(MT) / KH));  // its JW 16-row blocks
+  static_assert(Q == 0 || MT == 4, "one-byte weights for the 64-row tile only");
+  constexpr int TPL = Q ? 2 : 1;  // 32-K tiles per 16-byte lane load
+  constexpr int NWL = NT / TPL;   // weight loads per block per chunk
   const u32x4* wt[JW];
 #pragma unroll
-  for (int j = 0; j < JW; ++j) wt[j] = (const u32x4*)W + ((size_t)(rb0 + j) * (K / 32) + k0 / 32) * 64 + lane;
+  for (int j = 0; j < JW; ++j)
+    wt[j] = (const u32x4*)W + ((size_t)(rb0 + j) * (K / (32 * TPL)) + k0 / (32 * TPL)) * 64 + lane;
 
   // activation chunk: 2 x kRows rows x 16 pieces of 16 bytes, 4 (or 8) per thread
   constexpr int kAPer = 2 * kRows * (kKC / 8) / kThr;
@@ -206,7 +260,7 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
   // scratch memory when it sits in an array)
   struct Slot {
     u32x4 a[kAPer];
-    u32x4 w[JW][NT];
+    u32x4 w[JW][NWL];
   };
   auto load_chunk = [&](int c, Slot& sl) __attribute__((always_inline)) {
 #pragma unroll
@@ -219,7 +273,7 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
 #pragma unroll
     for (int j = 0; j < JW; ++j)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) sl.w[j][t] = __builtin_nontemporal_load(wt[j] + (size_t)(c * 4 + kh * NT + t) * 64);
+      for (int t = 0; t < NWL; ++t) sl.w[j][t] = __builtin_nontemporal_load(wt[j] + (size_t)(c * (4 / TPL) + kh * NWL + t) * 64);
   };
 
   f32x4 acc[JW][MT];
@@ -240,6 +294,9 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int tk = kh * NT + t;  // 32-K step of the chunk
+      bf16x8 bw[JW];
+#pragma unroll
+      for (int j = 0; j < JW; ++j) bw[j] = weight_frag<Q>(sl.w[j][t / TPL], t % TPL);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         // lane l supplies K = 32 tk + 8 (l / 16) .. + 8 of row 16 mt + l % 16: piece 4 tk + l / 16
@@ -248,9 +305,8 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
         const bf16x8 al = __builtin_bit_cast(bf16x8, As[buf][1][r][tk * 4 + q]);
 #pragma unroll
         for (int j = 0; j < JW; ++j) {
-          const bf16x8 bw = __builtin_bit_cast(bf16x8, sl.w[j][t]);
-          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[j][mt], 0, 0, 0);
-          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[j][mt], 0, 0, 0);
+          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw[j], acc[j][mt], 0, 0, 0);
+          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw[j], acc[j][mt], 0, 0, 0);
         }
       }
     }
@@ -262,6 +318,15 @@ __global__ __launch_bounds__(gemm_threads(MT)) void gemm_kernel(const uint16_t* 
 #pragma unroll
   for (int c = 0; c < NCH; ++c) step(c, ring[c % kPF]);
   const int cw = 16 * (rb0 - nb * (kNB / 16));  // this wave's first column within the workgroup
+  if constexpr (Q != 0) {
+    // one-byte weights: each output column times its row's scale
+#pragma unroll
+    for (int j = 0; j < JW; ++j) {
+      const float sc = scale[(rb0 + j) * 16 + (lane & 15)];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[j][mt] *= sc;
+    }
+  }
   if constexpr (KH == 2) {
     // the second K half's sums through LDS (As is free once every wave is past its last chunk),
     // added to the first half's; the waves of the second half then write nothing

@@ -18,7 +18,8 @@
 namespace kd {
 namespace bt {
 
-// One projection: W[N][K] (bf16, in the tile layout of tile_pack_kernel) times the activation block, split over KS K-ranges.
+// One projection: W[N][K] (bf16 in the tile layout of tile_pack_kernel, or one-byte codes in that of
+// tile_pack_q8_kernel) times the activation block, split over KS K-ranges.
 struct Gemm {
   int N = 0, K = 0, KS = 1;
 };
@@ -31,7 +32,11 @@ struct BatchState {
   float eps = 0.f;
   Gemm g_qkv, g_o, g_gu, g_d, g_lm;
   size_t layer_elems = 0;           // per-layer weight elements: qkv, o, gate/up (interleaved), down
-  uint16_t* w = nullptr;            // L layers, then the LM head
+  uint16_t* w = nullptr;            // L layers, then the LM head (bf16 tiles)
+  int q = 0;                        // session weights: 0 bf16 (w), 1 E4M3 or 2 int8 codes (w8, wscale)
+  uint8_t* w8 = nullptr;            // one-byte tiles, at the same element offsets as w
+  float* wscale = nullptr;          // row scales in packed row order: per layer qkv, o, gate/up, down; then the LM head
+  size_t srows = 0;                 // scale rows per layer
   uint16_t* embed = nullptr;        // [V][d]
   uint16_t* norms = nullptr;        // [L][2][d] then [d]
   float2* rope = nullptr;           // [S][hd/2]
@@ -78,24 +83,28 @@ inline int pick_ks(int N, int K, int B, int nwg) {
   return best;
 }
 typedef void (*GemmFn)(const uint16_t*, int, int, const uint16_t*, const uint16_t*, int, float*, int, int, const uint32_t*,
-                       uint16_t*, uint16_t*);
-template <bool SILU, int MT>
+                       uint16_t*, uint16_t*, const float*);
+template <bool SILU, int MT, int Q>
 inline GemmFn gemm_for_mt(int nch) {
   switch (nch) {
-    case 2: return gemm_kernel<2, SILU, MT>;
-    case 4: return gemm_kernel<4, SILU, MT>;
-    case 7: return gemm_kernel<7, SILU, MT>;
-    case 8: return gemm_kernel<8, SILU, MT>;
-    case 14: return gemm_kernel<14, SILU, MT>;
-    case 16: return gemm_kernel<16, SILU, MT>;
-    case 28: return gemm_kernel<28, SILU, MT>;
-    case 32: return gemm_kernel<32, SILU, MT>;
+    case 2: return gemm_kernel<2, SILU, MT, Q>;
+    case 4: return gemm_kernel<4, SILU, MT, Q>;
+    case 7: return gemm_kernel<7, SILU, MT, Q>;
+    case 8: return gemm_kernel<8, SILU, MT, Q>;
+    case 14: return gemm_kernel<14, SILU, MT, Q>;
+    case 16: return gemm_kernel<16, SILU, MT, Q>;
+    case 28: return gemm_kernel<28, SILU, MT, Q>;
+    case 32: return gemm_kernel<32, SILU, MT, Q>;
     default: return nullptr;
   }
 }
-// mt: 16-row tiles of the activation block (4 for up to 64 rows, 8 for up to 128)
+// mt: 16-row tiles of the activation block (4 for up to 64 rows, 8 for up to 128); q: weight
+// format (0 bf16, 1 E4M3, 2 int8; one-byte formats with 4 tiles only)
 template <bool SILU>
-inline GemmFn gemm_for(int nch, int mt) { return mt == 8 ? gemm_for_mt<SILU, 8>(nch) : gemm_for_mt<SILU, 4>(nch); }
+inline GemmFn gemm_for(int nch, int mt, int q) {
+  if (mt == 8) return q == 0 ? gemm_for_mt<SILU, 8, 0>(nch) : nullptr;
+  return q == 0 ? gemm_for_mt<SILU, 4, 0>(nch) : q == 1 ? gemm_for_mt<SILU, 4, 1>(nch) : gemm_for_mt<SILU, 4, 2>(nch);
+}
 // gate/up without a K split writes SiLU(gate) * up itself (no silu_kernel launch)
 inline bool fused_silu(const BatchState& st) { return st.g_gu.KS == 1; }
 
@@ -123,12 +132,13 @@ inline PrefillAttFn prefill_att_for(int G) {
   }
 }
 
-// max_rows: kM for session handles, kMPrefill for the prefill engine. The prefill engine also takes
-// fp8 and int8 models: it keeps its own copy of the weights, decoded to bf16.
-inline int batch_check(const kd_config* c, int max_rows = kM, bool prefill = false) {
+// max_rows: kM for session handles, kMPrefill for the prefill engine. Weights may be bf16, or fp8
+// or int8 codes with row scales: session handles stream the codes, the prefill engine keeps its
+// own copy decoded to bf16.
+inline int batch_check(const kd_config* c, int max_rows = kM) {
   if (c->batch < 2 || c->batch > max_rows) return KD_ERR_UNSUPPORTED;
   const bool q8 = c->weight_dtype == KD_DTYPE_FP8_E4M3 || c->weight_dtype == KD_DTYPE_INT8;
-  if ((c->weight_dtype != KD_DTYPE_BF16 && !(prefill && q8)) || c->kv_dtype != KD_DTYPE_BF16) return KD_ERR_UNSUPPORTED;
+  if ((c->weight_dtype != KD_DTYPE_BF16 && !q8) || c->kv_dtype != KD_DTYPE_BF16) return KD_ERR_UNSUPPORTED;
   if (c->head_dim != 128) return KD_ERR_UNSUPPORTED;
   const int G = c->n_q_heads / c->n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return KD_ERR_UNSUPPORTED;
@@ -147,7 +157,7 @@ inline int batch_check(const kd_config* c, int max_rows = kM, bool prefill = fal
 
 inline void batch_free(BatchState& st) {
   void* ptrs[] = {st.w,  st.embed, st.norms, st.rope, st.X,      st.Ahi,      st.Alo,      st.A2hi,
-                  st.A2lo, st.P,   st.Qs,    st.part, st.logits, st.rows_tok, st.rows_pos};
+                  st.A2lo, st.P,   st.Qs,    st.part, st.logits, st.rows_tok, st.rows_pos, st.w8, st.wscale};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   st = BatchState{};
@@ -203,7 +213,17 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, bool ses
   for (const Gemm* g : {&st.g_qkv, &st.g_o, &st.g_gu, &st.g_d})
     p_elems = std::max(p_elems, (size_t)g->KS * st.B * g->N);
 
-  KD_BT_ALLOC(st.w, blob * 2);
+  // session handles of fp8 and int8 models stream the codes (one byte per weight) and scale each
+  // output column; the prefill engine keeps a bf16 copy
+  const bool q8w = c->weight_dtype != KD_DTYPE_BF16;
+  st.q = sessions && q8w ? (c->weight_dtype == KD_DTYPE_INT8 ? 2 : 1) : 0;
+  st.srows = (size_t)st.nqkv + d + 2 * (size_t)st.F + d;
+  if (st.q) {
+    KD_BT_ALLOC(st.w8, blob);
+    KD_BT_ALLOC(st.wscale, ((size_t)st.L * st.srows + st.V) * 4);
+  } else {
+    KD_BT_ALLOC(st.w, blob * 2);
+  }
   KD_BT_ALLOC(st.embed, (size_t)st.V * d * 2);
   KD_BT_ALLOC(st.norms, (size_t)(2 * st.L + 1) * d * 2);
   KD_BT_ALLOC(st.rope, (size_t)st.S * (st.hd / 2) * sizeof(float2));
@@ -224,11 +244,10 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, bool ses
   KD_BT_TRY(hipMemset(st.A2hi, 0, rows * st.lda * 2));
   KD_BT_TRY(hipMemset(st.A2lo, 0, rows * st.lda * 2));
 
-  // Every matrix goes row-major into a staging buffer, then tile_pack_kernel writes it into the
-  // blob in the tile layout the GEMM streams. fp8 and int8 matrices (the prefill engine of such a
-  // model) first land as codes and row scales, and dequant_rows_kernel writes code x scale into
-  // the staging buffer as bf16.
-  const bool q8 = c->weight_dtype != KD_DTYPE_BF16;
+  // Every matrix goes row-major into a staging buffer, then tile_pack_kernel (tile_pack_q8_kernel
+  // for the codes a session handle streams) writes it into the blob in the tile layout the GEMM
+  // streams. For the prefill engine of an fp8 or int8 model the codes and row scales land first,
+  // and dequant_rows_kernel writes code x scale into the staging buffer as bf16.
   const int int8 = c->weight_dtype == KD_DTYPE_INT8;
   const size_t row = d * 2;
   uint16_t* stage = nullptr;
@@ -237,8 +256,8 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, bool ses
   {
     size_t most = std::max({(size_t)st.nqkv * d, d * st.qdim, 2 * (size_t)st.F * d, (size_t)st.V * d});
     size_t most_rows = std::max({(size_t)st.nqkv, d, (size_t)st.F, (size_t)st.V});
-    if (hipMalloc(&stage, most * 2) != hipSuccess ||
-        (q8 && (hipMalloc(&qcodes, most) != hipSuccess || hipMalloc(&qscale, most_rows * 4) != hipSuccess))) {
+    if ((!st.q && hipMalloc(&stage, most * 2) != hipSuccess) ||
+        (q8w && (hipMalloc(&qcodes, most) != hipSuccess || hipMalloc(&qscale, most_rows * 4) != hipSuccess))) {
       if (stage) (void)hipFree(stage);
       if (qcodes) (void)hipFree(qcodes);
       batch_free(st);
@@ -273,48 +292,56 @@ inline int batch_init(const kd_config* c, const kd_weights* w, int nwg, bool ses
                        dst, N, K);
     return hipDeviceSynchronize();  // the next copy reuses the staging buffer
   };
+  // session handles of one-byte models: codes row-major into qcodes, then tile_pack_q8_kernel; the
+  // row scales gathered on the host in packed row order
+  std::vector<float> hs(st.q ? (size_t)st.L * st.srows + st.V : 0);
+  auto pack_q8 = [&](size_t e, int N, int K) {
+    const int64_t pieces = (int64_t)N * K / 16;
+    hipLaunchKernelGGL(tile_pack_q8_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, 0, (const uint8_t*)qcodes,
+                       st.w8 + e, N, K);
+    return hipDeviceSynchronize();  // the next copy reuses the staging buffer
+  };
+  // rows [0, rows) of a host matrix [rows][cols] (bf16 patterns, or codes with row scales) into
+  // rows (r / bin) * bout + boff + r % bin of the staged matrix whose row 0 is row r0 of the packed
+  // one (bin = rows: in order)
+  auto stage_rows = [&](size_t r0, const void* host, const float* hscale, int rows, int cols, int bin, int bout,
+                        int boff, size_t srow0) -> hipError_t {
+    const size_t nblk = (size_t)rows / bin, eb = st.q ? 1 : 2;  // bytes per staged element
+    if (!q8w || st.q) {
+      uint8_t* dst = (st.q ? (uint8_t*)qcodes + r0 * cols : (uint8_t*)(stage + r0 * cols)) + (size_t)boff * cols * eb;
+      const hipError_t e = bin == rows ? hipMemcpy(dst, host, (size_t)rows * cols * eb, hipMemcpyHostToDevice)
+                                       : hipMemcpy2D(dst, (size_t)bout * cols * eb, host, (size_t)bin * cols * eb,
+                                                     (size_t)bin * cols * eb, nblk, hipMemcpyHostToDevice);
+      if (e != hipSuccess || !st.q) return e;
+      for (int r = 0; r < rows; ++r) hs[srow0 + r0 + (size_t)(r / bin) * bout + boff + r % bin] = hscale[r];
+      return hipSuccess;
+    }
+    return put_q8(stage + r0 * cols, host, hscale, rows, cols, bin, bout, boff);  // prefill engine: decoded to bf16
+  };
+  auto finish = [&](size_t e, int N, int K) { return st.q ? pack_q8(e, N, K) : pack(st.w + e, N, K); };
   for (int l = 0; l < st.L; ++l) {
     const kd_layer_weights& lw = w->layers[l];
-    uint16_t* lay = st.w + (size_t)l * st.layer_elems;
+    const size_t lay = (size_t)l * st.layer_elems, srl = (size_t)l * st.srows;
     const int kvdim = st.hkv * st.hd;
-    if (q8) {
-      KD_BT_STAGE_TRY(put_q8(stage, lw.wq, lw.s_wq, st.qdim, st.d, st.qdim, st.qdim, 0));
-      KD_BT_STAGE_TRY(put_q8(stage + (size_t)st.qdim * d, lw.wk, lw.s_wk, kvdim, st.d, kvdim, kvdim, 0));
-      KD_BT_STAGE_TRY(put_q8(stage + (size_t)(st.qdim + kvdim) * d, lw.wv, lw.s_wv, kvdim, st.d, kvdim, kvdim, 0));
-    } else {
-      KD_BT_STAGE_TRY(hipMemcpy(stage, lw.wq, (size_t)st.qdim * row, hipMemcpyHostToDevice));
-      KD_BT_STAGE_TRY(hipMemcpy(stage + (size_t)st.qdim * d, lw.wk, (size_t)kvdim * row, hipMemcpyHostToDevice));
-      KD_BT_STAGE_TRY(hipMemcpy(stage + (size_t)(st.qdim + kvdim) * d, lw.wv, (size_t)kvdim * row, hipMemcpyHostToDevice));
-    }
-    KD_BT_STAGE_TRY(pack(lay + st.w_qkv, st.nqkv, st.d));
-    if (q8)
-      KD_BT_STAGE_TRY(put_q8(stage, lw.wo, lw.s_wo, st.d, st.qdim, st.d, st.d, 0));
-    else
-      KD_BT_STAGE_TRY(hipMemcpy(stage, lw.wo, d * st.qdim * 2, hipMemcpyHostToDevice));
-    KD_BT_STAGE_TRY(pack(lay + st.w_o, st.d, st.qdim));
+    KD_BT_STAGE_TRY(stage_rows(0, lw.wq, lw.s_wq, st.qdim, st.d, st.qdim, st.qdim, 0, srl));
+    KD_BT_STAGE_TRY(stage_rows(st.qdim, lw.wk, lw.s_wk, kvdim, st.d, kvdim, kvdim, 0, srl));
+    KD_BT_STAGE_TRY(stage_rows((size_t)st.qdim + kvdim, lw.wv, lw.s_wv, kvdim, st.d, kvdim, kvdim, 0, srl));
+    KD_BT_STAGE_TRY(finish(lay + st.w_qkv, st.nqkv, st.d));
+    KD_BT_STAGE_TRY(stage_rows(0, lw.wo, lw.s_wo, st.d, st.qdim, st.d, st.d, 0, srl + st.nqkv));
+    KD_BT_STAGE_TRY(finish(lay + st.w_o, st.d, st.qdim));
     // gate/up interleaved in blocks of 32 rows: rows [64j, 64j+32) = gate rows [32j, 32j+32),
     // rows [64j+32, 64j+64) = the matching up rows, so every GEMM tile holds whole pairs
-    if (q8) {
-      KD_BT_STAGE_TRY(put_q8(stage, lw.w_gate, lw.s_gate, st.F, st.d, 32, 64, 0));
-      KD_BT_STAGE_TRY(put_q8(stage, lw.w_up, lw.s_up, st.F, st.d, 32, 64, 32));
-    } else {
-      KD_BT_STAGE_TRY(hipMemcpy2D(stage, 64 * row, lw.w_gate, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
-      KD_BT_STAGE_TRY(hipMemcpy2D(stage + 32 * d, 64 * row, lw.w_up, 32 * row, 32 * row, st.F / 32, hipMemcpyHostToDevice));
-    }
-    KD_BT_STAGE_TRY(pack(lay + st.w_gu, 2 * st.F, st.d));
-    if (q8)
-      KD_BT_STAGE_TRY(put_q8(stage, lw.w_down, lw.s_down, st.d, st.F, st.d, st.d, 0));
-    else
-      KD_BT_STAGE_TRY(hipMemcpy(stage, lw.w_down, d * st.F * 2, hipMemcpyHostToDevice));
-    KD_BT_STAGE_TRY(pack(lay + st.w_d, st.d, st.F));
+    KD_BT_STAGE_TRY(stage_rows(0, lw.w_gate, lw.s_gate, st.F, st.d, 32, 64, 0, srl + st.nqkv + d));
+    KD_BT_STAGE_TRY(stage_rows(0, lw.w_up, lw.s_up, st.F, st.d, 32, 64, 32, srl + st.nqkv + d));
+    KD_BT_STAGE_TRY(finish(lay + st.w_gu, 2 * st.F, st.d));
+    KD_BT_STAGE_TRY(stage_rows(0, lw.w_down, lw.s_down, st.d, st.F, st.d, st.d, 0, srl + st.nqkv + d + 2 * (size_t)st.F));
+    KD_BT_STAGE_TRY(finish(lay + st.w_d, st.d, st.F));
     KD_BT_STAGE_TRY(hipMemcpy(st.norms + (size_t)(2 * l) * d, lw.attn_norm, row, hipMemcpyHostToDevice));
     KD_BT_STAGE_TRY(hipMemcpy(st.norms + (size_t)(2 * l + 1) * d, lw.ffn_norm, row, hipMemcpyHostToDevice));
   }
-  if (q8)
-    KD_BT_STAGE_TRY(put_q8(stage, w->lm_head, w->s_lm_head, st.V, st.d, st.V, st.V, 0));
-  else
-    KD_BT_STAGE_TRY(hipMemcpy(stage, w->lm_head, (size_t)st.V * row, hipMemcpyHostToDevice));
-  KD_BT_STAGE_TRY(pack(st.w + st.w_lm, st.V, st.d));
+  KD_BT_STAGE_TRY(stage_rows(0, w->lm_head, w->s_lm_head, st.V, st.d, st.V, st.V, 0, (size_t)st.L * st.srows));
+  KD_BT_STAGE_TRY(finish(st.w_lm, st.V, st.d));
+  if (st.q) KD_BT_STAGE_TRY(hipMemcpy(st.wscale, hs.data(), hs.size() * sizeof(float), hipMemcpyHostToDevice));
 #undef KD_BT_STAGE_TRY
   (void)hipFree(stage);
   if (qcodes) (void)hipFree(qcodes);
@@ -363,10 +390,14 @@ inline int batch_tick(const BatchState& st, int nb, int32_t* tokens, int32_t* po
   const uint32_t* skip = flags + 2;
   uint16_t* kv = (uint16_t*)kvp;
   float* lg = logits ? logits : st.logits;
-  auto gemm = [&](const uint16_t* W, const Gemm& g, float* out) {
-    hipLaunchKernelGGL(gemm_for<false>(g.K / (g.KS * kKC), st.MT), dim3((g.N / kNB) * g.KS), dim3(gemm_threads(st.MT)), 0, s, W, g.N,
-                       g.K, (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, out, g.KS, nb, skip,
-                       (uint16_t*)nullptr, (uint16_t*)nullptr);
+  // weights at element offset e (bf16 tiles, or one-byte tiles at the same offsets) and the row
+  // scales from packed row r (one-byte weights only)
+  auto wp = [&](size_t e) { return st.q ? (const uint16_t*)(st.w8 + e) : (const uint16_t*)(st.w + e); };
+  auto sp = [&](size_t r) { return st.q ? (const float*)(st.wscale + r) : (const float*)nullptr; };
+  auto gemm = [&](size_t we, size_t sr, const Gemm& g, float* out) {
+    hipLaunchKernelGGL(gemm_for<false>(g.K / (g.KS * kKC), st.MT, st.q), dim3((g.N / kNB) * g.KS), dim3(gemm_threads(st.MT)), 0, s,
+                       wp(we), g.N, g.K, (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, out, g.KS, nb, skip,
+                       (uint16_t*)nullptr, (uint16_t*)nullptr, sp(sr));
   };
   auto norm = [&](int mode, const Gemm* g, int gain_index) {
     hipLaunchKernelGGL(residual_norm_kernel, dim3(nb), dim3(1024), 0, s, mode, (const uint16_t*)st.embed,
@@ -378,9 +409,9 @@ inline int batch_tick(const BatchState& st, int nb, int32_t* tokens, int32_t* po
                      st.max_seq, status, flags + 2, (const uint32_t*)(flags + 3));
   norm(0, nullptr, 0);
   for (int l = 0; l < st.L; ++l) {
-    const uint16_t* lay = st.w + (size_t)l * st.layer_elems;
+    const size_t lay = (size_t)l * st.layer_elems, srl = (size_t)l * st.srows;  // this layer's weights and scales
     uint16_t* kvl = kv + (int64_t)l * kvs.layer;
-    gemm(lay + st.w_qkv, st.g_qkv, st.P);
+    gemm(lay + st.w_qkv, srl, st.g_qkv, st.P);
     hipLaunchKernelGGL(qkv_epilogue_kernel, dim3(st.hq + 2 * st.hkv, nb), dim3(st.hd), 0, s, (const float*)st.P,
                        st.g_qkv.KS, st.nqkv, st.hq, st.hkv, st.hd, (const float2*)st.rope, (const int32_t*)positions,
                        st.Qs, kvl, kvs.slot, kvs.row, kvs.head, nb, skip);
@@ -397,28 +428,29 @@ inline int batch_tick(const BatchState& st, int nb, int32_t* tokens, int32_t* po
     }
     hipLaunchKernelGGL(merge_kernel, dim3(st.hq, nb), dim3(st.hd), 0, s, (const float*)st.part,
                        (const int32_t*)positions, st.hq, st.hd, st.CH, st.NCmax, st.Ahi, st.Alo, st.lda, skip);
-    gemm(lay + st.w_o, st.g_o, st.P);
+    gemm(lay + st.w_o, srl + st.nqkv, st.g_o, st.P);
     norm(1, &st.g_o, 2 * l + 1);
     if (fused_silu(st)) {
       // gate/up writes SiLU(gate) * up into the second activation block, which the down
       // projection reads (the first is still being read while gate/up runs)
       const Gemm& g = st.g_gu;
-      hipLaunchKernelGGL(gemm_for<true>(g.K / kKC, st.MT), dim3(g.N / kNB), dim3(gemm_threads(st.MT)), 0, s, lay + st.w_gu, g.N, g.K,
-                         (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, st.P, 1, nb, skip, st.A2hi, st.A2lo);
+      hipLaunchKernelGGL(gemm_for<true>(g.K / kKC, st.MT, st.q), dim3(g.N / kNB), dim3(gemm_threads(st.MT)), 0, s, wp(lay + st.w_gu),
+                         g.N, g.K, (const uint16_t*)st.Ahi, (const uint16_t*)st.Alo, st.lda, st.P, 1, nb, skip, st.A2hi,
+                         st.A2lo, sp(srl + st.nqkv + st.d));
       const Gemm& gd = st.g_d;
-      hipLaunchKernelGGL(gemm_for<false>(gd.K / (gd.KS * kKC), st.MT), dim3((gd.N / kNB) * gd.KS), dim3(gemm_threads(st.MT)), 0, s,
-                         lay + st.w_d, gd.N, gd.K, (const uint16_t*)st.A2hi, (const uint16_t*)st.A2lo, st.lda, st.P, gd.KS,
-                         nb, skip, (uint16_t*)nullptr, (uint16_t*)nullptr);
+      hipLaunchKernelGGL(gemm_for<false>(gd.K / (gd.KS * kKC), st.MT, st.q), dim3((gd.N / kNB) * gd.KS), dim3(gemm_threads(st.MT)), 0,
+                         s, wp(lay + st.w_d), gd.N, gd.K, (const uint16_t*)st.A2hi, (const uint16_t*)st.A2lo, st.lda, st.P,
+                         gd.KS, nb, skip, (uint16_t*)nullptr, (uint16_t*)nullptr, sp(srl + st.nqkv + st.d + 2 * (size_t)st.F));
     } else {
-      gemm(lay + st.w_gu, st.g_gu, st.P);
+      gemm(lay + st.w_gu, srl + st.nqkv + st.d, st.g_gu, st.P);
       hipLaunchKernelGGL(silu_kernel, dim3(st.F / 256, nb), dim3(256), 0, s, (const float*)st.P, st.g_gu.KS, st.F, st.Ahi,
                          st.Alo, st.lda, nb, skip);
-      gemm(lay + st.w_d, st.g_d, st.P);
+      gemm(lay + st.w_d, srl + st.nqkv + st.d + 2 * (size_t)st.F, st.g_d, st.P);
     }
     norm(1, &st.g_d, l + 1 < st.L ? 2 * (l + 1) : 2 * st.L);
   }
   if (lm) {
-    gemm(st.w + st.w_lm, st.g_lm, lg);
+    gemm(st.w_lm, (size_t)st.L * st.srows, st.g_lm, lg);
     hipLaunchKernelGGL(argmax_kernel, dim3(nb), dim3(1024), 0, s, (const float*)lg, st.V, tokens, positions, status, skip,
                        out);
   }

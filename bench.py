@@ -1,6 +1,6 @@
 """Decode-step benchmark: tokens/s on one MI355X and the fraction of the HBM roofline.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b|2b|2b_long|tiny|11b_x56|8b_fp8|2b_fp8|8b_int8|2b_int8]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b|2b|2b_long|tiny|11b_x56|8b_fp8|2b_fp8|8b_int8|2b_int8|11b_x56_fp8|11b_x56_int8]
 
 One "step" is one kd_step: a whole decode step of every session. At batch 1 it is one persistent
 kernel launch; for the 56 lockstep sessions it is one tick, a fixed kernel sequence on one stream.
@@ -314,7 +314,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="8b", choices=["tiny", "2b", "8b", "2b_long", "11b_x56", "2b_fp8", "8b_fp8", "2b_int8", "8b_int8"])
+    ap.add_argument("--workload", default="8b", choices=["tiny", "2b", "8b", "2b_long", "11b_x56", "2b_fp8", "8b_fp8", "2b_int8", "8b_int8",
+                                                    "11b_x56_fp8", "11b_x56_int8"])
     ap.add_argument("--prefill-chunk", type=int, default=128,
                     help="prompt positions per kd_prefill pass for batch-1 workloads (2..128)")
     ap.add_argument("--extra", default=None,

@@ -92,7 +92,9 @@ extern "C" {
  *   max_seq      capacity of the KV cache in positions (steps may use positions 0..max_seq-1).
  *   batch        sessions stepped together in lockstep. batch == 1 runs the single persistent
  *                kernel. 2 <= batch <= 64 runs the lockstep-sessions path: the projections become
- *                small-M GEMMs on the matrix cores. That path needs bf16 weights and cache,
+ *                small-M GEMMs on the matrix cores (with fp8 or int8 weights the GEMMs stream the
+ *                one-byte codes, decode them to bf16 in registers and scale each output column by
+ *                its row's scale). That path needs bf16, fp8 or int8 weights, a bf16 cache,
  *                head_dim 128, G of 1, 2 or 4, d_model one of 256, 512, 1024, 2048 or 4096, n_q_heads*head_dim
  *                and ffn_dim each split into 2, 4, 7, 8, 14, 16, 28 or 32 runs of 128 after halving
  *                (e.g. 256 times a power of two, or 14336), and d_model, 2*ffn_dim,
@@ -101,12 +103,12 @@ extern "C" {
  *   rope_base    RoPE base: pair (i, i + head_dim/2) turns by position * rope_base^(-2i/head_dim).
  *   prefill_chunk batch 1 only: 0, or 2..128 to set up kd_prefill, which runs a prompt in chunks of
  *                this many positions as small-M GEMMs on the matrix cores (the shape must meet the
- *                lockstep path's conditions above, except that fp8 and int8 weights are taken; the
+ *                lockstep path's conditions above; the
  *                library then holds a second copy of the weights, in bf16 in the matrix cores'
  *                tile layout: for fp8 and int8 models each code times its row's scale, rounded to
  *                bf16 once, so the prefill's results may differ from one-token steps by that rounding).
  *   weight_dtype KD_DTYPE_BF16 or KD_DTYPE_F32, with kv_dtype the same; or KD_DTYPE_FP8_E4M3 or
- *                KD_DTYPE_INT8 with kv_dtype KD_DTYPE_BF16 (batch 1, head_dim 128, d_model and q_dim multiples
+ *                KD_DTYPE_INT8 with kv_dtype KD_DTYPE_BF16 (at batch 1: head_dim 128, d_model and q_dim multiples
  *                of 1024, ffn_dim a multiple of 8 with ffn_dim/8 >= the GPU's compute units).
  */
 typedef struct kd_config {

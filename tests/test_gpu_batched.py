@@ -223,3 +223,38 @@ def test_11b_x56_sampled_sessions(torch, kdm):
                 assert np.max(np.abs(got[s] - exp)) <= BF16_TOL * np.max(np.abs(exp))
     assert dec.status() == 0 and bool(torch.all(dec.positions == last + 1))
     dec.close()
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "int8"])
+@pytest.mark.parametrize("dims", [(1024, 8, 2, 2048), (256, 2, 1, 16384)], ids=["split", "fused_silu"])
+def test_lockstep_one_byte_weights(torch, kdm, dtype, dims):
+    """Lockstep sessions with fp8 or int8 weights: the GEMMs stream the codes, decode them to bf16
+    in registers and scale each output column by its row's scale. Five sessions, 16 ticks from empty
+    caches, every tick against the oracle fed the same codes and scales. Two shapes: every GEMM
+    split over K (SiLU in its own kernel), and a wide FFN whose gate/up runs unsplit and applies
+    SiLU itself."""
+    d, hq, hkv, F = dims
+    m = ModelShape(2, d, hq, hkv, 128, F, 1024, rope_base=10000.0, weight_dtype=dtype, kv_dtype="bf16")
+    w = workloads.make_weights(m, seed=21)
+    B, T = 5, 16
+    dec = kdm.Decoder(m, w, max_seq=32, batch=B)
+    assert kdm.kd_get_info(dec.handle)["workgroups"] == 0  # the lockstep path
+    o = ref.Oracle(m, w, batch=B, max_seq=32)
+    tok = np.random.default_rng(22).integers(0, m.vocab, B).astype(np.int64)
+    dec.tokens.copy_(torch.from_numpy(tok.astype(np.int32)))
+    dec.positions.zero_()
+    worst, flips = 0.0, 0
+    for t in range(T):
+        dec.step()
+        gl = dec.logits.cpu().numpy()
+        g_tok = dec.tokens.cpu().numpy()
+        want = o.step(tok, [t] * B)
+        for b in range(B):
+            err, flip = _check_tick(gl[b], g_tok[b], want[b], (dtype, dims, t, b))
+            worst = max(worst, err)
+            flips += flip
+        tok = g_tok.astype(np.int64)
+    print(f"lockstep {dtype} {dims}: max rel logit err {worst:.3e} over {T} ticks x {B} sessions, tie-flips {flips}")
+    assert flips <= 2 and dec.status() == 0
+    assert np.all(dec.positions.cpu().numpy() == T)
+    dec.close()

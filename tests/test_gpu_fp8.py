@@ -108,11 +108,12 @@ def test_8b_fp8_sampled_steps(torch, kdm):
 
 
 def test_fp8_rejects_unsupported_configs(kdm):
-    """fp8 weights need a bf16 cache and batch 1."""
+    """fp8 weights need a bf16 cache, at batch 1 and in lockstep sessions."""
     import dataclasses
 
     w = workloads.make_weights(SMALL_FP8, seed=9)
-    for shape, batch in ((dataclasses.replace(SMALL_FP8, kv_dtype="f32"), 1), (SMALL_FP8, 4)):
+    f32_cache = dataclasses.replace(SMALL_FP8, kv_dtype="f32")
+    for shape, batch in ((f32_cache, 1), (f32_cache, 4)):
         cfg = kdm.make_config(shape, batch, 64)
         with pytest.raises(kdm.KDError) as e:
             kdm.kd_init(cfg, w)

@@ -131,10 +131,10 @@ def test_8b_int8_sampled_steps(torch, kdm):
 
 
 def test_int8_rejects_unsupported_configs(kdm):
-    """int8 weights need a bf16 cache, head_dim 128 and batch 1 (lockstep sessions take bf16 only)."""
+    """int8 weights need a bf16 cache: at batch 1, in lockstep sessions and for a prefill engine."""
     w = workloads.make_weights(SMALL_INT8, seed=9)
-    for shape, batch, chunk in ((dataclasses.replace(SMALL_INT8, kv_dtype="f32"), 1, 0), (SMALL_INT8, 4, 0),
-                                (dataclasses.replace(SMALL_INT8, kv_dtype="f32"), 1, 64)):
+    f32_cache = dataclasses.replace(SMALL_INT8, kv_dtype="f32")
+    for shape, batch, chunk in ((f32_cache, 1, 0), (f32_cache, 4, 0), (f32_cache, 1, 64)):
         cfg = kdm.make_config(shape, batch, 64, prefill_chunk=chunk)
         with pytest.raises(kdm.KDError) as e:
             kdm.kd_init(cfg, w)

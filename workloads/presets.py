@@ -22,6 +22,9 @@ The presets are the decode workloads this library is measured on:
                  row; embedding, norm gains and KV cache stay bf16 ("17k
                  tokens/sec" page, best practice 2 and FAQ 3: lower-precision
                  parameters cut the bytes each token reads).
+* ``11b_x56_fp8``, ``11b_x56_int8`` -- the 56-session workload with E4M3 or
+                 int8 projection matrices and LM head (lockstep sessions stream
+                 the codes).
 * ``2b_int8``, ``8b_int8`` -- the same with int8 codes: one float32 scale per
                  output row (its largest magnitude over 127), codes rounded to
                  nearest, ties to even (best practice 2 of the same page names
@@ -193,6 +196,8 @@ _2B_FP8 = replace(_2B, weight_dtype="fp8")
 _8B_FP8 = replace(_8B, weight_dtype="fp8")
 _2B_INT8 = replace(_2B, weight_dtype="int8")
 _8B_INT8 = replace(_8B, weight_dtype="int8")
+_11B_FP8 = replace(_11B, weight_dtype="fp8")
+_11B_INT8 = replace(_11B, weight_dtype="int8")
 
 PRESETS = {
     "tiny": Workload("tiny", _TINY, batch=1, prompt_len=32, gen_tokens=64,
@@ -205,6 +210,10 @@ PRESETS = {
                         description="2B decoder, KV pre-filled to 32768 positions"),
     "11b_x56": Workload("11b_x56", _11B, batch=56, prefill_len=4096, gen_tokens=200,
                         description="11B decoder, 56 lockstep sessions, KV at 4096"),
+    "11b_x56_fp8": Workload("11b_x56_fp8", _11B_FP8, batch=56, prefill_len=4096, gen_tokens=200,
+                            description="11B decoder, 56 lockstep sessions, KV at 4096, E4M3 weights with per-row scales"),
+    "11b_x56_int8": Workload("11b_x56_int8", _11B_INT8, batch=56, prefill_len=4096, gen_tokens=200,
+                             description="11B decoder, 56 lockstep sessions, KV at 4096, int8 weights with per-row scales"),
     "2b_fp8": Workload("2b_fp8", _2B_FP8, batch=1, prompt_len=512, gen_tokens=512,
                        description="2B decoder, batch 1, E4M3 weights with per-row scales"),
     "8b_fp8": Workload("8b_fp8", _8B_FP8, batch=1, prompt_len=1024, gen_tokens=256,
