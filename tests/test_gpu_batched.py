@@ -166,12 +166,14 @@ def test_clone_x56_bad_input_writes_nothing(torch, kdm):
     dec.close()
 
 
-def test_11b_x56_sampled_sessions(torch, kdm):
+@pytest.mark.parametrize("name", ["11b_x56", "11b_x56_fp8"])
+def test_11b_x56_sampled_sessions(torch, kdm, name):
     """The 11B-class decoder at its real shape, launch configuration and full extent: 56 sessions,
-    every cache pre-filled to 4096 positions, 200 ticks. Sessions 0, 27 and 55 are checked
-    against the oracle at ticks 1 and 2 (oracle fed the recipe's pre-filled cache) and at tick 200
-    (oracle started from the GPU's cache after 199 ticks), with the K/V the last tick appends."""
-    wl = workloads.get("11b_x56")
+    every cache pre-filled to 4096 positions, 200 ticks, with bf16 weights or E4M3 codes (the
+    one-byte session GEMMs). Sessions 0, 27 and 55 are checked against the oracle at ticks 1 and 2
+    (oracle fed the recipe's pre-filled cache) and at tick 200 (oracle started from the GPU's cache
+    after 199 ticks), with the K/V the last tick appends."""
+    wl = workloads.get(name)
     m = wl.model
     w = workloads.make_weights(m, seed=wl.weight_seed)
     print("11b: weights ready", flush=True)
